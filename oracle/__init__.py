@@ -1,0 +1,192 @@
+"""dmx oracle -- TEST INFRASTRUCTURE ONLY.
+
+Python access (ctypes + numpy float64) to the plain C oracle in
+``dmx_oracle.c``.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It never imports, loads or calls the
+HIP library, and the HIP library never uses it.
+
+Every function computes in float64 from the exact values it is given (bf16
+inputs are upcast exactly by the caller).  Citations of the pages are in the C
+source next to each step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dmx_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK, FALLBACK_EAGER = 0, 1
+ERR_INVALID_ARG, ERR_BAD_BUCKETS, ERR_PREFIX_TOO_LONG = -1, -2, -3
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C99, OpenMP over independent loops)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        dbl = ctypes.c_double
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = ctypes.c_int
+        lib.orc_select_bucket.argtypes = [i32, P, i32, i32, i32, P]
+        lib.orc_select_bucket.restype = ctypes.c_int
+        lib.orc_linear.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
+        lib.orc_linear.restype = None
+        lib.orc_adarms.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, dbl, P, P]
+        lib.orc_adarms.restype = None
+        lib.orc_qkv_qknorm_rope.argtypes = [P, P, P, P] + [ctypes.c_int] * 5 + [P, dbl, dbl, P, P, P]
+        lib.orc_qkv_qknorm_rope.restype = None
+        lib.orc_attention.argtypes = [P] * 6 + [ctypes.c_int] * 5 + [dbl, P, P]
+        lib.orc_attention.restype = None
+        lib.orc_oproj_gated_residual.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P]
+        lib.orc_oproj_gated_residual.restype = None
+        lib.orc_gelu_tanh.argtypes = [dbl]
+        lib.orc_gelu_tanh.restype = dbl
+        lib.orc_geglu_mlp.argtypes = [P] * 5 + [ctypes.c_int] * 3 + [P, P]
+        lib.orc_geglu_mlp.restype = None
+        lib.orc_layer.argtypes = [P] * 15 + [ctypes.c_int] * 7 + [i32, dbl, dbl] + [P] * 10
+        lib.orc_layer.restype = None
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> int:
+    """Set the OpenMP thread count; returns the count now in effect."""
+    return int(_load().orc_set_threads(int(n)))
+
+
+def select_bucket(prefix_len: int, buckets, cap: int, min_tokens: int = 0):
+    """Bucket rule; returns (status, index)."""
+    b = np.ascontiguousarray(np.asarray(buckets, dtype=np.int32))
+    idx = np.full(1, -7, dtype=np.int32)
+    st = _load().orc_select_bucket(int(prefix_len), _ptr(b), int(b.size), int(cap), int(min_tokens), _ptr(idx))
+    return int(st), int(idx[0])
+
+
+def linear(a, w):
+    a, w = _f64(a), _f64(w)
+    T, K = a.shape
+    N = w.shape[0]
+    y = np.empty((T, N))
+    _load().orc_linear(_ptr(a), _ptr(w), T, K, N, _ptr(y))
+    return y
+
+
+def adarms(x, cond, w_mod, b_mod, eps=1e-6):
+    """Returns (xn [T][H], mod [3H] = scale|shift|gate)."""
+    x, cond, w_mod, b_mod = _f64(x), _f64(cond), _f64(w_mod), _f64(b_mod)
+    T, H = x.shape
+    xn = np.empty((T, H))
+    mod = np.empty(3 * H)
+    _load().orc_adarms(_ptr(x), _ptr(cond), _ptr(w_mod), _ptr(b_mod), T, H, float(eps), _ptr(xn), _ptr(mod))
+    return xn, mod
+
+
+def qkv_qknorm_rope(xn, w_qkv, q_norm, k_norm, pos, hq, hk, d, base=10000.0, eps=1e-6):
+    """Returns q [T][hq][d], k [hk][T][d], v [hk][T][d]."""
+    xn, w_qkv, q_norm, k_norm = _f64(xn), _f64(w_qkv), _f64(q_norm), _f64(k_norm)
+    T, H = xn.shape
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int32).reshape(T))
+    q = np.empty((T, hq, d))
+    k = np.empty((hk, T, d))
+    v = np.empty((hk, T, d))
+    _load().orc_qkv_qknorm_rope(_ptr(xn), _ptr(w_qkv), _ptr(q_norm), _ptr(k_norm), T, H, hq, hk, d,
+                                _ptr(pos), float(base), float(eps), _ptr(q), _ptr(k), _ptr(v))
+    return q, k, v
+
+
+def attention(q, ks, vs, kp, vp, mask, scale=None, return_prob_sums=False):
+    """q [C][HQ][D]; ks, vs [HK][C][D]; kp, vp [HK][P][D]; mask [P] -> ctx [C][HQ][D]."""
+    q, ks, vs, kp, vp = _f64(q), _f64(ks), _f64(vs), _f64(kp), _f64(vp)
+    C, HQ_, D_ = q.shape
+    HK_, P, _ = kp.shape
+    mask = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8).reshape(P))
+    if scale is None:
+        scale = 1.0 / np.sqrt(D_)
+    ctx = np.empty((C, HQ_, D_))
+    ps = np.empty((C, HQ_))
+    _load().orc_attention(_ptr(q), _ptr(ks), _ptr(vs), _ptr(kp), _ptr(vp), _ptr(mask), C, P, HQ_, HK_, D_,
+                          float(scale), _ptr(ctx), _ptr(ps))
+    return (ctx, ps) if return_prob_sums else ctx
+
+
+def oproj_gated_residual(ctx, w_o, gate, resid):
+    ctx, w_o, gate, resid = _f64(ctx), _f64(w_o), _f64(gate), _f64(resid)
+    T = resid.shape[0]
+    H = w_o.shape[0]
+    K = w_o.shape[1]
+    out = np.empty((T, H))
+    _load().orc_oproj_gated_residual(_ptr(ctx.reshape(T, K)), _ptr(w_o), _ptr(gate), _ptr(resid), T, K, H, _ptr(out))
+    return out
+
+
+def gelu_tanh(z: float) -> float:
+    return float(_load().orc_gelu_tanh(float(z)))
+
+
+def geglu_mlp(xn2, w_gu, w_down, gate2, resid):
+    """Returns (out [T][H], h [T][I])."""
+    xn2, w_gu, w_down, gate2, resid = _f64(xn2), _f64(w_gu), _f64(w_down), _f64(gate2), _f64(resid)
+    T, H = xn2.shape
+    I_ = w_down.shape[1]
+    out = np.empty((T, H))
+    h = np.empty((T, I_))
+    _load().orc_geglu_mlp(_ptr(xn2), _ptr(w_gu), _ptr(w_down), _ptr(gate2), _ptr(resid), T, H, I_, _ptr(out), _ptr(h))
+    return out, h
+
+
+PROBE_KEYS = ("xn1", "mod1", "q", "ks", "vs", "ctx", "x1", "xn2", "mod2")
+
+
+def layer(x, cond, w: dict, kp, vp, mask, pos0: int, hq=8, hk=4, d=256,
+          base=10000.0, eps=1e-6, probes=False):
+    """One action-expert layer for one request.  x [C][H]; cond [H]; w: float
+    arrays keyed like the weight dict; kp, vp [HK][P][D]; mask [P].
+    Returns out [C][H], or (out, probes dict) when probes=True."""
+    x, cond = _f64(x), _f64(cond)
+    C, H = x.shape
+    I_ = w["w_down"].shape[1]
+    P = kp.shape[1]
+    ww = {k: _f64(v) for k, v in w.items()}
+    kp, vp = _f64(kp), _f64(vp)
+    mask = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8).reshape(P))
+    out = np.empty((C, H))
+    pr = None
+    if probes:
+        pr = {"xn1": np.empty((C, H)), "mod1": np.empty(3 * H), "q": np.empty((C, hq, d)),
+              "ks": np.empty((hk, C, d)), "vs": np.empty((hk, C, d)), "ctx": np.empty((C, hq, d)),
+              "x1": np.empty((C, H)), "xn2": np.empty((C, H)), "mod2": np.empty(3 * H)}
+    pp = [None] * 9 if pr is None else [pr[k] for k in PROBE_KEYS]
+    _load().orc_layer(_ptr(x), _ptr(cond), _ptr(ww["w_mod1"]), _ptr(ww["b_mod1"]), _ptr(ww["w_qkv"]),
+                      _ptr(ww["q_norm"]), _ptr(ww["k_norm"]), _ptr(ww["w_o"]), _ptr(ww["w_mod2"]),
+                      _ptr(ww["b_mod2"]), _ptr(ww["w_gu"]), _ptr(ww["w_down"]), _ptr(kp), _ptr(vp),
+                      _ptr(mask), C, P, H, I_, hq, hk, d, int(pos0), float(base), float(eps),
+                      _ptr(out), *[_ptr(a) for a in pp])
+    return (out, pr) if probes else out
