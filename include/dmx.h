@@ -1,0 +1,244 @@
+/*
+ * dmx.h -- C ABI of the MI355X (gfx950) action-expert layer library (libdmx.so).
+ *
+ * The library computes the forward pass of the action-expert ("suffix") layer
+ * that a DM0.5-style vision-language-action model runs in every diffusion
+ * denoising step, as described in:
+ *   [Art]   "TensorRT+Triton+FlexAttention：OpenDM VLA快速推理加速栈深度剖析"
+ *           (OpenDM DM0.5 fast-inference stack article).  §2.2 "Triton 大 Kernel"
+ *           gives the shapes (suffix: hidden 1024, intermediate 4096, head_dim 256,
+ *           8 query / 4 KV heads; prefix: hidden 2560) and the fused steps; §3
+ *           "CUDA Graph" gives the prefix-length buckets, graph capture per bucket
+ *           and the address-stable prefix KV cache.
+ *   [Guide] "DM05 推理指南" (OpenDM docs/zh/dm05_inference.md), §4 "Fast Backend
+ *           约束" (bucket-list rules, 1024-token cap, eager fallback), §6 (10
+ *           diffusion steps by default).
+ *
+ * Conventions (all entry points)
+ *   - dmx_bf16 is a bfloat16 bit pattern.  Tensors are contiguous, row-major, in
+ *     the layouts stated per call; there are no strides.
+ *   - Pointers are DEVICE pointers unless marked "host".  Every device pointer
+ *     must be 16-byte aligned (DMX_ERR_MISALIGNED otherwise).
+ *   - The caller owns all device memory.  Compute calls never allocate, free or
+ *     synchronise; they enqueue kernels on `stream` (a hipStream_t; NULL = the
+ *     null stream) and return.  The library owns only dmx_graph objects.
+ *   - Every argument is validated on the host before any launch.  A failed
+ *     validation launches nothing.  Status codes: 0 = OK, 1 = the explicit eager
+ *     fallback of the bucket rule, negative = error.  No exception crosses the ABI.
+ *     dmx_last_error_string() gives the calling thread's last error text.
+ *   - There is no silent fallback to another implementation.
+ *   - Arithmetic: bf16 storage, fp32 accumulation.
+ *   - Workspace: `ws` is caller-owned device scratch of at least
+ *     dmx_workspace_bytes(batch, tokens, p_bucket) bytes (a stack:
+ *     dmx_stack_workspace_bytes).  It needs no initialisation and holds nothing
+ *     between calls.  Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef DMX_H_
+#define DMX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dmx_bf16;
+
+/* Status codes. */
+#define DMX_OK 0
+#define DMX_FALLBACK_EAGER 1
+#define DMX_ERR_INVALID_ARG (-1)
+#define DMX_ERR_BAD_BUCKETS (-2)
+#define DMX_ERR_PREFIX_TOO_LONG (-3)
+#define DMX_ERR_UNSUPPORTED (-4)
+#define DMX_ERR_MISALIGNED (-5)
+#define DMX_ERR_WORKSPACE (-6)
+#define DMX_ERR_HIP (-7)
+
+/* Fixed shapes of the suffix layer ([Art §2.2] shape table). */
+#define DMX_HIDDEN 1024
+#define DMX_INTER 4096
+#define DMX_HEAD_DIM 256
+#define DMX_Q_HEADS 8
+#define DMX_KV_HEADS 4
+#define DMX_PREFIX_HIDDEN 2560
+#define DMX_MAX_CHUNK 64
+#define DMX_MAX_BATCH 64
+#define DMX_MAX_PREFIX 4096
+#define DMX_MAX_LAYERS 64
+
+/* ------------------------------------------------------------------------ */
+/* Bucket selection ([Art §3]; [Guide §4] constraints).  Pure host code.
+ *   prefix_len       current prefix length in tokens.
+ *   buckets (host)   candidate bucket sizes, n entries.
+ *   fast_prefix_len  the cap (1024 by default; 2048 for the single-2048-bucket
+ *                    memory-demo layout).
+ *   min_tokens       buckets below this (too small for the image tokens) are
+ *                    skipped, i.e. never chosen.
+ *   idx_out (host)   index into buckets of the chosen bucket, -1 if none.
+ * Returns, checked in this order:
+ *   DMX_ERR_INVALID_ARG      null pointer, prefix_len <= 0, cap <= 0,
+ *                            min_tokens < 0 or n < 0;
+ *   DMX_ERR_BAD_BUCKETS      list empty, not strictly increasing, or holding a
+ *                            value <= 0 or above the cap;
+ *   DMX_ERR_PREFIX_TOO_LONG  prefix_len > fast_prefix_len (rejected);
+ *   DMX_OK                   *idx_out = smallest non-skipped bucket >= prefix_len;
+ *   DMX_FALLBACK_EAGER       no such bucket: run unbucketed (P = prefix_len),
+ *                            without a captured graph. */
+int dmx_select_bucket(int32_t prefix_len, const int32_t* buckets, int32_t n,
+                      int32_t fast_prefix_len, int32_t min_tokens, int32_t* idx_out);
+
+/* Workspace bytes for `batch` requests of `tokens` tokens each against a prefix
+ * bucket of p_bucket rows; covers every compute call below at those sizes
+ * (including dmx_qkv_qknorm_rope with tokens up to 2048 at hidden 2560 when
+ * asked for those sizes).  Returns 0 for unsupported sizes. */
+size_t dmx_workspace_bytes(int32_t batch, int32_t tokens, int32_t p_bucket);
+
+/* Zero-fill a workspace (enqueued on `stream`, no allocation); optional. */
+int dmx_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* AdaRMS time-modulated prenorm ([Art §2.2] "Adarms 调制 prenorm").
+ *   mod[b] = W_mod * cond[b] + b_mod            (fp32, [batch][3][1024]:
+ *                                                 scale | shift | gate)
+ *   x_norm[b][t][j] = x[b][t][j] / sqrt(mean_j x^2 + 1e-6) * (1 + scale[j]) + shift[j]
+ *   x      [batch][tokens][1024] bf16     cond  [batch][1024] bf16
+ *   w_mod  [3072][1024] bf16              b_mod [3072] bf16
+ *   x_norm [batch][tokens][1024] bf16 (out)
+ *   mod    [batch][3072] fp32 (out); its last third is the residual gate. */
+int dmx_adarms_prenorm(const dmx_bf16* x, const dmx_bf16* cond, const dmx_bf16* w_mod,
+                       const dmx_bf16* b_mod, int32_t batch, int32_t tokens,
+                       dmx_bf16* x_norm, float* mod, void* stream);
+
+/* QKV projection + per-head QK-RMSNorm + RoPE "in one go" ([Art §2.2]).
+ *   qkv = x_norm * W_qkv^T, W_qkv [4096][hidden]: rows 0..2047 the 8 query
+ *   heads, 2048..3071 the 4 key heads, 3072..4095 the 4 value heads (256 rows
+ *   each).  q and k heads: u / sqrt(mean(u^2) + 1e-6) * (1 + w) with
+ *   w = q_norm_w / k_norm_w ([256], shared by the heads), then RoPE at position
+ *   pos0[b] + t: pairs (j, j + 128), angle pos * rope_base^(-j/128).
+ *   x_norm [batch][tokens][hidden] bf16, hidden = 1024 (suffix) or 2560 (prefix)
+ *   pos0   [batch] int32 (device)
+ *   q      [batch][tokens][8][256] bf16 (out)
+ *   k, v   [batch][4][kv_rows][256] bf16 (out); token t goes to row kv_row0 + t,
+ *          so kv_rows = p_bucket writes straight into a prefix KV cache.
+ *   Needs kv_row0 + tokens <= kv_rows. */
+int dmx_qkv_qknorm_rope(const dmx_bf16* x_norm, const dmx_bf16* w_qkv,
+                        const dmx_bf16* q_norm_w, const dmx_bf16* k_norm_w, int32_t batch,
+                        int32_t tokens, int32_t hidden, const int32_t* pos0, float rope_base,
+                        dmx_bf16* q, dmx_bf16* k, dmx_bf16* v, int32_t kv_rows,
+                        int32_t kv_row0, void* ws, size_t ws_bytes, void* stream);
+
+/* Masked GQA suffix attention ([Art §2.2]: logits read the prefix KV cache and
+ * the suffix KV together under the prefix-visibility mask, online softmax,
+ * value-weighted sum).  Query head h reads KV head h / 2.  Every query of a
+ * request sees the prefix rows j with mask[b][j] != 0 and all `chunk` suffix
+ * rows.  Masked rows are never read (their contents may be anything,
+ * NaN included).  Scale 1/16.
+ *   q      [batch][chunk][8][256] bf16
+ *   k_suf, v_suf [batch][4][chunk][256] bf16
+ *   k_pre, v_pre [batch][4][p_bucket][256] bf16 (post-norm, post-RoPE cache)
+ *   mask   [batch][p_bucket] uint8, nonzero = visible (p_bucket may be 0)
+ *   ctx    [batch][chunk][8][256] bf16 (out) */
+int dmx_suffix_attention(const dmx_bf16* q, const dmx_bf16* k_suf, const dmx_bf16* v_suf,
+                         const dmx_bf16* k_pre, const dmx_bf16* v_pre, const uint8_t* mask,
+                         int32_t batch, int32_t chunk, int32_t p_bucket, dmx_bf16* ctx,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* O-projection + gated residual:
+ *   out[b][t] = residual[b][t] + gate[b] * (ctx[b][t] * W_o^T),
+ *   gate[b] = mod[b][2048..3071] (the third chunk of dmx_adarms_prenorm's mod).
+ *   ctx [batch][tokens][2048] bf16; w_o [1024][2048] bf16;
+ *   mod [batch][3072] fp32; residual, out [batch][tokens][1024] bf16.
+ *   out may alias residual. */
+int dmx_oproj_gated_residual(const dmx_bf16* ctx, const dmx_bf16* w_o, const float* mod,
+                             const dmx_bf16* residual, int32_t batch, int32_t tokens,
+                             dmx_bf16* out, void* ws, size_t ws_bytes, void* stream);
+
+/* GEGLU gate-up, MLP down and the second gated residual ([Art §2.2]):
+ *   [a | u] = x_norm2 * W_gu^T (a: rows 0..4095, u: rows 4096..8191)
+ *   h = gelu_tanh(a) * u
+ *   out = residual + gate2 * (h * W_down^T),  gate2 = mod2[b][2048..3071]
+ *   x_norm2 [batch][tokens][1024] bf16; w_gu [8192][1024]; w_down [1024][4096];
+ *   mod2 [batch][3072] fp32; residual, out [batch][tokens][1024] bf16.
+ *   out may alias residual. */
+int dmx_geglu_mlp(const dmx_bf16* x_norm2, const dmx_bf16* w_gu, const dmx_bf16* w_down,
+                  const float* mod2, const dmx_bf16* residual, int32_t batch, int32_t tokens,
+                  dmx_bf16* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* One whole action-expert layer ([Art §2.2], suffix path): AdaRMS -> QKV +
+ * QK-norm + RoPE -> masked GQA attention over [visible prefix ; suffix] ->
+ * O-projection + gated residual -> AdaRMS -> GEGLU -> down + gated residual.
+ * Token t of request b sits at position pos0[b] + t. */
+typedef struct dmx_layer_weights {
+  const dmx_bf16* w_mod1; /* [3072][1024] */
+  const dmx_bf16* b_mod1; /* [3072] */
+  const dmx_bf16* w_qkv;  /* [4096][1024] */
+  const dmx_bf16* q_norm; /* [256] */
+  const dmx_bf16* k_norm; /* [256] */
+  const dmx_bf16* w_o;    /* [1024][2048] */
+  const dmx_bf16* w_mod2; /* [3072][1024] */
+  const dmx_bf16* b_mod2; /* [3072] */
+  const dmx_bf16* w_gu;   /* [8192][1024] */
+  const dmx_bf16* w_down; /* [1024][4096] */
+} dmx_layer_weights;
+
+typedef struct dmx_prefix_kv {
+  const dmx_bf16* k;    /* [batch][4][p_bucket][256] */
+  const dmx_bf16* v;    /* [batch][4][p_bucket][256] */
+  const uint8_t* mask;  /* [batch][p_bucket] */
+  int32_t p_bucket;
+} dmx_prefix_kv;
+
+/*   w, kv (host structs holding device pointers).
+ *   x_in, x_out [batch][chunk][1024] bf16 (x_out may alias x_in);
+ *   cond [batch][1024] bf16; pos0 [batch] int32. */
+int dmx_suffix_layer_forward(const dmx_layer_weights* w, const dmx_prefix_kv* kv,
+                             const dmx_bf16* x_in, const dmx_bf16* cond,
+                             const int32_t* pos0, int32_t batch, int32_t chunk,
+                             dmx_bf16* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The action-expert stack of one denoising run, replayed from a per-bucket
+ * hipGraph ([Art §3]: graphs captured once per prefix bucket, replayed per
+ * request, KV addresses fixed).  For step s in 0..n_steps-1 and layer l in
+ * 0..n_layers-1:  x <- layer_l(x, cond[s], k_pre[l], v_pre[l], mask).
+ * Everything that varies per request (x, cond, mask, pos0, KV contents) lives
+ * in the fixed buffers named here: write new values into them and replay. */
+typedef struct dmx_stack_desc {
+  int32_t n_layers, n_steps, batch, chunk, p_bucket;
+  const dmx_layer_weights* layers; /* host array [n_layers] */
+  const dmx_bf16* const* k_pre;    /* host array [n_layers] of device [batch][4][p_bucket][256] */
+  const dmx_bf16* const* v_pre;    /* host array [n_layers] of the same */
+  const uint8_t* mask;             /* device [batch][p_bucket] */
+  const dmx_bf16* cond;            /* device [n_steps][batch][1024] */
+  const int32_t* pos0;             /* device [batch] */
+  dmx_bf16* x;                     /* device [batch][chunk][1024], updated in place */
+  void* ws;                         /* >= dmx_stack_workspace_bytes(...) */
+  size_t ws_bytes;
+} dmx_stack_desc;
+
+typedef struct dmx_graph dmx_graph;
+
+/* Workspace bytes of a stack run: dmx_workspace_bytes(batch, chunk, p_bucket)
+ * plus the modulation vectors of every layer of one step.  0 if unsupported
+ * (n_layers above DMX_MAX_LAYERS included). */
+size_t dmx_stack_workspace_bytes(int32_t n_layers, int32_t batch, int32_t chunk, int32_t p_bucket);
+
+/* Eager run of the stack (same kernels as the graph). */
+int dmx_stack_forward(const dmx_stack_desc* d, void* stream);
+/* Capture the stack on `stream` into a graph (nothing runs).  *out (host). */
+int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** out);
+/* Replay a captured graph on `stream`. */
+int dmx_graph_launch(dmx_graph* g, void* stream);
+void dmx_graph_destroy(dmx_graph* g);
+
+/* ------------------------------------------------------------------------ */
+const char* dmx_status_string(int status);
+const char* dmx_last_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DMX_H_ */

@@ -1,0 +1,305 @@
+"""Python binding of libdmx, the MI355X (gfx950) action-expert layer library.
+
+Thin ctypes marshalling over the C ABI declared in ``include/dmx.h``: every
+function here has the C entry point's name without the ``dmx_`` prefix, takes
+torch tensors (device memory) and the current HIP stream, checks shapes and
+dtypes, and calls the library.  All arithmetic runs in the HIP kernels.  There
+is no fallback: if the library is missing or the call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdmx.so")
+
+OK, FALLBACK_EAGER = 0, 1
+ERR_INVALID_ARG, ERR_BAD_BUCKETS, ERR_PREFIX_TOO_LONG = -1, -2, -3
+ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = -4, -5, -6, -7
+
+H, I, D, HQ, HK = 1024, 4096, 256, 8, 4
+PREFIX_HIDDEN = 2560
+
+EXPORTED = (
+    "dmx_select_bucket", "dmx_workspace_bytes", "dmx_stack_workspace_bytes", "dmx_workspace_init", "dmx_adarms_prenorm",
+    "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
+    "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_graph_create", "dmx_graph_launch",
+    "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
+)
+
+
+class DmxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"dmx status {status}: {message}")
+        self.status = status
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("w_mod1", "b_mod1", "w_qkv", "q_norm", "k_norm", "w_o", "w_mod2", "b_mod2", "w_gu", "w_down")]
+
+
+class PrefixKV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("p_bucket", ctypes.c_int32)]
+
+
+class StackDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_steps", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("p_bucket", ctypes.c_int32),
+                ("layers", ctypes.POINTER(LayerWeights)),
+                ("k_pre", ctypes.POINTER(ctypes.c_void_p)), ("v_pre", ctypes.POINTER(ctypes.c_void_p)),
+                ("mask", ctypes.c_void_p), ("cond", ctypes.c_void_p), ("pos0", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdmx.so (building it first only if no build exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            _build.build_library()
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "dmx_select_bucket": ([i32, P, i32, i32, i32, P], ctypes.c_int),
+            "dmx_workspace_bytes": ([i32, i32, i32], sz),
+            "dmx_stack_workspace_bytes": ([i32, i32, i32, i32], sz),
+            "dmx_workspace_init": ([P, sz, P], ctypes.c_int),
+            "dmx_adarms_prenorm": ([P, P, P, P, i32, i32, P, P, P], ctypes.c_int),
+            "dmx_qkv_qknorm_rope": ([P, P, P, P, i32, i32, i32, P, ctypes.c_float, P, P, P, i32, i32, P, sz, P],
+                                    ctypes.c_int),
+            "dmx_suffix_attention": ([P, P, P, P, P, P, i32, i32, i32, P, P, sz, P], ctypes.c_int),
+            "dmx_oproj_gated_residual": ([P, P, P, P, i32, i32, P, P, sz, P], ctypes.c_int),
+            "dmx_geglu_mlp": ([P, P, P, P, P, i32, i32, P, P, sz, P], ctypes.c_int),
+            "dmx_suffix_layer_forward": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, P, P, i32, i32,
+                                          P, P, sz, P], ctypes.c_int),
+            "dmx_stack_forward": ([ctypes.POINTER(StackDesc), P], ctypes.c_int),
+            "dmx_stack_graph_create": ([ctypes.POINTER(StackDesc), P, ctypes.POINTER(P)], ctypes.c_int),
+            "dmx_graph_launch": ([P, P], ctypes.c_int),
+            "dmx_graph_destroy": ([P], None),
+            "dmx_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "dmx_last_error_string": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> int:
+    if status < 0:
+        raise DmxError(status, lib().dmx_last_error_string().decode())
+    return status
+
+
+def _p(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t, shape, dtype, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
+
+
+# --------------------------------------------------------------------------- host logic
+def select_bucket(prefix_len: int, buckets, fast_prefix_len: int = 1024, min_tokens: int = 0):
+    """Returns (status, index); status is OK, FALLBACK_EAGER or a negative error."""
+    arr = (ctypes.c_int32 * max(1, len(buckets)))(*[int(b) for b in buckets])
+    idx = ctypes.c_int32(-7)
+    st = lib().dmx_select_bucket(int(prefix_len), arr, len(buckets), int(fast_prefix_len), int(min_tokens),
+                                 ctypes.byref(idx))
+    return int(st), int(idx.value)
+
+
+def workspace_bytes(batch: int, tokens: int, p_bucket: int) -> int:
+    return int(lib().dmx_workspace_bytes(batch, tokens, p_bucket))
+
+
+def new_workspace(batch: int, tokens: int, p_bucket: int, device="cuda"):
+    n = workspace_bytes(batch, tokens, p_bucket)
+    if n == 0:
+        raise DmxError(ERR_UNSUPPORTED, f"no workspace size for batch={batch} tokens={tokens} p={p_bucket}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- stages
+def adarms_prenorm(x, cond, w_mod, b_mod, x_norm=None, mod=None, stream=None):
+    B, T, _ = x.shape
+    _want(x, (B, T, H), torch.bfloat16, "x")
+    _want(cond, (B, H), torch.bfloat16, "cond")
+    _want(w_mod, (3 * H, H), torch.bfloat16, "w_mod")
+    _want(b_mod, (3 * H,), torch.bfloat16, "b_mod")
+    x_norm = torch.empty_like(x) if x_norm is None else x_norm
+    mod = torch.empty(B, 3 * H, dtype=torch.float32, device=x.device) if mod is None else mod
+    _check(lib().dmx_adarms_prenorm(_p(x), _p(cond), _p(w_mod), _p(b_mod), B, T, _p(x_norm), _p(mod),
+                                    _stream(stream)))
+    return x_norm, mod
+
+
+def qkv_qknorm_rope(x_norm, w_qkv, q_norm, k_norm, pos0, ws, rope_base=10000.0, k=None, v=None, kv_rows=None,
+                    kv_row0=0, stream=None):
+    B, T, hidden = x_norm.shape
+    _want(x_norm, (B, T, hidden), torch.bfloat16, "x_norm")
+    _want(w_qkv, ((HQ + 2 * HK) * D, hidden), torch.bfloat16, "w_qkv")
+    _want(pos0, (B,), torch.int32, "pos0")
+    kv_rows = T if kv_rows is None else kv_rows
+    q = torch.empty(B, T, HQ, D, dtype=torch.bfloat16, device=x_norm.device)
+    if k is None:
+        k = torch.empty(B, HK, kv_rows, D, dtype=torch.bfloat16, device=x_norm.device)
+    if v is None:
+        v = torch.empty(B, HK, kv_rows, D, dtype=torch.bfloat16, device=x_norm.device)
+    _want(k, (B, HK, kv_rows, D), torch.bfloat16, "k")
+    _want(v, (B, HK, kv_rows, D), torch.bfloat16, "v")
+    _check(lib().dmx_qkv_qknorm_rope(_p(x_norm), _p(w_qkv), _p(q_norm), _p(k_norm), B, T, hidden, _p(pos0),
+                                     float(rope_base), _p(q), _p(k), _p(v), kv_rows, kv_row0, _p(ws), ws.numel(),
+                                     _stream(stream)))
+    return q, k, v
+
+
+def suffix_attention(q, k_suf, v_suf, k_pre, v_pre, mask, ws, ctx=None, stream=None):
+    B, C = q.shape[:2]
+    P = k_pre.shape[2]
+    _want(q, (B, C, HQ, D), torch.bfloat16, "q")
+    _want(k_suf, (B, HK, C, D), torch.bfloat16, "k_suf")
+    _want(v_suf, (B, HK, C, D), torch.bfloat16, "v_suf")
+    _want(k_pre, (B, HK, P, D), torch.bfloat16, "k_pre")
+    _want(v_pre, (B, HK, P, D), torch.bfloat16, "v_pre")
+    _want(mask, (B, P), torch.uint8, "mask")
+    ctx = torch.empty_like(q) if ctx is None else ctx
+    _check(lib().dmx_suffix_attention(_p(q), _p(k_suf), _p(v_suf), _p(k_pre), _p(v_pre), _p(mask), B, C, P, _p(ctx),
+                                      _p(ws), ws.numel(), _stream(stream)))
+    return ctx
+
+
+def oproj_gated_residual(ctx, w_o, mod, residual, ws, out=None, stream=None):
+    B, T = residual.shape[:2]
+    _want(ctx, (B, T, HQ, D), torch.bfloat16, "ctx")
+    _want(w_o, (H, HQ * D), torch.bfloat16, "w_o")
+    _want(mod, (B, 3 * H), torch.float32, "mod")
+    _want(residual, (B, T, H), torch.bfloat16, "residual")
+    out = torch.empty_like(residual) if out is None else out
+    _check(lib().dmx_oproj_gated_residual(_p(ctx), _p(w_o), _p(mod), _p(residual), B, T, _p(out), _p(ws),
+                                          ws.numel(), _stream(stream)))
+    return out
+
+
+def geglu_mlp(x_norm2, w_gu, w_down, mod2, residual, ws, out=None, stream=None):
+    B, T = residual.shape[:2]
+    _want(x_norm2, (B, T, H), torch.bfloat16, "x_norm2")
+    _want(w_gu, (2 * I, H), torch.bfloat16, "w_gu")
+    _want(w_down, (H, I), torch.bfloat16, "w_down")
+    _want(mod2, (B, 3 * H), torch.float32, "mod2")
+    _want(residual, (B, T, H), torch.bfloat16, "residual")
+    out = torch.empty_like(residual) if out is None else out
+    _check(lib().dmx_geglu_mlp(_p(x_norm2), _p(w_gu), _p(w_down), _p(mod2), _p(residual), B, T, _p(out), _p(ws),
+                               ws.numel(), _stream(stream)))
+    return out
+
+
+WEIGHT_SHAPES = {
+    "w_mod1": (3 * H, H), "b_mod1": (3 * H,), "w_qkv": ((HQ + 2 * HK) * D, H), "q_norm": (D,), "k_norm": (D,),
+    "w_o": (H, HQ * D), "w_mod2": (3 * H, H), "b_mod2": (3 * H,), "w_gu": (2 * I, H), "w_down": (H, I),
+}
+
+
+def layer_weights_struct(w: dict) -> LayerWeights:
+    for k, s in WEIGHT_SHAPES.items():
+        _want(w[k], s, torch.bfloat16, k)
+    return LayerWeights(**{k: w[k].data_ptr() for k in WEIGHT_SHAPES})
+
+
+def suffix_layer_forward(w: dict, k_pre, v_pre, mask, x, cond, pos0, ws, out=None, stream=None):
+    B, C, _ = x.shape
+    P = k_pre.shape[2]
+    _want(x, (B, C, H), torch.bfloat16, "x")
+    _want(cond, (B, H), torch.bfloat16, "cond")
+    _want(pos0, (B,), torch.int32, "pos0")
+    _want(k_pre, (B, HK, P, D), torch.bfloat16, "k_pre")
+    _want(v_pre, (B, HK, P, D), torch.bfloat16, "v_pre")
+    _want(mask, (B, P), torch.uint8, "mask")
+    out = torch.empty_like(x) if out is None else out
+    lw = layer_weights_struct(w)
+    kv = PrefixKV(k_pre.data_ptr(), v_pre.data_ptr(), mask.data_ptr(), P)
+    _check(lib().dmx_suffix_layer_forward(ctypes.byref(lw), ctypes.byref(kv), _p(x), _p(cond), _p(pos0), B, C,
+                                          _p(out), _p(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------- stack / graphs
+class Stack:
+    """The action-expert stack bound to fixed buffers.
+
+    layers: list of weight dicts; k_pre / v_pre: per-layer [B][4][P][256]
+    tensors; mask [B][P] uint8; cond [n_steps][B][1024]; pos0 [B] int32;
+    x [B][C][1024] (updated in place by run / replay)."""
+
+    def __init__(self, layers, k_pre, v_pre, mask, cond, pos0, x, ws=None):
+        self.n_layers = len(layers)
+        self.n_steps, B, _ = cond.shape
+        _, C, _ = x.shape
+        P = mask.shape[1]
+        self._keep = (layers, k_pre, v_pre, mask, cond, pos0, x)
+        if ws is None:
+            n = int(lib().dmx_stack_workspace_bytes(self.n_layers, B, C, P))
+            if n == 0:
+                raise DmxError(ERR_UNSUPPORTED, f"no stack workspace for {self.n_layers} layers B={B} C={C} P={P}")
+            ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+        self.ws = ws
+        self._lw = (LayerWeights * self.n_layers)(*[layer_weights_struct(w) for w in layers])
+        for t in k_pre + v_pre:
+            _want(t, (B, HK, P, D), torch.bfloat16, "k_pre/v_pre")
+        self._kp = (ctypes.c_void_p * self.n_layers)(*[t.data_ptr() for t in k_pre])
+        self._vp = (ctypes.c_void_p * self.n_layers)(*[t.data_ptr() for t in v_pre])
+        _want(cond, (self.n_steps, B, H), torch.bfloat16, "cond")
+        _want(mask, (B, P), torch.uint8, "mask")
+        self.desc = StackDesc(self.n_layers, self.n_steps, B, C, P, self._lw, self._kp, self._vp,
+                              mask.data_ptr(), cond.data_ptr(), pos0.data_ptr(), x.data_ptr(),
+                              self.ws.data_ptr(), self.ws.numel())
+        self._graph = None
+
+    def run(self, stream=None):
+        _check(lib().dmx_stack_forward(ctypes.byref(self.desc), _stream(stream)))
+
+    def capture(self, stream):
+        """Capture the stack into a hipGraph on a non-default stream."""
+        g = ctypes.c_void_p()
+        _check(lib().dmx_stack_graph_create(ctypes.byref(self.desc), _stream(stream), ctypes.byref(g)))
+        self._graph = g
+        return self
+
+    def replay(self, stream=None):
+        if self._graph is None:
+            raise DmxError(ERR_INVALID_ARG, "replay() before capture()")
+        _check(lib().dmx_graph_launch(self._graph, _stream(stream)))
+
+    def close(self):
+        if self._graph is not None:
+            lib().dmx_graph_destroy(self._graph)
+            self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

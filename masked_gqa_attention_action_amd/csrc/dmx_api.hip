@@ -1,0 +1,595 @@
+// C ABI of libdmx: argument validation, workspace layout and the order in
+// which the stage kernels run.  Citations of the pages are in include/dmx.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dmx.h"
+#include "dmx_device.hpp"
+#include "dmx_internal.hpp"
+
+using namespace dmx;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DMX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DMX_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define DMX_REQUIRE_PTR(p)                                                             \
+  do {                                                                                 \
+    if ((p) == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: %s is null", fn, #p);    \
+    if (!aligned16(p)) return fail(DMX_ERR_MISALIGNED, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+#define DMX_TRY(expr)             \
+  do {                            \
+    const int st_ = (expr);       \
+    if (st_ != DMX_OK) return st_; \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Workspace carve-up.  Everything a layer needs between its stages, plus
+// (for a stack) the modulation vectors of every layer of one step.
+struct WsLayout {
+  size_t mod1, mod2, xn, qkv, q, ks, vs, ctx, x1, h, part_o, part_ml, stack_mod, total;
+  AttnArgs attn;
+};
+
+bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
+  if (B < 1 || T < 1 || P < 0 || B > DMX_MAX_BATCH || T > 4096 || P > DMX_MAX_PREFIX || n_layers < 0 ||
+      n_layers > DMX_MAX_LAYERS)
+    return false;
+  const size_t M = (size_t)B * T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.mod1 = take((size_t)B * 3 * kH * 4);
+  L.mod2 = take((size_t)B * 3 * kH * 4);
+  L.xn = take(M * kH * 2);
+  L.qkv = take(M * kQKV * 4);
+  L.q = take(M * kHQ * kD * 2);
+  L.ks = take((size_t)B * kHK * T * kD * 2);
+  L.vs = take((size_t)B * kHK * T * kD * 2);
+  L.ctx = take(M * kHQ * kD * 2);
+  L.x1 = take(M * kH * 4);  // fp32 residual between the two halves of a layer
+  L.h = take(M * kI * 2);
+  attn_config(B, T, P, L.attn);
+  const size_t prow = (size_t)B * kHK * (L.attn.S + 1) * L.attn.R16;
+  L.part_o = take(prow * kD * 2);
+  L.part_ml = take(prow * 2 * 4);
+  L.stack_mod = take((size_t)n_layers * 2 * B * 3 * kH * 4);
+  L.total = off;
+  return true;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const char* fn, void* ws, size_t ws_bytes, int B, int T, int P, WsLayout& L, int n_layers = 0) {
+  if (!ws_layout(B, T, P, n_layers, L)) return fail(DMX_ERR_UNSUPPORTED, "%s: unsupported sizes", fn);
+  if (ws == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: ws is null", fn);
+  if (!aligned16(ws)) return fail(DMX_ERR_MISALIGNED, "%s: ws is not 16-byte aligned", fn);
+  if (ws_bytes < L.total)
+    return fail(DMX_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, L.total);
+  return DMX_OK;
+}
+
+int check_bt(const char* fn, int B, int T, int max_t) {
+  if (B < 1 || B > DMX_MAX_BATCH) return fail(DMX_ERR_UNSUPPORTED, "%s: batch %d not in [1, %d]", fn, B, DMX_MAX_BATCH);
+  if (T < 1 || T > max_t) return fail(DMX_ERR_UNSUPPORTED, "%s: tokens %d not in [1, %d]", fn, T, max_t);
+  return DMX_OK;
+}
+
+GemmArgs gemm_args() {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  return a;
+}
+
+// ---- stage enqueuers (arguments already validated) -------------------------
+int enq_mods(const ModJob* jobs, int n, int B, hipStream_t s) {
+  for (int j0 = 0; j0 < n; j0 += kMaxModJobs) {
+    ModBatch mb;
+    memset(&mb, 0, sizeof mb);
+    mb.B = B;
+    mb.n = n - j0 < kMaxModJobs ? n - j0 : kMaxModJobs;
+    for (int j = 0; j < mb.n; ++j) mb.job[j] = jobs[j0 + j];
+    DMX_TRY(hip_check(launch_mod_multi(mb, s), "modulation launch"));
+  }
+  return DMX_OK;
+}
+
+int enq_adarms(const dmx_bf16* x, const dmx_bf16* cond, const dmx_bf16* w_mod, const dmx_bf16* b_mod,
+               int B, int T, dmx_bf16* xn, float* mod, hipStream_t s) {
+  const ModJob job{w_mod, b_mod, cond, mod};
+  DMX_TRY(enq_mods(&job, 1, B, s));
+  return hip_check(launch_adarms_norm(x, mod, B * T, T, xn, s), "AdaRMS norm launch");
+}
+
+int enq_qkv(const dmx_bf16* xn, const dmx_bf16* w_qkv, const dmx_bf16* qn, const dmx_bf16* kn, int B, int T,
+            int hidden, const int32_t* pos0, float base, dmx_bf16* q, dmx_bf16* k, dmx_bf16* v,
+            int kv_rows, int kv_row0, float* raw, hipStream_t s) {
+  const GemmKind kind = hidden == kH ? GEMM_QKV1024 : GEMM_QKV2560;
+  GemmArgs a = gemm_args();
+  gemm_config(kind, a);
+  a.A = xn;
+  a.W = w_qkv;
+  a.M = B * T;
+  a.T = T;
+  a.out_f32 = raw;
+  a.ldo = kQKV;
+  DMX_TRY(hip_check(launch_gemm(kind, a, s), "QKV GEMM launch"));
+  return hip_check(launch_qknorm_rope(raw, qn, kn, pos0, base, B * T, T, q, k, v, kv_rows, kv_row0, s),
+                   "QK-norm/RoPE launch");
+}
+
+AttnArgs attn_args(const WsLayout& L, void* ws) {
+  AttnArgs a = L.attn;
+  a.q = a.ks = a.vs = a.kp = a.vp = nullptr;
+  a.raw = nullptr;
+  a.qn_w = a.kn_w = nullptr;
+  a.pos0 = nullptr;
+  a.rope_base = 10000.0f;
+  a.mask = nullptr;
+  a.part_o = at<uint16_t>(ws, L.part_o);
+  a.part_ml = at<float>(ws, L.part_ml);
+  return a;
+}
+
+int enq_attention(const dmx_bf16* q, const dmx_bf16* ks, const dmx_bf16* vs, const dmx_bf16* kp,
+                  const dmx_bf16* vp, const uint8_t* mask, dmx_bf16* ctx, void* ws, const WsLayout& L,
+                  hipStream_t s) {
+  AttnArgs a = attn_args(L, ws);
+  a.q = q;
+  a.ks = ks;
+  a.vs = vs;
+  a.kp = kp;
+  a.vp = vp;
+  a.mask = mask;
+  return hip_check(launch_attention(a, ctx, s), "attention launch");
+}
+
+// Gated-residual projection: out = resid + gate[b] * (A * W^T); the residual
+// and output are bf16 unless their fp32 pointer is given.
+int enq_resid_gemm(GemmKind kind, const dmx_bf16* A, const dmx_bf16* W, const float* mod,
+                   const dmx_bf16* resid, const float* resid_f32, int B, int T, dmx_bf16* out,
+                   float* out_f32, hipStream_t s) {
+  GemmArgs a = gemm_args();
+  gemm_config(kind, a);
+  a.A = A;
+  a.W = W;
+  a.M = B * T;
+  a.T = T;
+  a.out_bf16 = out;
+  a.out_f32 = out_f32;
+  a.ldo = kH;
+  a.gate = mod + 2 * kH;
+  a.gate_stride = 3 * kH;
+  a.resid = resid;
+  a.resid_f32 = resid_f32;
+  return hip_check(launch_gemm(kind, a, s), "projection GEMM launch");
+}
+
+int enq_geglu(const dmx_bf16* xn2, const dmx_bf16* w_gu, const dmx_bf16* w_down, const float* mod2,
+              const dmx_bf16* resid, int B, int T, dmx_bf16* out, void* ws, const WsLayout& L,
+              hipStream_t s) {
+  GemmArgs a = gemm_args();
+  gemm_config(GEMM_GATEUP, a);
+  a.A = xn2;
+  a.W = w_gu;
+  a.M = B * T;
+  a.T = T;
+  a.out_bf16 = at<uint16_t>(ws, L.h);
+  a.ldo = kI;
+  DMX_TRY(hip_check(launch_gemm(GEMM_GATEUP, a, s), "gate-up GEMM launch"));
+  return enq_resid_gemm(GEMM_DOWN, at<uint16_t>(ws, L.h), w_down, mod2, resid, nullptr, B, T, out, nullptr, s);
+}
+
+// The fused layer chain (modulation vectors mod1 / mod2 already computed):
+//   QKV GEMM with AdaRMS #1 prologue -> attention with QK-norm + RoPE on load
+//   -> combine -> O-projection + gated residual (fp32 x1) -> gate-up GEMM with
+//   AdaRMS #2 prologue + GEGLU -> down projection + gated residual.
+int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
+                    const int32_t* pos0, int B, int C, dmx_bf16* x_out, const float* mod1, const float* mod2,
+                    void* ws, const WsLayout& L, hipStream_t s) {
+  float* raw = at<float>(ws, L.qkv);
+  dmx_bf16* ctx = at<dmx_bf16>(ws, L.ctx);
+  float* x1 = at<float>(ws, L.x1);
+  dmx_bf16* h = at<dmx_bf16>(ws, L.h);
+  const int M = B * C;
+
+  GemmArgs g = gemm_args();
+  gemm_config(GEMM_QKV1024_NORM, g);
+  g.xb = x_in;
+  g.nmod = mod1;
+  g.W = w->w_qkv;
+  g.M = M;
+  g.T = C;
+  g.out_f32 = raw;
+  g.ldo = kQKV;
+  DMX_TRY(hip_check(launch_gemm(GEMM_QKV1024_NORM, g, s), "QKV GEMM launch"));
+
+  AttnArgs a = attn_args(L, ws);
+  a.raw = raw;
+  a.qn_w = w->q_norm;
+  a.kn_w = w->k_norm;
+  a.pos0 = pos0;
+  a.kp = kv->k;
+  a.vp = kv->v;
+  a.mask = kv->mask;
+  DMX_TRY(hip_check(launch_attention(a, ctx, s), "attention launch"));
+
+  // x1 = x + gate1 * (ctx W_o^T), kept in fp32
+  DMX_TRY(enq_resid_gemm(GEMM_OPROJ_F32, ctx, w->w_o, mod1, x_in, nullptr, B, C, nullptr, x1, s));
+
+  g = gemm_args();
+  gemm_config(GEMM_GATEUP_NORM_F32, g);
+  g.xf = x1;
+  g.nmod = mod2;
+  g.W = w->w_gu;
+  g.M = M;
+  g.T = C;
+  g.out_bf16 = h;
+  g.ldo = kI;
+  DMX_TRY(hip_check(launch_gemm(GEMM_GATEUP_NORM_F32, g, s), "gate-up GEMM launch"));
+
+  // out = x1 + gate2 * (GEGLU(xn2) W_down^T)
+  return enq_resid_gemm(GEMM_DOWN_F32RES, h, w->w_down, mod2, nullptr, x1, B, C, x_out, nullptr, s);
+}
+
+int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
+              const dmx_bf16* cond, const int32_t* pos0, int B, int C, dmx_bf16* x_out, void* ws,
+              const WsLayout& L, hipStream_t s) {
+  float* mod1 = at<float>(ws, L.mod1);
+  float* mod2 = at<float>(ws, L.mod2);
+  const ModJob jobs[2] = {{w->w_mod1, w->b_mod1, cond, mod1}, {w->w_mod2, w->b_mod2, cond, mod2}};
+  DMX_TRY(enq_mods(jobs, 2, B, s));
+  return enq_layer_chain(w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, L, s);
+}
+
+int check_layer_weights(const char* fn, const dmx_layer_weights* w) {
+  if (w == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: weights struct is null", fn);
+  DMX_REQUIRE_PTR(w->w_mod1);
+  DMX_REQUIRE_PTR(w->b_mod1);
+  DMX_REQUIRE_PTR(w->w_qkv);
+  DMX_REQUIRE_PTR(w->q_norm);
+  DMX_REQUIRE_PTR(w->k_norm);
+  DMX_REQUIRE_PTR(w->w_o);
+  DMX_REQUIRE_PTR(w->w_mod2);
+  DMX_REQUIRE_PTR(w->b_mod2);
+  DMX_REQUIRE_PTR(w->w_gu);
+  DMX_REQUIRE_PTR(w->w_down);
+  return DMX_OK;
+}
+
+int check_kv(const char* fn, const dmx_bf16* k, const dmx_bf16* v, const uint8_t* mask, int P) {
+  if (P < 0 || P > DMX_MAX_PREFIX)
+    return fail(DMX_ERR_UNSUPPORTED, "%s: p_bucket %d not in [0, %d]", fn, P, DMX_MAX_PREFIX);
+  if (P > 0) {
+    DMX_REQUIRE_PTR(k);
+    DMX_REQUIRE_PTR(v);
+    if (mask == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: mask is null", fn);
+  }
+  return DMX_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+int dmx_select_bucket(int32_t prefix_len, const int32_t* buckets, int32_t n, int32_t fast_prefix_len,
+                      int32_t min_tokens, int32_t* idx_out) {
+  if (idx_out) *idx_out = -1;
+  if (buckets == nullptr || idx_out == nullptr || prefix_len <= 0 || fast_prefix_len <= 0 ||
+      min_tokens < 0 || n < 0)
+    return fail(DMX_ERR_INVALID_ARG, "dmx_select_bucket: invalid argument");
+  if (n == 0) return fail(DMX_ERR_BAD_BUCKETS, "dmx_select_bucket: empty bucket list");
+  int32_t prev = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t bk = buckets[i];
+    if (bk <= 0 || bk > fast_prefix_len)
+      return fail(DMX_ERR_BAD_BUCKETS, "dmx_select_bucket: bucket %d outside (0, %d]", bk, fast_prefix_len);
+    if (i > 0 && bk <= prev)
+      return fail(DMX_ERR_BAD_BUCKETS, "dmx_select_bucket: buckets not strictly increasing");
+    prev = bk;
+  }
+  if (prefix_len > fast_prefix_len)
+    return fail(DMX_ERR_PREFIX_TOO_LONG, "dmx_select_bucket: prefix %d above cap %d", prefix_len,
+                fast_prefix_len);
+  // buckets are strictly increasing: the first eligible one that holds the prefix is the smallest
+  for (int32_t i = 0; i < n; ++i) {
+    if (buckets[i] >= min_tokens && buckets[i] >= prefix_len) {
+      *idx_out = i;
+      return DMX_OK;
+    }
+  }
+  return DMX_FALLBACK_EAGER;
+}
+
+size_t dmx_workspace_bytes(int32_t batch, int32_t tokens, int32_t p_bucket) {
+  WsLayout L;
+  if (!ws_layout(batch, tokens, p_bucket, 0, L)) return 0;
+  return L.total;
+}
+
+size_t dmx_stack_workspace_bytes(int32_t n_layers, int32_t batch, int32_t chunk, int32_t p_bucket) {
+  WsLayout L;
+  if (n_layers < 1 || !ws_layout(batch, chunk, p_bucket, n_layers, L)) return 0;
+  return L.total;
+}
+
+int dmx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dmx_workspace_init";
+  DMX_REQUIRE_PTR(ws);
+  return hip_check(launch_fill_zero(ws, ws_bytes & ~(size_t)15, (hipStream_t)stream), "workspace fill");
+}
+
+int dmx_adarms_prenorm(const dmx_bf16* x, const dmx_bf16* cond, const dmx_bf16* w_mod, const dmx_bf16* b_mod,
+                       int32_t batch, int32_t tokens, dmx_bf16* x_norm, float* mod, void* stream) {
+  const char* fn = "dmx_adarms_prenorm";
+  DMX_REQUIRE_PTR(x);
+  DMX_REQUIRE_PTR(cond);
+  DMX_REQUIRE_PTR(w_mod);
+  DMX_REQUIRE_PTR(b_mod);
+  DMX_REQUIRE_PTR(x_norm);
+  DMX_REQUIRE_PTR(mod);
+  DMX_TRY(check_bt(fn, batch, tokens, 4096));
+  return enq_adarms(x, cond, w_mod, b_mod, batch, tokens, x_norm, mod, (hipStream_t)stream);
+}
+
+int dmx_qkv_qknorm_rope(const dmx_bf16* x_norm, const dmx_bf16* w_qkv, const dmx_bf16* q_norm_w,
+                        const dmx_bf16* k_norm_w, int32_t batch, int32_t tokens, int32_t hidden,
+                        const int32_t* pos0, float rope_base, dmx_bf16* q, dmx_bf16* k, dmx_bf16* v,
+                        int32_t kv_rows, int32_t kv_row0, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dmx_qkv_qknorm_rope";
+  DMX_REQUIRE_PTR(x_norm);
+  DMX_REQUIRE_PTR(w_qkv);
+  DMX_REQUIRE_PTR(q_norm_w);
+  DMX_REQUIRE_PTR(k_norm_w);
+  DMX_REQUIRE_PTR(pos0);
+  DMX_REQUIRE_PTR(q);
+  DMX_REQUIRE_PTR(k);
+  DMX_REQUIRE_PTR(v);
+  DMX_TRY(check_bt(fn, batch, tokens, 4096));
+  if (hidden != kH && hidden != DMX_PREFIX_HIDDEN)
+    return fail(DMX_ERR_UNSUPPORTED, "%s: hidden %d (1024 or 2560 supported)", fn, hidden);
+  if (!(rope_base > 1.0f)) return fail(DMX_ERR_INVALID_ARG, "%s: rope_base must be > 1", fn);
+  if (kv_row0 < 0 || kv_rows < 1 || (int64_t)kv_row0 + tokens > kv_rows)
+    return fail(DMX_ERR_INVALID_ARG, "%s: rows [%d, %d) do not fit kv_rows %d", fn, kv_row0, kv_row0 + tokens,
+                kv_rows);
+  WsLayout L;
+  DMX_TRY(check_ws(fn, ws, ws_bytes, batch, tokens, 0, L));
+  return enq_qkv(x_norm, w_qkv, q_norm_w, k_norm_w, batch, tokens, hidden, pos0, rope_base, q, k, v, kv_rows,
+                 kv_row0, at<float>(ws, L.qkv), (hipStream_t)stream);
+}
+
+int dmx_suffix_attention(const dmx_bf16* q, const dmx_bf16* k_suf, const dmx_bf16* v_suf, const dmx_bf16* k_pre,
+                         const dmx_bf16* v_pre, const uint8_t* mask, int32_t batch, int32_t chunk,
+                         int32_t p_bucket, dmx_bf16* ctx, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dmx_suffix_attention";
+  DMX_REQUIRE_PTR(q);
+  DMX_REQUIRE_PTR(k_suf);
+  DMX_REQUIRE_PTR(v_suf);
+  DMX_REQUIRE_PTR(ctx);
+  DMX_TRY(check_bt(fn, batch, chunk, DMX_MAX_CHUNK));
+  DMX_TRY(check_kv(fn, k_pre, v_pre, mask, p_bucket));
+  WsLayout L;
+  DMX_TRY(check_ws(fn, ws, ws_bytes, batch, chunk, p_bucket, L));
+  return enq_attention(q, k_suf, v_suf, k_pre, v_pre, mask, ctx, ws, L, (hipStream_t)stream);
+}
+
+int dmx_oproj_gated_residual(const dmx_bf16* ctx, const dmx_bf16* w_o, const float* mod, const dmx_bf16* residual,
+                             int32_t batch, int32_t tokens, dmx_bf16* out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  const char* fn = "dmx_oproj_gated_residual";
+  DMX_REQUIRE_PTR(ctx);
+  DMX_REQUIRE_PTR(w_o);
+  DMX_REQUIRE_PTR(mod);
+  DMX_REQUIRE_PTR(residual);
+  DMX_REQUIRE_PTR(out);
+  DMX_TRY(check_bt(fn, batch, tokens, 4096));
+  WsLayout L;
+  DMX_TRY(check_ws(fn, ws, ws_bytes, batch, tokens, 0, L));
+  return enq_resid_gemm(GEMM_OPROJ, ctx, w_o, mod, residual, nullptr, batch, tokens, out, nullptr,
+                        (hipStream_t)stream);
+}
+
+int dmx_geglu_mlp(const dmx_bf16* x_norm2, const dmx_bf16* w_gu, const dmx_bf16* w_down, const float* mod2,
+                  const dmx_bf16* residual, int32_t batch, int32_t tokens, dmx_bf16* out, void* ws,
+                  size_t ws_bytes, void* stream) {
+  const char* fn = "dmx_geglu_mlp";
+  DMX_REQUIRE_PTR(x_norm2);
+  DMX_REQUIRE_PTR(w_gu);
+  DMX_REQUIRE_PTR(w_down);
+  DMX_REQUIRE_PTR(mod2);
+  DMX_REQUIRE_PTR(residual);
+  DMX_REQUIRE_PTR(out);
+  DMX_TRY(check_bt(fn, batch, tokens, 4096));
+  WsLayout L;
+  DMX_TRY(check_ws(fn, ws, ws_bytes, batch, tokens, 0, L));
+  return enq_geglu(x_norm2, w_gu, w_down, mod2, residual, batch, tokens, out, ws, L, (hipStream_t)stream);
+}
+
+int dmx_suffix_layer_forward(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
+                             const dmx_bf16* cond, const int32_t* pos0, int32_t batch, int32_t chunk,
+                             dmx_bf16* x_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dmx_suffix_layer_forward";
+  DMX_TRY(check_layer_weights(fn, w));
+  if (kv == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: kv struct is null", fn);
+  DMX_TRY(check_kv(fn, kv->k, kv->v, kv->mask, kv->p_bucket));
+  DMX_REQUIRE_PTR(x_in);
+  DMX_REQUIRE_PTR(cond);
+  DMX_REQUIRE_PTR(pos0);
+  DMX_REQUIRE_PTR(x_out);
+  DMX_TRY(check_bt(fn, batch, chunk, DMX_MAX_CHUNK));
+  WsLayout L;
+  DMX_TRY(check_ws(fn, ws, ws_bytes, batch, chunk, kv->p_bucket, L));
+  return enq_layer(w, kv, x_in, cond, pos0, batch, chunk, x_out, ws, L, (hipStream_t)stream);
+}
+
+// ---- stack and graphs -------------------------------------------------------
+struct dmx_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+static int check_stack(const char* fn, const dmx_stack_desc* d, WsLayout& L) {
+  if (d == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: desc is null", fn);
+  if (d->n_layers < 1 || d->n_layers > DMX_MAX_LAYERS || d->n_steps < 1 || d->layers == nullptr ||
+      d->k_pre == nullptr || d->v_pre == nullptr)
+    return fail(DMX_ERR_INVALID_ARG, "%s: bad layer / step description", fn);
+  DMX_TRY(check_bt(fn, d->batch, d->chunk, DMX_MAX_CHUNK));
+  for (int l = 0; l < d->n_layers; ++l) {
+    DMX_TRY(check_layer_weights(fn, &d->layers[l]));
+    DMX_TRY(check_kv(fn, d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket));
+  }
+  DMX_REQUIRE_PTR(d->cond);
+  DMX_REQUIRE_PTR(d->pos0);
+  DMX_REQUIRE_PTR(d->x);
+  return check_ws(fn, d->ws, d->ws_bytes, d->batch, d->chunk, d->p_bucket, L, d->n_layers);
+}
+
+// One pass of the stack.  With a side stream (graph capture), the modulation
+// vectors of layer l + 1 are computed on it while layer l runs on `s`; layer
+// l + 1 waits for them through an event.  Without one, everything runs on `s`.
+static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, hipStream_t side,
+                     hipEvent_t* ev) {
+  const int B = d->batch, NL = d->n_layers;
+  float* mods = at<float>(d->ws, L.stack_mod);
+  auto mod_of = [&](int l, int which) { return mods + ((size_t)l * 2 + which) * B * 3 * kH; };
+  for (int st = 0; st < d->n_steps; ++st) {
+    const dmx_bf16* cond = d->cond + (size_t)st * B * kH;
+    auto jobs_of = [&](int l, ModJob* j) {
+      j[0] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, mod_of(l, 0)};
+      j[1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, mod_of(l, 1)};
+    };
+    ModJob j[2];
+    jobs_of(0, j);
+    DMX_TRY(enq_mods(j, 2, B, s));
+    if (side) {
+      DMX_TRY(hip_check(hipEventRecord(ev[0], s), "hipEventRecord"));
+      DMX_TRY(hip_check(hipStreamWaitEvent(side, ev[0], 0), "hipStreamWaitEvent"));
+      for (int l = 1; l < NL; ++l) {
+        jobs_of(l, j);
+        DMX_TRY(enq_mods(j, 2, B, side));
+        DMX_TRY(hip_check(hipEventRecord(ev[l], side), "hipEventRecord"));
+      }
+    }
+    for (int l = 0; l < NL; ++l) {
+      if (l > 0) {
+        if (side) {
+          DMX_TRY(hip_check(hipStreamWaitEvent(s, ev[l], 0), "hipStreamWaitEvent"));
+        } else {
+          jobs_of(l, j);
+          DMX_TRY(enq_mods(j, 2, B, s));
+        }
+      }
+      dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
+      DMX_TRY(enq_layer_chain(&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1),
+                              d->ws, L, s));
+    }
+  }
+  return DMX_OK;
+}
+
+int dmx_stack_forward(const dmx_stack_desc* d, void* stream) {
+  WsLayout L;
+  DMX_TRY(check_stack("dmx_stack_forward", d, L));
+  return enq_stack(d, L, (hipStream_t)stream, nullptr, nullptr);
+}
+
+int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** out) {
+  const char* fn = "dmx_stack_graph_create";
+  if (out == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: out is null", fn);
+  *out = nullptr;
+  if (stream == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: capture needs a non-null stream", fn);
+  WsLayout L;
+  DMX_TRY(check_stack(fn, d, L));
+  hipStream_t s = (hipStream_t)stream;
+  // capture-time helpers: a side stream at the default priority and one event per layer
+  hipStream_t side = nullptr;
+  DMX_TRY(hip_check(hipStreamCreateWithFlags(&side, hipStreamNonBlocking), "hipStreamCreate"));
+  hipEvent_t ev[DMX_MAX_LAYERS];
+  int nev = 0;
+  int st = DMX_OK;
+  for (; nev < d->n_layers && st == DMX_OK; ++nev)
+    st = hip_check(hipEventCreateWithFlags(&ev[nev], hipEventDisableTiming), "hipEventCreate");
+  hipGraph_t g = nullptr;
+  if (st == DMX_OK) {
+    st = hip_check(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+    if (st == DMX_OK) {
+      st = enq_stack(d, L, s, side, ev);
+      const hipError_t ce = hipStreamEndCapture(s, &g);
+      if (st == DMX_OK) st = hip_check(ce, "hipStreamEndCapture");
+    }
+  }
+  hipGraphExec_t e = nullptr;
+  if (st == DMX_OK) st = hip_check(hipGraphInstantiate(&e, g, nullptr, nullptr, 0), "hipGraphInstantiate");
+  for (int i = 0; i < nev; ++i) (void)hipEventDestroy(ev[i]);
+  (void)hipStreamDestroy(side);
+  if (st != DMX_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  *out = new dmx_graph{g, e};
+  return DMX_OK;
+}
+
+int dmx_graph_launch(dmx_graph* g, void* stream) {
+  if (g == nullptr) return fail(DMX_ERR_INVALID_ARG, "dmx_graph_launch: graph is null");
+  return hip_check(hipGraphLaunch(g->exec, (hipStream_t)stream), "hipGraphLaunch");
+}
+
+void dmx_graph_destroy(dmx_graph* g) {
+  if (g == nullptr) return;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
+}
+
+const char* dmx_status_string(int status) {
+  switch (status) {
+    case DMX_OK: return "ok";
+    case DMX_FALLBACK_EAGER: return "fallback: run eagerly, unbucketed";
+    case DMX_ERR_INVALID_ARG: return "invalid argument";
+    case DMX_ERR_BAD_BUCKETS: return "bad bucket list";
+    case DMX_ERR_PREFIX_TOO_LONG: return "prefix too long";
+    case DMX_ERR_UNSUPPORTED: return "unsupported size";
+    case DMX_ERR_MISALIGNED: return "misaligned pointer";
+    case DMX_ERR_WORKSPACE: return "workspace too small";
+    case DMX_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dmx_last_error_string(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

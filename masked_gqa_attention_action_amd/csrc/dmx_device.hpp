@@ -1,0 +1,84 @@
+// Device-side helpers shared by the dmx kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dmx {
+
+// Suffix-layer shape constants (shape table of the OpenDM DM0.5 fast-stack
+// article, §2.2).
+constexpr int kH = 1024;          // hidden
+constexpr int kI = 4096;          // intermediate
+constexpr int kD = 256;           // head_dim
+constexpr int kHQ = 8;            // query heads
+constexpr int kHK = 4;            // KV heads
+constexpr int kGroup = kHQ / kHK; // query heads per KV head
+constexpr int kQKV = (kHQ + 2 * kHK) * kD;  // 4096 projected features
+constexpr float kEps = 1e-6f;
+
+// MFMA operand types: 8 bf16 (as raw 16-bit) per lane, fp32 accumulators.
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = 0;
+  return z;
+}
+
+__device__ __forceinline__ f32x4 zero_f32x4() {
+  f32x4 z;
+  z[0] = z[1] = z[2] = z[3] = 0.f;
+  return z;
+}
+
+// D += A * B for a 16x16 output tile over 32 reduction elements.
+// Lane l: A row l%16, B column l%16, both at reduction offsets 8*(l/16)..+7;
+// D holds rows 4*(l/16)+0..3 of column l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// reductions inside each aligned group of 16 lanes
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+
+}  // namespace dmx

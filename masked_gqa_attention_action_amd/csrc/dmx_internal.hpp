@@ -1,0 +1,99 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dmx {
+
+// Epilogues.  RESID variants: out = resid + gate[b] * y with the residual and
+// output stored as bf16 (B) or fp32 (F): RESID_BB, RESID_BF (bf16 in, fp32
+// out), RESID_FB (fp32 in, bf16 out).
+enum Epi { EPI_F32 = 0, EPI_MOD = 1, EPI_RESID_BB = 2, EPI_GEGLU = 3, EPI_RESID_BF = 4, EPI_RESID_FB = 5 };
+
+// A-operand sources of the GEMM (see dmx_gemm.hip).
+enum ASrc { A_GLOBAL = 0, A_NORM_B = 1, A_NORM_F = 2 };
+
+// Skinny GEMM y[m][n] = sum_k A[m][k] * W[n][k] with a fused epilogue.
+struct GemmArgs {
+  const uint16_t* A;  // A_GLOBAL: [M][K] bf16
+  const uint16_t* xb; // A_NORM_B: bf16 residual rows [M][1024]
+  const float* xf;    // A_NORM_F: fp32 residual rows [M][1024]
+  const float* nmod;  // A_NORM_*: modulation [B][3][1024] (scale | shift | gate)
+  const uint16_t* W;  // weight rows of K bf16
+  int M, K;
+  int ntiles;         // grid = ntiles work-groups
+  int T;              // tokens per request: row m belongs to request m / T
+  int wrow_up;        // GEGLU: W row of the first "up" feature
+  float* out_f32;     // EPI_F32 / EPI_MOD / EPI_RESID_BF output
+  uint16_t* out_bf16; // EPI_RESID_BB / EPI_RESID_FB / EPI_GEGLU output
+  int ldo;            // row stride of the output (and of resid)
+  const uint16_t* bias;    // EPI_MOD: per-feature bias
+  const float* gate;       // EPI_RESID_*: gate of request b at gate + b * gate_stride
+  int gate_stride;
+  const uint16_t* resid;   // EPI_RESID_B*: bf16 residual, same layout as the output
+  const float* resid_f32;  // EPI_RESID_FB: fp32 residual
+};
+
+// Gemm shape presets (host picks one per projection).
+enum GemmKind {
+  GEMM_MOD = 0,             // N = 3072, K = 1024, + bias, fp32 out
+  GEMM_QKV1024 = 1,         // N = 4096, K = 1024, fp32 out, A given
+  GEMM_QKV1024_NORM = 2,    // as above with the AdaRMS prenorm of bf16 x fused
+  GEMM_QKV2560 = 3,         // N = 4096, K = 2560, fp32 out
+  GEMM_OPROJ = 4,           // N = 1024, K = 2048, gated residual (bf16 -> bf16)
+  GEMM_OPROJ_F32 = 5,       // as GEMM_OPROJ, fp32 output (layer-internal residual)
+  GEMM_GATEUP = 6,          // N = 2 x 4096, K = 1024, GEGLU, A given
+  GEMM_GATEUP_NORM_F32 = 7, // as above with the AdaRMS prenorm of fp32 x1 fused
+  GEMM_DOWN = 8,            // N = 1024, K = 4096, gated residual (bf16 -> bf16)
+  GEMM_DOWN_F32RES = 9,     // as GEMM_DOWN, fp32 residual input
+};
+int gemm_config(GemmKind kind, GemmArgs& a);
+hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s);
+
+// Several modulation GEMVs in one launch: out_j[b] = W_j cond_j[b] + bias_j.
+struct ModJob {
+  const uint16_t* w;     // [3072][1024]
+  const uint16_t* bias;  // [3072]
+  const uint16_t* cond;  // [B][1024]
+  float* out;            // [B][3072]
+};
+constexpr int kMaxModJobs = 40;
+struct ModBatch {
+  ModJob job[kMaxModJobs];
+  int n, B;
+};
+hipError_t launch_mod_multi(const ModBatch& mb, hipStream_t s);
+
+hipError_t launch_adarms_norm(const uint16_t* x, const float* mod, int M, int T, uint16_t* xn,
+                              hipStream_t s);
+hipError_t launch_adarms_norm_f32(const float* x, const float* mod, int M, int T, uint16_t* xn,
+                                  hipStream_t s);
+
+hipError_t launch_qknorm_rope(const float* raw, const uint16_t* qn_w, const uint16_t* kn_w,
+                              const int32_t* pos0, float base, int M, int T, uint16_t* q,
+                              uint16_t* k, uint16_t* v, int kv_rows, int kv_row0, hipStream_t s);
+
+struct AttnArgs {
+  const uint16_t *q, *ks, *vs, *kp, *vp;
+  // fused path: when raw != nullptr, q / ks / vs are ignored and built from the
+  // raw fp32 QKV projection [B*C][4096] with QK-norm (1 + w) and RoPE at
+  // pos0[b] + t, base rope_base
+  const float* raw;
+  const uint16_t *qn_w, *kn_w;
+  const int32_t* pos0;
+  float rope_base;
+  const uint8_t* mask;
+  int B, C, P;
+  int S;        // prefix splits; split index S holds the suffix keys
+  int kps;      // prefix keys per split (multiple of 32)
+  int R16;      // stacked query rows (2 * C) rounded up to 16
+  uint16_t* part_o;  // [B][HK][S + 1][R16][D] bf16, normalised partial outputs
+  float* part_ml;    // [B][HK][S + 1][R16][2] running max (log2 domain) and sum
+};
+void attn_config(int B, int C, int P, AttnArgs& a);
+hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace dmx

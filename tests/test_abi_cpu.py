@@ -1,0 +1,96 @@
+"""CPU-side checks of the C ABI: the library loads and exports every entry
+point that include/dmx.h declares; the host bucket rule equals the oracle's
+bit for bit over every length; argument validation fails before any launch."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def dmx():
+    import masked_gqa_attention_action_amd as m
+    m.lib()
+    return m
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dmx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmx_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(dmx):
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(dmx.lib(), n), n
+    assert set(names) == set(dmx.EXPORTED)
+
+
+@pytest.mark.parametrize("buckets,cap,mt", [
+    ((576, 704, 768, 896, 1024), 1024, 0), ((576, 704, 768, 896, 1024), 1024, 650), ((2048,), 2048, 0),
+    ((576, 704), 1024, 0), ((576, 704, 768, 896, 1024), 2048, 0), ((704, 576), 1024, 0), ((), 1024, 0),
+    ((576, 2048), 1024, 0), ((1, 2, 3), 3, 2), ((576, 576), 1024, 0), ((0, 576), 1024, 0),
+])
+def test_bucket_rule_bit_exact_against_oracle(dmx, buckets, cap, mt):
+    for ln in range(-3, cap + 100):
+        assert dmx.select_bucket(ln, buckets, cap, mt) == orc.select_bucket(ln, buckets, cap, mt), (ln, buckets)
+    for cap2, mt2 in ((0, 0), (cap, -1)):
+        assert dmx.select_bucket(10, buckets, cap2, mt2) == orc.select_bucket(10, buckets, cap2, mt2)
+
+
+def test_workspace_sizes(dmx):
+    assert dmx.workspace_bytes(1, 50, 1024) > 0
+    assert dmx.workspace_bytes(16, 50, 1024) > dmx.workspace_bytes(1, 50, 1024)
+    assert dmx.workspace_bytes(1, 2048, 0) >= 2048 * 4096 * 4
+    assert dmx.workspace_bytes(0, 50, 1024) == 0
+    assert dmx.workspace_bytes(1, 0, 1024) == 0
+    assert dmx.workspace_bytes(1, 50, -1) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+ODD = ctypes.c_void_p(0x10001)
+
+
+def test_validation_errors_before_launch(dmx):
+    L = dmx.lib()
+    st = L.dmx_adarms_prenorm(None, FAKE, FAKE, FAKE, 1, 50, FAKE, FAKE, None)
+    assert st == dmx.ERR_INVALID_ARG and b"x is null" in L.dmx_last_error_string()
+    assert L.dmx_adarms_prenorm(ODD, FAKE, FAKE, FAKE, 1, 50, FAKE, FAKE, None) == dmx.ERR_MISALIGNED
+    assert L.dmx_adarms_prenorm(FAKE, FAKE, FAKE, FAKE, 0, 50, FAKE, FAKE, None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_qkv_qknorm_rope(FAKE, FAKE, FAKE, FAKE, 1, 50, 2048, FAKE, 10000.0, FAKE, FAKE, FAKE, 50, 0,
+                                 FAKE, 1 << 30, None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_qkv_qknorm_rope(FAKE, FAKE, FAKE, FAKE, 1, 50, 1024, FAKE, 10000.0, FAKE, FAKE, FAKE, 60, 20,
+                                 FAKE, 1 << 30, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_qkv_qknorm_rope(FAKE, FAKE, FAKE, FAKE, 1, 50, 1024, FAKE, 10000.0, FAKE, FAKE, FAKE, 50, 0,
+                                 FAKE, 1024, None) == dmx.ERR_WORKSPACE
+    assert L.dmx_suffix_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 65, 1024, FAKE, FAKE, 1 << 30,
+                                  None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_suffix_attention(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 50, 1024, FAKE, FAKE, 1 << 30,
+                                  None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_suffix_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 50, 5000, FAKE, FAKE, 1 << 30,
+                                  None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_oproj_gated_residual(FAKE, FAKE, FAKE, FAKE, 1, 50, FAKE, None, 1 << 30,
+                                      None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_geglu_mlp(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 50, FAKE, FAKE, 1 << 30, None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_suffix_layer_forward(None, None, FAKE, FAKE, FAKE, 1, 50, FAKE, FAKE, 1 << 30,
+                                      None) == dmx.ERR_INVALID_ARG
+    lw = dmx.LayerWeights(*([0x10000] * 9 + [0x10008]))
+    kv = dmx.PrefixKV(0x10000, 0x10000, 0x10000, 1024)
+    assert L.dmx_suffix_layer_forward(ctypes.byref(lw), ctypes.byref(kv), FAKE, FAKE, FAKE, 1, 50, FAKE, FAKE,
+                                      1 << 30, None) == dmx.ERR_MISALIGNED
+    assert b"w_down" in L.dmx_last_error_string()
+    g = ctypes.c_void_p()
+    assert L.dmx_stack_graph_create(None, FAKE, ctypes.byref(g)) == dmx.ERR_INVALID_ARG
+    assert L.dmx_graph_launch(None, None) == dmx.ERR_INVALID_ARG
+    L.dmx_graph_destroy(None)
+    for s in (0, 1, -1, -2, -3, -4, -5, -6, -7, -99):
+        assert L.dmx_status_string(s)
