@@ -53,7 +53,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // Workspace carve-up.  Everything a layer needs between its stages, plus
 // (for a stack) the modulation vectors of every layer of one step.
 struct WsLayout {
-  size_t mod1, mod2, xn, qkv, q, ks, vs, ctx, x1, h, part_o, part_ml, stack_mod, total;
+  size_t mod1, mod2, xn, qkv, q, ks, vs, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
   AttnArgs attn;
 };
 
@@ -76,12 +76,15 @@ bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
   L.ks = take((size_t)B * kHK * T * kD * 2);
   L.vs = take((size_t)B * kHK * T * kD * 2);
   L.ctx = take(M * kHQ * kD * 2);
-  L.x1 = take(M * kH * 4);  // fp32 residual between the two halves of a layer
+  L.x1 = take(M * kH * 4);   // fp32 residual between the two halves of a layer
+  L.x1s = take(M * kH * 2);  // bf16(x1 * (1 + scale2)), the gate-up A operand
   L.h = take(M * kI * 2);
   attn_config(B, T, P, L.attn);
   const size_t prow = (size_t)B * kHK * (L.attn.S + 1) * L.attn.R16;
   L.part_o = take(prow * kD * 2);
   L.part_ml = take(prow * 2 * 4);
+  L.ss_a = take(M * kSsParts * 4);  // row sums of squares of x1, one per O-projection tile
+  L.ss_b = take(M * kSsParts * 4);  // ... of a layer input (row pass or the down tiles)
   L.stack_mod = take((size_t)n_layers * 2 * B * 3 * kH * 4);
   L.total = off;
   return true;
@@ -212,29 +215,37 @@ int enq_geglu(const dmx_bf16* xn2, const dmx_bf16* w_gu, const dmx_bf16* w_down,
   return enq_resid_gemm(GEMM_DOWN, at<uint16_t>(ws, L.h), w_down, mod2, resid, nullptr, B, T, out, nullptr, s);
 }
 
-// The fused layer chain (modulation vectors mod1 / mod2 already computed):
-//   QKV GEMM with AdaRMS #1 prologue -> attention with QK-norm + RoPE on load
-//   -> combine -> O-projection + gated residual (fp32 x1) -> gate-up GEMM with
-//   AdaRMS #2 prologue + GEGLU -> down projection + gated residual.
+// The fused layer chain (modulation vectors mod1 / mod2 already computed,
+// the workspace's ss_b holding the row sums of squares of x_in, 64 per row):
+//   QKV GEMM with AdaRMS #1 fused -> attention with QK-norm + RoPE on load ->
+//   combine -> O-projection + gated residual (fp32 x1, bf16(x1 * (1 + scale2)),
+//   row sums of squares of x1) -> gate-up GEMM with AdaRMS #2 fused + GEGLU ->
+//   down projection +
+//   gated residual (row sums of squares of the output, for the next layer).
 int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
-                    const int32_t* pos0, int B, int C, dmx_bf16* x_out, const float* mod1, const float* mod2,
-                    void* ws, const WsLayout& L, hipStream_t s) {
+                    const int32_t* pos0, int B, int C, dmx_bf16* x_out,
+                    const float* mod1, const float* mod2, void* ws, const WsLayout& L, hipStream_t s) {
   float* raw = at<float>(ws, L.qkv);
   dmx_bf16* ctx = at<dmx_bf16>(ws, L.ctx);
   float* x1 = at<float>(ws, L.x1);
+  dmx_bf16* x1s = at<dmx_bf16>(ws, L.x1s);
   dmx_bf16* h = at<dmx_bf16>(ws, L.h);
+  float* ss_a = at<float>(ws, L.ss_a);
+  float* ss_b = at<float>(ws, L.ss_b);
   const int M = B * C;
 
   GemmArgs g = gemm_args();
-  gemm_config(GEMM_QKV1024_NORM, g);
+  gemm_config(GEMM_QKV1024_MOD, g);
   g.xb = x_in;
   g.nmod = mod1;
+  g.ss_in = ss_b;
+  g.ss_in_n = kSsParts;
   g.W = w->w_qkv;
   g.M = M;
   g.T = C;
   g.out_f32 = raw;
   g.ldo = kQKV;
-  DMX_TRY(hip_check(launch_gemm(GEMM_QKV1024_NORM, g, s), "QKV GEMM launch"));
+  DMX_TRY(hip_check(launch_gemm(GEMM_QKV1024_MOD, g, s), "QKV GEMM launch"));
 
   AttnArgs a = attn_args(L, ws);
   a.raw = raw;
@@ -246,22 +257,52 @@ int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const d
   a.mask = kv->mask;
   DMX_TRY(hip_check(launch_attention(a, ctx, s), "attention launch"));
 
-  // x1 = x + gate1 * (ctx W_o^T), kept in fp32
-  DMX_TRY(enq_resid_gemm(GEMM_OPROJ_F32, ctx, w->w_o, mod1, x_in, nullptr, B, C, nullptr, x1, s));
+  // x1 = x + gate1 * (ctx W_o^T): fp32, the scaled bf16 copy and row sums of squares
+  g = gemm_args();
+  gemm_config(GEMM_OPROJ_F32, g);
+  g.A = ctx;
+  g.W = w->w_o;
+  g.M = M;
+  g.T = C;
+  g.out_f32 = x1;
+  g.out_bf16 = x1s;
+  g.xs_scale = mod2;
+  g.ldo = kH;
+  g.gate = mod1 + 2 * kH;
+  g.gate_stride = 3 * kH;
+  g.resid = x_in;
+  g.ss_out = ss_a;
+  g.ss_out_n = kSsParts;
+  DMX_TRY(hip_check(launch_gemm(GEMM_OPROJ_F32, g, s), "O-projection launch"));
 
   g = gemm_args();
-  gemm_config(GEMM_GATEUP_NORM_F32, g);
-  g.xf = x1;
+  gemm_config(GEMM_GATEUP_MOD, g);
+  g.xb = x1s;
   g.nmod = mod2;
+  g.ss_in = ss_a;
+  g.ss_in_n = kSsParts;
   g.W = w->w_gu;
   g.M = M;
   g.T = C;
   g.out_bf16 = h;
   g.ldo = kI;
-  DMX_TRY(hip_check(launch_gemm(GEMM_GATEUP_NORM_F32, g, s), "gate-up GEMM launch"));
+  DMX_TRY(hip_check(launch_gemm(GEMM_GATEUP_MOD, g, s), "gate-up GEMM launch"));
 
-  // out = x1 + gate2 * (GEGLU(xn2) W_down^T)
-  return enq_resid_gemm(GEMM_DOWN_F32RES, h, w->w_down, mod2, nullptr, x1, B, C, x_out, nullptr, s);
+  // out = x1 + gate2 * (GEGLU(xn2) W_down^T), plus its row sums of squares
+  g = gemm_args();
+  gemm_config(GEMM_DOWN_F32RES, g);
+  g.A = h;
+  g.W = w->w_down;
+  g.M = M;
+  g.T = C;
+  g.out_bf16 = x_out;
+  g.ldo = kH;
+  g.gate = mod2 + 2 * kH;
+  g.gate_stride = 3 * kH;
+  g.resid_f32 = x1;
+  g.ss_out = ss_b;
+  g.ss_out_n = kSsParts;
+  return hip_check(launch_gemm(GEMM_DOWN_F32RES, g, s), "down projection launch");
 }
 
 int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
@@ -271,6 +312,7 @@ int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf1
   float* mod2 = at<float>(ws, L.mod2);
   const ModJob jobs[2] = {{w->w_mod1, w->b_mod1, cond, mod1}, {w->w_mod2, w->b_mod2, cond, mod2}};
   DMX_TRY(enq_mods(jobs, 2, B, s));
+  DMX_TRY(hip_check(launch_row_ssq(x_in, B * C, at<float>(ws, L.ss_b), s), "row statistics launch"));
   return enq_layer_chain(w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, L, s);
 }
 
@@ -477,44 +519,29 @@ static int check_stack(const char* fn, const dmx_stack_desc* d, WsLayout& L) {
   return check_ws(fn, d->ws, d->ws_bytes, d->batch, d->chunk, d->p_bucket, L, d->n_layers);
 }
 
-// One pass of the stack.  With a side stream (graph capture), the modulation
-// vectors of layer l + 1 are computed on it while layer l runs on `s`; layer
-// l + 1 waits for them through an event.  Without one, everything runs on `s`.
-static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, hipStream_t side,
-                     hipEvent_t* ev) {
+// One pass of the stack.  Per step, one launch computes the modulation
+// vectors of every layer (they depend only on the step's conditioning), then
+// the layers run their fused chains.
+static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) {
   const int B = d->batch, NL = d->n_layers;
   float* mods = at<float>(d->ws, L.stack_mod);
   auto mod_of = [&](int l, int which) { return mods + ((size_t)l * 2 + which) * B * 3 * kH; };
+  ModJob jobs[2 * DMX_MAX_LAYERS];
   for (int st = 0; st < d->n_steps; ++st) {
     const dmx_bf16* cond = d->cond + (size_t)st * B * kH;
-    auto jobs_of = [&](int l, ModJob* j) {
-      j[0] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, mod_of(l, 0)};
-      j[1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, mod_of(l, 1)};
-    };
-    ModJob j[2];
-    jobs_of(0, j);
-    DMX_TRY(enq_mods(j, 2, B, s));
-    if (side) {
-      DMX_TRY(hip_check(hipEventRecord(ev[0], s), "hipEventRecord"));
-      DMX_TRY(hip_check(hipStreamWaitEvent(side, ev[0], 0), "hipStreamWaitEvent"));
-      for (int l = 1; l < NL; ++l) {
-        jobs_of(l, j);
-        DMX_TRY(enq_mods(j, 2, B, side));
-        DMX_TRY(hip_check(hipEventRecord(ev[l], side), "hipEventRecord"));
-      }
-    }
     for (int l = 0; l < NL; ++l) {
-      if (l > 0) {
-        if (side) {
-          DMX_TRY(hip_check(hipStreamWaitEvent(s, ev[l], 0), "hipStreamWaitEvent"));
-        } else {
-          jobs_of(l, j);
-          DMX_TRY(enq_mods(j, 2, B, s));
-        }
-      }
+      jobs[2 * l] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, mod_of(l, 0)};
+      jobs[2 * l + 1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, mod_of(l, 1)};
+    }
+    DMX_TRY(enq_mods(jobs, 2 * NL, B, s));
+    // row statistics of x: a row pass for the first layer of the run, after
+    // that the down projection of the layer before
+    if (st == 0)
+      DMX_TRY(hip_check(launch_row_ssq(d->x, B * d->chunk, at<float>(d->ws, L.ss_b), s), "row statistics launch"));
+    for (int l = 0; l < NL; ++l) {
       dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
-      DMX_TRY(enq_layer_chain(&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1),
-                              d->ws, L, s));
+      DMX_TRY(enq_layer_chain(&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1), d->ws,
+                              L, s));
     }
   }
   return DMX_OK;
@@ -523,7 +550,7 @@ static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, 
 int dmx_stack_forward(const dmx_stack_desc* d, void* stream) {
   WsLayout L;
   DMX_TRY(check_stack("dmx_stack_forward", d, L));
-  return enq_stack(d, L, (hipStream_t)stream, nullptr, nullptr);
+  return enq_stack(d, L, (hipStream_t)stream);
 }
 
 int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** out) {
@@ -534,27 +561,15 @@ int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** ou
   WsLayout L;
   DMX_TRY(check_stack(fn, d, L));
   hipStream_t s = (hipStream_t)stream;
-  // capture-time helpers: a side stream at the default priority and one event per layer
-  hipStream_t side = nullptr;
-  DMX_TRY(hip_check(hipStreamCreateWithFlags(&side, hipStreamNonBlocking), "hipStreamCreate"));
-  hipEvent_t ev[DMX_MAX_LAYERS];
-  int nev = 0;
-  int st = DMX_OK;
-  for (; nev < d->n_layers && st == DMX_OK; ++nev)
-    st = hip_check(hipEventCreateWithFlags(&ev[nev], hipEventDisableTiming), "hipEventCreate");
   hipGraph_t g = nullptr;
+  int st = hip_check(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
   if (st == DMX_OK) {
-    st = hip_check(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
-    if (st == DMX_OK) {
-      st = enq_stack(d, L, s, side, ev);
-      const hipError_t ce = hipStreamEndCapture(s, &g);
-      if (st == DMX_OK) st = hip_check(ce, "hipStreamEndCapture");
-    }
+    st = enq_stack(d, L, s);
+    const hipError_t ce = hipStreamEndCapture(s, &g);
+    if (st == DMX_OK) st = hip_check(ce, "hipStreamEndCapture");
   }
   hipGraphExec_t e = nullptr;
   if (st == DMX_OK) st = hip_check(hipGraphInstantiate(&e, g, nullptr, nullptr, 0), "hipGraphInstantiate");
-  for (int i = 0; i < nev; ++i) (void)hipEventDestroy(ev[i]);
-  (void)hipStreamDestroy(side);
   if (st != DMX_OK) {
     if (g) (void)hipGraphDestroy(g);
     return st;

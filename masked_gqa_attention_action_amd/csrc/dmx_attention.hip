@@ -53,86 +53,85 @@ __device__ __forceinline__ void rope_sincos(double pos, double f, float& sn, flo
 // Q fragments of one stacked query row built from the raw fp32 projection:
 // lane (lr, lq) holds dims lq*8 + ks*32 + e (ks < 8, e < 8) of its row, which
 // includes both halves (ks and ks + 4) of every rotation pair it touches.
-__device__ __forceinline__ void q_from_raw(const AttnArgs& a, const double* ftab, int b, int i, int head, bool ok,
-                                           int lq, bf16x8 qf[8]) {
-  float u[8][8];
+struct QRaw {
+  float4 x[8][2];
+};
+
+__device__ __forceinline__ void q_load(const AttnArgs& a, int b, int i, int head, int lq, QRaw& q) {
   const float* src = a.raw + (size_t)(b * a.C + i) * kQKV + head * kD + lq * 8;
-  float w[8][8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    if (ok) {
-      const float4 x0 = *reinterpret_cast<const float4*>(src + ks * 32);
-      const float4 x1 = *reinterpret_cast<const float4*>(src + ks * 32 + 4);
-      u[ks][0] = x0.x; u[ks][1] = x0.y; u[ks][2] = x0.z; u[ks][3] = x0.w;
-      u[ks][4] = x1.x; u[ks][5] = x1.y; u[ks][6] = x1.z; u[ks][7] = x1.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) u[ks][e] = 0.f;
-    }
-    const uint4 wr = *reinterpret_cast<const uint4*>(a.qn_w + lq * 8 + ks * 32);
-    const uint32_t ww[4] = {wr.x, wr.y, wr.z, wr.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[ks][2 * e] = 1.f + bf2f((uint16_t)(ww[e] & 0xffffu));
-      w[ks][2 * e + 1] = 1.f + bf2f((uint16_t)(ww[e] >> 16));
-    }
+    q.x[ks][0] = *reinterpret_cast<const float4*>(src + ks * 32);
+    q.x[ks][1] = *reinterpret_cast<const float4*>(src + ks * 32 + 4);
   }
+}
+
+__device__ __forceinline__ void q_finish(const AttnArgs& a, const double* ftab, const uint16_t* qn, const QRaw& q,
+                                         int b, int i, bool ok, int lq, bf16x8 qf[8]) {
   float ss = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += u[ks][e] * u[ks][e];
+  for (int ks = 0; ks < 8; ++ks) {
+    const float4 x0 = q.x[ks][0], x1 = q.x[ks][1];
+    ss += x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w + x1.x * x1.x + x1.y * x1.y + x1.z * x1.z +
+          x1.w * x1.w;
+  }
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
   const float rn = 1.0f / sqrtf(ss * (1.0f / kD) + kEps);
   const double pos = (double)a.pos0[b] + (double)i;
+  // rotation pairs: dims lq*8 + ks*32 + e (ks < 4) and the same + 128 (ks + 4)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    const float lo[8] = {q.x[ks][0].x, q.x[ks][0].y, q.x[ks][0].z, q.x[ks][0].w,
+                         q.x[ks][1].x, q.x[ks][1].y, q.x[ks][1].z, q.x[ks][1].w};
+    const float hi[8] = {q.x[ks + 4][0].x, q.x[ks + 4][0].y, q.x[ks + 4][0].z, q.x[ks + 4][0].w,
+                         q.x[ks + 4][1].x, q.x[ks + 4][1].y, q.x[ks + 4][1].z, q.x[ks + 4][1].w};
+    const uint4 wl4 = *reinterpret_cast<const uint4*>(qn + lq * 8 + ks * 32);
+    const uint4 wh4 = *reinterpret_cast<const uint4*>(qn + 128 + lq * 8 + ks * 32);
+    const uint32_t wl[4] = {wl4.x, wl4.y, wl4.z, wl4.w}, wh[4] = {wh4.x, wh4.y, wh4.z, wh4.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float sn, cs;
       rope_sincos(pos, ftab[lq * 8 + ks * 32 + e], sn, cs);
-      const float x0 = u[ks][e] * rn * w[ks][e];
-      const float x1 = u[ks + 4][e] * rn * w[ks + 4][e];
-      u[ks][e] = x0 * cs - x1 * sn;
-      u[ks + 4][e] = x1 * cs + x0 * sn;
+      const float w0 = 1.f + bf2f((uint16_t)((e & 1) ? (wl[e >> 1] >> 16) : (wl[e >> 1] & 0xffffu)));
+      const float w1 = 1.f + bf2f((uint16_t)((e & 1) ? (wh[e >> 1] >> 16) : (wh[e >> 1] & 0xffffu)));
+      const float x0 = lo[e] * rn * w0, x1 = hi[e] * rn * w1;
+      qf[ks][e] = ok ? (short)f2bf(x0 * cs - x1 * sn) : (short)0;
+      qf[ks + 4][e] = ok ? (short)f2bf(x1 * cs + x0 * sn) : (short)0;
     }
   }
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[ks][e] = ok ? (short)f2bf(u[ks][e]) : (short)0;
 }
 
 // Suffix keys of one 32-key block built from the raw projection into LDS:
 // thread t handles key j = t / 16 and dims d0 = (t % 16) * 8 .. +7 plus their
 // rotation partners d0 + 128 (K), and the 16 V dims (t % 16) * 16 .. +15.
-__device__ __forceinline__ void suffix_kv_from_raw(const AttnArgs& a, const double* ftab, int b, int g, int kb0,
-                                                   const int* vis, uint16_t* sK, uint16_t* sVt) {
+struct SufRaw {
+  float4 k[4], v[4];
+};
+
+__device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int kb0, SufRaw& r) {
+  const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
+  const int key = min(kb0 + j, a.C - 1);  // rows past the chunk read a valid row and are zeroed later
+  const float* row = a.raw + (size_t)(b * a.C + key) * kQKV;
+  const float* kr = row + (kHQ + g) * kD;
+  r.k[0] = *reinterpret_cast<const float4*>(kr + c * 8);
+  r.k[1] = *reinterpret_cast<const float4*>(kr + c * 8 + 4);
+  r.k[2] = *reinterpret_cast<const float4*>(kr + 128 + c * 8);
+  r.k[3] = *reinterpret_cast<const float4*>(kr + 128 + c * 8 + 4);
+  const float* vr = row + (kHQ + kHK + g) * kD + c * 16;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) r.v[q4] = *reinterpret_cast<const float4*>(vr + q4 * 4);
+}
+
+__device__ __forceinline__ void suffix_store(const AttnArgs& a, const double* ftab, const uint16_t* kn, const SufRaw& r,
+                                             int b, int kb0, const int* vis, uint16_t* sK, uint16_t* sVt) {
   const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int key = kb0 + j;
   const bool ok = vis[j] != 0;
-  const float* row = a.raw + (size_t)(b * a.C + (ok ? key : 0)) * kQKV;
-  float lo[8], hi[8], vv[16];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) lo[e] = hi[e] = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) vv[e] = 0.f;
-  if (ok) {
-    const float* kr = row + (kHQ + g) * kD;
-    const float4 a0 = *reinterpret_cast<const float4*>(kr + c * 8);
-    const float4 a1 = *reinterpret_cast<const float4*>(kr + c * 8 + 4);
-    const float4 b0 = *reinterpret_cast<const float4*>(kr + 128 + c * 8);
-    const float4 b1 = *reinterpret_cast<const float4*>(kr + 128 + c * 8 + 4);
-    lo[0] = a0.x; lo[1] = a0.y; lo[2] = a0.z; lo[3] = a0.w; lo[4] = a1.x; lo[5] = a1.y; lo[6] = a1.z; lo[7] = a1.w;
-    hi[0] = b0.x; hi[1] = b0.y; hi[2] = b0.z; hi[3] = b0.w; hi[4] = b1.x; hi[5] = b1.y; hi[6] = b1.z; hi[7] = b1.w;
-    const float* vr = row + (kHQ + kHK + g) * kD + c * 16;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 t = *reinterpret_cast<const float4*>(vr + q4 * 4);
-      vv[q4 * 4] = t.x; vv[q4 * 4 + 1] = t.y; vv[q4 * 4 + 2] = t.z; vv[q4 * 4 + 3] = t.w;
-    }
-  }
+  const float lo[8] = {r.k[0].x, r.k[0].y, r.k[0].z, r.k[0].w, r.k[1].x, r.k[1].y, r.k[1].z, r.k[1].w};
+  const float hi[8] = {r.k[2].x, r.k[2].y, r.k[2].z, r.k[2].w, r.k[3].x, r.k[3].y, r.k[3].z, r.k[3].w};
+  const uint4 wlo = *reinterpret_cast<const uint4*>(kn + c * 8), whi = *reinterpret_cast<const uint4*>(kn + 128 + c * 8);
+  const uint32_t wl[4] = {wlo.x, wlo.y, wlo.z, wlo.w}, wh[4] = {whi.x, whi.y, whi.z, whi.w};
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
@@ -140,55 +139,61 @@ __device__ __forceinline__ void suffix_kv_from_raw(const AttnArgs& a, const doub
   for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
   const float rn = 1.0f / sqrtf(ss * (1.0f / kD) + kEps);
   const double pos = (double)a.pos0[b] + (double)key;
-  uint16_t ko[8], kh[8];
+  uint32_t ko[4], kh[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = c * 8 + e;
-    float sn, cs;
-    rope_sincos(pos, ftab[d], sn, cs);
-    const float x0 = lo[e] * rn * (1.f + bf2f(a.kn_w[d]));
-    const float x1 = hi[e] * rn * (1.f + bf2f(a.kn_w[d + 128]));
-    ko[e] = ok ? f2bf(x0 * cs - x1 * sn) : (uint16_t)0;
-    kh[e] = ok ? f2bf(x1 * cs + x0 * sn) : (uint16_t)0;
+  for (int e2 = 0; e2 < 4; ++e2) {
+    float o0[2], o1[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * e2 + h;
+      float sn, cs;
+      rope_sincos(pos, ftab[c * 8 + e], sn, cs);
+      const float w0 = 1.f + bf2f((uint16_t)(h ? (wl[e2] >> 16) : (wl[e2] & 0xffffu)));
+      const float w1 = 1.f + bf2f((uint16_t)(h ? (wh[e2] >> 16) : (wh[e2] & 0xffffu)));
+      const float x0 = lo[e] * rn * w0, x1 = hi[e] * rn * w1;
+      o0[h] = ok ? x0 * cs - x1 * sn : 0.f;
+      o1[h] = ok ? x1 * cs + x0 * sn : 0.f;
+    }
+    ko[e2] = pack2(o0[0], o0[1]);
+    kh[e2] = pack2(o1[0], o1[1]);
   }
-  uint4 p0, p1;
-  p0.x = ko[0] | ((uint32_t)ko[1] << 16); p0.y = ko[2] | ((uint32_t)ko[3] << 16);
-  p0.z = ko[4] | ((uint32_t)ko[5] << 16); p0.w = ko[6] | ((uint32_t)ko[7] << 16);
-  p1.x = kh[0] | ((uint32_t)kh[1] << 16); p1.y = kh[2] | ((uint32_t)kh[3] << 16);
-  p1.z = kh[4] | ((uint32_t)kh[5] << 16); p1.w = kh[6] | ((uint32_t)kh[7] << 16);
-  *reinterpret_cast<uint4*>(sK + j * KLD + c * 8) = p0;
-  *reinterpret_cast<uint4*>(sK + j * KLD + 128 + c * 8) = p1;
+  *reinterpret_cast<uint4*>(sK + j * KLD + c * 8) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+  *reinterpret_cast<uint4*>(sK + j * KLD + 128 + c * 8) = make_uint4(kh[0], kh[1], kh[2], kh[3]);
+  const float vv[16] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w,
+                        r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w, r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) sVt[(c * 16 + e) * VLD + j] = f2bf(vv[e]);
+  for (int e = 0; e < 16; ++e) sVt[(c * 16 + e) * VLD + j] = ok ? f2bf(vv[e]) : (uint16_t)0;
 }
 
 // K / V rows (bf16, from global) of one 32-key block: thread t owns 16-byte
-// chunks t and t + 512 of the 32 x 32 chunk grid.  Invisible rows are not read.
+// chunks t and t + 512 of the 32 x 32 chunk grid.  Rows are read whether
+// visible or not (rows past the split's end read its last row); invisible rows
+// are replaced by zeros when staged, so their contents never reach the math.
 struct KVRegs {
   uint4 k[2], v[2];
 };
 
-__device__ __forceinline__ void kv_load(const uint16_t* Kb, const uint16_t* Vb, int kb0, const int* vis,
-                                        KVRegs& r) {
+__device__ __forceinline__ void kv_load(const uint16_t* Kb, const uint16_t* Vb, int kb0, int key_hi, KVRegs& r) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = threadIdx.x + h * 512;
     const int j = c >> 5, ch = c & 31;
-    r.k[h] = r.v[h] = make_uint4(0, 0, 0, 0);
-    if (vis[j]) {
-      r.k[h] = *reinterpret_cast<const uint4*>(Kb + (size_t)(kb0 + j) * kD + ch * 8);
-      r.v[h] = *reinterpret_cast<const uint4*>(Vb + (size_t)(kb0 + j) * kD + ch * 8);
-    }
+    const size_t row = (size_t)min(kb0 + j, key_hi - 1);
+    r.k[h] = *reinterpret_cast<const uint4*>(Kb + row * kD + ch * 8);
+    r.v[h] = *reinterpret_cast<const uint4*>(Vb + row * kD + ch * 8);
   }
 }
 
-__device__ __forceinline__ void kv_store(const KVRegs& r, uint16_t* sK, uint16_t* sVt) {
+__device__ __forceinline__ void kv_store(const KVRegs& r, const int* vis, uint16_t* sK, uint16_t* sVt) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = threadIdx.x + h * 512;
     const int j = c >> 5, ch = c & 31;
-    *reinterpret_cast<uint4*>(sK + j * KLD + ch * 8) = r.k[h];
-    const uint32_t w4[4] = {r.v[h].x, r.v[h].y, r.v[h].z, r.v[h].w};
+    const bool ok = vis[j] != 0;
+    const uint4 kk = ok ? r.k[h] : make_uint4(0, 0, 0, 0);
+    const uint4 vv = ok ? r.v[h] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(sK + j * KLD + ch * 8) = kk;
+    const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sVt[(ch * 8 + 2 * e) * VLD + j] = (uint16_t)(w4[e] & 0xffffu);
@@ -197,13 +202,17 @@ __device__ __forceinline__ void kv_store(const KVRegs& r, uint16_t* sK, uint16_t
   }
 }
 
+// One split of one (request, KV head): every global load of the split (mask,
+// query rows, both K/V blocks or the raw suffix rows) is issued up front, then
+// the blocks are staged through LDS and processed.
 template <bool FUSED>
-__global__ __launch_bounds__(512) void k_attn_partial(AttnArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_partial(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[KB * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * VLD];
   __shared__ __attribute__((aligned(16))) uint16_t sP[8][16 * PLD];
   __shared__ int sVis[kMaxKps];
   __shared__ double sF[kD / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t sNW[2][kD];  // q / k norm weights
 
   const int nsplit = a.S + 1;
   const int split = blockIdx.x % nsplit;
@@ -217,47 +226,61 @@ __global__ __launch_bounds__(512) void k_attn_partial(AttnArgs a) {
   const int key_lo = suffix ? 0 : split * a.kps;
   const int key_hi = suffix ? a.C : min(a.P, key_lo + a.kps);
   const int nkeys = key_hi - key_lo;
+  const int nblk = (nkeys + KB - 1) / KB;  // <= 2
   const size_t kv_rows = suffix ? (size_t)a.C : (size_t)a.P;
   const uint16_t* Kb = (suffix ? a.ks : a.kp) + (size_t)(b * kHK + g) * kv_rows * kD;
   const uint16_t* Vb = (suffix ? a.vs : a.vp) + (size_t)(b * kHK + g) * kv_rows * kD;
-
-  if (threadIdx.x < kMaxKps)
-    sVis[threadIdx.x] = threadIdx.x < nkeys && (suffix || a.mask[(size_t)b * a.P + key_lo + threadIdx.x] != 0);
-  if (FUSED) rope_table(sF, a.rope_base);
-  __syncthreads();
-
-  // first visible block of the prefix: start its loads before the Q prologue
-  const int nblk = (nkeys + KB - 1) / KB;
-  auto blk_any = [&](int bi) {
-    int any = 0;
-    for (int j = 0; j < KB; ++j) any |= sVis[bi * KB + j];
-    return any != 0;
-  };
-  auto next_blk = [&](int bi) {
-    while (bi < nblk && !blk_any(bi)) ++bi;
-    return bi;
-  };
-  KVRegs kv;
-  int cur = next_blk(0);
   const bool from_global = !(FUSED && suffix);
-  if (from_global && cur < nblk) kv_load(Kb, Vb, key_lo + cur * KB, sVis + cur * KB, kv);
 
-  // query fragments of this wave's row tile (wave w owns stacked rows 16w..16w+15)
+  // ---- load phase: everything this WG reads from global memory
   const int mt = wave;
   const bool active = mt < MT;
+  const int row = mt * 16 + lr;
+  const bool qok = active && (row < R);
+  const int hh = qok ? row / a.C : 0;
+  const int qi = qok ? row - hh * a.C : 0;
+  KVRegs kv[2];
+  SufRaw sr[2];
+  QRaw qr;
   bf16x8 qf[8];
-  {
-    const int row = mt * 16 + lr;
-    const bool ok = active && (row < R);
-    const int hh = ok ? row / a.C : 0;
-    const int i = ok ? row - hh * a.C : 0;
-    if (FUSED) {
-      q_from_raw(a, sF, b, i, kGroup * g + hh, ok, lq, qf);
-    } else {
-      const uint16_t* qp = a.q + ((size_t)(b * a.C + i) * kHQ + (kGroup * g + hh)) * kD + lq * 8;
+  int mvis = 0;
+  uint4 nw = make_uint4(0, 0, 0, 0);
+  if (FUSED && threadIdx.x >= 64 && threadIdx.x < 128) {
+    const int t = threadIdx.x - 64;  // 64 threads x 16 B = both 512-B weight vectors
+    nw = *reinterpret_cast<const uint4*>((t < 32 ? a.qn_w : a.kn_w) + (t & 31) * 8);
+  }
+  if (threadIdx.x < kMaxKps && threadIdx.x < nkeys)
+    mvis = suffix || a.mask[(size_t)b * a.P + key_lo + threadIdx.x] != 0;
+  if (from_global) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[ks] = ok ? load_bf16x8(qp + ks * 32) : zero_bf16x8();
-    }
+    for (int bi = 0; bi < 2; ++bi)
+      if (bi < nblk) kv_load(Kb, Vb, key_lo + bi * KB, key_hi, kv[bi]);
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+      if (bi < nblk) suffix_load(a, b, g, bi * KB, sr[bi]);
+  }
+  if (FUSED) {
+    q_load(a, b, qi, kGroup * g + hh, lq, qr);
+  } else {
+    const uint16_t* qp = a.q + ((size_t)(b * a.C + qi) * kHQ + (kGroup * g + hh)) * kD + lq * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 32);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- compute phase
+  if (threadIdx.x < kMaxKps) sVis[threadIdx.x] = mvis;
+  if (FUSED && threadIdx.x >= 64 && threadIdx.x < 128) {
+    const int t = threadIdx.x - 64;
+    *reinterpret_cast<uint4*>(&sNW[t >> 5][(t & 31) * 8]) = nw;
+  }
+  if (FUSED) rope_table(sF, a.rope_base);
+  __syncthreads();
+  if (FUSED) q_finish(a, sF, sNW[0], qr, b, qi, qok, lq, qf);
+  else if (!qok) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = zero_bf16x8();
   }
 
   f32x4 o[16];
@@ -272,15 +295,18 @@ __global__ __launch_bounds__(512) void k_attn_partial(AttnArgs a) {
   const float sl2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(head_dim)
   uint16_t* pt = &sP[wave][0];
 
-  while (cur < nblk) {
-    const int* vis = sVis + cur * KB;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    if (bi >= nblk) break;
+    const int* vis = sVis + bi * KB;
+    int any = 0;
+    for (int j = 0; j < KB; ++j) any |= vis[j];
+    if (!any) continue;  // uniform across the WG
     if (from_global)
-      kv_store(kv, sK, sVt);
+      kv_store(kv[bi], vis, sK, sVt);
     else
-      suffix_kv_from_raw(a, sF, b, g, cur * KB, vis, sK, sVt);
+      suffix_store(a, sF, sNW[1], sr[bi], b, bi * KB, vis, sK, sVt);
     __syncthreads();
-    const int nxt = next_blk(cur + 1);
-    if (from_global && nxt < nblk) kv_load(Kb, Vb, key_lo + nxt * KB, sVis + nxt * KB, kv);
     if (active) {
       const bool vis0 = vis[lr] != 0, vis1 = vis[16 + lr] != 0;
       f32x4 s0 = zero_f32x4(), s1 = zero_f32x4();
@@ -318,7 +344,6 @@ __global__ __launch_bounds__(512) void k_attn_partial(AttnArgs a) {
       }
     }
     __syncthreads();
-    cur = nxt;
   }
 
   // write this split's partial rows: running max, running sum, output / sum
@@ -326,8 +351,8 @@ __global__ __launch_bounds__(512) void k_attn_partial(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float l = group16_sum(lrun[r]);
-      const int row = mt * 16 + lq * 4 + r;
-      const size_t prow = ((size_t)bg * nsplit + split) * a.R16 + row;
+      const int prow_i = mt * 16 + lq * 4 + r;
+      const size_t prow = ((size_t)bg * nsplit + split) * a.R16 + prow_i;
       const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) a.part_o[prow * kD + dt * 16 + lr] = f2bf(o[dt][r] * inv);

@@ -22,16 +22,15 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
+// float -> bf16 bits with the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two floats -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
@@ -58,21 +57,37 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ float group16_sum(float v);
+
+// sum over the 64 lanes: DPP inside each 16-lane row, then across the 4 rows
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = group16_sum(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
   return v;
 }
 
-// reductions inside each aligned group of 16 lanes
+// Reductions inside each aligned row of 16 lanes with DPP row rotations (no
+// LDS crossbar traffic): after the four steps every lane of the row holds the
+// result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
 __device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = fmaxf(v, dpp_f<kRowRor1>(v));
+  v = fmaxf(v, dpp_f<kRowRor2>(v));
+  v = fmaxf(v, dpp_f<kRowRor4>(v));
+  v = fmaxf(v, dpp_f<kRowRor8>(v));
   return v;
 }
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_f<kRowRor1>(v);
+  v += dpp_f<kRowRor2>(v);
+  v += dpp_f<kRowRor4>(v);
+  v += dpp_f<kRowRor8>(v);
   return v;
 }
 

@@ -12,14 +12,20 @@ namespace dmx {
 enum Epi { EPI_F32 = 0, EPI_MOD = 1, EPI_RESID_BB = 2, EPI_GEGLU = 3, EPI_RESID_BF = 4, EPI_RESID_FB = 5 };
 
 // A-operand sources of the GEMM (see dmx_gemm.hip).
-enum ASrc { A_GLOBAL = 0, A_NORM_B = 1, A_NORM_F = 2 };
+enum ASrc { A_GLOBAL = 0, A_MOD = 1, A_MODPRE = 2 };
 
 // Skinny GEMM y[m][n] = sum_k A[m][k] * W[n][k] with a fused epilogue.
 struct GemmArgs {
   const uint16_t* A;  // A_GLOBAL: [M][K] bf16
-  const uint16_t* xb; // A_NORM_B: bf16 residual rows [M][1024]
-  const float* xf;    // A_NORM_F: fp32 residual rows [M][1024]
-  const float* nmod;  // A_NORM_*: modulation [B][3][1024] (scale | shift | gate)
+  const uint16_t* xb; // A_MOD: bf16 residual rows x [M][1024];
+                      // A_MODPRE: the rows already scaled, bf16(x * (1 + scale))
+  const float* nmod;  // A_MOD*: modulation [B][3][1024] (scale | shift | gate)
+  const float* ss_in; // A_MOD*: row sums of squares of x, [M][ss_in_n] partials
+  int ss_in_n;        //   a multiple of 4 up to 64
+  float* ss_out;      // EPI_RESID_BF / _FB: optional [M][ss_out_n] partials, one
+  int ss_out_n;       //   per N-tile of 16 features (ntiles == ss_out_n)
+  const float* xs_scale;  // EPI_RESID_BF: out_bf16 = bf16(out * (1 + xs_scale[b][n])),
+                          //   row b at xs_scale + b * gate_stride (null: bf16(out))
   const uint16_t* W;  // weight rows of K bf16
   int M, K;
   int ntiles;         // grid = ntiles work-groups
@@ -39,17 +45,21 @@ struct GemmArgs {
 enum GemmKind {
   GEMM_MOD = 0,             // N = 3072, K = 1024, + bias, fp32 out
   GEMM_QKV1024 = 1,         // N = 4096, K = 1024, fp32 out, A given
-  GEMM_QKV1024_NORM = 2,    // as above with the AdaRMS prenorm of bf16 x fused
+  GEMM_QKV1024_MOD = 2,     // as above with the AdaRMS prenorm of bf16 x fused
   GEMM_QKV2560 = 3,         // N = 4096, K = 2560, fp32 out
   GEMM_OPROJ = 4,           // N = 1024, K = 2048, gated residual (bf16 -> bf16)
   GEMM_OPROJ_F32 = 5,       // as GEMM_OPROJ, fp32 output (layer-internal residual)
   GEMM_GATEUP = 6,          // N = 2 x 4096, K = 1024, GEGLU, A given
-  GEMM_GATEUP_NORM_F32 = 7, // as above with the AdaRMS prenorm of fp32 x1 fused
+  GEMM_GATEUP_MOD = 7,      // as above with the AdaRMS prenorm of bf16 x1 fused
   GEMM_DOWN = 8,            // N = 1024, K = 4096, gated residual (bf16 -> bf16)
   GEMM_DOWN_F32RES = 9,     // as GEMM_DOWN, fp32 residual input
 };
 int gemm_config(GemmKind kind, GemmArgs& a);
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s);
+// Row sums of squares of bf16 rows [M][1024] as 64 partials of 16 columns,
+// the same values (and summation order) a down-projection epilogue writes.
+constexpr int kSsParts = 1024 / 16;
+hipError_t launch_row_ssq(const uint16_t* x, int M, float* ss, hipStream_t s);
 
 // Several modulation GEMVs in one launch: out_j[b] = W_j cond_j[b] + bias_j.
 struct ModJob {
