@@ -7,15 +7,21 @@
 //   kps consecutive prefix rows each; split S owns the chunk's own suffix keys.
 //   The 2 query heads that share KV head g are stacked into one tile of
 //   2*chunk query rows (row r: head 2g + r / chunk, token r % chunk), so every
-//   K/V row is read from HBM once per request.
-//   Keys stream through LDS in blocks of 32: K as [key][dim], V transposed to
-//   [dim][key] so both MFMA operands read 16 contiguous bytes per lane.
-//   QK^T and PV run on v_mfma_f32_16x16x32_bf16; row max / sum use cross-lane
-//   shuffles inside each 16-lane row group; the softmax runs in the log2
-//   domain.  A block whose 32 keys are all invisible is skipped without
-//   reading its K/V; invisible keys inside a block are zero-filled in LDS and
-//   their logits replaced by -inf (selection, never multiplication), so masked
-//   rows may hold anything, NaN included.
+//   K/V row is read from HBM once per request; wave w owns stacked rows
+//   16w .. 16w+15.
+//   All K/V blocks (32 keys) of the split are staged row-major in LDS at once.
+//   The products run transposed on v_mfma_f32_16x16x32_bf16:
+//     S^T = K Q^T   (A = K rows from LDS, B = the wave's query fragments),
+//     O^T = V^T P^T (A = V^T through the gfx950 LDS transpose read, B = P^T
+//                    straight from the S^T accumulators: each lane holds keys
+//                    4q..4q+3 and 16+4q..16+4q+3 of its row, and V^T is read
+//                    with the same key order, so P never leaves registers).
+//   Each lane therefore owns one query row: the online-softmax rescale is one
+//   scalar per lane, and the output dims 16t + 4q .. +3 go out as 8-byte
+//   stores.  The softmax runs in the log2 domain.  A block whose 32 keys are
+//   all invisible is skipped; invisible keys inside a block are zero-filled
+//   in LDS and their logits replaced by -inf (selection, never
+//   multiplication), so masked rows may hold anything, NaN included.
 // Each split writes (running max, running sum, output / sum) per row; a
 // combine kernel merges the S + 1 partials per row.
 #include "dmx_device.hpp"
@@ -24,12 +30,13 @@
 namespace dmx {
 
 namespace {
-constexpr int KB = 32;          // keys per LDS block
-constexpr int KLD = kD + 8;     // K row stride in LDS (bf16 elements), padded
-constexpr int VLD = KB + 8;     // V^T row stride in LDS (bf16 elements), padded
-constexpr int PLD = KB + 8;     // P tile row stride (bf16 elements)
-constexpr int kMaxKps = 64;     // prefix keys per split (upper bound)
+constexpr int KB = 32;          // keys per block
+constexpr int KLD = kD + 8;     // K row stride in LDS (bf16): 528 B, 16 B past a bank period
+constexpr int VLD = kD + 16;    // V row stride in LDS (bf16): 544 B, 32 B past a bank period
+constexpr int kMaxNB = 4;       // blocks per split (upper bound)
 constexpr float kNegBig = -1e30f;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 }  // namespace
 
 // RoPE frequency table in LDS, in revolutions per position:
@@ -103,8 +110,9 @@ __device__ __forceinline__ void q_finish(const AttnArgs& a, const double* ftab, 
 }
 
 // Suffix keys of one 32-key block built from the raw projection into LDS:
-// thread t handles key j = t / 16 and dims d0 = (t % 16) * 8 .. +7 plus their
-// rotation partners d0 + 128 (K), and the 16 V dims (t % 16) * 16 .. +15.
+// thread t (< 512) handles key j = t / 16 and dims d0 = (t % 16) * 8 .. +7
+// plus their rotation partners d0 + 128 (K), and the 16 V dims
+// (t % 16) * 16 .. +15.
 struct SufRaw {
   float4 k[4], v[4];
 };
@@ -124,10 +132,10 @@ __device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int
 }
 
 __device__ __forceinline__ void suffix_store(const AttnArgs& a, const double* ftab, const uint16_t* kn, const SufRaw& r,
-                                             int b, int kb0, const int* vis, uint16_t* sK, uint16_t* sVt) {
+                                             int b, int kb0, uint32_t vis, uint16_t* sK, uint16_t* sV) {
   const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int key = kb0 + j;
-  const bool ok = vis[j] != 0;
+  const bool ok = (vis >> j) & 1u;
   const float lo[8] = {r.k[0].x, r.k[0].y, r.k[0].z, r.k[0].w, r.k[1].x, r.k[1].y, r.k[1].z, r.k[1].w};
   const float hi[8] = {r.k[2].x, r.k[2].y, r.k[2].z, r.k[2].w, r.k[3].x, r.k[3].y, r.k[3].z, r.k[3].w};
   const uint4 wlo = *reinterpret_cast<const uint4*>(kn + c * 8), whi = *reinterpret_cast<const uint4*>(kn + 128 + c * 8);
@@ -135,8 +143,7 @@ __device__ __forceinline__ void suffix_store(const AttnArgs& a, const double* ft
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  ss = group16_sum(ss);  // the 16 threads of key j form one DPP row
   const float rn = 1.0f / sqrtf(ss * (1.0f / kD) + kEps);
   const double pos = (double)a.pos0[b] + (double)key;
   uint32_t ko[4], kh[4];
@@ -161,8 +168,11 @@ __device__ __forceinline__ void suffix_store(const AttnArgs& a, const double* ft
   *reinterpret_cast<uint4*>(sK + j * KLD + 128 + c * 8) = make_uint4(kh[0], kh[1], kh[2], kh[3]);
   const float vv[16] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w,
                         r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w, r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
+  uint32_t vp[8];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) sVt[(c * 16 + e) * VLD + j] = ok ? f2bf(vv[e]) : (uint16_t)0;
+  for (int e2 = 0; e2 < 8; ++e2) vp[e2] = ok ? pack2(vv[2 * e2], vv[2 * e2 + 1]) : 0u;
+  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16) = make_uint4(vp[0], vp[1], vp[2], vp[3]);
+  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16 + 8) = make_uint4(vp[4], vp[5], vp[6], vp[7]);
 }
 
 // K / V rows (bf16, from global) of one 32-key block: thread t owns 16-byte
@@ -184,33 +194,47 @@ __device__ __forceinline__ void kv_load(const uint16_t* Kb, const uint16_t* Vb, 
   }
 }
 
-__device__ __forceinline__ void kv_store(const KVRegs& r, const int* vis, uint16_t* sK, uint16_t* sVt) {
+__device__ __forceinline__ void kv_store(const KVRegs& r, uint32_t vis, uint16_t* sK, uint16_t* sV) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = threadIdx.x + h * 512;
     const int j = c >> 5, ch = c & 31;
-    const bool ok = vis[j] != 0;
-    const uint4 kk = ok ? r.k[h] : make_uint4(0, 0, 0, 0);
-    const uint4 vv = ok ? r.v[h] : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(sK + j * KLD + ch * 8) = kk;
-    const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sVt[(ch * 8 + 2 * e) * VLD + j] = (uint16_t)(w4[e] & 0xffffu);
-      sVt[(ch * 8 + 2 * e + 1) * VLD + j] = (uint16_t)(w4[e] >> 16);
-    }
+    const bool ok = (vis >> j) & 1u;
+    *reinterpret_cast<uint4*>(sK + j * KLD + ch * 8) = ok ? r.k[h] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(sV + j * VLD + ch * 8) = ok ? r.v[h] : make_uint4(0, 0, 0, 0);
   }
 }
 
+// V^T operand of O^T = V^T P^T for dims 16t .. 16t+15 of a block staged
+// row-major: lane (i, q) gets V[key][16t + i] for keys 4q .. 4q+3 (elements
+// 0..3) and 16+4q .. 16+4q+3 (elements 4..7), the key order of the P^T
+// fragment.  In the transpose read, lane k of each 16-lane group names the
+// 4-element chunk V[key0 + k/4][16t + 4(k%4) ..], and lane i receives
+// element i%4 of the chunks named by lanes i/4 + 4e, e = 0..3.
+__device__ __forceinline__ bf16x8 v_frag(const uint16_t* sV, int t, int lane) {
+  const int k = lane & 15, q = lane >> 4;
+  const uint16_t* p0 = sV + (4 * q + (k >> 2)) * VLD + t * 16 + 4 * (k & 3);
+  const uint16_t* p1 = p0 + 16 * VLD;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(p0));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(p1));
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = lo[e];
+    r[4 + e] = hi[e];
+  }
+  return r;
+}
+
 // One split of one (request, KV head): every global load of the split (mask,
-// query rows, both K/V blocks or the raw suffix rows) is issued up front, then
-// the blocks are staged through LDS and processed.
-template <bool FUSED>
+// query rows, all K/V blocks or the raw suffix rows) is issued up front; the
+// blocks are then staged into LDS together and processed without further
+// work-group barriers.
+template <bool FUSED, int NB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_partial(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KB * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kD * VLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sP[8][16 * PLD];
-  __shared__ int sVis[kMaxKps];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NB][KB * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NB][KB * VLD];
+  __shared__ uint32_t sMask[NB];
   __shared__ double sF[kD / 2];
   __shared__ __attribute__((aligned(16))) uint16_t sNW[2][kD];  // q / k norm weights
 
@@ -226,7 +250,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int key_lo = suffix ? 0 : split * a.kps;
   const int key_hi = suffix ? a.C : min(a.P, key_lo + a.kps);
   const int nkeys = key_hi - key_lo;
-  const int nblk = (nkeys + KB - 1) / KB;  // <= 2
+  const int nblk = (nkeys + KB - 1) / KB;  // <= NB
   const size_t kv_rows = suffix ? (size_t)a.C : (size_t)a.P;
   const uint16_t* Kb = (suffix ? a.ks : a.kp) + (size_t)(b * kHK + g) * kv_rows * kD;
   const uint16_t* Vb = (suffix ? a.vs : a.vp) + (size_t)(b * kHK + g) * kv_rows * kD;
@@ -239,21 +263,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const bool qok = active && (row < R);
   const int hh = qok ? row / a.C : 0;
   const int qi = qok ? row - hh * a.C : 0;
-  KVRegs kv[2];
+  KVRegs kv[NB];
   SufRaw sr[2];
   QRaw qr;
   bf16x8 qf[8];
   int mvis = 0;
   uint4 nw = make_uint4(0, 0, 0, 0);
-  if (FUSED && threadIdx.x >= 64 && threadIdx.x < 128) {
-    const int t = threadIdx.x - 64;  // 64 threads x 16 B = both 512-B weight vectors
+  if (FUSED && threadIdx.x >= 384 && threadIdx.x < 448) {
+    const int t = threadIdx.x - 384;  // 64 threads x 16 B = both 512-B weight vectors
     nw = *reinterpret_cast<const uint4*>((t < 32 ? a.qn_w : a.kn_w) + (t & 31) * 8);
   }
-  if (threadIdx.x < kMaxKps && threadIdx.x < nkeys)
+  if (threadIdx.x < NB * KB && threadIdx.x < nkeys)
     mvis = suffix || a.mask[(size_t)b * a.P + key_lo + threadIdx.x] != 0;
   if (from_global) {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < NB; ++bi)
       if (bi < nblk) kv_load(Kb, Vb, key_lo + bi * KB, key_hi, kv[bi]);
   } else {
 #pragma unroll
@@ -270,148 +294,148 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- compute phase
-  if (threadIdx.x < kMaxKps) sVis[threadIdx.x] = mvis;
-  if (FUSED && threadIdx.x >= 64 && threadIdx.x < 128) {
-    const int t = threadIdx.x - 64;
+  if (wave < (NB * KB) / 64) {  // visibility words: bit j of word bi = key bi * 32 + j
+    const uint64_t bal = __ballot(mvis);
+    if (lane == 0) sMask[2 * wave] = (uint32_t)bal;
+    if (lane == 0 && 2 * wave + 1 < NB) sMask[2 * wave + 1] = (uint32_t)(bal >> 32);
+  }
+  if (FUSED && threadIdx.x >= 384 && threadIdx.x < 448) {
+    const int t = threadIdx.x - 384;
     *reinterpret_cast<uint4*>(&sNW[t >> 5][(t & 31) * 8]) = nw;
   }
   if (FUSED) rope_table(sF, a.rope_base);
   __syncthreads();
+  // stage every block (zero rows for invisible keys)
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi) {
+    if (bi >= nblk) break;
+    const uint32_t vis = sMask[bi];
+    if (vis == 0u) continue;
+    if (from_global)
+      kv_store(kv[bi], vis, sK[bi], sV[bi]);
+    else if (bi < 2)
+      suffix_store(a, sF, sNW[1], sr[bi], b, bi * KB, vis, sK[bi], sV[bi]);
+  }
   if (FUSED) q_finish(a, sF, sNW[0], qr, b, qi, qok, lq, qf);
   else if (!qok) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = zero_bf16x8();
   }
+  __syncthreads();
+  if (!active) return;
 
+  // lane (lr, lq) owns stacked row mt*16 + lr; o[t][e] = O[row][16t + 4lq + e]
   f32x4 o[16];
-  float mrun[4], lrun[4];
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) o[dt] = zero_f32x4();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mrun[r] = kNegBig;
-    lrun[r] = 0.f;
-  }
+  for (int t = 0; t < 16; ++t) o[t] = zero_f32x4();
+  float mrun = kNegBig, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(head_dim)
-  uint16_t* pt = &sP[wave][0];
 
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi) {
+  for (int bi = 0; bi < NB; ++bi) {
     if (bi >= nblk) break;
-    const int* vis = sVis + bi * KB;
-    int any = 0;
-    for (int j = 0; j < KB; ++j) any |= vis[j];
-    if (!any) continue;  // uniform across the WG
-    if (from_global)
-      kv_store(kv[bi], vis, sK, sVt);
-    else
-      suffix_store(a, sF, sNW[1], sr[bi], b, bi * KB, vis, sK, sVt);
-    __syncthreads();
-    if (active) {
-      const bool vis0 = vis[lr] != 0, vis1 = vis[16 + lr] != 0;
-      f32x4 s0 = zero_f32x4(), s1 = zero_f32x4();
+    const uint32_t vis = sMask[bi];
+    if (vis == 0u) continue;  // uniform across the WG
+    const uint16_t* bK = sK[bi];
+    // S^T tiles: s0 keys 0..15, s1 keys 16..31; s?[r] = S[row][key 4lq + r (+16)]
+    f32x4 s0 = zero_f32x4(), s1 = zero_f32x4();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(sK + lr * KLD + ks * 32 + lq * 8);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(sK + (16 + lr) * KLD + ks * 32 + lq * 8);
-        s0 = mfma16(qf[ks], k0, s0);
-        s1 = mfma16(qf[ks], k1, s1);
-      }
-      float alpha[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x0 = vis0 ? s0[r] * sl2 : -INFINITY;
-        const float x1 = vis1 ? s1[r] * sl2 : -INFINITY;
-        const float mloc = group16_max(fmaxf(x0, x1));
-        const float mnew = fmaxf(mrun[r], mloc);
-        alpha[r] = exp2f(mrun[r] - mnew);
-        mrun[r] = mnew;
-        const float p0 = exp2f(x0 - mnew), p1 = exp2f(x1 - mnew);
-        lrun[r] = lrun[r] * alpha[r] + p0 + p1;
-        pt[(lq * 4 + r) * PLD + lr] = f2bf(p0);
-        pt[(lq * 4 + r) * PLD + 16 + lr] = f2bf(p1);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[dt][r] *= alpha[r];
-      __builtin_amdgcn_wave_barrier();
-      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(pt + lr * PLD + lq * 8);
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sVt + (dt * 16 + lr) * VLD + lq * 8);
-        o[dt] = mfma16(pa, vf, o[dt]);
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(bK + lr * KLD + ks * 32 + lq * 8);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(bK + (16 + lr) * KLD + ks * 32 + lq * 8);
+      s0 = mfma16(k0, qf[ks], s0);
+      s1 = mfma16(k1, qf[ks], s1);
     }
-    __syncthreads();
-  }
-
-  // write this split's partial rows: running max, running sum, output / sum
-  if (active) {
+    float x[8];
+    float mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float l = group16_sum(lrun[r]);
-      const int prow_i = mt * 16 + lq * 4 + r;
-      const size_t prow = ((size_t)bg * nsplit + split) * a.R16 + prow_i;
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      x[r] = ((vis >> (4 * lq + r)) & 1u) ? s0[r] * sl2 : -INFINITY;
+      x[4 + r] = ((vis >> (16 + 4 * lq + r)) & 1u) ? s1[r] * sl2 : -INFINITY;
+      mloc = fmaxf(mloc, fmaxf(x[r], x[4 + r]));
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(mrun, mloc);
+    const float alpha = exp2f(mrun - mnew);
+    mrun = mnew;
+    float psum = 0.f;
+    bf16x8 pf;
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) a.part_o[prow * kD + dt * 16 + lr] = f2bf(o[dt][r] * inv);
-      if (lr == 0) {
-        a.part_ml[prow * 2] = mrun[r];
-        a.part_ml[prow * 2 + 1] = l;
-      }
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = exp2f(x[e] - mnew), p1 = exp2f(x[e + 1] - mnew);
+      psum += p0 + p1;
+      const uint32_t pk = pack2(p0, p1);
+      pf[e] = (short)(pk & 0xffffu);
+      pf[e + 1] = (short)(pk >> 16);
+    }
+    lrun = lrun * alpha + psum;
+    const uint16_t* bV = sV[bi];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      o[t] *= alpha;
+      o[t] = mfma16(v_frag(bV, t, lane), pf, o[t]);
     }
   }
+
+  // this split's partial row: running max, running sum, output / sum
+  float l = lrun + __shfl_xor(lrun, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  const size_t prow = ((size_t)bg * nsplit + split) * a.R16 + row;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  uint16_t* dst = a.part_o + prow * kD + 4 * lq;
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    *reinterpret_cast<uint2*>(dst + t * 16) = make_uint2(pack2(o[t][0] * inv, o[t][1] * inv),
+                                                         pack2(o[t][2] * inv, o[t][3] * inv));
+  if (lq == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(mrun, l);
 }
 
 // One wave per (request, KV head, stacked row): merge the split partials.
-// Lane s first fetches split s's (max, sum); then every lane accumulates its
-// 4 output dims over the splits with all loads of a batch in flight.
+// Lane s fetches split s's (max, sum) while every lane fetches its 4 output
+// dims of the first batch of splits, all in flight together.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
+  constexpr int CB = 24;  // splits per batch of loads
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int R = 2 * a.C;
   const int wid = blockIdx.x * 4 + wave;
   if (wid >= a.B * kHK * R) return;
   const int row = wid % R, bg = wid / R;
   const int g = bg % kHK, b = bg / kHK;
-  const int nsplit = a.S + 1;  // <= 65
+  const int nsplit = a.S + 1;  // <= 128
   const size_t base = (size_t)bg * nsplit * a.R16 + row;
-  float m0 = kNegBig, l0 = 0.f, m1 = kNegBig, l1 = 0.f;
-  if (lane < nsplit) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)lane * a.R16) * 2);
-    m0 = ml.x;
-    l0 = ml.y;
-  }
-  if (lane + 64 < nsplit) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)(lane + 64) * a.R16) * 2);
-    m1 = ml.x;
-    l1 = ml.y;
-  }
-  float M = fmaxf(l0 > 0.f ? m0 : kNegBig, l1 > 0.f ? m1 : kNegBig);
+  float2 ml0 = make_float2(kNegBig, 0.f), ml1 = ml0;
+  if (lane < nsplit) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)lane * a.R16) * 2);
+  if (lane + 64 < nsplit) ml1 = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)(lane + 64) * a.R16) * 2);
+  uint2 raw[CB];
+#pragma unroll
+  for (int u = 0; u < CB; ++u)
+    raw[u] = u < nsplit ? *reinterpret_cast<const uint2*>(a.part_o + (base + (size_t)u * a.R16) * kD + lane * 4)
+                        : make_uint2(0, 0);
+  float M = fmaxf(ml0.y > 0.f ? ml0.x : kNegBig, ml1.y > 0.f ? ml1.x : kNegBig);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const float w0 = l0 > 0.f ? l0 * exp2f(m0 - M) : 0.f;
-  const float w1 = l1 > 0.f ? l1 * exp2f(m1 - M) : 0.f;
+  const float w0 = ml0.y > 0.f ? ml0.y * exp2f(ml0.x - M) : 0.f;
+  const float w1 = ml1.y > 0.f ? ml1.y * exp2f(ml1.x - M) : 0.f;
   const float L = wave_sum(w0 + w1);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    uint2 raw[8];
-    float ws[8];
+  for (int s0 = 0; s0 < nsplit; s0 += CB) {
+    if (s0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      ws[u] = s < 64 ? __shfl(w0, s & 63, 64) : __shfl(w1, s & 63, 64);
-      raw[u] = make_uint2(0, 0);
-      if (s < nsplit && ws[u] != 0.f)
-        raw[u] = *reinterpret_cast<const uint2*>(a.part_o + (base + (size_t)s * a.R16) * kD + lane * 4);
+      for (int u = 0; u < CB; ++u)
+        raw[u] = s0 + u < nsplit
+                     ? *reinterpret_cast<const uint2*>(a.part_o + (base + (size_t)(s0 + u) * a.R16) * kD + lane * 4)
+                     : make_uint2(0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (s0 + u < nsplit && ws[u] != 0.f) {
-        acc[0] += ws[u] * bf2f((uint16_t)(raw[u].x & 0xffffu));
-        acc[1] += ws[u] * bf2f((uint16_t)(raw[u].x >> 16));
-        acc[2] += ws[u] * bf2f((uint16_t)(raw[u].y & 0xffffu));
-        acc[3] += ws[u] * bf2f((uint16_t)(raw[u].y >> 16));
+    for (int u = 0; u < CB; ++u) {
+      const int s = s0 + u;
+      const float ws = s < 64 ? __shfl(w0, s & 63, 64) : __shfl(w1, s & 63, 64);
+      if (s < nsplit && ws != 0.f) {
+        acc[0] += ws * bf2f((uint16_t)(raw[u].x & 0xffffu));
+        acc[1] += ws * bf2f((uint16_t)(raw[u].x >> 16));
+        acc[2] += ws * bf2f((uint16_t)(raw[u].y & 0xffffu));
+        acc[3] += ws * bf2f((uint16_t)(raw[u].y >> 16));
       }
     }
   }
@@ -428,16 +452,19 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
   a.B = B;
   a.C = C;
   a.P = P;
-  a.kps = kMaxKps;
+  a.kps = kAttnKps;
   a.S = (P + a.kps - 1) / a.kps;
   a.R16 = ((2 * C + 15) / 16) * 16;
 }
 
 hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
+  constexpr int NB = kAttnKps / KB;
+  static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
+  const dim3 grid(a.B * kHK * (a.S + 1));
   if (a.raw)
-    k_attn_partial<true><<<dim3(a.B * kHK * (a.S + 1)), dim3(512), 0, s>>>(a);
+    k_attn_partial<true, NB><<<grid, dim3(512), 0, s>>>(a);
   else
-    k_attn_partial<false><<<dim3(a.B * kHK * (a.S + 1)), dim3(512), 0, s>>>(a);
+    k_attn_partial<false, NB><<<grid, dim3(512), 0, s>>>(a);
   const int rows = a.B * kHK * 2 * a.C;
   k_attn_combine<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(a, ctx);
   return hipGetLastError();

@@ -101,6 +101,7 @@ struct AttnArgs {
   uint16_t* part_o;  // [B][HK][S + 1][R16][D] bf16, normalised partial outputs
   float* part_ml;    // [B][HK][S + 1][R16][2] running max (log2 domain) and sum
 };
+constexpr int kAttnKps = 64;  // prefix keys per attention split (32 .. 128, multiple of 32)
 void attn_config(int B, int C, int P, AttnArgs& a);
 hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s);
 
