@@ -92,7 +92,7 @@ def main():
     visible = int(rq.mask.sum())
 
     torch.cuda.set_device(0)
-    wd = [{k: dev(v) for k, v in w.items()} for w in wbits]
+    wd = [dmx.pack_layer_weights({k: dev(v) for k, v in w.items()}) for w in wbits]
     kp = [dev(rq.k_pre[l][None]) for l in range(L)]
     vp = [dev(rq.v_pre[l][None]) for l in range(L)]
     mask = dev(rq.mask[None], raw=True)

@@ -27,6 +27,10 @@
  *     fallback of the bucket rule, negative = error.  No exception crosses the ABI.
  *     dmx_last_error_string() gives the calling thread's last error text.
  *   - There is no silent fallback to another implementation.
+ *   - Weight matrices (w_mod*, w_qkv, w_o, w_gu, w_down) are passed TILED:
+ *     dmx_pack_weight() converts a row-major [rows][cols] matrix once, at load
+ *     time.  Shapes below are the logical row-major ones.  Bias and norm
+ *     vectors stay plain.
  *   - Arithmetic: bf16 storage, fp32 accumulation.
  *   - Workspace: `ws` is caller-owned device scratch of at least
  *     dmx_workspace_bytes(batch, tokens, p_bucket) bytes (a stack:
@@ -98,13 +102,23 @@ size_t dmx_workspace_bytes(int32_t batch, int32_t tokens, int32_t p_bucket);
 /* Zero-fill a workspace (enqueued on `stream`, no allocation); optional. */
 int dmx_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
+/* Weight tiling.  Copies the row-major bf16 matrix w [rows][cols] into `out`
+ * (rows * cols elements, not overlapping w) in the tiled layout every weight
+ * argument of this library takes: 16-row x 32-column tiles of 512 elements,
+ * tile (rt, ct) at element (rt * cols/32 + ct) * 512; inside a tile, the 8
+ * elements w[rt*16 + l%16][ct*32 + 8*(l/16) .. +7] sit at l * 8 (l < 64): the
+ * per-lane operand fragments of the gfx950 16x16x32 bf16 matrix instruction,
+ * so a projection streams each weight tile as 1 KB of contiguous memory.
+ * rows % 16 == 0, cols % 32 == 0, cols <= 16384.  Enqueued on `stream`. */
+int dmx_pack_weight(const dmx_bf16* w, int32_t rows, int32_t cols, dmx_bf16* out, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* AdaRMS time-modulated prenorm ([Art §2.2] "Adarms 调制 prenorm").
  *   mod[b] = W_mod * cond[b] + b_mod            (fp32, [batch][3][1024]:
  *                                                 scale | shift | gate)
  *   x_norm[b][t][j] = x[b][t][j] / sqrt(mean_j x^2 + 1e-6) * (1 + scale[j]) + shift[j]
  *   x      [batch][tokens][1024] bf16     cond  [batch][1024] bf16
- *   w_mod  [3072][1024] bf16              b_mod [3072] bf16
+ *   w_mod  [3072][1024] bf16 (tiled)      b_mod [3072] bf16
  *   x_norm [batch][tokens][1024] bf16 (out)
  *   mod    [batch][3072] fp32 (out); its last third is the residual gate. */
 int dmx_adarms_prenorm(const dmx_bf16* x, const dmx_bf16* cond, const dmx_bf16* w_mod,
@@ -148,7 +162,7 @@ int dmx_suffix_attention(const dmx_bf16* q, const dmx_bf16* k_suf, const dmx_bf1
 /* O-projection + gated residual:
  *   out[b][t] = residual[b][t] + gate[b] * (ctx[b][t] * W_o^T),
  *   gate[b] = mod[b][2048..3071] (the third chunk of dmx_adarms_prenorm's mod).
- *   ctx [batch][tokens][2048] bf16; w_o [1024][2048] bf16;
+ *   ctx [batch][tokens][2048] bf16; w_o [1024][2048] bf16 (tiled);
  *   mod [batch][3072] fp32; residual, out [batch][tokens][1024] bf16.
  *   out may alias residual. */
 int dmx_oproj_gated_residual(const dmx_bf16* ctx, const dmx_bf16* w_o, const float* mod,
@@ -159,7 +173,7 @@ int dmx_oproj_gated_residual(const dmx_bf16* ctx, const dmx_bf16* w_o, const flo
  *   [a | u] = x_norm2 * W_gu^T (a: rows 0..4095, u: rows 4096..8191)
  *   h = gelu_tanh(a) * u
  *   out = residual + gate2 * (h * W_down^T),  gate2 = mod2[b][2048..3071]
- *   x_norm2 [batch][tokens][1024] bf16; w_gu [8192][1024]; w_down [1024][4096];
+ *   x_norm2 [batch][tokens][1024] bf16; w_gu [8192][1024], w_down [1024][4096] (tiled);
  *   mod2 [batch][3072] fp32; residual, out [batch][tokens][1024] bf16.
  *   out may alias residual. */
 int dmx_geglu_mlp(const dmx_bf16* x_norm2, const dmx_bf16* w_gu, const dmx_bf16* w_down,

@@ -27,7 +27,8 @@ H, I, D, HQ, HK = 1024, 4096, 256, 8, 4
 PREFIX_HIDDEN = 2560
 
 EXPORTED = (
-    "dmx_select_bucket", "dmx_workspace_bytes", "dmx_stack_workspace_bytes", "dmx_workspace_init", "dmx_adarms_prenorm",
+    "dmx_select_bucket", "dmx_workspace_bytes", "dmx_stack_workspace_bytes", "dmx_workspace_init", "dmx_pack_weight",
+    "dmx_adarms_prenorm",
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
     "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_graph_create", "dmx_graph_launch",
     "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
@@ -75,6 +76,7 @@ def lib():
             "dmx_workspace_bytes": ([i32, i32, i32], sz),
             "dmx_stack_workspace_bytes": ([i32, i32, i32, i32], sz),
             "dmx_workspace_init": ([P, sz, P], ctypes.c_int),
+            "dmx_pack_weight": ([P, i32, i32, P, P], ctypes.c_int),
             "dmx_adarms_prenorm": ([P, P, P, P, i32, i32, P, P, P], ctypes.c_int),
             "dmx_qkv_qknorm_rope": ([P, P, P, P, i32, i32, i32, P, ctypes.c_float, P, P, P, i32, i32, P, sz, P],
                                     ctypes.c_int),
@@ -144,6 +146,27 @@ def new_workspace(batch: int, tokens: int, p_bucket: int, device="cuda"):
 
 
 # --------------------------------------------------------------------------- stages
+def pack_weight(w, stream=None):
+    """Tiled copy of a row-major bf16 weight matrix [rows][cols] (the layout
+    every weight argument takes).  The result keeps w's shape for bookkeeping;
+    its memory holds the tiles, not rows."""
+    if w.dim() != 2:
+        raise ValueError(f"pack_weight: expected a 2-D matrix, got shape {tuple(w.shape)}")
+    _want(w, w.shape, torch.bfloat16, "w")
+    out = torch.empty_like(w)
+    _check(lib().dmx_pack_weight(_p(w), w.shape[0], w.shape[1], _p(out), _stream(stream)))
+    return out
+
+
+WEIGHT_MATRICES = ("w_mod1", "w_qkv", "w_o", "w_mod2", "w_gu", "w_down")
+
+
+def pack_layer_weights(w: dict, stream=None) -> dict:
+    """A layer's weights as the library takes them: the matrices tiled by
+    pack_weight, the bias and norm vectors unchanged."""
+    return {k: pack_weight(v, stream) if k in WEIGHT_MATRICES else v for k, v in w.items()}
+
+
 def adarms_prenorm(x, cond, w_mod, b_mod, x_norm=None, mod=None, stream=None):
     B, T, _ = x.shape
     _want(x, (B, T, H), torch.bfloat16, "x")

@@ -10,6 +10,7 @@
 #include "../../include/dmx.h"
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
+#include "dmx_tiles.hpp"
 
 using namespace dmx;
 
@@ -51,9 +52,11 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Workspace carve-up.  Everything a layer needs between its stages, plus
-// (for a stack) the modulation vectors of every layer of one step.
+// (for a stack) the modulation vectors of every layer of one step.  Rows of
+// the tiled / fp32 intermediates are tiled rows (each request padded to TP).
 struct WsLayout {
-  size_t mod1, mod2, xn, qkv, q, ks, vs, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
+  size_t mod1, mod2, apk, xp, raw, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
+  int TP;
   AttnArgs attn;
 };
 
@@ -61,7 +64,8 @@ bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
   if (B < 1 || T < 1 || P < 0 || B > DMX_MAX_BATCH || T > 4096 || P > DMX_MAX_PREFIX || n_layers < 0 ||
       n_layers > DMX_MAX_LAYERS)
     return false;
-  const size_t M = (size_t)B * T;
+  L.TP = padded_tokens(T);
+  const size_t M = (size_t)B * L.TP;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -70,21 +74,19 @@ bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
   };
   L.mod1 = take((size_t)B * 3 * kH * 4);
   L.mod2 = take((size_t)B * 3 * kH * 4);
-  L.xn = take(M * kH * 2);
-  L.qkv = take(M * kQKV * 4);
-  L.q = take(M * kHQ * kD * 2);
-  L.ks = take((size_t)B * kHK * T * kD * 2);
-  L.vs = take((size_t)B * kHK * T * kD * 2);
-  L.ctx = take(M * kHQ * kD * 2);
+  L.apk = take(M * DMX_PREFIX_HIDDEN * 2);  // tiled copy of a row-major A operand
+  L.xp = take(M * kH * 2);                  // tiled layer input
+  L.raw = take(M * kQKV * 4);               // fp32 QKV projection
+  L.ctx = take(M * kHQ * kD * 2);           // tiled attention output
   L.x1 = take(M * kH * 4);   // fp32 residual between the two halves of a layer
-  L.x1s = take(M * kH * 2);  // bf16(x1 * (1 + scale2)), the gate-up A operand
-  L.h = take(M * kI * 2);
+  L.x1s = take(M * kH * 2);  // tiled bf16(x1 * (1 + scale2)), the gate-up A operand
+  L.h = take(M * kI * 2);    // tiled GEGLU output
   attn_config(B, T, P, L.attn);
   const size_t prow = (size_t)B * kHK * (L.attn.S + 1) * L.attn.R16;
   L.part_o = take(prow * kD * 2);
   L.part_ml = take(prow * 2 * 4);
   L.ss_a = take(M * kSsParts * 4);  // row sums of squares of x1, one per O-projection tile
-  L.ss_b = take(M * kSsParts * 4);  // ... of a layer input (row pass or the down tiles)
+  L.ss_b = take(M * kSsParts * 4);  // ... of a layer input (pack pass or the down tiles)
   L.stack_mod = take((size_t)n_layers * 2 * B * 3 * kH * 4);
   L.total = off;
   return true;
@@ -138,18 +140,22 @@ int enq_adarms(const dmx_bf16* x, const dmx_bf16* cond, const dmx_bf16* w_mod, c
 
 int enq_qkv(const dmx_bf16* xn, const dmx_bf16* w_qkv, const dmx_bf16* qn, const dmx_bf16* kn, int B, int T,
             int hidden, const int32_t* pos0, float base, dmx_bf16* q, dmx_bf16* k, dmx_bf16* v,
-            int kv_rows, int kv_row0, float* raw, hipStream_t s) {
+            int kv_rows, int kv_row0, void* ws, const WsLayout& L, hipStream_t s) {
   const GemmKind kind = hidden == kH ? GEMM_QKV1024 : GEMM_QKV2560;
+  uint16_t* apk = at<uint16_t>(ws, L.apk);
+  float* raw = at<float>(ws, L.raw);
+  DMX_TRY(hip_check(launch_pack_rows(xn, B, T, L.TP, hidden, apk, nullptr, s), "pack launch"));
   GemmArgs a = gemm_args();
   gemm_config(kind, a);
-  a.A = xn;
+  a.A = apk;
   a.W = w_qkv;
-  a.M = B * T;
+  a.M = B * L.TP;
   a.T = T;
+  a.TP = L.TP;
   a.out_f32 = raw;
   a.ldo = kQKV;
   DMX_TRY(hip_check(launch_gemm(kind, a, s), "QKV GEMM launch"));
-  return hip_check(launch_qknorm_rope(raw, qn, kn, pos0, base, B * T, T, q, k, v, kv_rows, kv_row0, s),
+  return hip_check(launch_qknorm_rope(raw, qn, kn, pos0, base, B, T, L.TP, q, k, v, kv_rows, kv_row0, s),
                    "QK-norm/RoPE launch");
 }
 
@@ -163,6 +169,7 @@ AttnArgs attn_args(const WsLayout& L, void* ws) {
   a.mask = nullptr;
   a.part_o = at<uint16_t>(ws, L.part_o);
   a.part_ml = at<float>(ws, L.part_ml);
+  a.ctx_tiled = 0;
   return a;
 }
 
@@ -179,70 +186,89 @@ int enq_attention(const dmx_bf16* q, const dmx_bf16* ks, const dmx_bf16* vs, con
   return hip_check(launch_attention(a, ctx, s), "attention launch");
 }
 
-// Gated-residual projection: out = resid + gate[b] * (A * W^T); the residual
-// and output are bf16 unless their fp32 pointer is given.
-int enq_resid_gemm(GemmKind kind, const dmx_bf16* A, const dmx_bf16* W, const float* mod,
-                   const dmx_bf16* resid, const float* resid_f32, int B, int T, dmx_bf16* out,
-                   float* out_f32, hipStream_t s) {
+// Gated-residual projection of a row-major A operand (tiled into the
+// workspace first): out = resid + gate[b] * (A * W^T), all bf16 row-major.
+int enq_resid_gemm(GemmKind kind, const dmx_bf16* A, int K, const dmx_bf16* W, const float* mod,
+                   const dmx_bf16* resid, int B, int T, dmx_bf16* out, void* ws, const WsLayout& L, hipStream_t s) {
+  uint16_t* apk = at<uint16_t>(ws, L.apk);
+  DMX_TRY(hip_check(launch_pack_rows(A, B, T, L.TP, K, apk, nullptr, s), "pack launch"));
   GemmArgs a = gemm_args();
   gemm_config(kind, a);
-  a.A = A;
+  a.A = apk;
   a.W = W;
-  a.M = B * T;
+  a.M = B * L.TP;
   a.T = T;
+  a.TP = L.TP;
   a.out_bf16 = out;
-  a.out_f32 = out_f32;
   a.ldo = kH;
   a.gate = mod + 2 * kH;
   a.gate_stride = 3 * kH;
   a.resid = resid;
-  a.resid_f32 = resid_f32;
   return hip_check(launch_gemm(kind, a, s), "projection GEMM launch");
 }
 
 int enq_geglu(const dmx_bf16* xn2, const dmx_bf16* w_gu, const dmx_bf16* w_down, const float* mod2,
               const dmx_bf16* resid, int B, int T, dmx_bf16* out, void* ws, const WsLayout& L,
               hipStream_t s) {
+  uint16_t* apk = at<uint16_t>(ws, L.apk);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  DMX_TRY(hip_check(launch_pack_rows(xn2, B, T, L.TP, kH, apk, nullptr, s), "pack launch"));
   GemmArgs a = gemm_args();
   gemm_config(GEMM_GATEUP, a);
-  a.A = xn2;
+  a.A = apk;
   a.W = w_gu;
-  a.M = B * T;
+  a.M = B * L.TP;
   a.T = T;
-  a.out_bf16 = at<uint16_t>(ws, L.h);
+  a.TP = L.TP;
+  a.out_pk = h;
   a.ldo = kI;
   DMX_TRY(hip_check(launch_gemm(GEMM_GATEUP, a, s), "gate-up GEMM launch"));
-  return enq_resid_gemm(GEMM_DOWN, at<uint16_t>(ws, L.h), w_down, mod2, resid, nullptr, B, T, out, nullptr, s);
+  a = gemm_args();
+  gemm_config(GEMM_DOWN, a);
+  a.A = h;
+  a.W = w_down;
+  a.M = B * L.TP;
+  a.T = T;
+  a.TP = L.TP;
+  a.out_bf16 = out;
+  a.ldo = kH;
+  a.gate = mod2 + 2 * kH;
+  a.gate_stride = 3 * kH;
+  a.resid = resid;
+  return hip_check(launch_gemm(GEMM_DOWN, a, s), "down projection launch");
 }
 
 // The fused layer chain (modulation vectors mod1 / mod2 already computed,
-// the workspace's ss_b holding the row sums of squares of x_in, 64 per row):
+// the workspace holding x_in tiled in xp and its row sums of squares in ss_b,
+// 64 per row):
 //   QKV GEMM with AdaRMS #1 fused -> attention with QK-norm + RoPE on load ->
-//   combine -> O-projection + gated residual (fp32 x1, bf16(x1 * (1 + scale2)),
-//   row sums of squares of x1) -> gate-up GEMM with AdaRMS #2 fused + GEGLU ->
-//   down projection +
-//   gated residual (row sums of squares of the output, for the next layer).
+//   combine (tiled context) -> O-projection + gated residual (fp32 x1, tiled
+//   bf16(x1 * (1 + scale2)), row sums of squares of x1) -> gate-up GEMM with
+//   AdaRMS #2 fused + GEGLU -> down projection + gated residual (row-major
+//   x_out, its tiled copy and row sums of squares, for the next layer).
 int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
                     const int32_t* pos0, int B, int C, dmx_bf16* x_out,
                     const float* mod1, const float* mod2, void* ws, const WsLayout& L, hipStream_t s) {
-  float* raw = at<float>(ws, L.qkv);
+  float* raw = at<float>(ws, L.raw);
+  uint16_t* xp = at<uint16_t>(ws, L.xp);
   dmx_bf16* ctx = at<dmx_bf16>(ws, L.ctx);
   float* x1 = at<float>(ws, L.x1);
   dmx_bf16* x1s = at<dmx_bf16>(ws, L.x1s);
   dmx_bf16* h = at<dmx_bf16>(ws, L.h);
   float* ss_a = at<float>(ws, L.ss_a);
   float* ss_b = at<float>(ws, L.ss_b);
-  const int M = B * C;
+  const int M = B * L.TP;
 
   GemmArgs g = gemm_args();
   gemm_config(GEMM_QKV1024_MOD, g);
-  g.xb = x_in;
+  g.A = xp;
   g.nmod = mod1;
   g.ss_in = ss_b;
   g.ss_in_n = kSsParts;
   g.W = w->w_qkv;
   g.M = M;
   g.T = C;
+  g.TP = L.TP;
   g.out_f32 = raw;
   g.ldo = kQKV;
   DMX_TRY(hip_check(launch_gemm(GEMM_QKV1024_MOD, g, s), "QKV GEMM launch"));
@@ -255,17 +281,19 @@ int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const d
   a.kp = kv->k;
   a.vp = kv->v;
   a.mask = kv->mask;
+  a.ctx_tiled = 1;
   DMX_TRY(hip_check(launch_attention(a, ctx, s), "attention launch"));
 
-  // x1 = x + gate1 * (ctx W_o^T): fp32, the scaled bf16 copy and row sums of squares
+  // x1 = x + gate1 * (ctx W_o^T): fp32, the scaled tiled copy and row sums of squares
   g = gemm_args();
   gemm_config(GEMM_OPROJ_F32, g);
   g.A = ctx;
   g.W = w->w_o;
   g.M = M;
   g.T = C;
+  g.TP = L.TP;
   g.out_f32 = x1;
-  g.out_bf16 = x1s;
+  g.out_pk = x1s;
   g.xs_scale = mod2;
   g.ldo = kH;
   g.gate = mod1 + 2 * kH;
@@ -277,25 +305,28 @@ int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const d
 
   g = gemm_args();
   gemm_config(GEMM_GATEUP_MOD, g);
-  g.xb = x1s;
+  g.A = x1s;
   g.nmod = mod2;
   g.ss_in = ss_a;
   g.ss_in_n = kSsParts;
   g.W = w->w_gu;
   g.M = M;
   g.T = C;
-  g.out_bf16 = h;
+  g.TP = L.TP;
+  g.out_pk = h;
   g.ldo = kI;
   DMX_TRY(hip_check(launch_gemm(GEMM_GATEUP_MOD, g, s), "gate-up GEMM launch"));
 
-  // out = x1 + gate2 * (GEGLU(xn2) W_down^T), plus its row sums of squares
+  // out = x1 + gate2 * (GEGLU(xn2) W_down^T), its tiled copy and row sums of squares
   g = gemm_args();
   gemm_config(GEMM_DOWN_F32RES, g);
   g.A = h;
   g.W = w->w_down;
   g.M = M;
   g.T = C;
+  g.TP = L.TP;
   g.out_bf16 = x_out;
+  g.out_pk = xp;
   g.ldo = kH;
   g.gate = mod2 + 2 * kH;
   g.gate_stride = 3 * kH;
@@ -305,6 +336,12 @@ int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const d
   return hip_check(launch_gemm(GEMM_DOWN_F32RES, g, s), "down projection launch");
 }
 
+// tiled copy and row statistics of a row-major layer input
+int enq_pack_input(const dmx_bf16* x, int B, int C, void* ws, const WsLayout& L, hipStream_t s) {
+  return hip_check(launch_pack_rows(x, B, C, L.TP, kH, at<uint16_t>(ws, L.xp), at<float>(ws, L.ss_b), s),
+                   "input pack launch");
+}
+
 int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
               const dmx_bf16* cond, const int32_t* pos0, int B, int C, dmx_bf16* x_out, void* ws,
               const WsLayout& L, hipStream_t s) {
@@ -312,7 +349,7 @@ int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf1
   float* mod2 = at<float>(ws, L.mod2);
   const ModJob jobs[2] = {{w->w_mod1, w->b_mod1, cond, mod1}, {w->w_mod2, w->b_mod2, cond, mod2}};
   DMX_TRY(enq_mods(jobs, 2, B, s));
-  DMX_TRY(hip_check(launch_row_ssq(x_in, B * C, at<float>(ws, L.ss_b), s), "row statistics launch"));
+  DMX_TRY(enq_pack_input(x_in, B, C, ws, L, s));
   return enq_layer_chain(w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, L, s);
 }
 
@@ -394,6 +431,18 @@ int dmx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return hip_check(launch_fill_zero(ws, ws_bytes & ~(size_t)15, (hipStream_t)stream), "workspace fill");
 }
 
+int dmx_pack_weight(const dmx_bf16* w, int32_t rows, int32_t cols, dmx_bf16* out, void* stream) {
+  const char* fn = "dmx_pack_weight";
+  DMX_REQUIRE_PTR(w);
+  DMX_REQUIRE_PTR(out);
+  if (rows < 16 || cols < 32 || rows % 16 != 0 || cols % 32 != 0 || cols > 16384 || rows > (1 << 20))
+    return fail(DMX_ERR_UNSUPPORTED, "%s: %d x %d (rows a multiple of 16, cols of 32 up to 16384)", fn, rows, cols);
+  const uintptr_t wa = reinterpret_cast<uintptr_t>(w), oa = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t bytes = (uintptr_t)rows * cols * 2;
+  if (wa < oa + bytes && oa < wa + bytes) return fail(DMX_ERR_INVALID_ARG, "%s: out overlaps w", fn);
+  return hip_check(launch_pack_rows(w, 1, rows, rows, cols, out, nullptr, (hipStream_t)stream), "pack launch");
+}
+
 int dmx_adarms_prenorm(const dmx_bf16* x, const dmx_bf16* cond, const dmx_bf16* w_mod, const dmx_bf16* b_mod,
                        int32_t batch, int32_t tokens, dmx_bf16* x_norm, float* mod, void* stream) {
   const char* fn = "dmx_adarms_prenorm";
@@ -430,7 +479,7 @@ int dmx_qkv_qknorm_rope(const dmx_bf16* x_norm, const dmx_bf16* w_qkv, const dmx
   WsLayout L;
   DMX_TRY(check_ws(fn, ws, ws_bytes, batch, tokens, 0, L));
   return enq_qkv(x_norm, w_qkv, q_norm_w, k_norm_w, batch, tokens, hidden, pos0, rope_base, q, k, v, kv_rows,
-                 kv_row0, at<float>(ws, L.qkv), (hipStream_t)stream);
+                 kv_row0, ws, L, (hipStream_t)stream);
 }
 
 int dmx_suffix_attention(const dmx_bf16* q, const dmx_bf16* k_suf, const dmx_bf16* v_suf, const dmx_bf16* k_pre,
@@ -460,7 +509,7 @@ int dmx_oproj_gated_residual(const dmx_bf16* ctx, const dmx_bf16* w_o, const flo
   DMX_TRY(check_bt(fn, batch, tokens, 4096));
   WsLayout L;
   DMX_TRY(check_ws(fn, ws, ws_bytes, batch, tokens, 0, L));
-  return enq_resid_gemm(GEMM_OPROJ, ctx, w_o, mod, residual, nullptr, batch, tokens, out, nullptr,
+  return enq_resid_gemm(GEMM_OPROJ, ctx, kHQ * kD, w_o, mod, residual, batch, tokens, out, ws, L,
                         (hipStream_t)stream);
 }
 
@@ -534,10 +583,9 @@ static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) 
       jobs[2 * l + 1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, mod_of(l, 1)};
     }
     DMX_TRY(enq_mods(jobs, 2 * NL, B, s));
-    // row statistics of x: a row pass for the first layer of the run, after
-    // that the down projection of the layer before
-    if (st == 0)
-      DMX_TRY(hip_check(launch_row_ssq(d->x, B * d->chunk, at<float>(d->ws, L.ss_b), s), "row statistics launch"));
+    // tiled x and its row statistics: a pack pass for the first layer of the
+    // run, after that the down projection of the layer before
+    if (st == 0) DMX_TRY(enq_pack_input(d->x, B, d->chunk, d->ws, L, s));
     for (int l = 0; l < NL; ++l) {
       dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
       DMX_TRY(enq_layer_chain(&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1), d->ws,

@@ -26,6 +26,7 @@
 // combine kernel merges the S + 1 partials per row.
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
+#include "dmx_tiles.hpp"
 
 namespace dmx {
 
@@ -65,7 +66,7 @@ struct QRaw {
 };
 
 __device__ __forceinline__ void q_load(const AttnArgs& a, int b, int i, int head, int lq, QRaw& q) {
-  const float* src = a.raw + (size_t)(b * a.C + i) * kQKV + head * kD + lq * 8;
+  const float* src = a.raw + (size_t)(b * a.TP + i) * kQKV + head * kD + lq * 8;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     q.x[ks][0] = *reinterpret_cast<const float4*>(src + ks * 32);
@@ -120,7 +121,7 @@ struct SufRaw {
 __device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int kb0, SufRaw& r) {
   const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int key = min(kb0 + j, a.C - 1);  // rows past the chunk read a valid row and are zeroed later
-  const float* row = a.raw + (size_t)(b * a.C + key) * kQKV;
+  const float* row = a.raw + (size_t)(b * a.TP + key) * kQKV;
   const float* kr = row + (kHQ + g) * kD;
   r.k[0] = *reinterpret_cast<const float4*>(kr + c * 8);
   r.k[1] = *reinterpret_cast<const float4*>(kr + c * 8 + 4);
@@ -441,7 +442,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, uint16_t* ctx)
   }
   const float inv = 1.0f / L;
   const int hh = row / a.C, i = row - hh * a.C;
-  uint16_t* dst = ctx + ((size_t)(b * a.C + i) * kHQ + kGroup * g + hh) * kD + lane * 4;
+  const int col = (kGroup * g + hh) * kD + lane * 4;
+  uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
+                              : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
   uint2 outv;
   outv.x = pack2(acc[0] * inv, acc[1] * inv);
   outv.y = pack2(acc[2] * inv, acc[3] * inv);
@@ -455,6 +458,7 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
   a.kps = kAttnKps;
   a.S = (P + a.kps - 1) / a.kps;
   a.R16 = ((2 * C + 15) / 16) * 16;
+  a.TP = padded_tokens(C);
 }
 
 hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
@@ -515,11 +519,6 @@ hipError_t launch_adarms_norm(const uint16_t* x, const float* mod, int M, int T,
   return hipGetLastError();
 }
 
-hipError_t launch_adarms_norm_f32(const float* x, const float* mod, int M, int T, uint16_t* xn,
-                                  hipStream_t s) {
-  k_adarms_norm<float><<<dim3(M), dim3(256), 0, s>>>(x, mod, T, xn);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // QK-RMSNorm ((1 + w) weights) + RoPE (pairs j, j + 128) on the raw fp32 QKV
@@ -529,7 +528,7 @@ hipError_t launch_adarms_norm_f32(const float* x, const float* mod, int M, int T
 // modulo 2*pi in double precision before the fp32 sine / cosine.
 __global__ __launch_bounds__(256) void k_qknorm_rope(const float* raw, const uint16_t* qn_w,
                                                      const uint16_t* kn_w, const int32_t* pos0,
-                                                     float base, int M, int T, uint16_t* q,
+                                                     float base, int M, int T, int TP, uint16_t* q,
                                                      uint16_t* k, uint16_t* v, int kv_rows,
                                                      int kv_row0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -547,7 +546,7 @@ __global__ __launch_bounds__(256) void k_qknorm_rope(const float* raw, const uin
     th -= floor(th / two_pi) * two_pi;
     sincosf((float)th, &sn[e], &cs[e]);
   }
-  const float* src = raw + (size_t)m * kQKV;
+  const float* src = raw + (size_t)(b * TP + t) * kQKV;
   for (int h = 0; h < kHQ + kHK; ++h) {
     const bool isq = h < kHQ;
     const uint16_t* wn = isq ? qn_w : kn_w;
@@ -574,9 +573,10 @@ __global__ __launch_bounds__(256) void k_qknorm_rope(const float* raw, const uin
 }
 
 hipError_t launch_qknorm_rope(const float* raw, const uint16_t* qn_w, const uint16_t* kn_w,
-                              const int32_t* pos0, float base, int M, int T, uint16_t* q,
+                              const int32_t* pos0, float base, int B, int T, int TP, uint16_t* q,
                               uint16_t* k, uint16_t* v, int kv_rows, int kv_row0, hipStream_t s) {
-  k_qknorm_rope<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(raw, qn_w, kn_w, pos0, base, M, T, q, k, v,
+  const int M = B * T;
+  k_qknorm_rope<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(raw, qn_w, kn_w, pos0, base, M, T, TP, q, k, v,
                                                         kv_rows, kv_row0);
   return hipGetLastError();
 }

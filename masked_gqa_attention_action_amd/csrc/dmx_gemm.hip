@@ -5,16 +5,21 @@
 // streaming W from HBM once.  One work-group (WG) owns NT output features and
 // the whole K range; its NWAVES waves split K.  Every wave issues all of its
 // weight loads at kernel start, straight into registers in the MFMA B-operand
-// layout (lane l: 16 contiguous bytes of feature row l%16), then runs the M
-// rows of A past them in 64-row blocks on v_mfma_f32_16x16x32_bf16.  The
-// waves' partial tiles are summed in LDS in a fixed order and the WG applies
-// the epilogue.  No WG ever waits for another WG: every reduction stays
-// inside the WG, so results are deterministic and need no device-scope
-// fences.
+// layout, then runs the rows of A past them in blocks of MT 16-row tiles on
+// v_mfma_f32_16x16x32_bf16.  The waves' partial tiles are summed in LDS in a
+// fixed order and the WG applies the epilogue.  No WG ever waits for another
+// WG: every reduction stays inside the WG, so results are deterministic and
+// need no device-scope fences.
+//
+// Both operands are stored tiled (dmx_tiles.hpp): one 16-row x 32-column tile
+// is 1 KB laid out as the 64 lanes' MFMA fragments, so every load instruction
+// of a wave reads 1 KB of contiguous memory.  Weights are tiled once by the
+// caller; activations are written tiled by the kernel that produces them, with
+// each request's rows padded to a multiple of 16 (padding rows hold anything
+// and their outputs are never stored).
 //
 // A operand sources:
-//   A_GLOBAL   bf16 rows read from global memory (context, GEGLU hidden,
-//              prefix-side normed inputs).
+//   A_GLOBAL   tiled bf16 rows (context, GEGLU hidden, normed inputs).
 //   A_MOD /    AdaRMS prenorm fused into the projection (OpenDM DM0.5
 //              fast-stack article, §2.2, "Adarms 调制 prenorm"):
 //                xn W^T = r * ((x * (1 + scale)) W^T) + shift W^T,
@@ -22,64 +27,49 @@
 //              bf16 residual row scaled by (1 + scale) (one bf16 rounding, as
 //              rounding xn would be); shift W^T is one extra MFMA tile whose
 //              row 0 is the shift vector; r comes from per-tile row sums of
-//              squares that the GEMM producing x wrote in its epilogue (or
-//              from a row-statistics kernel), summed in a fixed order.
+//              squares that the kernel producing x wrote, summed in a fixed
+//              order.
 //   A_MODPRE   as A_MOD with the A rows already bf16(x * (1 + scale)): the
 //              O-projection epilogue writes them from fp32 x1, so x1 is
 //              rounded once on its way into the gate-up projection.
 // Epilogues (the same article's chaining of time modulation with GEGLU
-// gate-up and MLP down):
+// gate-up and MLP down); every store moves 8 consecutive features:
 //   EPI_F32    raw fp32 store (QKV before QK-norm / RoPE)
-//   EPI_MOD    + bias, fp32 store (AdaRMS modulation vectors)
 //   EPI_RESID_* out = resid + gate[b] * y, bf16 / fp32 variants
 //   EPI_GEGLU  tile = 16 gate + 16 up features; h = gelu_tanh(gate) * up
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
+#include "dmx_tiles.hpp"
 
 #include <algorithm>
 
 namespace dmx {
 
-namespace {
-constexpr int XLD = kH + 8;  // LDS row stride (bf16) of the normed activation block
-}
-
-template <int EPI, int NT>
-__device__ __forceinline__ int w_row(const GemmArgs& a, int tile, int r) {
-  if (EPI == EPI_GEGLU) return r < 16 ? tile * 16 + r : a.wrow_up + tile * 16 + (r - 16);
-  return tile * NT + r;
-}
-
-// Stores one output element; returns the value the next AdaRMS normalises
-// (the stored bf16 value, or the fp32 residual x1) for the row statistics.
-template <int EPI, int NT>
-__device__ __forceinline__ float epi_store(const GemmArgs& a, int tile, int m, int c, float v) {
-  const int n = tile * NT + c;
-  const size_t idx = (size_t)m * a.ldo + n;
-  if (EPI == EPI_F32) {
-    a.out_f32[idx] = v;
-  } else if (EPI == EPI_MOD) {
-    a.out_f32[idx] = v + bf2f(a.bias[n]);
-  } else {
-    const size_t b = (size_t)(m / a.T) * a.gate_stride;
-    const float gv = a.gate[b + n];
-    if (EPI == EPI_RESID_BB) a.out_bf16[idx] = f2bf(bf2f(a.resid[idx]) + gv * v);
-    if (EPI == EPI_RESID_BF) {
-      const float x1 = bf2f(a.resid[idx]) + gv * v;
-      a.out_f32[idx] = x1;
-      if (a.out_bf16) a.out_bf16[idx] = f2bf(a.xs_scale ? x1 * (1.0f + a.xs_scale[b + n]) : x1);
-      return x1;
-    }
-    if (EPI == EPI_RESID_FB) {
-      const uint16_t hb = f2bf(a.resid_f32[idx] + gv * v);
-      a.out_bf16[idx] = hb;
-      return bf2f(hb);
-    }
+// Row sums of squares of this WG's outputs as the next AdaRMS sees them: LDS
+// holds the squares of the block's outputs in `sq`; the sum runs over the
+// tile's columns in order (k_pack_rows reproduces it).
+template <int NT>
+__device__ __forceinline__ void write_row_ssq(const GemmArgs& a, int tile, int m0, int nrows, const float* sq) {
+  for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+    if (!row_valid(m0 + r, a.T, a.TP)) continue;
+    float t = 0.f;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) t += sq[r * NT + c];
+    a.ss_out[(size_t)(m0 + r) * a.ss_out_n + tile] = t;
   }
-  return 0.f;
 }
 
-__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+__device__ __forceinline__ void ld8f(const float* p, float v[8]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  const float4 y = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+__device__ __forceinline__ void st8f(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void ld8b(const uint16_t* p, float v[8]) {
   const uint4 r = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -88,23 +78,53 @@ __device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
     v[2 * i + 1] = bf2f((uint16_t)(w[i] >> 16));
   }
 }
-__device__ __forceinline__ void load8(const float* p, float v[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+__device__ __forceinline__ uint4 pack8(const float v[8]) {
+  return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
 }
 
-// Row sums of squares of this WG's outputs as the next AdaRMS sees them: LDS
-// holds the squares of the block's outputs in `sq`; the sum runs over the
-// tile's columns in order (k_row_ssq reproduces it).
-template <int NT>
-__device__ __forceinline__ void write_row_ssq(const GemmArgs& a, int tile, int m0, int rows, const float* sq) {
-  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-    float t = 0.f;
+// Epilogue of 8 consecutive output features n .. n+7 of tiled row prow.
+// Returns in `seen` the values the next AdaRMS normalises (for row sums).
+template <int EPI>
+__device__ __forceinline__ void epi_store8(const GemmArgs& a, int prow, int n, float v[8], float seen[8]) {
+  const int b = prow / a.TP, t = prow - b * a.TP;
+  const size_t lrow = (size_t)b * a.T + t;  // row of a row-major [batch][tokens] tensor
+  if (EPI == EPI_F32) {
+    st8f(a.out_f32 + (size_t)prow * a.ldo + n, v);
+    return;
+  }
+  float g[8];
+  ld8f(a.gate + (size_t)b * a.gate_stride + n, g);
+  if (EPI == EPI_RESID_BB) {
+    float r[8];
+    ld8b(a.resid + lrow * a.ldo + n, r);
 #pragma unroll
-    for (int c = 0; c < NT; ++c) t += sq[r * NT + c];
-    a.ss_out[(size_t)(m0 + r) * a.ss_out_n + tile] = t;
+    for (int i = 0; i < 8; ++i) v[i] = r[i] + g[i] * v[i];
+    *reinterpret_cast<uint4*>(a.out_bf16 + lrow * a.ldo + n) = pack8(v);
+  } else if (EPI == EPI_RESID_BF) {
+    float r[8];
+    ld8b(a.resid + lrow * a.ldo + n, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = r[i] + g[i] * v[i];
+      seen[i] = v[i];
+    }
+    st8f(a.out_f32 + (size_t)prow * a.ldo + n, v);
+    if (a.xs_scale) {
+      float sc[8];
+      ld8f(a.xs_scale + (size_t)b * a.gate_stride + n, sc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * (1.0f + sc[i]);
+    }
+    *reinterpret_cast<uint4*>(a.out_pk + tile_off(prow, n, a.ldo)) = pack8(v);
+  } else if (EPI == EPI_RESID_FB) {
+    float r[8];
+    ld8f(a.resid_f32 + (size_t)prow * a.ldo + n, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = r[i] + g[i] * v[i];
+    const uint4 hb = pack8(v);
+    *reinterpret_cast<uint4*>(a.out_bf16 + lrow * a.ldo + n) = hb;
+    if (a.out_pk) *reinterpret_cast<uint4*>(a.out_pk + tile_off(prow, n, a.ldo)) = hb;
+    ld8b(reinterpret_cast<const uint16_t*>(&hb), seen);
   }
 }
 
@@ -116,33 +136,37 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr bool SCALE = ASRC == A_MOD;    // ... and the (1 + scale) product on A
   constexpr int MB = MT * 16;      // rows per block
   constexpr int RROWS = MB + (MOD ? 16 : 0);  // + the shift tile
+  constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
+  constexpr int NOUT = EPI == EPI_GEGLU ? 16 : NT;  // output features per row
   static_assert(!MOD || NWAVES * KW == kH, "the modulated A operand spans one hidden row");
-  __shared__ float red[NWAVES * RROWS * NT];
-  __shared__ float sq[MB * NT];
-  __shared__ float sS[SCALE ? kH : 4], sH[MOD ? kH : 1], sR[MOD ? MB : 1];
+  __shared__ __attribute__((aligned(16))) float red[NWAVES * RROWS * NT];
+  __shared__ float sq[SSQ ? MB * NOUT : 1];
+  __shared__ __attribute__((aligned(16))) float sS[SCALE ? kH : 4], sH[MOD ? kH : 4], sR[MOD ? MB : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
+  const int kst = a.K >> 5;           // 32-column steps of a row
+  const int ks0 = wave * KSTEPS;      // this wave's first step
   const int k0 = wave * KW;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
-  constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
+  const int lk = (lane >> 4) * 8;
+  const int lr = lane & 15;
 
   // weight slab of this wave: NT rows x KW columns, every load in flight now
   bf16x8 wf[KSTEPS][NTT];
 #pragma unroll
   for (int nt = 0; nt < NTT; ++nt) {
-    const uint16_t* wp = a.W + (size_t)w_row<EPI, NT>(a, tile, nt * 16 + lr) * a.K + k0 + lk;
+    const int wt = EPI == EPI_GEGLU ? (nt == 0 ? tile : a.wtile_up + tile) : tile * NTT + nt;
+    const uint16_t* wp = a.W + ((size_t)wt * kst + ks0) * 512 + lane * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) wf[ks][nt] = load_bf16x8(wp + ks * 32);
+    for (int ks = 0; ks < KSTEPS; ++ks) wf[ks][nt] = load_bf16x8(wp + ks * 512);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // row blocks: MOD kernels take one request's rows per block (T <= MB);
-  // others take MB consecutive rows, blockIdx.y, blockIdx.y + gridDim.y, ...
-  const int bstride = MOD ? a.T : MB;
+  // row blocks: MOD kernels take one request (TP rows) per block; others MB
+  // consecutive tiled rows; block blockIdx.y, blockIdx.y + gridDim.y, ...
+  const int bstride = MOD ? a.TP : MB;
   for (int m0 = blockIdx.y * bstride; m0 < a.M; m0 += gridDim.y * bstride) {
-    const int rows = min(MOD ? a.T : MB, a.M - m0);
-    const int mts = (rows + 15) >> 4;
+    const int mts = min(MT, (MOD ? a.TP : a.M - m0) >> 4);  // tiles in this block
     f32x4 acc[MT][NTT], accs[NTT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -155,15 +179,15 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
     bf16x8 av[KSTEPS][MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int r = min(m0 + mt * 16 + lr, m0 + rows - 1);  // rows past the block feed unused outputs
-      const uint16_t* ap = (MOD ? a.xb : a.A) + (size_t)r * a.K + k0 + lk;
+      const int mtile = (m0 >> 4) + min(mt, mts - 1);  // tiles past the block re-read the last one
+      const uint16_t* ap = a.A + ((size_t)mtile * kst + ks0) * 512 + lane * 8;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) av[ks][mt] = load_bf16x8(ap + ks * 32);
+      for (int ks = 0; ks < KSTEPS; ++ks) av[ks][mt] = load_bf16x8(ap + ks * 512);
     }
     float4 msc = make_float4(0.f, 0.f, 0.f, 0.f), msh = msc;
     float4 ssp[4];
     if (MOD) {
-      const float* mb = a.nmod + (size_t)(m0 / a.T) * 3 * kH;
+      const float* mb = a.nmod + (size_t)(m0 / a.TP) * 3 * kH;
       if (SCALE) msc = *reinterpret_cast<const float4*>(mb + threadIdx.x * 4);  // 256 threads x 4 = 1024
       msh = *reinterpret_cast<const float4*>(mb + kH + threadIdx.x * 4);
       // row statistics: thread (row rr, quarter qq) sums a quarter of the row's partials
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       const int per = a.ss_in_n >> 2;  // ss_in_n is a multiple of 4, at most 64
 #pragma unroll
       for (int i = 0; i < 4; ++i) ssp[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (rr < rows) {
+      if (rr < a.T) {
         const float* sp = a.ss_in + (size_t)(m0 + rr) * a.ss_in_n + qq * per;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -196,20 +220,22 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       // A <- bf16(x * (1 + scale)) (A_MOD); the shift tile's row 0 <- bf16(shift)
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const float4 s0 = *reinterpret_cast<const float4*>(sS + (SCALE ? k0 + ks * 32 + lk : 0));
-        const float4 s1 = *reinterpret_cast<const float4*>(sS + (SCALE ? k0 + ks * 32 + lk + 4 : 0));
-        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        if (SCALE) {
+          const float4 s0 = *reinterpret_cast<const float4*>(sS + k0 + ks * 32 + lk);
+          const float4 s1 = *reinterpret_cast<const float4*>(sS + k0 + ks * 32 + lk + 4);
+          const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (!SCALE) break;
-          bf16x8 t8;
+          for (int mt = 0; mt < MT; ++mt) {
+            bf16x8 t8;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const uint32_t p = pack2(bf2f((uint16_t)av[ks][mt][e]) * sv[e], bf2f((uint16_t)av[ks][mt][e + 1]) * sv[e + 1]);
-            t8[e] = (short)(p & 0xffffu);
-            t8[e + 1] = (short)(p >> 16);
+            for (int e = 0; e < 8; e += 2) {
+              const uint32_t p =
+                  pack2(bf2f((uint16_t)av[ks][mt][e]) * sv[e], bf2f((uint16_t)av[ks][mt][e + 1]) * sv[e + 1]);
+              t8[e] = (short)(p & 0xffffu);
+              t8[e + 1] = (short)(p >> 16);
+            }
+            av[ks][mt] = t8;
           }
-          av[ks][mt] = t8;
         }
         bf16x8 hs = zero_bf16x8();
         if (lr == 0) {
@@ -252,60 +278,69 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       for (int nt = 0; nt < NTT; ++nt) red[(wave * RROWS + MB) * NT + nt * 16 + lr] = accs[nt][0];
     }
     __syncthreads();
-    if (EPI == EPI_GEGLU) {
-      for (int e = threadIdx.x; e < rows * 16; e += NWAVES * 64) {
-        const int r = e >> 4, c = e & 15;
-        float g = 0.f, u = 0.f, gs = 0.f, us = 0.f;
+    const int nrows = mts * 16;
+    for (int e = threadIdx.x; e < nrows * (NOUT / 8); e += NWAVES * 64) {
+      const int r = e / (NOUT / 8), c0 = (e - r * (NOUT / 8)) * 8;
+      if (!row_valid(m0 + r, a.T, a.TP)) continue;
+      float v[8], seen[8];
+      if (EPI == EPI_GEGLU) {
 #pragma unroll
-        for (int w = 0; w < NWAVES; ++w) {
-          g += red[(w * RROWS + r) * NT + c];
-          u += red[(w * RROWS + r) * NT + 16 + c];
-          if (MOD) {
-            gs += red[(w * RROWS + MB) * NT + c];
-            us += red[(w * RROWS + MB) * NT + 16 + c];
+        for (int i = 0; i < 8; ++i) {
+          float g = 0.f, u = 0.f, gs = 0.f, us = 0.f;
+#pragma unroll
+          for (int w = 0; w < NWAVES; ++w) {
+            g += red[(w * RROWS + r) * NT + c0 + i];
+            u += red[(w * RROWS + r) * NT + 16 + c0 + i];
+            if (MOD) {
+              gs += red[(w * RROWS + MB) * NT + c0 + i];
+              us += red[(w * RROWS + MB) * NT + 16 + c0 + i];
+            }
           }
+          if (MOD) {
+            g = sR[r] * g + gs;
+            u = sR[r] * u + us;
+          }
+          v[i] = gelu_tanh(g) * u;
         }
-        if (MOD) {
-          g = sR[r] * g + gs;
-          u = sR[r] * u + us;
-        }
-        a.out_bf16[(size_t)(m0 + r) * a.ldo + tile * 16 + c] = f2bf(gelu_tanh(g) * u);
-      }
-    } else {
-      for (int e = threadIdx.x; e < rows * NT; e += NWAVES * 64) {
-        const int r = e / NT, c = e - (e / NT) * NT;
-        float v = 0.f, vs = 0.f;
+        *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, tile * 16 + c0, a.ldo)) = pack8(v);
+      } else {
 #pragma unroll
-        for (int w = 0; w < NWAVES; ++w) {
-          v += red[(w * RROWS + r) * NT + c];
-          if (MOD) vs += red[(w * RROWS + MB) * NT + c];
+        for (int i = 0; i < 8; ++i) {
+          float t = 0.f, ts = 0.f;
+#pragma unroll
+          for (int w = 0; w < NWAVES; ++w) {
+            t += red[(w * RROWS + r) * NT + c0 + i];
+            if (MOD) ts += red[(w * RROWS + MB) * NT + c0 + i];
+          }
+          v[i] = MOD ? sR[r] * t + ts : t;
         }
-        if (MOD) v = sR[r] * v + vs;
-        const float seen = epi_store<EPI, NT>(a, tile, m0 + r, c, v);
-        if (SSQ) sq[r * NT + c] = seen * seen;
+        epi_store8<EPI>(a, m0 + r, tile * NT + c0, v, seen);
+        if (SSQ) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sq[r * NOUT + c0 + i] = seen[i] * seen[i];
+        }
       }
-      if (SSQ && a.ss_out) {
-        __syncthreads();
-        write_row_ssq<NT>(a, tile, m0, rows, sq);
-      }
+    }
+    if (SSQ && a.ss_out) {
+      __syncthreads();
+      write_row_ssq<NOUT>(a, tile, m0, nrows, sq);
     }
     __syncthreads();
   }
 }
 
-#define DMX_GEMM(EPI, NT, NW, KS, SRC, MT, MSPLIT) \
-  k_gemm<EPI, NT, NW, KS, SRC, MT><<<dim3(a.ntiles, MSPLIT), dim3((NW) * 64), 0, s>>>(a)
+#define DMX_GEMM(EPI, NT, NW, KS, SRC, MT, GY) \
+  k_gemm<EPI, NT, NW, KS, SRC, MT><<<dim3(a.ntiles, GY), dim3((NW) * 64), 0, s>>>(a)
 
 int gemm_config(GemmKind kind, GemmArgs& a) {
   switch (kind) {
-    case GEMM_MOD: a.ntiles = 3 * kH / 16; a.K = kH; break;
     case GEMM_QKV1024: a.ntiles = kQKV / 16; a.K = kH; break;
     case GEMM_QKV1024_MOD: a.ntiles = kQKV / 16; a.K = kH; break;
     case GEMM_QKV2560: a.ntiles = kQKV / 16; a.K = 2560; break;
     case GEMM_OPROJ: a.ntiles = kH / 16; a.K = kHQ * kD; break;
     case GEMM_OPROJ_F32: a.ntiles = kH / 16; a.K = kHQ * kD; break;
-    case GEMM_GATEUP: a.ntiles = kI / 16; a.K = kH; a.wrow_up = kI; break;
-    case GEMM_GATEUP_MOD: a.ntiles = kI / 16; a.K = kH; a.wrow_up = kI; break;
+    case GEMM_GATEUP: a.ntiles = kI / 16; a.K = kH; a.wtile_up = kI / 16; break;
+    case GEMM_GATEUP_MOD: a.ntiles = kI / 16; a.K = kH; a.wtile_up = kI / 16; break;
     case GEMM_DOWN: a.ntiles = kH / 16; a.K = kI; break;
     case GEMM_DOWN_F32RES: a.ntiles = kH / 16; a.K = kI; break;
   }
@@ -313,54 +348,69 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
 }
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
-  // row blocks: one per WG up to 4 (more rows loop inside the WG)
-  const int mb16 = std::min(4, (a.M + 15) / 16), mb32 = std::min(4, (a.M + 31) / 32);
-  const int nreq = std::min(4, a.T > 0 ? (a.M + a.T - 1) / a.T : 1);  // MOD: one request per block
+  // row blocks: one per WG up to 4 (more blocks loop inside the WG)
+  const int tiles = a.M / 16;
+  const int mb1 = std::min(4, tiles), mb2 = std::min(4, (tiles + 1) / 2);
+  const int nreq = std::min(4, a.M / a.TP);  // MOD: one request per block
   switch (kind) {
-    case GEMM_MOD: DMX_GEMM(EPI_MOD, 16, 4, 8, A_GLOBAL, 1, mb16); break;
-    case GEMM_QKV1024: DMX_GEMM(EPI_F32, 16, 4, 8, A_GLOBAL, 2, mb32); break;
+    case GEMM_QKV1024: DMX_GEMM(EPI_F32, 16, 4, 8, A_GLOBAL, 2, mb2); break;
     case GEMM_QKV1024_MOD: DMX_GEMM(EPI_F32, 16, 4, 8, A_MOD, 4, nreq); break;
     case GEMM_QKV2560: DMX_GEMM(EPI_F32, 16, 4, 20, A_GLOBAL, 1, 4); break;
-    case GEMM_OPROJ: DMX_GEMM(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 1, mb16); break;
-    case GEMM_OPROJ_F32: DMX_GEMM(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 1, mb16); break;
-    case GEMM_GATEUP: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 2, mb32); break;
+    case GEMM_OPROJ: DMX_GEMM(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 1, mb1); break;
+    case GEMM_OPROJ_F32: DMX_GEMM(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 1, mb1); break;
+    case GEMM_GATEUP: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 2, mb2); break;
     case GEMM_GATEUP_MOD: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, nreq); break;
-    case GEMM_DOWN: DMX_GEMM(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 1, mb16); break;
-    case GEMM_DOWN_F32RES: DMX_GEMM(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 1, mb16); break;
+    case GEMM_DOWN: DMX_GEMM(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 1, mb1); break;
+    case GEMM_DOWN_F32RES: DMX_GEMM(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 1, mb1); break;
   }
   return hipGetLastError();
 }
 
-// Row sums of squares of bf16 rows x [M][1024] -> ss[M][64]: lane p of the
-// row's wave sums the squares of columns 16p .. 16p+15 in column order, with
-// every square rounded before the add, exactly as write_row_ssq does.
-__global__ __launch_bounds__(256) void k_row_ssq(const uint16_t* x, int M, float* ss) {
+// Row-major bf16 rows [B][T][K] -> tiled rows [B*TP][K] (request b's token t
+// at tiled row b*TP + t).  One wave per row; lane j takes the 16-column
+// groups j, j + 64, ...  With ss != null (K = 1024) it also writes the row's
+// 64 sums of squares of 16 columns, summed in column order with every square
+// rounded before the add, exactly as the GEMM epilogues do.
+__global__ __launch_bounds__(256) void k_pack_rows(const uint16_t* x, int B, int T, int TP, int K, uint16_t* out,
+                                                   float* ss) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63, m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  const uint4 r0 = *reinterpret_cast<const uint4*>(x + (size_t)m * kH + lane * 16);
-  const uint4 r1 = *reinterpret_cast<const uint4*>(x + (size_t)m * kH + lane * 16 + 8);
-  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  float t = 0.f;
+  if (m >= B * T) return;
+  const int b = m / T, t = m - b * T;
+  const int prow = b * TP + t;
+  const uint16_t* src = x + (size_t)m * K;
+  for (int j = lane; j < K / 16; j += 64) {
+    const uint4 r0 = *reinterpret_cast<const uint4*>(src + j * 16);
+    const uint4 r1 = *reinterpret_cast<const uint4*>(src + j * 16 + 8);
+    *reinterpret_cast<uint4*>(out + tile_off(prow, j * 16, K)) = r0;
+    *reinterpret_cast<uint4*>(out + tile_off(prow, j * 16 + 8, K)) = r1;
+    if (ss) {
+      const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float lo = bf2f((uint16_t)(w[i] & 0xffffu)), hi = bf2f((uint16_t)(w[i] >> 16));
-    const float l2 = lo * lo, h2 = hi * hi;
-    t += l2;
-    t += h2;
+      for (int i = 0; i < 8; ++i) {
+        const float lo = bf2f((uint16_t)(w[i] & 0xffffu)), hi = bf2f((uint16_t)(w[i] >> 16));
+        const float l2 = lo * lo, h2 = hi * hi;
+        acc += l2;
+        acc += h2;
+      }
+      ss[(size_t)prow * kSsParts + j] = acc;
+    }
   }
-  ss[(size_t)m * kSsParts + lane] = t;
 }
 
-hipError_t launch_row_ssq(const uint16_t* x, int M, float* ss, hipStream_t s) {
-  k_row_ssq<<<dim3((M + 3) / 4), dim3(256), 0, s>>>(x, M, ss);
+hipError_t launch_pack_rows(const uint16_t* x, int B, int T, int TP, int K, uint16_t* out, float* ss,
+                            hipStream_t s) {
+  const int rows = B * T;
+  k_pack_rows<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(x, B, T, TP, K, out, ss);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Modulation vectors of several (W_mod, b_mod) pairs in one launch:
 // out_j[b] = W_j * cond[b] + b_j.  Work-group (j, tile) owns 16 features of
-// matrix j; all loads of its 32 KB weight slab are issued up front.
+// matrix j (tiled weights); all loads of its 32 KB weight slab are issued up
+// front.
 __global__ __launch_bounds__(256) void k_mod_multi(ModBatch mb) {
   const int j = blockIdx.x / (3 * kH / 16), tile = blockIdx.x - j * (3 * kH / 16);
   const ModJob& job = mb.job[j];
@@ -369,9 +419,9 @@ __global__ __launch_bounds__(256) void k_mod_multi(ModBatch mb) {
   const int lr = lane & 15, lk = (lane >> 4) * 8;
   const int k0 = wave * 256;
   bf16x8 wf[8];
-  const uint16_t* wp = job.w + (size_t)(tile * 16 + lr) * kH + k0 + lk;
+  const uint16_t* wp = job.w + ((size_t)tile * (kH / 32) + wave * 8) * 512 + lane * 8;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) wf[ks] = load_bf16x8(wp + ks * 32);
+  for (int ks = 0; ks < 8; ++ks) wf[ks] = load_bf16x8(wp + ks * 512);
   const uint16_t* cond = job.cond;
   for (int b0 = 0; b0 < mb.B; b0 += 16) {
     const int rows = min(16, mb.B - b0);

@@ -9,57 +9,61 @@ namespace dmx {
 // Epilogues.  RESID variants: out = resid + gate[b] * y with the residual and
 // output stored as bf16 (B) or fp32 (F): RESID_BB, RESID_BF (bf16 in, fp32
 // out), RESID_FB (fp32 in, bf16 out).
-enum Epi { EPI_F32 = 0, EPI_MOD = 1, EPI_RESID_BB = 2, EPI_GEGLU = 3, EPI_RESID_BF = 4, EPI_RESID_FB = 5 };
+enum Epi { EPI_F32 = 0, EPI_RESID_BB = 2, EPI_GEGLU = 3, EPI_RESID_BF = 4, EPI_RESID_FB = 5 };
 
 // A-operand sources of the GEMM (see dmx_gemm.hip).
 enum ASrc { A_GLOBAL = 0, A_MOD = 1, A_MODPRE = 2 };
 
-// Skinny GEMM y[m][n] = sum_k A[m][k] * W[n][k] with a fused epilogue.
+// Skinny GEMM y[m][n] = sum_k A[m][k] * W[n][k] with a fused epilogue.  A and W
+// are tiled (dmx_tiles.hpp); rows are tiled rows (request b, token t at
+// b * TP + t).  Row-major [batch][tokens] tensors (resid / out_bf16 of the
+// bf16-residual epilogues) are indexed by b * T + t; fp32 intermediates and
+// out_f32 by the tiled row.
 struct GemmArgs {
-  const uint16_t* A;  // A_GLOBAL: [M][K] bf16
-  const uint16_t* xb; // A_MOD: bf16 residual rows x [M][1024];
-                      // A_MODPRE: the rows already scaled, bf16(x * (1 + scale))
+  const uint16_t* A;  // tiled bf16 [M][K]; A_MOD: x, A_MODPRE: bf16(x * (1 + scale))
   const float* nmod;  // A_MOD*: modulation [B][3][1024] (scale | shift | gate)
   const float* ss_in; // A_MOD*: row sums of squares of x, [M][ss_in_n] partials
   int ss_in_n;        //   a multiple of 4 up to 64
   float* ss_out;      // EPI_RESID_BF / _FB: optional [M][ss_out_n] partials, one
   int ss_out_n;       //   per N-tile of 16 features (ntiles == ss_out_n)
-  const float* xs_scale;  // EPI_RESID_BF: out_bf16 = bf16(out * (1 + xs_scale[b][n])),
+  const float* xs_scale;  // EPI_RESID_BF: out_pk = bf16(out * (1 + xs_scale[b][n])),
                           //   row b at xs_scale + b * gate_stride (null: bf16(out))
-  const uint16_t* W;  // weight rows of K bf16
-  int M, K;
-  int ntiles;         // grid = ntiles work-groups
-  int T;              // tokens per request: row m belongs to request m / T
-  int wrow_up;        // GEGLU: W row of the first "up" feature
-  float* out_f32;     // EPI_F32 / EPI_MOD / EPI_RESID_BF output
-  uint16_t* out_bf16; // EPI_RESID_BB / EPI_RESID_FB / EPI_GEGLU output
-  int ldo;            // row stride of the output (and of resid)
-  const uint16_t* bias;    // EPI_MOD: per-feature bias
+  const uint16_t* W;  // tiled weights [N][K]
+  int M, K;           // M = B * TP tiled rows
+  int T, TP;          // tokens per request and their padded count
+  int ntiles;         // grid.x = ntiles work-groups
+  int wtile_up;       // GEGLU: weight tile of the first "up" feature
+  float* out_f32;     // EPI_F32 / EPI_RESID_BF output [M][ldo]
+  uint16_t* out_bf16; // EPI_RESID_BB / EPI_RESID_FB row-major output
+  uint16_t* out_pk;   // tiled bf16 output (GEGLU h, RESID_BF x1s, RESID_FB copy)
+  int ldo;            // features per output row
   const float* gate;       // EPI_RESID_*: gate of request b at gate + b * gate_stride
   int gate_stride;
-  const uint16_t* resid;   // EPI_RESID_B*: bf16 residual, same layout as the output
-  const float* resid_f32;  // EPI_RESID_FB: fp32 residual
+  const uint16_t* resid;   // EPI_RESID_B*: bf16 residual, row-major
+  const float* resid_f32;  // EPI_RESID_FB: fp32 residual [M][ldo]
 };
 
 // Gemm shape presets (host picks one per projection).
 enum GemmKind {
-  GEMM_MOD = 0,             // N = 3072, K = 1024, + bias, fp32 out
   GEMM_QKV1024 = 1,         // N = 4096, K = 1024, fp32 out, A given
   GEMM_QKV1024_MOD = 2,     // as above with the AdaRMS prenorm of bf16 x fused
   GEMM_QKV2560 = 3,         // N = 4096, K = 2560, fp32 out
   GEMM_OPROJ = 4,           // N = 1024, K = 2048, gated residual (bf16 -> bf16)
   GEMM_OPROJ_F32 = 5,       // as GEMM_OPROJ, fp32 output (layer-internal residual)
   GEMM_GATEUP = 6,          // N = 2 x 4096, K = 1024, GEGLU, A given
-  GEMM_GATEUP_MOD = 7,      // as above with the AdaRMS prenorm of bf16 x1 fused
+  GEMM_GATEUP_MOD = 7,      // as above with the AdaRMS prenorm of x1 fused
   GEMM_DOWN = 8,            // N = 1024, K = 4096, gated residual (bf16 -> bf16)
   GEMM_DOWN_F32RES = 9,     // as GEMM_DOWN, fp32 residual input
 };
 int gemm_config(GemmKind kind, GemmArgs& a);
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s);
-// Row sums of squares of bf16 rows [M][1024] as 64 partials of 16 columns,
-// the same values (and summation order) a down-projection epilogue writes.
+
+// Row-major bf16 [B][T][K] -> tiled [B*TP][K]; with ss (K = 1024) also the 64
+// row sums of squares of 16 columns per row, the values and summation order
+// of the GEMM epilogues.
 constexpr int kSsParts = 1024 / 16;
-hipError_t launch_row_ssq(const uint16_t* x, int M, float* ss, hipStream_t s);
+hipError_t launch_pack_rows(const uint16_t* x, int B, int T, int TP, int K, uint16_t* out, float* ss,
+                            hipStream_t s);
 
 // Several modulation GEMVs in one launch: out_j[b] = W_j cond_j[b] + bias_j.
 struct ModJob {
@@ -77,24 +81,25 @@ hipError_t launch_mod_multi(const ModBatch& mb, hipStream_t s);
 
 hipError_t launch_adarms_norm(const uint16_t* x, const float* mod, int M, int T, uint16_t* xn,
                               hipStream_t s);
-hipError_t launch_adarms_norm_f32(const float* x, const float* mod, int M, int T, uint16_t* xn,
-                                  hipStream_t s);
 
+// raw: fp32 QKV projection [B*TP][4096] (tiled rows); q / k / v row-major
 hipError_t launch_qknorm_rope(const float* raw, const uint16_t* qn_w, const uint16_t* kn_w,
-                              const int32_t* pos0, float base, int M, int T, uint16_t* q,
+                              const int32_t* pos0, float base, int B, int T, int TP, uint16_t* q,
                               uint16_t* k, uint16_t* v, int kv_rows, int kv_row0, hipStream_t s);
 
 struct AttnArgs {
   const uint16_t *q, *ks, *vs, *kp, *vp;
   // fused path: when raw != nullptr, q / ks / vs are ignored and built from the
-  // raw fp32 QKV projection [B*C][4096] with QK-norm (1 + w) and RoPE at
-  // pos0[b] + t, base rope_base
+  // raw fp32 QKV projection [B*TP][4096] (tiled rows) with QK-norm (1 + w) and
+  // RoPE at pos0[b] + t, base rope_base
   const float* raw;
   const uint16_t *qn_w, *kn_w;
   const int32_t* pos0;
   float rope_base;
   const uint8_t* mask;
   int B, C, P;
+  int TP;       // padded chunk (tiled rows per request)
+  int ctx_tiled;  // 1: ctx is written tiled [B*TP][2048]; 0: row-major [B][C][2048]
   int S;        // prefix splits; split index S holds the suffix keys
   int kps;      // prefix keys per split (multiple of 32)
   int R16;      // stacked query rows (2 * C) rounded up to 16

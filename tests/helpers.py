@@ -89,8 +89,16 @@ def delta_gate(name, got_out, ref_out, base, rel=ERR_REL_RMS, min_cos=0.999):
     assert cos >= min_cos, msg
 
 
+def to_dev_w(bits):
+    """A weight matrix on the device in the library's tiled layout."""
+    import masked_gqa_attention_action_amd as dmx
+    return dmx.pack_weight(to_dev(bits))
+
+
 def device_weights(wbits: dict) -> dict:
-    return {k: to_dev(v) for k, v in wbits.items()}
+    """Layer weights on the device: matrices tiled, vectors plain."""
+    import masked_gqa_attention_action_amd as dmx
+    return dmx.pack_layer_weights({k: to_dev(v) for k, v in wbits.items()})
 
 
 def oracle_weights(wbits: dict) -> dict:

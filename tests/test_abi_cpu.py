@@ -88,6 +88,11 @@ def test_validation_errors_before_launch(dmx):
     assert L.dmx_suffix_layer_forward(ctypes.byref(lw), ctypes.byref(kv), FAKE, FAKE, FAKE, 1, 50, FAKE, FAKE,
                                       1 << 30, None) == dmx.ERR_MISALIGNED
     assert b"w_down" in L.dmx_last_error_string()
+    assert L.dmx_pack_weight(None, 16, 32, FAKE, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_pack_weight(FAKE, 24, 32, ctypes.c_void_p(0x90000), None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_pack_weight(FAKE, 16, 48, ctypes.c_void_p(0x90000), None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_pack_weight(FAKE, 16, 32, ctypes.c_void_p(0x10200), None) == dmx.ERR_INVALID_ARG  # overlap
+    assert b"overlaps" in L.dmx_last_error_string()
     g = ctypes.c_void_p()
     assert L.dmx_stack_graph_create(None, FAKE, ctypes.byref(g)) == dmx.ERR_INVALID_ARG
     assert L.dmx_graph_launch(None, None) == dmx.ERR_INVALID_ARG

@@ -13,7 +13,8 @@ import pytest
 
 import oracle as orc
 from masked_gqa_attention_action_amd import synth
-from tests.helpers import LAYER_BRANCH_REL, delta_gate, device_weights, f64, from_dev, gate, oracle_weights, stage_gate, to_dev
+from tests.helpers import (LAYER_BRANCH_REL, delta_gate, device_weights, f64, from_dev, gate, oracle_weights, stage_gate,
+                           to_dev, to_dev_w)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -40,13 +41,27 @@ def rand_bf16(r, shape, std=1.0):
     return synth.bf16_bits(r.standard_normal(shape, dtype=np.float32) * np.float32(std))
 
 
+# ---------------------------------------------------------------- weight tiling
+@pytest.mark.parametrize("rows,cols", [(16, 32), (48, 96), (4096, 1024), (1024, 4096)])
+def test_pack_weight_layout(rows, cols):
+    """Bit-exact: tile (rt, ct) at (rt * cols/32 + ct) * 512, inside it the
+    8 columns 8q..8q+7 of tile row i at (i + 16 q) * 8."""
+    r = rng(rows + cols)
+    w = rand_bf16(r, (rows, cols))
+    got = dmx.pack_weight(to_dev(w))
+    torch.cuda.synchronize()
+    got_bits = got.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    want = w.reshape(rows // 16, 16, cols // 32, 4, 8).transpose(0, 2, 3, 1, 4).ravel()
+    assert np.array_equal(got_bits, want)
+
+
 # ---------------------------------------------------------------- AdaRMS
 @pytest.mark.parametrize("B,T", [(1, 10), (1, 50), (16, 50), (3, 1)])
 def test_adarms_prenorm(B, T):
     r = rng(100 + B * 7 + T)
     x, cond = rand_bf16(r, (B, T, synth.H)), rand_bf16(r, (B, synth.H))
     w, bias = rand_bf16(r, (3 * synth.H, synth.H), 0.02), rand_bf16(r, (3 * synth.H,), 0.02)
-    xn, mod = dmx.adarms_prenorm(to_dev(x), to_dev(cond), to_dev(w), to_dev(bias))
+    xn, mod = dmx.adarms_prenorm(to_dev(x), to_dev(cond), to_dev_w(w), to_dev(bias))
     torch.cuda.synchronize()
     for b in range(B):
         xr, mr = orc.adarms(f64(x[b]), f64(cond[b]), f64(w), f64(bias))
@@ -63,7 +78,7 @@ def test_qkv_qknorm_rope_suffix(B, T, pos0):
     qn, kn = rand_bf16(r, (256,), 0.02), rand_bf16(r, (256,), 0.02)
     pos = np.array([pos0 + 13 * b for b in range(B)], dtype=np.int32)
     ws = dmx.new_workspace(B, T, 0)
-    q, k, v = dmx.qkv_qknorm_rope(to_dev(xn), to_dev(w), to_dev(qn), to_dev(kn), to_dev(pos, "raw"), ws)
+    q, k, v = dmx.qkv_qknorm_rope(to_dev(xn), to_dev_w(w), to_dev(qn), to_dev(kn), to_dev(pos, "raw"), ws)
     torch.cuda.synchronize()
     for b in range(B):
         qr, kr, vr = orc.qkv_qknorm_rope(f64(xn[b]), f64(w), f64(qn), f64(kn), pos[b] + np.arange(T), 8, 4, 256)
@@ -82,7 +97,7 @@ def test_qkv_prefix_hidden2560_into_cache():
     kc = torch.full((1, 4, P, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
     vc = torch.full((1, 4, P, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
     pos = to_dev(np.zeros(1, dtype=np.int32), "raw")
-    q, k, v = dmx.qkv_qknorm_rope(to_dev(inp["x"]).view(1, T, 2560), to_dev(inp["w_qkv"]), to_dev(inp["q_norm"]),
+    q, k, v = dmx.qkv_qknorm_rope(to_dev(inp["x"]).view(1, T, 2560), to_dev_w(inp["w_qkv"]), to_dev(inp["q_norm"]),
                                   to_dev(inp["k_norm"]), pos, ws, k=kc, v=vc, kv_rows=P)
     torch.cuda.synchronize()
     assert torch.isfinite(k).all() and torch.isfinite(v).all()
@@ -104,7 +119,7 @@ def test_qkv_writes_only_its_cache_rows():
     ws = dmx.new_workspace(1, T, 0)
     kc = torch.full((1, 4, P, 256), 7.0, dtype=torch.bfloat16, device="cuda")
     vc = torch.full((1, 4, P, 256), 7.0, dtype=torch.bfloat16, device="cuda")
-    dmx.qkv_qknorm_rope(to_dev(xn), to_dev(w), to_dev(qn), to_dev(kn), to_dev(np.array([5], np.int32), "raw"), ws,
+    dmx.qkv_qknorm_rope(to_dev(xn), to_dev_w(w), to_dev(qn), to_dev(kn), to_dev(np.array([5], np.int32), "raw"), ws,
                         k=kc, v=vc, kv_rows=P, kv_row0=row0)
     torch.cuda.synchronize()
     untouched = torch.ones(P, dtype=torch.bool)
@@ -214,8 +229,8 @@ def test_oproj_gated_residual(B, T):
     mod = r.standard_normal((B, 3072)).astype(np.float32)
     resid = rand_bf16(r, (B, T, 1024))
     ws = dmx.new_workspace(B, T, 0)
-    out = dmx.oproj_gated_residual(to_dev(ctx), to_dev(w_o), to_dev(mod, "raw"), to_dev(resid), ws)
-    out2 = dmx.oproj_gated_residual(to_dev(ctx), to_dev(w_o), to_dev(mod, "raw"), to_dev(resid), ws)
+    out = dmx.oproj_gated_residual(to_dev(ctx), to_dev_w(w_o), to_dev(mod, "raw"), to_dev(resid), ws)
+    out2 = dmx.oproj_gated_residual(to_dev(ctx), to_dev_w(w_o), to_dev(mod, "raw"), to_dev(resid), ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
     for b in range(B):
@@ -235,7 +250,7 @@ def test_geglu_mlp(B, T):
     mod2 = r.standard_normal((B, 3072)).astype(np.float32)
     resid = rand_bf16(r, (B, T, 1024))
     ws = dmx.new_workspace(B, T, 0)
-    out = dmx.geglu_mlp(to_dev(xn2), to_dev(w_gu), to_dev(w_d), to_dev(mod2, "raw"), to_dev(resid), ws)
+    out = dmx.geglu_mlp(to_dev(xn2), to_dev_w(w_gu), to_dev_w(w_d), to_dev(mod2, "raw"), to_dev(resid), ws)
     torch.cuda.synchronize()
     for b in range(B):
         ref, _ = orc.geglu_mlp(f64(xn2[b]), f64(w_gu), f64(w_d), mod2[b, 2048:].astype(np.float64), f64(resid[b]))
