@@ -55,7 +55,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // (for a stack) the modulation vectors of every layer of one step.  Rows of
 // the tiled / fp32 intermediates are tiled rows (each request padded to TP).
 struct WsLayout {
-  size_t mod1, mod2, apk, xp, raw, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
+  size_t mod1, mod2, apk, xp, raw, ss_q, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
   int TP;
   AttnArgs attn;
 };
@@ -76,7 +76,8 @@ bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
   L.mod2 = take((size_t)B * 3 * kH * 4);
   L.apk = take(M * DMX_PREFIX_HIDDEN * 2);  // tiled copy of a row-major A operand
   L.xp = take(M * kH * 2);                  // tiled layer input
-  L.raw = take(M * kQKV * 4);               // fp32 QKV projection
+  L.raw = take(M * kQKV * 4);               // fp32 QKV projection (tiled in the fused layer)
+  L.ss_q = take(M * kQkvTiles * 4);         // its q / k head sums of squares
   L.ctx = take(M * kHQ * kD * 2);           // tiled attention output
   L.x1 = take(M * kH * 4);   // fp32 residual between the two halves of a layer
   L.x1s = take(M * kH * 2);  // tiled bf16(x1 * (1 + scale2)), the gate-up A operand
@@ -162,10 +163,8 @@ int enq_qkv(const dmx_bf16* xn, const dmx_bf16* w_qkv, const dmx_bf16* qn, const
 AttnArgs attn_args(const WsLayout& L, void* ws) {
   AttnArgs a = L.attn;
   a.q = a.ks = a.vs = a.kp = a.vp = nullptr;
-  a.raw = nullptr;
-  a.qn_w = a.kn_w = nullptr;
-  a.pos0 = nullptr;
-  a.rope_base = 10000.0f;
+  a.y = nullptr;
+  a.ss_q = nullptr;
   a.mask = nullptr;
   a.part_o = at<uint16_t>(ws, L.part_o);
   a.part_ml = at<float>(ws, L.part_ml);
@@ -241,7 +240,8 @@ int enq_geglu(const dmx_bf16* xn2, const dmx_bf16* w_gu, const dmx_bf16* w_down,
 // The fused layer chain (modulation vectors mod1 / mod2 already computed,
 // the workspace holding x_in tiled in xp and its row sums of squares in ss_b,
 // 64 per row):
-//   QKV GEMM with AdaRMS #1 fused -> attention with QK-norm + RoPE on load ->
+//   QKV GEMM with AdaRMS #1 and QK-norm weights + RoPE fused -> attention
+//   (1 / rms of q, k on load) ->
 //   combine (tiled context) -> O-projection + gated residual (fp32 x1, tiled
 //   bf16(x1 * (1 + scale2)), row sums of squares of x1) -> gate-up GEMM with
 //   AdaRMS #2 fused + GEGLU -> down projection + gated residual (row-major
@@ -259,6 +259,7 @@ int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const d
   float* ss_b = at<float>(ws, L.ss_b);
   const int M = B * L.TP;
 
+  float* ss_q = at<float>(ws, L.ss_q);
   GemmArgs g = gemm_args();
   gemm_config(GEMM_QKV1024_MOD, g);
   g.A = xp;
@@ -271,13 +272,16 @@ int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const d
   g.TP = L.TP;
   g.out_f32 = raw;
   g.ldo = kQKV;
+  g.qn_w = w->q_norm;
+  g.kn_w = w->k_norm;
+  g.pos0 = pos0;
+  g.rope_base = 10000.0f;
+  g.ss_q = ss_q;
   DMX_TRY(hip_check(launch_gemm(GEMM_QKV1024_MOD, g, s), "QKV GEMM launch"));
 
   AttnArgs a = attn_args(L, ws);
-  a.raw = raw;
-  a.qn_w = w->q_norm;
-  a.kn_w = w->k_norm;
-  a.pos0 = pos0;
+  a.y = raw;
+  a.ss_q = ss_q;
   a.kp = kv->k;
   a.vp = kv->v;
   a.mask = kv->mask;

@@ -5,10 +5,14 @@
 // Work decomposition (flash-decoding style, split over the prefix):
 //   one work-group per (request b, KV head g, key split s).  Splits 0..S-1 own
 //   kps consecutive prefix rows each; split S owns the chunk's own suffix keys.
-//   The 2 query heads that share KV head g are stacked into one tile of
-//   2*chunk query rows (row r: head 2g + r / chunk, token r % chunk), so every
+//   The 2 query heads that share KV head g are stacked into 2*TP query rows
+//   (TP = chunk padded to 16; row r: head 2g + r / TP, token r % TP), so every
 //   K/V row is read from HBM once per request; wave w owns stacked rows
-//   16w .. 16w+15.
+//   16w .. 16w+15 (one token tile of one head).
+//   In the fused layer the queries and suffix keys arrive from the QKV
+//   epilogue already rotated: q = r * y with y = rope((1 + w) * x) and
+//   r = 1 / sqrt(mean x^2 + eps) from the epilogue's sums of squares, so this
+//   kernel only scales and rounds them.
 //   All K/V blocks (32 keys) of the split are staged row-major in LDS at once.
 //   The products run transposed on v_mfma_f32_16x16x32_bf16:
 //     S^T = K Q^T   (A = K rows from LDS, B = the wave's query fragments),
@@ -40,138 +44,84 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 }  // namespace
 
-// RoPE frequency table in LDS, in revolutions per position:
-// f[j] = rope_base^(-j/128) / (2 pi), j < 128 (pairs j, j + 128).
-__device__ __forceinline__ void rope_table(double* f, float base) {
-  if (threadIdx.x < kD / 2) {
-    const double lb = log2((double)base);
-    f[threadIdx.x] = exp2(-(double)threadIdx.x / (kD / 2) * lb) * 0.15915494309189533577;
-  }
-}
-
-// sin / cos of pos * f (revolutions), reduced exactly in double first.
-__device__ __forceinline__ void rope_sincos(double pos, double f, float& sn, float& cs) {
-  double rev = pos * f;
-  rev -= floor(rev);
-  const float r = (float)rev;
-  sn = __builtin_amdgcn_sinf(r);
-  cs = __builtin_amdgcn_cosf(r);
-}
-
-// Q fragments of one stacked query row built from the raw fp32 projection:
-// lane (lr, lq) holds dims lq*8 + ks*32 + e (ks < 8, e < 8) of its row, which
-// includes both halves (ks and ks + 4) of every rotation pair it touches.
+// Q fragments of one stacked query row from the tiled fp32 epilogue output:
+// lane (lr, lq) holds dims ks*32 + lq*8 + e (ks < 8, e < 8) of its row; each
+// load instruction of the wave reads 1 KB of contiguous memory.
 struct QRaw {
   float4 x[8][2];
+  float4 ss[2];
 };
 
-__device__ __forceinline__ void q_load(const AttnArgs& a, int b, int i, int head, int lq, QRaw& q) {
-  const float* src = a.raw + (size_t)(b * a.TP + i) * kQKV + head * kD + lq * 8;
+__device__ __forceinline__ void q_load(const AttnArgs& a, int prow, int head, int lq, QRaw& q) {
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    q.x[ks][0] = *reinterpret_cast<const float4*>(src + ks * 32);
-    q.x[ks][1] = *reinterpret_cast<const float4*>(src + ks * 32 + 4);
+    const float* src = a.y + tile_off_f32(prow, head * kD + ks * 32 + lq * 8, kQKV);
+    q.x[ks][0] = *reinterpret_cast<const float4*>(src);
+    q.x[ks][1] = *reinterpret_cast<const float4*>(src + 256);
   }
+  const float* ss = a.ss_q + (size_t)prow * kQkvTiles + head * 8;
+  q.ss[0] = *reinterpret_cast<const float4*>(ss);
+  q.ss[1] = *reinterpret_cast<const float4*>(ss + 4);
 }
 
-__device__ __forceinline__ void q_finish(const AttnArgs& a, const double* ftab, const uint16_t* qn, const QRaw& q,
-                                         int b, int i, bool ok, int lq, bf16x8 qf[8]) {
-  float ss = 0.f;
+__device__ __forceinline__ void q_finish(const QRaw& q, bool ok, bf16x8 qf[8]) {
+  const float t = ((q.ss[0].x + q.ss[0].y) + (q.ss[0].z + q.ss[0].w)) +
+                  ((q.ss[1].x + q.ss[1].y) + (q.ss[1].z + q.ss[1].w));
+  const float rn = 1.0f / sqrtf(t * (1.0f / kD) + kEps);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const float4 x0 = q.x[ks][0], x1 = q.x[ks][1];
-    ss += x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w + x1.x * x1.x + x1.y * x1.y + x1.z * x1.z +
-          x1.w * x1.w;
-  }
-  ss += __shfl_xor(ss, 16, 64);
-  ss += __shfl_xor(ss, 32, 64);
-  const float rn = 1.0f / sqrtf(ss * (1.0f / kD) + kEps);
-  const double pos = (double)a.pos0[b] + (double)i;
-  // rotation pairs: dims lq*8 + ks*32 + e (ks < 4) and the same + 128 (ks + 4)
+    const float v[8] = {q.x[ks][0].x, q.x[ks][0].y, q.x[ks][0].z, q.x[ks][0].w,
+                        q.x[ks][1].x, q.x[ks][1].y, q.x[ks][1].z, q.x[ks][1].w};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const float lo[8] = {q.x[ks][0].x, q.x[ks][0].y, q.x[ks][0].z, q.x[ks][0].w,
-                         q.x[ks][1].x, q.x[ks][1].y, q.x[ks][1].z, q.x[ks][1].w};
-    const float hi[8] = {q.x[ks + 4][0].x, q.x[ks + 4][0].y, q.x[ks + 4][0].z, q.x[ks + 4][0].w,
-                         q.x[ks + 4][1].x, q.x[ks + 4][1].y, q.x[ks + 4][1].z, q.x[ks + 4][1].w};
-    const uint4 wl4 = *reinterpret_cast<const uint4*>(qn + lq * 8 + ks * 32);
-    const uint4 wh4 = *reinterpret_cast<const uint4*>(qn + 128 + lq * 8 + ks * 32);
-    const uint32_t wl[4] = {wl4.x, wl4.y, wl4.z, wl4.w}, wh[4] = {wh4.x, wh4.y, wh4.z, wh4.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float sn, cs;
-      rope_sincos(pos, ftab[lq * 8 + ks * 32 + e], sn, cs);
-      const float w0 = 1.f + bf2f((uint16_t)((e & 1) ? (wl[e >> 1] >> 16) : (wl[e >> 1] & 0xffffu)));
-      const float w1 = 1.f + bf2f((uint16_t)((e & 1) ? (wh[e >> 1] >> 16) : (wh[e >> 1] & 0xffffu)));
-      const float x0 = lo[e] * rn * w0, x1 = hi[e] * rn * w1;
-      qf[ks][e] = ok ? (short)f2bf(x0 * cs - x1 * sn) : (short)0;
-      qf[ks + 4][e] = ok ? (short)f2bf(x1 * cs + x0 * sn) : (short)0;
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t p = ok ? pack2(v[e] * rn, v[e + 1] * rn) : 0u;
+      qf[ks][e] = (short)(p & 0xffffu);
+      qf[ks][e + 1] = (short)(p >> 16);
     }
   }
 }
 
-// Suffix keys of one 32-key block built from the raw projection into LDS:
-// thread t (< 512) handles key j = t / 16 and dims d0 = (t % 16) * 8 .. +7
-// plus their rotation partners d0 + 128 (K), and the 16 V dims
-// (t % 16) * 16 .. +15.
+// Suffix keys of one 32-key block from the epilogue output into LDS: thread
+// t (< 512) handles key j = t / 16 and the 16 dims (t % 16) * 16 .. +15 of
+// K (scaled by the key row's 1 / rms) and V.
 struct SufRaw {
   float4 k[4], v[4];
+  float ss;
 };
 
 __device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int kb0, SufRaw& r) {
   const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
   const int key = min(kb0 + j, a.C - 1);  // rows past the chunk read a valid row and are zeroed later
-  const float* row = a.raw + (size_t)(b * a.TP + key) * kQKV;
-  const float* kr = row + (kHQ + g) * kD;
-  r.k[0] = *reinterpret_cast<const float4*>(kr + c * 8);
-  r.k[1] = *reinterpret_cast<const float4*>(kr + c * 8 + 4);
-  r.k[2] = *reinterpret_cast<const float4*>(kr + 128 + c * 8);
-  r.k[3] = *reinterpret_cast<const float4*>(kr + 128 + c * 8 + 4);
-  const float* vr = row + (kHQ + kHK + g) * kD + c * 16;
+  const int prow = b * a.TP + key;
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) r.v[q4] = *reinterpret_cast<const float4*>(vr + q4 * 4);
+  for (int h = 0; h < 2; ++h) {
+    const float* kr = a.y + tile_off_f32(prow, (kHQ + g) * kD + c * 16 + h * 8, kQKV);
+    const float* vr = a.y + tile_off_f32(prow, (kHQ + kHK + g) * kD + c * 16 + h * 8, kQKV);
+    r.k[2 * h] = *reinterpret_cast<const float4*>(kr);
+    r.k[2 * h + 1] = *reinterpret_cast<const float4*>(kr + 256);
+    r.v[2 * h] = *reinterpret_cast<const float4*>(vr);
+    r.v[2 * h + 1] = *reinterpret_cast<const float4*>(vr + 256);
+  }
+  r.ss = c < 8 ? a.ss_q[(size_t)prow * kQkvTiles + (kHQ + g) * 8 + c] : 0.f;
 }
 
-__device__ __forceinline__ void suffix_store(const AttnArgs& a, const double* ftab, const uint16_t* kn, const SufRaw& r,
-                                             int b, int kb0, uint32_t vis, uint16_t* sK, uint16_t* sV) {
+__device__ __forceinline__ void suffix_store(const SufRaw& r, uint32_t vis, uint16_t* sK, uint16_t* sV) {
   const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
-  const int key = kb0 + j;
   const bool ok = (vis >> j) & 1u;
-  const float lo[8] = {r.k[0].x, r.k[0].y, r.k[0].z, r.k[0].w, r.k[1].x, r.k[1].y, r.k[1].z, r.k[1].w};
-  const float hi[8] = {r.k[2].x, r.k[2].y, r.k[2].z, r.k[2].w, r.k[3].x, r.k[3].y, r.k[3].z, r.k[3].w};
-  const uint4 wlo = *reinterpret_cast<const uint4*>(kn + c * 8), whi = *reinterpret_cast<const uint4*>(kn + 128 + c * 8);
-  const uint32_t wl[4] = {wlo.x, wlo.y, wlo.z, wlo.w}, wh[4] = {whi.x, whi.y, whi.z, whi.w};
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
-  ss = group16_sum(ss);  // the 16 threads of key j form one DPP row
-  const float rn = 1.0f / sqrtf(ss * (1.0f / kD) + kEps);
-  const double pos = (double)a.pos0[b] + (double)key;
-  uint32_t ko[4], kh[4];
-#pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2) {
-    float o0[2], o1[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = 2 * e2 + h;
-      float sn, cs;
-      rope_sincos(pos, ftab[c * 8 + e], sn, cs);
-      const float w0 = 1.f + bf2f((uint16_t)(h ? (wl[e2] >> 16) : (wl[e2] & 0xffffu)));
-      const float w1 = 1.f + bf2f((uint16_t)(h ? (wh[e2] >> 16) : (wh[e2] & 0xffffu)));
-      const float x0 = lo[e] * rn * w0, x1 = hi[e] * rn * w1;
-      o0[h] = ok ? x0 * cs - x1 * sn : 0.f;
-      o1[h] = ok ? x1 * cs + x0 * sn : 0.f;
-    }
-    ko[e2] = pack2(o0[0], o0[1]);
-    kh[e2] = pack2(o1[0], o1[1]);
-  }
-  *reinterpret_cast<uint4*>(sK + j * KLD + c * 8) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
-  *reinterpret_cast<uint4*>(sK + j * KLD + 128 + c * 8) = make_uint4(kh[0], kh[1], kh[2], kh[3]);
+  const float t = group16_sum(r.ss);  // the 16 threads of key j form one DPP row
+  const float rn = 1.0f / sqrtf(t * (1.0f / kD) + kEps);
+  const float kv[16] = {r.k[0].x, r.k[0].y, r.k[0].z, r.k[0].w, r.k[1].x, r.k[1].y, r.k[1].z, r.k[1].w,
+                        r.k[2].x, r.k[2].y, r.k[2].z, r.k[2].w, r.k[3].x, r.k[3].y, r.k[3].z, r.k[3].w};
   const float vv[16] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w,
                         r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w, r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
-  uint32_t vp[8];
+  uint32_t kp[8], vp[8];
 #pragma unroll
-  for (int e2 = 0; e2 < 8; ++e2) vp[e2] = ok ? pack2(vv[2 * e2], vv[2 * e2 + 1]) : 0u;
+  for (int e2 = 0; e2 < 8; ++e2) {
+    kp[e2] = ok ? pack2(kv[2 * e2] * rn, kv[2 * e2 + 1] * rn) : 0u;
+    vp[e2] = ok ? pack2(vv[2 * e2], vv[2 * e2 + 1]) : 0u;
+  }
+  *reinterpret_cast<uint4*>(sK + j * KLD + c * 16) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
+  *reinterpret_cast<uint4*>(sK + j * KLD + c * 16 + 8) = make_uint4(kp[4], kp[5], kp[6], kp[7]);
   *reinterpret_cast<uint4*>(sV + j * VLD + c * 16) = make_uint4(vp[0], vp[1], vp[2], vp[3]);
   *reinterpret_cast<uint4*>(sV + j * VLD + c * 16 + 8) = make_uint4(vp[4], vp[5], vp[6], vp[7]);
 }
@@ -236,8 +186,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   __shared__ __attribute__((aligned(16))) uint16_t sK[NB][KB * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NB][KB * VLD];
   __shared__ uint32_t sMask[NB];
-  __shared__ double sF[kD / 2];
-  __shared__ __attribute__((aligned(16))) uint16_t sNW[2][kD];  // q / k norm weights
 
   const int nsplit = a.S + 1;
   const int split = blockIdx.x % nsplit;
@@ -245,7 +193,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int g = bg % kHK, b = bg / kHK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  const int R = 2 * a.C, MT = (R + 15) >> 4;
+  const int TT = a.TP >> 4, MT = 2 * TT;  // token tiles per head, stacked row tiles
 
   const bool suffix = (split == a.S);
   const int key_lo = suffix ? 0 : split * a.kps;
@@ -260,20 +208,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // ---- load phase: everything this WG reads from global memory
   const int mt = wave;
   const bool active = mt < MT;
-  const int row = mt * 16 + lr;
-  const bool qok = active && (row < R);
-  const int hh = qok ? row / a.C : 0;
-  const int qi = qok ? row - hh * a.C : 0;
+  const int row = mt * 16 + lr;            // stacked row
+  const int hh = active ? mt / TT : 0;     // head within the group
+  const int qi = (mt - hh * TT) * 16 + lr; // token
+  const bool qok = active && qi < a.C;
   KVRegs kv[NB];
   SufRaw sr[2];
   QRaw qr;
   bf16x8 qf[8];
   int mvis = 0;
-  uint4 nw = make_uint4(0, 0, 0, 0);
-  if (FUSED && threadIdx.x >= 384 && threadIdx.x < 448) {
-    const int t = threadIdx.x - 384;  // 64 threads x 16 B = both 512-B weight vectors
-    nw = *reinterpret_cast<const uint4*>((t < 32 ? a.qn_w : a.kn_w) + (t & 31) * 8);
-  }
   if (threadIdx.x < NB * KB && threadIdx.x < nkeys)
     mvis = suffix || a.mask[(size_t)b * a.P + key_lo + threadIdx.x] != 0;
   if (from_global) {
@@ -286,9 +229,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       if (bi < nblk) suffix_load(a, b, g, bi * KB, sr[bi]);
   }
   if (FUSED) {
-    q_load(a, b, qi, kGroup * g + hh, lq, qr);
+    q_load(a, b * a.TP + min(qi, a.C - 1), kGroup * g + hh, lq, qr);
   } else {
-    const uint16_t* qp = a.q + ((size_t)(b * a.C + qi) * kHQ + (kGroup * g + hh)) * kD + lq * 8;
+    const uint16_t* qp = a.q + ((size_t)(b * a.C + min(qi, a.C - 1)) * kHQ + (kGroup * g + hh)) * kD + lq * 8;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 32);
   }
@@ -300,11 +243,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     if (lane == 0) sMask[2 * wave] = (uint32_t)bal;
     if (lane == 0 && 2 * wave + 1 < NB) sMask[2 * wave + 1] = (uint32_t)(bal >> 32);
   }
-  if (FUSED && threadIdx.x >= 384 && threadIdx.x < 448) {
-    const int t = threadIdx.x - 384;
-    *reinterpret_cast<uint4*>(&sNW[t >> 5][(t & 31) * 8]) = nw;
-  }
-  if (FUSED) rope_table(sF, a.rope_base);
   __syncthreads();
   // stage every block (zero rows for invisible keys)
 #pragma unroll
@@ -315,9 +253,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     if (from_global)
       kv_store(kv[bi], vis, sK[bi], sV[bi]);
     else if (bi < 2)
-      suffix_store(a, sF, sNW[1], sr[bi], b, bi * KB, vis, sK[bi], sV[bi]);
+      suffix_store(sr[bi], vis, sK[bi], sV[bi]);
   }
-  if (FUSED) q_finish(a, sF, sNW[0], qr, b, qi, qok, lq, qf);
+  if (FUSED) q_finish(qr, qok, qf);
   else if (!qok) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = zero_bf16x8();
@@ -401,10 +339,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, uint16_t* ctx)
   const int R = 2 * a.C;
   const int wid = blockIdx.x * 4 + wave;
   if (wid >= a.B * kHK * R) return;
-  const int row = wid % R, bg = wid / R;
+  const int r = wid % R, bg = wid / R;
   const int g = bg % kHK, b = bg / kHK;
+  const int hh = r / a.C, i = r - hh * a.C;
   const int nsplit = a.S + 1;  // <= 128
-  const size_t base = (size_t)bg * nsplit * a.R16 + row;
+  const size_t base = (size_t)bg * nsplit * a.R16 + hh * a.TP + i;  // stacked row hh * TP + i
   float2 ml0 = make_float2(kNegBig, 0.f), ml1 = ml0;
   if (lane < nsplit) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)lane * a.R16) * 2);
   if (lane + 64 < nsplit) ml1 = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)(lane + 64) * a.R16) * 2);
@@ -441,7 +380,6 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, uint16_t* ctx)
     }
   }
   const float inv = 1.0f / L;
-  const int hh = row / a.C, i = row - hh * a.C;
   const int col = (kGroup * g + hh) * kD + lane * 4;
   uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
                               : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
@@ -457,15 +395,15 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
   a.P = P;
   a.kps = kAttnKps;
   a.S = (P + a.kps - 1) / a.kps;
-  a.R16 = ((2 * C + 15) / 16) * 16;
   a.TP = padded_tokens(C);
+  a.R16 = 2 * a.TP;
 }
 
 hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
   constexpr int NB = kAttnKps / KB;
   static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
   const dim3 grid(a.B * kHK * (a.S + 1));
-  if (a.raw)
+  if (a.y)
     k_attn_partial<true, NB><<<grid, dim3(512), 0, s>>>(a);
   else
     k_attn_partial<false, NB><<<grid, dim3(512), 0, s>>>(a);

@@ -35,6 +35,13 @@
 // Epilogues (the same article's chaining of time modulation with GEGLU
 // gate-up and MLP down); every store moves 8 consecutive features:
 //   EPI_F32    raw fp32 store (QKV before QK-norm / RoPE)
+//   EPI_QKV    QK-norm weights and RoPE on rotation-pair tiles (the article's
+//              "QKV projection, QK-Norm and RoPE in one go"): tile u holds the
+//              16 features j .. j+15 of head u/8's first half and their
+//              partners j+128 ..; the epilogue stores rope((1 + w) * x) for q
+//              and k heads (x for v heads) as tiled fp32 with the tile's row
+//              sums of squares of x.  RoPE is linear, so the per-row RMS factor
+//              is applied by the consumer: q = rope(x * r * (1 + w)) = r * y.
 //   EPI_RESID_* out = resid + gate[b] * y, bf16 / fp32 variants
 //   EPI_GEGLU  tile = 16 gate + 16 up features; h = gelu_tanh(gate) * up
 #include "dmx_device.hpp"
@@ -137,11 +144,15 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr int MB = MT * 16;      // rows per block
   constexpr int RROWS = MB + (MOD ? 16 : 0);  // + the shift tile
   constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
-  constexpr int NOUT = EPI == EPI_GEGLU ? 16 : NT;  // output features per row
+  constexpr bool QKV = EPI == EPI_QKV;
+  static_assert(!QKV || NT == 32, "rotation-pair tiles");
+  constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;  // output features (pairs for QKV) per row
   static_assert(!MOD || NWAVES * KW == kH, "the modulated A operand spans one hidden row");
   __shared__ __attribute__((aligned(16))) float red[NWAVES * RROWS * NT];
   __shared__ float sq[SSQ ? MB * NOUT : 1];
   __shared__ __attribute__((aligned(16))) float sS[SCALE ? kH : 4], sH[MOD ? kH : 4], sR[MOD ? MB : 1];
+  __shared__ double sF[QKV ? 16 : 1];   // rotation frequencies of the tile (revolutions per position)
+  __shared__ float sQ[QKV ? MB * 2 : 1];  // half-tile sums of squares
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
@@ -155,18 +166,27 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
   bf16x8 wf[KSTEPS][NTT];
 #pragma unroll
   for (int nt = 0; nt < NTT; ++nt) {
-    const int wt = EPI == EPI_GEGLU ? (nt == 0 ? tile : a.wtile_up + tile) : tile * NTT + nt;
+    const int wt = EPI == EPI_GEGLU ? (nt == 0 ? tile : a.wtile_up + tile)
+                   : QKV ? (tile >> 3) * 16 + nt * 8 + (tile & 7)
+                         : tile * NTT + nt;
     const uint16_t* wp = a.W + ((size_t)wt * kst + ks0) * 512 + lane * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) wf[ks][nt] = load_bf16x8(wp + ks * 512);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if (QKV && threadIdx.x < 16) {
+    const int j = (tile & 7) * 16 + threadIdx.x;  // dim of the head's first half
+    sF[threadIdx.x] = exp2(-(double)j / 128.0 * log2((double)a.rope_base)) * 0.15915494309189533577;
+  }
 
-  // row blocks: MOD kernels take one request (TP rows) per block; others MB
-  // consecutive tiled rows; block blockIdx.y, blockIdx.y + gridDim.y, ...
-  const int bstride = MOD ? a.TP : MB;
-  for (int m0 = blockIdx.y * bstride; m0 < a.M; m0 += gridDim.y * bstride) {
-    const int mts = min(MT, (MOD ? a.TP : a.M - m0) >> 4);  // tiles in this block
+  // row blocks of MB rows; MOD kernels keep every block inside one request
+  // (TP / 16 tiles per request, nsub blocks per request); blocks blockIdx.y,
+  // blockIdx.y + gridDim.y, ...
+  const int nsub = MOD ? (a.TP + MB - 1) / MB : 1;
+  const int nblk = MOD ? (a.M / a.TP) * nsub : (a.M + MB - 1) / MB;
+  for (int blk = blockIdx.y; blk < nblk; blk += gridDim.y) {
+    const int m0 = MOD ? (blk / nsub) * a.TP + (blk % nsub) * MB : blk * MB;
+    const int mts = min(MT, (MOD ? a.TP - (blk % nsub) * MB : a.M - m0) >> 4);  // tiles in this block
     f32x4 acc[MT][NTT], accs[NTT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -186,6 +206,7 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
     }
     float4 msc = make_float4(0.f, 0.f, 0.f, 0.f), msh = msc;
     float4 ssp[4];
+    const int pos_b = QKV ? a.pos0[m0 / a.TP] : 0;
     if (MOD) {
       const float* mb = a.nmod + (size_t)(m0 / a.TP) * 3 * kH;
       if (SCALE) msc = *reinterpret_cast<const float4*>(mb + threadIdx.x * 4);  // 256 threads x 4 = 1024
@@ -195,7 +216,7 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       const int per = a.ss_in_n >> 2;  // ss_in_n is a multiple of 4, at most 64
 #pragma unroll
       for (int i = 0; i < 4; ++i) ssp[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (rr < a.T) {
+      if (rr < mts * 16 && row_valid(m0 + rr, a.T, a.TP)) {
         const float* sp = a.ss_in + (size_t)(m0 + rr) * a.ss_in_n + qq * per;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -283,7 +304,51 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       const int r = e / (NOUT / 8), c0 = (e - r * (NOUT / 8)) * 8;
       if (!row_valid(m0 + r, a.T, a.TP)) continue;
       float v[8], seen[8];
-      if (EPI == EPI_GEGLU) {
+      if (QKV) {
+        // 8 rotation pairs: first-half features f .. f+7 and partners f+128 ..
+        const int h = tile >> 3, jb = (tile & 7) * 16 + c0;  // head, dim in the first half
+        const int f = h * kD + jb;
+        float lo[8], hi[8], sq8 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float tl = 0.f, th = 0.f, sl = 0.f, sh = 0.f;
+#pragma unroll
+          for (int w = 0; w < NWAVES; ++w) {
+            tl += red[(w * RROWS + r) * NT + c0 + i];
+            th += red[(w * RROWS + r) * NT + 16 + c0 + i];
+            if (MOD) {
+              sl += red[(w * RROWS + MB) * NT + c0 + i];
+              sh += red[(w * RROWS + MB) * NT + 16 + c0 + i];
+            }
+          }
+          lo[i] = MOD ? sR[r] * tl + sl : tl;
+          hi[i] = MOD ? sR[r] * th + sh : th;
+          sq8 += lo[i] * lo[i] + hi[i] * hi[i];
+        }
+        if (h < kHQ + kHK) {
+          const uint16_t* wn = h < kHQ ? a.qn_w : a.kn_w;
+          float wl[8], wh[8];
+          ld8b(wn + jb, wl);
+          ld8b(wn + 128 + jb, wh);
+          const double pos = (double)pos_b + (double)((m0 + r) % a.TP);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            double rev = pos * sF[c0 + i];
+            rev -= floor(rev);
+            const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+            const float x0 = lo[i] * (1.f + wl[i]), x1 = hi[i] * (1.f + wh[i]);
+            lo[i] = x0 * cs - x1 * sn;
+            hi[i] = x1 * cs + x0 * sn;
+          }
+        }
+        float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
+        float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
+        *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
+        *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
+        sQ[r * 2 + (c0 >> 3)] = sq8;
+      } else if (EPI == EPI_GEGLU) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float g = 0.f, u = 0.f, gs = 0.f, us = 0.f;
@@ -325,6 +390,11 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       __syncthreads();
       write_row_ssq<NOUT>(a, tile, m0, nrows, sq);
     }
+    if (QKV && (tile >> 3) < kHQ + kHK) {
+      __syncthreads();
+      for (int r = threadIdx.x; r < nrows; r += blockDim.x)
+        if (row_valid(m0 + r, a.T, a.TP)) a.ss_q[(size_t)(m0 + r) * kQkvTiles + tile] = sQ[r * 2] + sQ[r * 2 + 1];
+    }
     __syncthreads();
   }
 }
@@ -335,7 +405,7 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
 int gemm_config(GemmKind kind, GemmArgs& a) {
   switch (kind) {
     case GEMM_QKV1024: a.ntiles = kQKV / 16; a.K = kH; break;
-    case GEMM_QKV1024_MOD: a.ntiles = kQKV / 16; a.K = kH; break;
+    case GEMM_QKV1024_MOD: a.ntiles = kQKV / 32; a.K = kH; break;
     case GEMM_QKV2560: a.ntiles = kQKV / 16; a.K = 2560; break;
     case GEMM_OPROJ: a.ntiles = kH / 16; a.K = kHQ * kD; break;
     case GEMM_OPROJ_F32: a.ntiles = kH / 16; a.K = kHQ * kD; break;
@@ -351,10 +421,11 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   // row blocks: one per WG up to 4 (more blocks loop inside the WG)
   const int tiles = a.M / 16;
   const int mb1 = std::min(4, tiles), mb2 = std::min(4, (tiles + 1) / 2);
-  const int nreq = std::min(4, a.M / a.TP);  // MOD: one request per block
+  const int nreq = std::min(4, a.M / a.TP);  // MOD: blocks inside one request
+  const int nreq2 = std::min(8, (a.M / a.TP) * ((a.TP + 31) / 32));
   switch (kind) {
     case GEMM_QKV1024: DMX_GEMM(EPI_F32, 16, 4, 8, A_GLOBAL, 2, mb2); break;
-    case GEMM_QKV1024_MOD: DMX_GEMM(EPI_F32, 16, 4, 8, A_MOD, 4, nreq); break;
+    case GEMM_QKV1024_MOD: DMX_GEMM(EPI_QKV, 32, 4, 8, A_MOD, 2, nreq2); break;
     case GEMM_QKV2560: DMX_GEMM(EPI_F32, 16, 4, 20, A_GLOBAL, 1, 4); break;
     case GEMM_OPROJ: DMX_GEMM(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 1, mb1); break;
     case GEMM_OPROJ_F32: DMX_GEMM(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 1, mb1); break;

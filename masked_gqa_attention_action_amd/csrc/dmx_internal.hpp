@@ -9,7 +9,10 @@ namespace dmx {
 // Epilogues.  RESID variants: out = resid + gate[b] * y with the residual and
 // output stored as bf16 (B) or fp32 (F): RESID_BB, RESID_BF (bf16 in, fp32
 // out), RESID_FB (fp32 in, bf16 out).
-enum Epi { EPI_F32 = 0, EPI_RESID_BB = 2, EPI_GEGLU = 3, EPI_RESID_BF = 4, EPI_RESID_FB = 5 };
+// EPI_QKV: tile = 16 features j.. of a head's first half + their rotation
+// partners j+128..; stores rope((1 + w) * x) (q, k heads) or x (v heads) as
+// tiled fp32 plus per-(row, tile) sums of squares of x.
+enum Epi { EPI_F32 = 0, EPI_RESID_BB = 2, EPI_GEGLU = 3, EPI_RESID_BF = 4, EPI_RESID_FB = 5, EPI_QKV = 6 };
 
 // A-operand sources of the GEMM (see dmx_gemm.hip).
 enum ASrc { A_GLOBAL = 0, A_MOD = 1, A_MODPRE = 2 };
@@ -41,12 +44,18 @@ struct GemmArgs {
   int gate_stride;
   const uint16_t* resid;   // EPI_RESID_B*: bf16 residual, row-major
   const float* resid_f32;  // EPI_RESID_FB: fp32 residual [M][ldo]
+  // EPI_QKV: out_f32 is tiled fp32 [M][4096]; ss_q [M][kQkvTiles] sums of squares
+  const uint16_t *qn_w, *kn_w;  // (1 + w) weights of the q / k heads, [256]
+  const int32_t* pos0;          // token t of request b at position pos0[b] + t
+  float rope_base;
+  float* ss_q;
 };
+constexpr int kQkvTiles = 96;  // 32-feature tiles of the 12 q / k heads (8 per head)
 
 // Gemm shape presets (host picks one per projection).
 enum GemmKind {
   GEMM_QKV1024 = 1,         // N = 4096, K = 1024, fp32 out, A given
-  GEMM_QKV1024_MOD = 2,     // as above with the AdaRMS prenorm of bf16 x fused
+  GEMM_QKV1024_MOD = 2,     // N = 4096 as rotation-pair tiles, AdaRMS of bf16 x fused, EPI_QKV
   GEMM_QKV2560 = 3,         // N = 4096, K = 2560, fp32 out
   GEMM_OPROJ = 4,           // N = 1024, K = 2048, gated residual (bf16 -> bf16)
   GEMM_OPROJ_F32 = 5,       // as GEMM_OPROJ, fp32 output (layer-internal residual)
@@ -89,13 +98,12 @@ hipError_t launch_qknorm_rope(const float* raw, const uint16_t* qn_w, const uint
 
 struct AttnArgs {
   const uint16_t *q, *ks, *vs, *kp, *vp;
-  // fused path: when raw != nullptr, q / ks / vs are ignored and built from the
-  // raw fp32 QKV projection [B*TP][4096] (tiled rows) with QK-norm (1 + w) and
-  // RoPE at pos0[b] + t, base rope_base
-  const float* raw;
-  const uint16_t *qn_w, *kn_w;
-  const int32_t* pos0;
-  float rope_base;
+  // fused path: when y != nullptr, q / ks / vs are ignored and built from the
+  // QKV epilogue's output: y tiled fp32 [B*TP][4096] (rope((1 + w) * x) for q,
+  // k heads, x for v heads) and ss_q [B*TP][96] (8 sums of squares of x per
+  // q / k head): q = y / sqrt(mean x^2 + eps).
+  const float* y;
+  const float* ss_q;
   const uint8_t* mask;
   int B, C, P;
   int TP;       // padded chunk (tiled rows per request)

@@ -21,6 +21,13 @@ __host__ __device__ __forceinline__ size_t tile_off(int row, int col, int K) {
   return ((size_t)(row >> 4) * (size_t)(K >> 5) + (size_t)(col >> 5)) * 512 + (size_t)((row & 15) + 16 * ((col >> 3) & 3)) * 8;
 }
 
+// fp32 tiles (a 16 x 32 tile is 2 KB: two 1 KB halves holding columns
+// 8q..8q+3 and 8q+4..8q+7 of the lane's 8-column group): float offset of the
+// first half of chunk (row, col .. col+7); the second half is 256 floats on.
+__host__ __device__ __forceinline__ size_t tile_off_f32(int row, int col, int N) {
+  return ((size_t)(row >> 4) * (size_t)(N >> 5) + (size_t)(col >> 5)) * 512 + (size_t)((row & 15) + 16 * ((col >> 3) & 3)) * 4;
+}
+
 __host__ __device__ __forceinline__ int padded_tokens(int tokens) { return (tokens + 15) & ~15; }
 
 __host__ __device__ __forceinline__ bool row_valid(int prow, int tokens, int tp) { return prow % tp < tokens; }
