@@ -91,9 +91,14 @@ __device__ __forceinline__ float group16_sum(float v) {
   return v;
 }
 
+// GELU, tanh form: 0.5 z (1 + tanh u), u = sqrt(2/pi) (z + 0.044715 z^3),
+// evaluated through the identity 0.5 (1 + tanh u) = 1 / (1 + e^(-2u)) with
+// the hardware base-2 exponential and reciprocal (each ~1 ulp).  Large |u|
+// saturate correctly: e^(-2u) -> inf gives -0, -> 0 gives z.
 __device__ __forceinline__ float gelu_tanh(float z) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+  const float c2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float e = __builtin_amdgcn_exp2f(c2 * (z + 0.044715f * z * z * z));
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 }  // namespace dmx

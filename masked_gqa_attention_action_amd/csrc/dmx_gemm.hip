@@ -76,8 +76,49 @@ __device__ __forceinline__ void st8f(float* p, const float v[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
-__device__ __forceinline__ void ld8b(const uint16_t* p, float v[8]) {
-  const uint4 r = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ uint4 pack8(const float v[8]) {
+  return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+}
+
+// Global operands of one epilogue task (8 features n .. n+7 of tiled row
+// prow), fetched while the MFMA operands are still in flight.
+struct EpiPre {
+  float4 g[2], sc[2], rf[2];  // gate, scale (x1 copy), fp32 residual
+  uint4 rb;                   // bf16 residual
+  uint4 wl, wh;               // QKV: norm weights of the pair's two halves
+};
+
+template <int EPI>
+__device__ __forceinline__ void epi_fetch(const GemmArgs& a, int prow, int n, EpiPre& p) {
+  const int b = prow / a.TP, t = prow - b * a.TP;
+  const size_t lrow = (size_t)b * a.T + t;  // row of a row-major [batch][tokens] tensor
+  if (EPI == EPI_RESID_BB || EPI == EPI_RESID_BF || EPI == EPI_RESID_FB) {
+    const float* gp = a.gate + (size_t)b * a.gate_stride + n;
+    p.g[0] = *reinterpret_cast<const float4*>(gp);
+    p.g[1] = *reinterpret_cast<const float4*>(gp + 4);
+  }
+  if (EPI == EPI_RESID_BB || EPI == EPI_RESID_BF) p.rb = *reinterpret_cast<const uint4*>(a.resid + lrow * a.ldo + n);
+  if (EPI == EPI_RESID_BF && a.xs_scale) {
+    const float* sp = a.xs_scale + (size_t)b * a.gate_stride + n;
+    p.sc[0] = *reinterpret_cast<const float4*>(sp);
+    p.sc[1] = *reinterpret_cast<const float4*>(sp + 4);
+  }
+  if (EPI == EPI_RESID_FB) {
+    const float* rp = a.resid_f32 + (size_t)prow * a.ldo + n;
+    p.rf[0] = *reinterpret_cast<const float4*>(rp);
+    p.rf[1] = *reinterpret_cast<const float4*>(rp + 4);
+  }
+  if (EPI == EPI_QKV) {  // n = dim of the first half within the head, head = the tile's
+    const int h = n >> 8;
+    if (h < kHQ + kHK) {
+      const uint16_t* wn = h < kHQ ? a.qn_w : a.kn_w;
+      p.wl = *reinterpret_cast<const uint4*>(wn + (n & 127));
+      p.wh = *reinterpret_cast<const uint4*>(wn + 128 + (n & 127));
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack8(uint4 r, float v[8]) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -85,31 +126,33 @@ __device__ __forceinline__ void ld8b(const uint16_t* p, float v[8]) {
     v[2 * i + 1] = bf2f((uint16_t)(w[i] >> 16));
   }
 }
-__device__ __forceinline__ uint4 pack8(const float v[8]) {
-  return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+__device__ __forceinline__ void f4x2(const float4 q[2], float v[8]) {
+  v[0] = q[0].x; v[1] = q[0].y; v[2] = q[0].z; v[3] = q[0].w;
+  v[4] = q[1].x; v[5] = q[1].y; v[6] = q[1].z; v[7] = q[1].w;
 }
 
 // Epilogue of 8 consecutive output features n .. n+7 of tiled row prow.
 // Returns in `seen` the values the next AdaRMS normalises (for row sums).
 template <int EPI>
-__device__ __forceinline__ void epi_store8(const GemmArgs& a, int prow, int n, float v[8], float seen[8]) {
+__device__ __forceinline__ void epi_store8(const GemmArgs& a, int prow, int n, const EpiPre& p, float v[8],
+                                           float seen[8]) {
   const int b = prow / a.TP, t = prow - b * a.TP;
-  const size_t lrow = (size_t)b * a.T + t;  // row of a row-major [batch][tokens] tensor
+  const size_t lrow = (size_t)b * a.T + t;
   if (EPI == EPI_F32) {
     st8f(a.out_f32 + (size_t)prow * a.ldo + n, v);
     return;
   }
   float g[8];
-  ld8f(a.gate + (size_t)b * a.gate_stride + n, g);
+  f4x2(p.g, g);
   if (EPI == EPI_RESID_BB) {
     float r[8];
-    ld8b(a.resid + lrow * a.ldo + n, r);
+    unpack8(p.rb, r);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = r[i] + g[i] * v[i];
     *reinterpret_cast<uint4*>(a.out_bf16 + lrow * a.ldo + n) = pack8(v);
   } else if (EPI == EPI_RESID_BF) {
     float r[8];
-    ld8b(a.resid + lrow * a.ldo + n, r);
+    unpack8(p.rb, r);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       v[i] = r[i] + g[i] * v[i];
@@ -118,20 +161,20 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& a, int prow, int n, f
     st8f(a.out_f32 + (size_t)prow * a.ldo + n, v);
     if (a.xs_scale) {
       float sc[8];
-      ld8f(a.xs_scale + (size_t)b * a.gate_stride + n, sc);
+      f4x2(p.sc, sc);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = v[i] * (1.0f + sc[i]);
     }
     *reinterpret_cast<uint4*>(a.out_pk + tile_off(prow, n, a.ldo)) = pack8(v);
   } else if (EPI == EPI_RESID_FB) {
     float r[8];
-    ld8f(a.resid_f32 + (size_t)prow * a.ldo + n, r);
+    f4x2(p.rf, r);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = r[i] + g[i] * v[i];
     const uint4 hb = pack8(v);
     *reinterpret_cast<uint4*>(a.out_bf16 + lrow * a.ldo + n) = hb;
     if (a.out_pk) *reinterpret_cast<uint4*>(a.out_pk + tile_off(prow, n, a.ldo)) = hb;
-    ld8b(reinterpret_cast<const uint16_t*>(&hb), seen);
+    unpack8(hb, seen);
   }
 }
 
@@ -147,6 +190,8 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr bool QKV = EPI == EPI_QKV;
   static_assert(!QKV || NT == 32, "rotation-pair tiles");
   constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;  // output features (pairs for QKV) per row
+  constexpr int OUTW = EPI == EPI_GEGLU ? 4 : 8;  // outputs per epilogue task
+  constexpr int TPR = NOUT / OUTW;                // epilogue tasks per row
   static_assert(!MOD || NWAVES * KW == kH, "the modulated A operand spans one hidden row");
   __shared__ __attribute__((aligned(16))) float red[NWAVES * RROWS * NT];
   __shared__ float sq[SSQ ? MB * NOUT : 1];
@@ -222,6 +267,13 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
         for (int i = 0; i < 4; ++i)
           if (i * 4 < per) ssp[i] = *reinterpret_cast<const float4*>(sp + i * 4);
       }
+    }
+    // the epilogue's global operands of this thread's first task
+    EpiPre pre;
+    {
+      const int r = threadIdx.x / TPR, c0 = (threadIdx.x % TPR) * OUTW;
+      if (r < mts * 16 && row_valid(m0 + r, a.T, a.TP))
+        epi_fetch<EPI>(a, m0 + r, QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0, pre);
     }
     __builtin_amdgcn_sched_barrier(0);  // the whole block is in flight before any use
 
@@ -300,14 +352,20 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
     }
     __syncthreads();
     const int nrows = mts * 16;
-    for (int e = threadIdx.x; e < nrows * (NOUT / 8); e += NWAVES * 64) {
-      const int r = e / (NOUT / 8), c0 = (e - r * (NOUT / 8)) * 8;
+    for (int e = threadIdx.x; e < nrows * TPR; e += NWAVES * 64) {
+      const int r = e / TPR, c0 = (e - r * TPR) * OUTW;
       if (!row_valid(m0 + r, a.T, a.TP)) continue;
+      const int n = QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0;
+      EpiPre cur;
+      if (e == (int)threadIdx.x)
+        cur = pre;
+      else
+        epi_fetch<EPI>(a, m0 + r, n, cur);
       float v[8], seen[8];
       if (QKV) {
         // 8 rotation pairs: first-half features f .. f+7 and partners f+128 ..
         const int h = tile >> 3, jb = (tile & 7) * 16 + c0;  // head, dim in the first half
-        const int f = h * kD + jb;
+        const int f = n;
         float lo[8], hi[8], sq8 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -326,10 +384,9 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
           sq8 += lo[i] * lo[i] + hi[i] * hi[i];
         }
         if (h < kHQ + kHK) {
-          const uint16_t* wn = h < kHQ ? a.qn_w : a.kn_w;
           float wl[8], wh[8];
-          ld8b(wn + jb, wl);
-          ld8b(wn + 128 + jb, wh);
+          unpack8(cur.wl, wl);
+          unpack8(cur.wh, wh);
           const double pos = (double)pos_b + (double)((m0 + r) % a.TP);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -350,7 +407,7 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
         sQ[r * 2 + (c0 >> 3)] = sq8;
       } else if (EPI == EPI_GEGLU) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
           float g = 0.f, u = 0.f, gs = 0.f, us = 0.f;
 #pragma unroll
           for (int w = 0; w < NWAVES; ++w) {
@@ -367,7 +424,8 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
           }
           v[i] = gelu_tanh(g) * u;
         }
-        *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, tile * 16 + c0, a.ldo)) = pack8(v);
+        *reinterpret_cast<uint2*>(a.out_pk + tile_off(m0 + r, tile * 16 + (c0 & ~7), a.ldo) + (c0 & 7)) =
+            make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -379,7 +437,7 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
           }
           v[i] = MOD ? sR[r] * t + ts : t;
         }
-        epi_store8<EPI>(a, m0 + r, tile * NT + c0, v, seen);
+        epi_store8<EPI>(a, m0 + r, n, cur, v, seen);
         if (SSQ) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) sq[r * NOUT + c0 + i] = seen[i] * seen[i];
