@@ -55,7 +55,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // (for a stack) the modulation vectors of every layer of one step.  Rows of
 // the tiled / fp32 intermediates are tiled rows (each request padded to TP).
 struct WsLayout {
-  size_t mod1, mod2, apk, xp, raw, ss_q, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
+  size_t mod1, mod2, apk, xp, raw, ss_q, vb, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
   int TP;
   AttnArgs attn;
 };
@@ -78,12 +78,13 @@ bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
   L.xp = take(M * kH * 2);                  // tiled layer input
   L.raw = take(M * kQKV * 4);               // fp32 QKV projection (tiled in the fused layer)
   L.ss_q = take(M * kQkvTiles * 4);         // its q / k head sums of squares
+  L.vb = take(M * kHK * kD * 2);            // tiled bf16 v heads of the chunk
   L.ctx = take(M * kHQ * kD * 2);           // tiled attention output
   L.x1 = take(M * kH * 4);   // fp32 residual between the two halves of a layer
   L.x1s = take(M * kH * 2);  // tiled bf16(x1 * (1 + scale2)), the gate-up A operand
   L.h = take(M * kI * 2);    // tiled GEGLU output
   attn_config(B, T, P, L.attn);
-  const size_t prow = (size_t)B * kHK * (L.attn.S + 1) * L.attn.R16;
+  const size_t prow = (size_t)B * kHK * (L.attn.S + L.attn.NS) * L.attn.R16;
   L.part_o = take(prow * kD * 2);
   L.part_ml = take(prow * 2 * 4);
   L.ss_a = take(M * kSsParts * 4);  // row sums of squares of x1, one per O-projection tile
@@ -165,6 +166,7 @@ AttnArgs attn_args(const WsLayout& L, void* ws) {
   a.q = a.ks = a.vs = a.kp = a.vp = nullptr;
   a.y = nullptr;
   a.ss_q = nullptr;
+  a.vb = nullptr;
   a.mask = nullptr;
   a.part_o = at<uint16_t>(ws, L.part_o);
   a.part_ml = at<float>(ws, L.part_ml);
@@ -277,11 +279,13 @@ int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const d
   g.pos0 = pos0;
   g.rope_base = 10000.0f;
   g.ss_q = ss_q;
+  g.out_pk = at<uint16_t>(ws, L.vb);
   DMX_TRY(hip_check(launch_gemm(GEMM_QKV1024_MOD, g, s), "QKV GEMM launch"));
 
   AttnArgs a = attn_args(L, ws);
   a.y = raw;
   a.ss_q = ss_q;
+  a.vb = at<uint16_t>(ws, L.vb);
   a.kp = kv->k;
   a.vp = kv->v;
   a.mask = kv->mask;

@@ -4,7 +4,8 @@
 //
 // Work decomposition (flash-decoding style, split over the prefix):
 //   one work-group per (request b, KV head g, key split s).  Splits 0..S-1 own
-//   kps consecutive prefix rows each; split S owns the chunk's own suffix keys.
+//   kps consecutive prefix rows each; splits S..S+NS-1 own the chunk's own
+//   suffix keys, 32 each.
 //   The 2 query heads that share KV head g are stacked into 2*TP query rows
 //   (TP = chunk padded to 16; row r: head 2g + r / TP, token r % TP), so every
 //   K/V row is read from HBM once per request; wave w owns stacked rows
@@ -26,8 +27,10 @@
 //   all invisible is skipped; invisible keys inside a block are zero-filled
 //   in LDS and their logits replaced by -inf (selection, never
 //   multiplication), so masked rows may hold anything, NaN included.
-// Each split writes (running max, running sum, output / sum) per row; a
-// combine kernel merges the S + 1 partials per row.
+// Each split writes (running max, running sum, output / sum) per row, the
+// outputs as 16 x 256 row tiles laid out by lane (every store instruction of a
+// wave covers 512 contiguous bytes); a combine kernel merges the S + NS
+// partials of each row in split order.
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
 #include "dmx_tiles.hpp"
@@ -83,9 +86,10 @@ __device__ __forceinline__ void q_finish(const QRaw& q, bool ok, bf16x8 qf[8]) {
 
 // Suffix keys of one 32-key block from the epilogue output into LDS: thread
 // t (< 512) handles key j = t / 16 and the 16 dims (t % 16) * 16 .. +15 of
-// K (scaled by the key row's 1 / rms) and V.
+// K (fp32, scaled by the key row's 1 / rms) and V (bf16 already).
 struct SufRaw {
-  float4 k[4], v[4];
+  float4 k[4];
+  uint4 v[2];
   float ss;
 };
 
@@ -96,11 +100,9 @@ __device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const float* kr = a.y + tile_off_f32(prow, (kHQ + g) * kD + c * 16 + h * 8, kQKV);
-    const float* vr = a.y + tile_off_f32(prow, (kHQ + kHK + g) * kD + c * 16 + h * 8, kQKV);
     r.k[2 * h] = *reinterpret_cast<const float4*>(kr);
     r.k[2 * h + 1] = *reinterpret_cast<const float4*>(kr + 256);
-    r.v[2 * h] = *reinterpret_cast<const float4*>(vr);
-    r.v[2 * h + 1] = *reinterpret_cast<const float4*>(vr + 256);
+    r.v[h] = *reinterpret_cast<const uint4*>(a.vb + tile_off(prow, g * kD + c * 16 + h * 8, kHK * kD));
   }
   r.ss = c < 8 ? a.ss_q[(size_t)prow * kQkvTiles + (kHQ + g) * 8 + c] : 0.f;
 }
@@ -112,18 +114,14 @@ __device__ __forceinline__ void suffix_store(const SufRaw& r, uint32_t vis, uint
   const float rn = 1.0f / sqrtf(t * (1.0f / kD) + kEps);
   const float kv[16] = {r.k[0].x, r.k[0].y, r.k[0].z, r.k[0].w, r.k[1].x, r.k[1].y, r.k[1].z, r.k[1].w,
                         r.k[2].x, r.k[2].y, r.k[2].z, r.k[2].w, r.k[3].x, r.k[3].y, r.k[3].z, r.k[3].w};
-  const float vv[16] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w,
-                        r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w, r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
-  uint32_t kp[8], vp[8];
+  uint32_t kp[8];
 #pragma unroll
-  for (int e2 = 0; e2 < 8; ++e2) {
-    kp[e2] = ok ? pack2(kv[2 * e2] * rn, kv[2 * e2 + 1] * rn) : 0u;
-    vp[e2] = ok ? pack2(vv[2 * e2], vv[2 * e2 + 1]) : 0u;
-  }
+  for (int e2 = 0; e2 < 8; ++e2) kp[e2] = ok ? pack2(kv[2 * e2] * rn, kv[2 * e2 + 1] * rn) : 0u;
+  const uint4 z = make_uint4(0, 0, 0, 0);
   *reinterpret_cast<uint4*>(sK + j * KLD + c * 16) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
   *reinterpret_cast<uint4*>(sK + j * KLD + c * 16 + 8) = make_uint4(kp[4], kp[5], kp[6], kp[7]);
-  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16) = make_uint4(vp[0], vp[1], vp[2], vp[3]);
-  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16 + 8) = make_uint4(vp[4], vp[5], vp[6], vp[7]);
+  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16) = ok ? r.v[0] : z;
+  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16 + 8) = ok ? r.v[1] : z;
 }
 
 // K / V rows (bf16, from global) of one 32-key block: thread t owns 16-byte
@@ -187,7 +185,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   __shared__ __attribute__((aligned(16))) uint16_t sV[NB][KB * VLD];
   __shared__ uint32_t sMask[NB];
 
-  const int nsplit = a.S + 1;
+  const int nsplit = a.S + a.NS;
   const int split = blockIdx.x % nsplit;
   const int bg = blockIdx.x / nsplit;
   const int g = bg % kHK, b = bg / kHK;
@@ -195,9 +193,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int lr = lane & 15, lq = lane >> 4;
   const int TT = a.TP >> 4, MT = 2 * TT;  // token tiles per head, stacked row tiles
 
-  const bool suffix = (split == a.S);
-  const int key_lo = suffix ? 0 : split * a.kps;
-  const int key_hi = suffix ? a.C : min(a.P, key_lo + a.kps);
+  const bool suffix = split >= a.S;
+  const int key_lo = suffix ? (split - a.S) * KB : split * a.kps;
+  const int key_hi = suffix ? min(a.C, key_lo + KB) : min(a.P, key_lo + a.kps);
   const int nkeys = key_hi - key_lo;
   const int nblk = (nkeys + KB - 1) / KB;  // <= NB
   const size_t kv_rows = suffix ? (size_t)a.C : (size_t)a.P;
@@ -213,7 +211,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int qi = (mt - hh * TT) * 16 + lr; // token
   const bool qok = active && qi < a.C;
   KVRegs kv[NB];
-  SufRaw sr[2];
+  SufRaw sr;
   QRaw qr;
   bf16x8 qf[8];
   int mvis = 0;
@@ -224,9 +222,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int bi = 0; bi < NB; ++bi)
       if (bi < nblk) kv_load(Kb, Vb, key_lo + bi * KB, key_hi, kv[bi]);
   } else {
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-      if (bi < nblk) suffix_load(a, b, g, bi * KB, sr[bi]);
+    suffix_load(a, b, g, key_lo, sr);  // one block
   }
   if (FUSED) {
     q_load(a, b * a.TP + min(qi, a.C - 1), kGroup * g + hh, lq, qr);
@@ -252,8 +248,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     if (vis == 0u) continue;
     if (from_global)
       kv_store(kv[bi], vis, sK[bi], sV[bi]);
-    else if (bi < 2)
-      suffix_store(sr[bi], vis, sK[bi], sV[bi]);
+    else if (bi == 0)
+      suffix_store(sr, vis, sK[0], sV[0]);
   }
   if (FUSED) q_finish(qr, qok, qf);
   else if (!qok) {
@@ -317,76 +313,81 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
   }
 
-  // this split's partial row: running max, running sum, output / sum
+  // this split's partial row: running max, running sum, output / sum; the
+  // outputs of row tile mt as [t][lane][4] (dims 16t + 4lq .. of row lr)
   float l = lrun + __shfl_xor(lrun, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  const size_t prow = ((size_t)bg * nsplit + split) * a.R16 + row;
+  const size_t pidx = (size_t)bg * nsplit + split;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  uint16_t* dst = a.part_o + prow * kD + 4 * lq;
+  uint16_t* dst = a.part_o + (pidx * MT + mt) * (16 * kD) + lane * 4;
 #pragma unroll
   for (int t = 0; t < 16; ++t)
-    *reinterpret_cast<uint2*>(dst + t * 16) = make_uint2(pack2(o[t][0] * inv, o[t][1] * inv),
-                                                         pack2(o[t][2] * inv, o[t][3] * inv));
-  if (lq == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(mrun, l);
+    *reinterpret_cast<uint2*>(dst + t * 256) = make_uint2(pack2(o[t][0] * inv, o[t][1] * inv),
+                                                          pack2(o[t][2] * inv, o[t][3] * inv));
+  if (lq == 0) *reinterpret_cast<float2*>(a.part_ml + (pidx * a.R16 + row) * 2) = make_float2(mrun, l);
 }
 
-// One wave per (request, KV head, stacked row): merge the split partials.
-// Lane s fetches split s's (max, sum) while every lane fetches its 4 output
-// dims of the first batch of splits, all in flight together.
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
-  constexpr int CB = 24;  // splits per batch of loads
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int R = 2 * a.C;
-  const int wid = blockIdx.x * 4 + wave;
-  if (wid >= a.B * kHK * R) return;
-  const int r = wid % R, bg = wid / R;
+// One wave per (request, KV head, stacked row tile, quarter of the dims):
+// merges the S + NS split partials of 16 rows x 64 dims in split order with
+// a running maximum.  Lane (lr, lq) owns row lr and dims 16t + 4lq .. +3 of
+// the quarter's 4 dim tiles t; all loads of a batch of splits are in flight
+// together, each instruction reading 512 contiguous bytes.
+__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
+  constexpr int CB = 20;  // splits per batch of loads
+  const int lane = threadIdx.x, lr = lane & 15, lq = lane >> 4;
+  const int TT = a.TP >> 4, MT = 2 * TT;
+  const int q4 = blockIdx.x & 3, rest = blockIdx.x >> 2;
+  const int mt = rest % MT, bg = rest / MT;
   const int g = bg % kHK, b = bg / kHK;
-  const int hh = r / a.C, i = r - hh * a.C;
-  const int nsplit = a.S + 1;  // <= 128
-  const size_t base = (size_t)bg * nsplit * a.R16 + hh * a.TP + i;  // stacked row hh * TP + i
-  float2 ml0 = make_float2(kNegBig, 0.f), ml1 = ml0;
-  if (lane < nsplit) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)lane * a.R16) * 2);
-  if (lane + 64 < nsplit) ml1 = *reinterpret_cast<const float2*>(a.part_ml + (base + (size_t)(lane + 64) * a.R16) * 2);
-  uint2 raw[CB];
+  const int nsplit = a.S + a.NS;
+  const int row = mt * 16 + lr;
+  const int hh = mt / TT, i = (mt - hh * TT) * 16 + lr;
+  const size_t ml0 = (size_t)bg * nsplit * a.R16 + row;
+  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + (q4 * 4) * 256 + lane * 4;
+  float M = kNegBig, L = 0.f;
+  float acc[4][4];
 #pragma unroll
-  for (int u = 0; u < CB; ++u)
-    raw[u] = u < nsplit ? *reinterpret_cast<const uint2*>(a.part_o + (base + (size_t)u * a.R16) * kD + lane * 4)
-                        : make_uint2(0, 0);
-  float M = fmaxf(ml0.y > 0.f ? ml0.x : kNegBig, ml1.y > 0.f ? ml1.x : kNegBig);
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const float w0 = ml0.y > 0.f ? ml0.y * exp2f(ml0.x - M) : 0.f;
-  const float w1 = ml1.y > 0.f ? ml1.y * exp2f(ml1.x - M) : 0.f;
-  const float L = wave_sum(w0 + w1);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += CB) {
-    if (s0 > 0) {
+    float2 ml[CB];
+    uint2 ov[CB][4];
 #pragma unroll
-      for (int u = 0; u < CB; ++u)
-        raw[u] = s0 + u < nsplit
-                     ? *reinterpret_cast<const uint2*>(a.part_o + (base + (size_t)(s0 + u) * a.R16) * kD + lane * 4)
-                     : make_uint2(0, 0);
+    for (int u = 0; u < CB; ++u) {
+      const int s = min(s0 + u, nsplit - 1);  // past the end: re-read the last split, skipped below
+      ml[u] = *reinterpret_cast<const float2*>(a.part_ml + (ml0 + (size_t)s * a.R16) * 2);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        ov[u][t] = *reinterpret_cast<const uint2*>(a.part_o + o0 + (size_t)s * MT * (16 * kD) + t * 256);
     }
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const int s = s0 + u;
-      const float ws = s < 64 ? __shfl(w0, s & 63, 64) : __shfl(w1, s & 63, 64);
-      if (s < nsplit && ws != 0.f) {
-        acc[0] += ws * bf2f((uint16_t)(raw[u].x & 0xffffu));
-        acc[1] += ws * bf2f((uint16_t)(raw[u].x >> 16));
-        acc[2] += ws * bf2f((uint16_t)(raw[u].y & 0xffffu));
-        acc[3] += ws * bf2f((uint16_t)(raw[u].y >> 16));
+      if (s0 + u < nsplit && ml[u].y > 0.f) {
+        const float Mn = fmaxf(M, ml[u].x);
+        const float so = exp2f(M - Mn), w = ml[u].y * exp2f(ml[u].x - Mn);
+        L = L * so + w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[t][0] = acc[t][0] * so + w * bf2f((uint16_t)(ov[u][t].x & 0xffffu));
+          acc[t][1] = acc[t][1] * so + w * bf2f((uint16_t)(ov[u][t].x >> 16));
+          acc[t][2] = acc[t][2] * so + w * bf2f((uint16_t)(ov[u][t].y & 0xffffu));
+          acc[t][3] = acc[t][3] * so + w * bf2f((uint16_t)(ov[u][t].y >> 16));
+        }
+        M = Mn;
       }
     }
   }
+  if (i >= a.C) return;
   const float inv = 1.0f / L;
-  const int col = (kGroup * g + hh) * kD + lane * 4;
-  uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
-                              : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
-  uint2 outv;
-  outv.x = pack2(acc[0] * inv, acc[1] * inv);
-  outv.y = pack2(acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<uint2*>(dst) = outv;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = (kGroup * g + hh) * kD + (q4 * 4 + t) * 16 + 4 * lq;
+    uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
+                                : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[t][0] * inv, acc[t][1] * inv),
+                                                pack2(acc[t][2] * inv, acc[t][3] * inv));
+  }
 }
 
 void attn_config(int B, int C, int P, AttnArgs& a) {
@@ -395,6 +396,7 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
   a.P = P;
   a.kps = kAttnKps;
   a.S = (P + a.kps - 1) / a.kps;
+  a.NS = (C + KB - 1) / KB;
   a.TP = padded_tokens(C);
   a.R16 = 2 * a.TP;
 }
@@ -402,13 +404,12 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
 hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
   constexpr int NB = kAttnKps / KB;
   static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
-  const dim3 grid(a.B * kHK * (a.S + 1));
+  const dim3 grid(a.B * kHK * (a.S + a.NS));
   if (a.y)
     k_attn_partial<true, NB><<<grid, dim3(512), 0, s>>>(a);
   else
     k_attn_partial<false, NB><<<grid, dim3(512), 0, s>>>(a);
-  const int rows = a.B * kHK * 2 * a.C;
-  k_attn_combine<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(a, ctx);
+  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 4), dim3(64), 0, s>>>(a, ctx);
   return hipGetLastError();
 }
 

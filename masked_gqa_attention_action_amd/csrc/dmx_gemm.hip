@@ -39,8 +39,8 @@
 //              "QKV projection, QK-Norm and RoPE in one go"): tile u holds the
 //              16 features j .. j+15 of head u/8's first half and their
 //              partners j+128 ..; the epilogue stores rope((1 + w) * x) for q
-//              and k heads (x for v heads) as tiled fp32 with the tile's row
-//              sums of squares of x.  RoPE is linear, so the per-row RMS factor
+//              and k heads as tiled fp32 with the tile's row sums of squares
+//              of x, and x of the v heads as tiled bf16.  RoPE is linear, so the per-row RMS factor
 //              is applied by the consumer: q = rope(x * r * (1 + w)) = r * y.
 //   EPI_RESID_* out = resid + gate[b] * y, bf16 / fp32 variants
 //   EPI_GEGLU  tile = 16 gate + 16 up features; h = gelu_tanh(gate) * up
@@ -398,12 +398,18 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
             hi[i] = x1 * cs + x0 * sn;
           }
         }
-        float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
-        float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
-        *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
-        *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
-        *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
+        if (h < kHQ + kHK) {
+          float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
+          float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
+          *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+          *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
+          *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+          *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
+        } else {  // v heads: bf16, as the attention consumes them
+          const int fv = f - (kHQ + kHK) * kD;
+          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fv, kHK * kD)) = pack8(lo);
+          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fv + 128, kHK * kD)) = pack8(hi);
+        }
         sQ[r * 2 + (c0 >> 3)] = sq8;
       } else if (EPI == EPI_GEGLU) {
 #pragma unroll

@@ -44,7 +44,8 @@ struct GemmArgs {
   int gate_stride;
   const uint16_t* resid;   // EPI_RESID_B*: bf16 residual, row-major
   const float* resid_f32;  // EPI_RESID_FB: fp32 residual [M][ldo]
-  // EPI_QKV: out_f32 is tiled fp32 [M][4096]; ss_q [M][kQkvTiles] sums of squares
+  // EPI_QKV: out_f32 is tiled fp32 [M][4096] (the v heads' columns unused), the
+  // v heads go to out_pk as tiled bf16 [M][1024]; ss_q [M][kQkvTiles] sums of squares
   const uint16_t *qn_w, *kn_w;  // (1 + w) weights of the q / k heads, [256]
   const int32_t* pos0;          // token t of request b at position pos0[b] + t
   float rope_base;
@@ -104,15 +105,17 @@ struct AttnArgs {
   // q / k head): q = y / sqrt(mean x^2 + eps).
   const float* y;
   const float* ss_q;
+  const uint16_t* vb;  // fused path: the chunk's V heads, tiled bf16 [B*TP][1024]
   const uint8_t* mask;
   int B, C, P;
   int TP;       // padded chunk (tiled rows per request)
   int ctx_tiled;  // 1: ctx is written tiled [B*TP][2048]; 0: row-major [B][C][2048]
-  int S;        // prefix splits; split index S holds the suffix keys
+  int S;        // prefix splits; splits S .. S+NS-1 hold the suffix keys
+  int NS;       // suffix splits (32 keys each)
   int kps;      // prefix keys per split (multiple of 32)
   int R16;      // stacked query rows (2 * C) rounded up to 16
-  uint16_t* part_o;  // [B][HK][S + 1][R16][D] bf16, normalised partial outputs
-  float* part_ml;    // [B][HK][S + 1][R16][2] running max (log2 domain) and sum
+  uint16_t* part_o;  // [B][HK][S + NS][R16 / 16][16][64 lanes][4] bf16, normalised partial outputs
+  float* part_ml;    // [B][HK][S + NS][R16][2] running max (log2 domain) and sum
 };
 constexpr int kAttnKps = 64;  // prefix keys per attention split (32 .. 128, multiple of 32)
 void attn_config(int B, int C, int P, AttnArgs& a);
