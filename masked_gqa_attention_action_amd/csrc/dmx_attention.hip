@@ -117,11 +117,10 @@ __device__ __forceinline__ void suffix_store(const SufRaw& r, uint32_t vis, uint
   uint32_t kp[8];
 #pragma unroll
   for (int e2 = 0; e2 < 8; ++e2) kp[e2] = ok ? pack2(kv[2 * e2] * rn, kv[2 * e2 + 1] * rn) : 0u;
-  const uint4 z = make_uint4(0, 0, 0, 0);
   *reinterpret_cast<uint4*>(sK + j * KLD + c * 16) = make_uint4(kp[0], kp[1], kp[2], kp[3]);
   *reinterpret_cast<uint4*>(sK + j * KLD + c * 16 + 8) = make_uint4(kp[4], kp[5], kp[6], kp[7]);
-  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16) = ok ? r.v[0] : z;
-  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16 + 8) = ok ? r.v[1] : z;
+  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16) = keep_or_zero(ok, r.v[0]);
+  *reinterpret_cast<uint4*>(sV + j * VLD + c * 16 + 8) = keep_or_zero(ok, r.v[1]);
 }
 
 // K / V rows (bf16, from global) of one 32-key block: thread t owns 16-byte
@@ -149,8 +148,8 @@ __device__ __forceinline__ void kv_store(const KVRegs& r, uint32_t vis, uint16_t
     const int c = threadIdx.x + h * 512;
     const int j = c >> 5, ch = c & 31;
     const bool ok = (vis >> j) & 1u;
-    *reinterpret_cast<uint4*>(sK + j * KLD + ch * 8) = ok ? r.k[h] : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(sV + j * VLD + ch * 8) = ok ? r.v[h] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(sK + j * KLD + ch * 8) = keep_or_zero(ok, r.k[h]);
+    *reinterpret_cast<uint4*>(sV + j * VLD + ch * 8) = keep_or_zero(ok, r.v[h]);
   }
 }
 
@@ -327,38 +326,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   if (lq == 0) *reinterpret_cast<float2*>(a.part_ml + (pidx * a.R16 + row) * 2) = make_float2(mrun, l);
 }
 
-// One wave per (request, KV head, stacked row tile, quarter of the dims):
-// merges the S + NS split partials of 16 rows x 64 dims in split order with
+// One wave per (request, KV head, stacked row tile, eighth of the dims):
+// merges the S + NS split partials of 16 rows x 32 dims in split order with
 // a running maximum.  Lane (lr, lq) owns row lr and dims 16t + 4lq .. +3 of
-// the quarter's 4 dim tiles t; all loads of a batch of splits are in flight
+// the eighth's 2 dim tiles t; all loads of a batch of splits are in flight
 // together, each instruction reading 512 contiguous bytes.
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
-  constexpr int CB = 20;  // splits per batch of loads
+  constexpr int CB = 24;  // splits per batch of loads
+  constexpr int NT = 2;   // dim tiles per wave
   const int lane = threadIdx.x, lr = lane & 15, lq = lane >> 4;
   const int TT = a.TP >> 4, MT = 2 * TT;
-  const int q4 = blockIdx.x & 3, rest = blockIdx.x >> 2;
+  const int q4 = blockIdx.x & 7, rest = blockIdx.x >> 3;
   const int mt = rest % MT, bg = rest / MT;
   const int g = bg % kHK, b = bg / kHK;
   const int nsplit = a.S + a.NS;
   const int row = mt * 16 + lr;
   const int hh = mt / TT, i = (mt - hh * TT) * 16 + lr;
   const size_t ml0 = (size_t)bg * nsplit * a.R16 + row;
-  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + (q4 * 4) * 256 + lane * 4;
+  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + (q4 * NT) * 256 + lane * 4;
   float M = kNegBig, L = 0.f;
-  float acc[4][4];
+  float acc[NT][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += CB) {
     float2 ml[CB];
-    uint2 ov[CB][4];
+    uint2 ov[CB][NT];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const int s = min(s0 + u, nsplit - 1);  // past the end: re-read the last split, skipped below
       ml[u] = *reinterpret_cast<const float2*>(a.part_ml + (ml0 + (size_t)s * a.R16) * 2);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < NT; ++t)
         ov[u][t] = *reinterpret_cast<const uint2*>(a.part_o + o0 + (size_t)s * MT * (16 * kD) + t * 256);
     }
 #pragma unroll
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) 
         const float so = exp2f(M - Mn), w = ml[u].y * exp2f(ml[u].x - Mn);
         L = L * so + w;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < NT; ++t) {
           acc[t][0] = acc[t][0] * so + w * bf2f((uint16_t)(ov[u][t].x & 0xffffu));
           acc[t][1] = acc[t][1] * so + w * bf2f((uint16_t)(ov[u][t].x >> 16));
           acc[t][2] = acc[t][2] * so + w * bf2f((uint16_t)(ov[u][t].y & 0xffffu));
@@ -381,8 +381,8 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) 
   if (i >= a.C) return;
   const float inv = 1.0f / L;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int col = (kGroup * g + hh) * kD + (q4 * 4 + t) * 16 + 4 * lq;
+  for (int t = 0; t < NT; ++t) {
+    const int col = (kGroup * g + hh) * kD + (q4 * NT + t) * 16 + 4 * lq;
     uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
                                 : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
     *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[t][0] * inv, acc[t][1] * inv),
@@ -409,7 +409,7 @@ hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
     k_attn_partial<true, NB><<<grid, dim3(512), 0, s>>>(a);
   else
     k_attn_partial<false, NB><<<grid, dim3(512), 0, s>>>(a);
-  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 4), dim3(64), 0, s>>>(a, ctx);
+  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 8), dim3(64), 0, s>>>(a, ctx);
   return hipGetLastError();
 }
 

@@ -33,6 +33,12 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// v if keep, else zeros, selected per component (a select of whole vector
+// structs can be lowered through private memory)
+__device__ __forceinline__ uint4 keep_or_zero(bool keep, uint4 v) {
+  return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }

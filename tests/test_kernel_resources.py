@@ -1,0 +1,42 @@
+"""Every HIP kernel compiles for gfx950 without private-memory use: no VGPR
+or SGPR spills and no scratch (a private array the compiler could not keep in
+registers turns every access into a memory round trip).  Host-only check: it
+reads the compiler's resource-usage report."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from masked_gqa_attention_action_amd import build
+
+CSRC = os.path.join(os.path.dirname(build.__file__), "csrc")
+
+
+def _report(src):
+    cmd = [build.hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+           "-Rpass-analysis=kernel-resource-usage"]
+    out = subprocess.run(cmd, capture_output=True, text=True, check=True).stderr
+    kernels, name = {}, None
+    for line in out.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            kernels[name] = {}
+            continue
+        m = re.search(r"remark: (ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill|VGPRs|AGPRs): (\d+)", line)
+        if m and name:
+            kernels[name][m.group(1)] = int(m.group(2))
+    return kernels
+
+
+@pytest.mark.parametrize("src", build.SOURCES)
+def test_no_private_memory(src):
+    kernels = _report(src)
+    if src != "dmx_api.hip":
+        assert kernels, f"no kernels reported for {src}"
+    for name, r in kernels.items():
+        assert r.get("ScratchSize [bytes/lane]", 0) == 0, (name, r)
+        assert r.get("VGPRs Spill", 0) == 0 and r.get("SGPRs Spill", 0) == 0, (name, r)
+        assert r.get("VGPRs", 0) + r.get("AGPRs", 0) <= 512, (name, r)
