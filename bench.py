@@ -1,6 +1,6 @@
 """Benchmark: ms per denoise step of the 18-layer action-expert stack at the
-P_b=1024 prefix bucket, chunk 50, batch 1, and its fraction of the MI355X HBM
-roofline.
+P_b=1024 prefix bucket, chunk 50, batch 1, and the HBM roofline fraction of
+its dominant kernel.
 
 One step = the whole hot path once: 18 action-expert layers (AdaRMS, QKV +
 QK-norm + RoPE, masked GQA attention over prefix + suffix KV, gated residuals,
@@ -8,11 +8,18 @@ GEGLU MLP) for one denoising step, replayed from a hipGraph captured for the
 1024 bucket.  Inputs (seeded synthetic weights, KV cache, mask, time
 embedding) are resident in HBM before timing starts.
 
+Per-kernel timing: every kernel of the step is also launched on its own,
+through dmx_stack_stage_launch, in a captured graph that runs it for all 18
+layers in stack order (so weights and KV stream as they do in the stack), and
+timed with events on the same stream.  The kernel with the largest share of
+the step is the "dominant" one whose roofline fraction is reported.
+
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,21 +31,44 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-LAYER_WEIGHT_BYTES = 50_344_960  # 10 weight tensors of one layer, bf16
+H, I, HQ, HK, D = 1024, 4096, 8, 4, 256
+W_QKV, W_O, W_GU, W_DOWN = 4096 * H * 2, H * 2048 * 2, 8192 * H * 2, H * I * 2
+W_MOD = 3072 * H * 2 + 3072 * 2  # one modulation matrix + bias
+LAYER_WEIGHT_BYTES = W_QKV + W_O + W_GU + W_DOWN + 2 * W_MOD + 2 * D * 2  # 50,344,960
 
 
 def algorithmic_bytes_per_layer(batch, chunk, p_bucket, visible_rows_total):
     """Bytes one layer must move: its weights, the visible prefix K/V rows, and
     its own inputs and outputs (x in and out, cond, mask, pos0)."""
-    kv = 2 * 4 * 256 * 2 * visible_rows_total
-    io = batch * (2 * chunk * 1024 * 2 + 1024 * 2 + p_bucket + 4)
+    kv = 2 * HK * D * 2 * visible_rows_total
+    io = batch * (2 * chunk * H * 2 + H * 2 + p_bucket + 4)
     return LAYER_WEIGHT_BYTES + kv + io
 
 
+def stage_bytes(stage, batch, chunk, p_bucket, visible, n_layers):
+    """Algorithmic bytes of one launch of a stack kernel: the weights, KV rows
+    and layer inputs / outputs that its operation must read or write (bf16
+    activations).  Intermediates another fused design keeps on chip are not
+    counted; the attention combine therefore has none of its own."""
+    import masked_gqa_attention_action_amd as dmx
+    M = batch * chunk
+    act = lambda n: M * n * 2
+    return {
+        dmx.STAGE_MODS: n_layers * 2 * W_MOD + batch * H * 2 + n_layers * 2 * batch * 3072 * 4,
+        dmx.STAGE_PACK: act(H) * 2,
+        dmx.STAGE_QKV: W_QKV + act(H) + act(4096) + 2 * D * 2,
+        dmx.STAGE_ATTN: 2 * HK * D * 2 * visible + act(4096) + act(2048) + batch * p_bucket,
+        dmx.STAGE_COMBINE: 0,
+        dmx.STAGE_OPROJ: W_O + act(2048) + 2 * act(H),
+        dmx.STAGE_GATEUP: W_GU + act(H) + act(I),
+        dmx.STAGE_DOWN: W_DOWN + act(I) + 2 * act(H),
+    }[stage]
+
+
 def layer_flops(batch, chunk, visible_rows_total):
-    proj = 2 * batch * chunk * (1024 * 4096 + 2048 * 1024 + 1024 * 8192 + 4096 * 1024)
-    mod = 2 * batch * 2 * 1024 * 3072
-    attn = 4 * 8 * 256 * chunk * (visible_rows_total + batch * chunk)
+    proj = 2 * batch * chunk * (H * 4096 + 2048 * H + H * 8192 + I * H)
+    mod = 2 * batch * 2 * H * 3072
+    attn = 4 * HQ * D * chunk * (visible_rows_total + batch * chunk)
     return proj + mod + attn
 
 
@@ -49,23 +79,89 @@ def dev(bits, raw=False):
     return t.cuda()
 
 
-def cpu_baseline(wl, wbits, rq, conds, n_layers_sample):
-    """Time the float64 oracle on the host for a few layers of the same
-    workload and scale to one denoise step."""
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "masked_gqa_attention_action_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = ("dmx_attention.hip", "dmx_gemm.hip", "dmx_device.hpp", "dmx_internal.hpp", "dmx_tiles.hpp")
+
+
+def recorded_traffic(kernel_tag):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (profiles/traffic_<tag>.txt: 'bytes_per_launch' and the digest of the
+    kernel sources it was taken with); None if absent or taken with other
+    sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest(*KERNEL_SOURCES):
+        return None
+    try:
+        return int(float(vals["bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def time_stage(st, stage, n_layers, stream, reps):
+    """Average launch duration (us) of one stack kernel: a captured graph runs
+    it once per layer in stack order (so each launch streams another layer's
+    weights and KV, as in the stack); replays are timed with events on the
+    same stream."""
+    import torch
+    import masked_gqa_attention_action_amd as dmx
+    g = torch.cuda.CUDAGraph()
+    per_graph = n_layers  # per-step kernels (modulation, input pack) repeat n_layers times too
+    with torch.cuda.stream(stream):
+        for l in range(per_graph):  # eager warm-up of the same launches
+            st.stage_launch(l, stage, 1, stream)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for l in range(per_graph):
+                st.stage_launch(l, stage, 1, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):  # replay() launches on the current stream
+        for _ in range(3):
+            g.replay()
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+
+
+def cpu_baseline(wl, wbits, rq, conds, n_steps_sample):
+    """Time the float64 oracle on the host for whole denoise steps (all layers)
+    of the same workload; report ms per step."""
     import oracle as orc
     from masked_gqa_attention_action_amd import synth
     threads = orc.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
     f = synth.bf16_to_f64
+    ow = [{k: f(v) for k, v in w.items()} for w in wbits]
+    kp = [f(rq.k_pre[l]) for l in range(wl.n_layers)]
+    vp = [f(rq.v_pre[l]) for l in range(wl.n_layers)]
+    cond = f(conds[0])
     x = f(rq.x)
     t0 = time.perf_counter()
-    for l in range(n_layers_sample):
-        ow = {k: f(v) for k, v in wbits[l].items()}
-        x = orc.layer(x, f(conds[0]), ow, f(rq.k_pre[l]), f(rq.v_pre[l]), rq.mask, rq.pos0)
+    for _ in range(n_steps_sample):
+        for l in range(wl.n_layers):
+            x = orc.layer(x, cond, ow[l], kp[l], vp[l], rq.mask, rq.pos0)
     dt = time.perf_counter() - t0
-    ms_step = dt / n_layers_sample * wl.n_layers * 1e3
-    return {"value": round(ms_step, 3), "unit": "ms/step", "cores": threads, "kind": "oracle",
-            "sample": f"{n_layers_sample} of the step's {wl.n_layers} layers (float64 C oracle, same inputs), "
-                      f"{dt:.2f} s wall, scaled to one step"}
+    return {"value": round(dt / n_steps_sample * 1e3, 2), "unit": "ms/step", "cores": threads, "kind": "oracle",
+            "sample": f"{n_steps_sample} whole denoise steps ({n_steps_sample * wl.n_layers} layer evaluations) of "
+                      f"the same workload by the float64 C oracle on {threads} threads, {dt:.1f} s wall"}
 
 
 def main():
@@ -74,7 +170,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="step1024")
-    ap.add_argument("--cpu-layers", type=int, default=3, help="oracle layers timed for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=16, help="denoise steps the oracle runs for the CPU baseline "
+                                                             "(0: skip)")
+    ap.add_argument("--kernel-reps", type=int, default=20, help="replays per kernel for per-kernel timing (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; --gpus must be 1", file=sys.stderr)
@@ -98,8 +196,7 @@ def main():
     mask = dev(rq.mask[None], raw=True)
     cond = dev(conds[:1, None, :])          # one denoise step per replay
     pos0 = dev(np.array([rq.pos0], np.int32), raw=True)
-    x0 = dev(rq.x[None])
-    x = x0.clone()
+    x = dev(rq.x[None])
     st = dmx.Stack(wd, kp, vp, mask, cond, pos0, x)
     stream = torch.cuda.Stream()
     st.capture(stream)
@@ -117,12 +214,41 @@ def main():
     ev1.synchronize()
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    st.close()
     assert torch.isfinite(x.float()).all(), "non-finite activations"
 
     step_bytes = L * algorithmic_bytes_per_layer(B, C, P, visible)
     step_flops = L * layer_flops(B, C, visible)
-    achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # per-kernel timing (after the timed region) and the dominant kernel
+    kernels = {}
+    if args.kernel_reps > 0:
+        for stage, name in enumerate(dmx.STAGE_NAMES):
+            us = time_stage(st, stage, L, stream, args.kernel_reps)
+            per_step = 1 if stage in (dmx.STAGE_MODS, dmx.STAGE_PACK) else L
+            nbytes = stage_bytes(stage, B, C, P, visible, L)
+            kernels[name] = {"us_per_launch": round(us, 3), "launches_per_step": per_step,
+                             "share_of_step": round(us * per_step / (ms_step * 1e3), 4),
+                             "algorithmic_bytes": nbytes,
+                             "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if nbytes else None}
+        torch.cuda.synchronize()
+    st.close()
+    # a plain 256 MiB device copy: the reference dispatch for HBM byte counters
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+    roofline = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": None,
+                "traffic": None}
+    if kernels:
+        name = max(kernels, key=lambda k: kernels[k]["share_of_step"])
+        k = kernels[name]
+        tag = name.replace(" ", "_").replace("+", "_")
+        roofline.update({"kernel": name, "achieved": k["gbs"],
+                         "frac": round(k["gbs"] / PEAK_HBM_GBS, 4) if k["gbs"] else None,
+                         "traffic": recorded_traffic(f"{tag}_{args.workload}"),
+                         "us_per_launch": k["us_per_launch"], "algorithmic_bytes_per_launch": k["algorithmic_bytes"]})
     out = {
         "metric": "ms per denoise step (action-expert stack) at P=1024, chunk 50; % HBM roofline",
         "value": round(ms_step, 4),
@@ -138,13 +264,13 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix KV, sin/cos time embedding)",
         "config": {"workload": wl.note, "layers": L, "batch": B, "chunk": C, "p_bucket": P,
                    "visible_prefix_rows": visible, "steps_per_replay": 1},
-        "roofline": {"bound": "hbm", "kernel": "denoise-step graph (all kernels of 18 layers)",
-                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "algorithmic_bytes": step_bytes, "flops": step_flops},
+        "roofline": roofline,
+        "step": {"algorithmic_bytes": step_bytes, "flops": step_flops, "achieved_gbs": round(step_gbs, 1),
+                 "frac_of_hbm_peak": round(step_gbs / PEAK_HBM_GBS, 4)},
+        "kernels": kernels,
     }
-    if args.cpu_layers > 0:
-        out["cpu_baseline"] = cpu_baseline(wl, wbits, rq, conds, args.cpu_layers)
+    if args.cpu_steps > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, wbits, rq, conds, args.cpu_steps)
     print(json.dumps(out), flush=True)
 
 

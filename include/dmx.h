@@ -248,6 +248,24 @@ int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** ou
 int dmx_graph_launch(dmx_graph* g, void* stream);
 void dmx_graph_destroy(dmx_graph* g);
 
+/* Per-kernel timing (no citation: a measurement entry point).  Enqueues
+ * `reps` back-to-back launches of ONE kernel of the stack, with the arguments
+ * the stack passes it for layer `layer` at step 0, so that the kernel's
+ * average launch duration can be timed with events (e.g. inside a graph).
+ * Run the stack once first: the kernel then reads the intermediates a real
+ * pass leaves in the workspace.  A stage that writes x (DMX_STAGE_DOWN)
+ * changes the stack's state; others only rewrite workspace intermediates.
+ * stage: one of DMX_STAGE_*; reps in [1, 100000]. */
+#define DMX_STAGE_MODS 0     /* modulation vectors of every layer (one launch per step) */
+#define DMX_STAGE_PACK 1     /* tiled copy + row statistics of the stack input */
+#define DMX_STAGE_QKV 2      /* QKV + AdaRMS + QK-norm weights + RoPE */
+#define DMX_STAGE_ATTN 3     /* masked GQA attention splits */
+#define DMX_STAGE_COMBINE 4  /* merge of the splits */
+#define DMX_STAGE_OPROJ 5    /* O-projection + gated residual */
+#define DMX_STAGE_GATEUP 6   /* AdaRMS + GEGLU gate-up */
+#define DMX_STAGE_DOWN 7     /* MLP down + gated residual */
+int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage, int32_t reps, void* stream);
+
 /* ------------------------------------------------------------------------ */
 const char* dmx_status_string(int status);
 const char* dmx_last_error_string(void);

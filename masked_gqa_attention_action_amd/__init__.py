@@ -24,13 +24,18 @@ ERR_INVALID_ARG, ERR_BAD_BUCKETS, ERR_PREFIX_TOO_LONG = -1, -2, -3
 ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = -4, -5, -6, -7
 
 H, I, D, HQ, HK = 1024, 4096, 256, 8, 4
+
+# kernels of the stack, for per-kernel timing (Stack.stage_launch)
+STAGE_MODS, STAGE_PACK, STAGE_QKV, STAGE_ATTN, STAGE_COMBINE, STAGE_OPROJ, STAGE_GATEUP, STAGE_DOWN = range(8)
+STAGE_NAMES = ("modulation", "input pack", "qkv+norm+rope", "attention", "attention combine", "o-projection",
+               "gate-up", "down")
 PREFIX_HIDDEN = 2560
 
 EXPORTED = (
     "dmx_select_bucket", "dmx_workspace_bytes", "dmx_stack_workspace_bytes", "dmx_workspace_init", "dmx_pack_weight",
     "dmx_adarms_prenorm",
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
-    "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_graph_create", "dmx_graph_launch",
+    "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_stage_launch", "dmx_stack_graph_create", "dmx_graph_launch",
     "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
 )
 
@@ -86,6 +91,7 @@ def lib():
             "dmx_suffix_layer_forward": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, P, P, i32, i32,
                                           P, P, sz, P], ctypes.c_int),
             "dmx_stack_forward": ([ctypes.POINTER(StackDesc), P], ctypes.c_int),
+            "dmx_stack_stage_launch": ([ctypes.POINTER(StackDesc), i32, i32, i32, P], ctypes.c_int),
             "dmx_stack_graph_create": ([ctypes.POINTER(StackDesc), P, ctypes.POINTER(P)], ctypes.c_int),
             "dmx_graph_launch": ([P, P], ctypes.c_int),
             "dmx_graph_destroy": ([P], None),
@@ -303,6 +309,11 @@ class Stack:
 
     def run(self, stream=None):
         _check(lib().dmx_stack_forward(ctypes.byref(self.desc), _stream(stream)))
+
+    def stage_launch(self, layer, stage, reps=1, stream=None):
+        """reps back-to-back launches of one kernel of the stack (per-kernel timing)."""
+        _check(lib().dmx_stack_stage_launch(ctypes.byref(self.desc), int(layer), int(stage), int(reps),
+                                            _stream(stream)))
 
     def capture(self, stream):
         """Capture the stack into a hipGraph on a non-default stream."""

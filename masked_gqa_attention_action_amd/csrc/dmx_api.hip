@@ -239,109 +239,111 @@ int enq_geglu(const dmx_bf16* xn2, const dmx_bf16* w_gu, const dmx_bf16* w_down,
   return hip_check(launch_gemm(GEMM_DOWN, a, s), "down projection launch");
 }
 
-// The fused layer chain (modulation vectors mod1 / mod2 already computed,
-// the workspace holding x_in tiled in xp and its row sums of squares in ss_b,
-// 64 per row):
-//   QKV GEMM with AdaRMS #1 and QK-norm weights + RoPE fused -> attention
-//   (1 / rms of q, k on load) ->
-//   combine (tiled context) -> O-projection + gated residual (fp32 x1, tiled
-//   bf16(x1 * (1 + scale2)), row sums of squares of x1) -> gate-up GEMM with
-//   AdaRMS #2 fused + GEGLU -> down projection + gated residual (row-major
-//   x_out, its tiled copy and row sums of squares, for the next layer).
-int enq_layer_chain(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
-                    const int32_t* pos0, int B, int C, dmx_bf16* x_out,
-                    const float* mod1, const float* mod2, void* ws, const WsLayout& L, hipStream_t s) {
-  float* raw = at<float>(ws, L.raw);
-  uint16_t* xp = at<uint16_t>(ws, L.xp);
-  dmx_bf16* ctx = at<dmx_bf16>(ws, L.ctx);
-  float* x1 = at<float>(ws, L.x1);
-  dmx_bf16* x1s = at<dmx_bf16>(ws, L.x1s);
-  dmx_bf16* h = at<dmx_bf16>(ws, L.h);
-  float* ss_a = at<float>(ws, L.ss_a);
-  float* ss_b = at<float>(ws, L.ss_b);
-  const int M = B * L.TP;
+// One stage of the fused layer chain (modulation vectors mod1 / mod2 already
+// computed, the workspace holding x_in tiled in xp and its row sums of squares
+// in ss_b, 64 per row).  In order:
+//   DMX_STAGE_QKV      QKV GEMM with AdaRMS #1, QK-norm weights and RoPE fused
+//   DMX_STAGE_ATTN     attention splits (1 / rms of q, k applied on load)
+//   DMX_STAGE_COMBINE  merge of the splits into the tiled context
+//   DMX_STAGE_OPROJ    O-projection + gated residual: fp32 x1, tiled
+//                      bf16(x1 * (1 + scale2)) and row sums of squares of x1
+//   DMX_STAGE_GATEUP   gate-up GEMM with AdaRMS #2 fused + GEGLU
+//   DMX_STAGE_DOWN     down projection + gated residual: row-major x_out, its
+//                      tiled copy and row sums of squares, for the next layer
+struct LayerCtx {
+  const dmx_layer_weights* w;
+  const dmx_prefix_kv* kv;
+  const dmx_bf16* x_in;
+  const int32_t* pos0;
+  int B, C;
+  dmx_bf16* x_out;
+  const float *mod1, *mod2;
+  void* ws;
+  const WsLayout* L;
+};
 
-  float* ss_q = at<float>(ws, L.ss_q);
+int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
+  const WsLayout& L = *c.L;
+  void* ws = c.ws;
+  const int M = c.B * L.TP;
   GemmArgs g = gemm_args();
-  gemm_config(GEMM_QKV1024_MOD, g);
-  g.A = xp;
-  g.nmod = mod1;
-  g.ss_in = ss_b;
-  g.ss_in_n = kSsParts;
-  g.W = w->w_qkv;
   g.M = M;
-  g.T = C;
+  g.T = c.C;
   g.TP = L.TP;
-  g.out_f32 = raw;
-  g.ldo = kQKV;
-  g.qn_w = w->q_norm;
-  g.kn_w = w->k_norm;
-  g.pos0 = pos0;
-  g.rope_base = 10000.0f;
-  g.ss_q = ss_q;
-  g.out_pk = at<uint16_t>(ws, L.vb);
-  DMX_TRY(hip_check(launch_gemm(GEMM_QKV1024_MOD, g, s), "QKV GEMM launch"));
+  switch (stage) {
+    case DMX_STAGE_QKV:
+      gemm_config(GEMM_QKV1024_MOD, g);
+      g.A = at<uint16_t>(ws, L.xp);
+      g.nmod = c.mod1;
+      g.ss_in = at<float>(ws, L.ss_b);
+      g.ss_in_n = kSsParts;
+      g.W = c.w->w_qkv;
+      g.out_f32 = at<float>(ws, L.raw);
+      g.ldo = kQKV;
+      g.qn_w = c.w->q_norm;
+      g.kn_w = c.w->k_norm;
+      g.pos0 = c.pos0;
+      g.rope_base = 10000.0f;
+      g.ss_q = at<float>(ws, L.ss_q);
+      g.out_pk = at<uint16_t>(ws, L.vb);
+      return hip_check(launch_gemm(GEMM_QKV1024_MOD, g, s), "QKV GEMM launch");
+    case DMX_STAGE_ATTN:
+    case DMX_STAGE_COMBINE: {
+      AttnArgs a = attn_args(L, ws);
+      a.y = at<float>(ws, L.raw);
+      a.ss_q = at<float>(ws, L.ss_q);
+      a.vb = at<uint16_t>(ws, L.vb);
+      a.kp = c.kv->k;
+      a.vp = c.kv->v;
+      a.mask = c.kv->mask;
+      a.ctx_tiled = 1;
+      if (stage == DMX_STAGE_ATTN) return hip_check(launch_attn_partial(a, s), "attention launch");
+      return hip_check(launch_attn_combine(a, at<uint16_t>(ws, L.ctx), s), "attention combine launch");
+    }
+    case DMX_STAGE_OPROJ:  // x1 = x + gate1 * (ctx W_o^T)
+      gemm_config(GEMM_OPROJ_F32, g);
+      g.A = at<uint16_t>(ws, L.ctx);
+      g.W = c.w->w_o;
+      g.out_f32 = at<float>(ws, L.x1);
+      g.out_pk = at<uint16_t>(ws, L.x1s);
+      g.xs_scale = c.mod2;
+      g.ldo = kH;
+      g.gate = c.mod1 + 2 * kH;
+      g.gate_stride = 3 * kH;
+      g.resid = c.x_in;
+      g.ss_out = at<float>(ws, L.ss_a);
+      g.ss_out_n = kSsParts;
+      return hip_check(launch_gemm(GEMM_OPROJ_F32, g, s), "O-projection launch");
+    case DMX_STAGE_GATEUP:
+      gemm_config(GEMM_GATEUP_MOD, g);
+      g.A = at<uint16_t>(ws, L.x1s);
+      g.nmod = c.mod2;
+      g.ss_in = at<float>(ws, L.ss_a);
+      g.ss_in_n = kSsParts;
+      g.W = c.w->w_gu;
+      g.out_pk = at<uint16_t>(ws, L.h);
+      g.ldo = kI;
+      return hip_check(launch_gemm(GEMM_GATEUP_MOD, g, s), "gate-up GEMM launch");
+    case DMX_STAGE_DOWN:  // out = x1 + gate2 * (GEGLU(xn2) W_down^T)
+      gemm_config(GEMM_DOWN_F32RES, g);
+      g.A = at<uint16_t>(ws, L.h);
+      g.W = c.w->w_down;
+      g.out_bf16 = c.x_out;
+      g.out_pk = at<uint16_t>(ws, L.xp);
+      g.ldo = kH;
+      g.gate = c.mod2 + 2 * kH;
+      g.gate_stride = 3 * kH;
+      g.resid_f32 = at<float>(ws, L.x1);
+      g.ss_out = at<float>(ws, L.ss_b);
+      g.ss_out_n = kSsParts;
+      return hip_check(launch_gemm(GEMM_DOWN_F32RES, g, s), "down projection launch");
+  }
+  return fail(DMX_ERR_INVALID_ARG, "unknown layer stage %d", stage);
+}
 
-  AttnArgs a = attn_args(L, ws);
-  a.y = raw;
-  a.ss_q = ss_q;
-  a.vb = at<uint16_t>(ws, L.vb);
-  a.kp = kv->k;
-  a.vp = kv->v;
-  a.mask = kv->mask;
-  a.ctx_tiled = 1;
-  DMX_TRY(hip_check(launch_attention(a, ctx, s), "attention launch"));
-
-  // x1 = x + gate1 * (ctx W_o^T): fp32, the scaled tiled copy and row sums of squares
-  g = gemm_args();
-  gemm_config(GEMM_OPROJ_F32, g);
-  g.A = ctx;
-  g.W = w->w_o;
-  g.M = M;
-  g.T = C;
-  g.TP = L.TP;
-  g.out_f32 = x1;
-  g.out_pk = x1s;
-  g.xs_scale = mod2;
-  g.ldo = kH;
-  g.gate = mod1 + 2 * kH;
-  g.gate_stride = 3 * kH;
-  g.resid = x_in;
-  g.ss_out = ss_a;
-  g.ss_out_n = kSsParts;
-  DMX_TRY(hip_check(launch_gemm(GEMM_OPROJ_F32, g, s), "O-projection launch"));
-
-  g = gemm_args();
-  gemm_config(GEMM_GATEUP_MOD, g);
-  g.A = x1s;
-  g.nmod = mod2;
-  g.ss_in = ss_a;
-  g.ss_in_n = kSsParts;
-  g.W = w->w_gu;
-  g.M = M;
-  g.T = C;
-  g.TP = L.TP;
-  g.out_pk = h;
-  g.ldo = kI;
-  DMX_TRY(hip_check(launch_gemm(GEMM_GATEUP_MOD, g, s), "gate-up GEMM launch"));
-
-  // out = x1 + gate2 * (GEGLU(xn2) W_down^T), its tiled copy and row sums of squares
-  g = gemm_args();
-  gemm_config(GEMM_DOWN_F32RES, g);
-  g.A = h;
-  g.W = w->w_down;
-  g.M = M;
-  g.T = C;
-  g.TP = L.TP;
-  g.out_bf16 = x_out;
-  g.out_pk = xp;
-  g.ldo = kH;
-  g.gate = mod2 + 2 * kH;
-  g.gate_stride = 3 * kH;
-  g.resid_f32 = x1;
-  g.ss_out = ss_b;
-  g.ss_out_n = kSsParts;
-  return hip_check(launch_gemm(GEMM_DOWN_F32RES, g, s), "down projection launch");
+int enq_layer_chain(const LayerCtx& c, hipStream_t s) {
+  for (int stage = DMX_STAGE_QKV; stage <= DMX_STAGE_DOWN; ++stage) DMX_TRY(enq_layer_stage(c, stage, s));
+  return DMX_OK;
 }
 
 // tiled copy and row statistics of a row-major layer input
@@ -358,7 +360,8 @@ int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf1
   const ModJob jobs[2] = {{w->w_mod1, w->b_mod1, cond, mod1}, {w->w_mod2, w->b_mod2, cond, mod2}};
   DMX_TRY(enq_mods(jobs, 2, B, s));
   DMX_TRY(enq_pack_input(x_in, B, C, ws, L, s));
-  return enq_layer_chain(w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, L, s);
+  const LayerCtx c{w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, &L};
+  return enq_layer_chain(c, s);
 }
 
 int check_layer_weights(const char* fn, const dmx_layer_weights* w) {
@@ -579,25 +582,33 @@ static int check_stack(const char* fn, const dmx_stack_desc* d, WsLayout& L) {
 // One pass of the stack.  Per step, one launch computes the modulation
 // vectors of every layer (they depend only on the step's conditioning), then
 // the layers run their fused chains.
+static float* stack_mod(const dmx_stack_desc* d, const WsLayout& L, int l, int which) {
+  return at<float>(d->ws, L.stack_mod) + ((size_t)l * 2 + which) * d->batch * 3 * kH;
+}
+
+// the modulation vectors of every layer for step st, in one launch
+static int enq_stack_mods(const dmx_stack_desc* d, const WsLayout& L, int st, hipStream_t s) {
+  ModJob jobs[2 * DMX_MAX_LAYERS];
+  const dmx_bf16* cond = d->cond + (size_t)st * d->batch * kH;
+  for (int l = 0; l < d->n_layers; ++l) {
+    jobs[2 * l] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, stack_mod(d, L, l, 0)};
+    jobs[2 * l + 1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, stack_mod(d, L, l, 1)};
+  }
+  return enq_mods(jobs, 2 * d->n_layers, d->batch, s);
+}
+
 static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) {
   const int B = d->batch, NL = d->n_layers;
-  float* mods = at<float>(d->ws, L.stack_mod);
-  auto mod_of = [&](int l, int which) { return mods + ((size_t)l * 2 + which) * B * 3 * kH; };
-  ModJob jobs[2 * DMX_MAX_LAYERS];
+  auto mod_of = [&](int l, int which) { return stack_mod(d, L, l, which); };
   for (int st = 0; st < d->n_steps; ++st) {
-    const dmx_bf16* cond = d->cond + (size_t)st * B * kH;
-    for (int l = 0; l < NL; ++l) {
-      jobs[2 * l] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, mod_of(l, 0)};
-      jobs[2 * l + 1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, mod_of(l, 1)};
-    }
-    DMX_TRY(enq_mods(jobs, 2 * NL, B, s));
+    DMX_TRY(enq_stack_mods(d, L, st, s));
     // tiled x and its row statistics: a pack pass for the first layer of the
     // run, after that the down projection of the layer before
     if (st == 0) DMX_TRY(enq_pack_input(d->x, B, d->chunk, d->ws, L, s));
     for (int l = 0; l < NL; ++l) {
-      dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
-      DMX_TRY(enq_layer_chain(&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1), d->ws,
-                              L, s));
+      const dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
+      const LayerCtx c{&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1), d->ws, &L};
+      DMX_TRY(enq_layer_chain(c, s));
     }
   }
   return DMX_OK;
@@ -607,6 +618,29 @@ int dmx_stack_forward(const dmx_stack_desc* d, void* stream) {
   WsLayout L;
   DMX_TRY(check_stack("dmx_stack_forward", d, L));
   return enq_stack(d, L, (hipStream_t)stream);
+}
+
+int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage, int32_t reps, void* stream) {
+  const char* fn = "dmx_stack_stage_launch";
+  WsLayout L;
+  DMX_TRY(check_stack(fn, d, L));
+  if (layer < 0 || layer >= d->n_layers) return fail(DMX_ERR_INVALID_ARG, "%s: layer %d out of range", fn, layer);
+  if (stage < DMX_STAGE_MODS || stage > DMX_STAGE_DOWN)
+    return fail(DMX_ERR_INVALID_ARG, "%s: unknown stage %d", fn, stage);
+  if (reps < 1 || reps > 100000) return fail(DMX_ERR_INVALID_ARG, "%s: reps %d not in [1, 100000]", fn, reps);
+  hipStream_t s = (hipStream_t)stream;
+  const dmx_prefix_kv kv{d->k_pre[layer], d->v_pre[layer], d->mask, d->p_bucket};
+  const LayerCtx c{&d->layers[layer], &kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, layer, 0),
+                   stack_mod(d, L, layer, 1), d->ws, &L};
+  for (int r = 0; r < reps; ++r) {
+    if (stage == DMX_STAGE_MODS)
+      DMX_TRY(enq_stack_mods(d, L, 0, s));
+    else if (stage == DMX_STAGE_PACK)
+      DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, d->ws, L, s));
+    else
+      DMX_TRY(enq_layer_stage(c, stage, s));
+  }
+  return DMX_OK;
 }
 
 int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** out) {

@@ -174,6 +174,69 @@ __device__ __forceinline__ bf16x8 v_frag(const uint16_t* sV, int t, int lane) {
   return r;
 }
 
+// Merge of the split partials of one unit: 16 stacked rows (row tile mt) x
+// 32 dims (eighth q4 of the head dims) of request / KV head bg, in split
+// order with a running maximum.  One wave: lane (lr, lq) owns row lr and
+// dims 16t + 4lq .. +3 of the eighth's 2 dim tiles t; all loads of a batch
+// of splits are in flight together, each instruction reading 512 contiguous
+// bytes.
+__device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, int bg, int mt, int q4, int lane) {
+  constexpr int CB = 24;  // splits per batch of loads
+  constexpr int NT = 2;   // dim tiles per wave
+  const int lr = lane & 15, lq = lane >> 4;
+  const int TT = a.TP >> 4, MT = 2 * TT;
+  const int g = bg % kHK, b = bg / kHK;
+  const int nsplit = a.S + a.NS;
+  const int row = mt * 16 + lr;
+  const int hh = mt / TT, i = (mt - hh * TT) * 16 + lr;
+  const size_t ml0 = (size_t)bg * nsplit * a.R16 + row;
+  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + (q4 * NT) * 256 + lane * 4;
+  float M = kNegBig, L = 0.f;
+  float acc[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += CB) {
+    float2 ml[CB];
+    uint2 ov[CB][NT];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int s = min(s0 + u, nsplit - 1);  // past the end: re-read the last split, skipped below
+      ml[u] = *reinterpret_cast<const float2*>(a.part_ml + (ml0 + (size_t)s * a.R16) * 2);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        ov[u][t] = *reinterpret_cast<const uint2*>(a.part_o + o0 + (size_t)s * MT * (16 * kD) + t * 256);
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (s0 + u < nsplit && ml[u].y > 0.f) {
+        const float Mn = fmaxf(M, ml[u].x);
+        const float so = exp2f(M - Mn), w = ml[u].y * exp2f(ml[u].x - Mn);
+        L = L * so + w;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[t][0] = acc[t][0] * so + w * bf2f((uint16_t)(ov[u][t].x & 0xffffu));
+          acc[t][1] = acc[t][1] * so + w * bf2f((uint16_t)(ov[u][t].x >> 16));
+          acc[t][2] = acc[t][2] * so + w * bf2f((uint16_t)(ov[u][t].y & 0xffffu));
+          acc[t][3] = acc[t][3] * so + w * bf2f((uint16_t)(ov[u][t].y >> 16));
+        }
+        M = Mn;
+      }
+    }
+  }
+  if (i >= a.C) return;
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = (kGroup * g + hh) * kD + (q4 * NT + t) * 16 + 4 * lq;
+    uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
+                                : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[t][0] * inv, acc[t][1] * inv),
+                                                pack2(acc[t][2] * inv, acc[t][3] * inv));
+  }
+}
+
 // One split of one (request, KV head): every global load of the split (mask,
 // query rows, all K/V blocks or the raw suffix rows) is issued up front; the
 // blocks are then staged into LDS together and processed without further
@@ -256,7 +319,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int ks = 0; ks < 8; ++ks) qf[ks] = zero_bf16x8();
   }
   __syncthreads();
-  if (!active) return;
+  if (active) {
 
   // lane (lr, lq) owns stacked row mt*16 + lr; o[t][e] = O[row][16t + 4lq + e]
   f32x4 o[16];
@@ -324,70 +387,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     *reinterpret_cast<uint2*>(dst + t * 256) = make_uint2(pack2(o[t][0] * inv, o[t][1] * inv),
                                                           pack2(o[t][2] * inv, o[t][3] * inv));
   if (lq == 0) *reinterpret_cast<float2*>(a.part_ml + (pidx * a.R16 + row) * 2) = make_float2(mrun, l);
+  }  // active
 }
 
-// One wave per (request, KV head, stacked row tile, eighth of the dims):
-// merges the S + NS split partials of 16 rows x 32 dims in split order with
-// a running maximum.  Lane (lr, lq) owns row lr and dims 16t + 4lq .. +3 of
-// the eighth's 2 dim tiles t; all loads of a batch of splits are in flight
-// together, each instruction reading 512 contiguous bytes.
+// Separate merge kernel: one wave per (request, KV head, row tile, eighth).
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
-  constexpr int CB = 24;  // splits per batch of loads
-  constexpr int NT = 2;   // dim tiles per wave
-  const int lane = threadIdx.x, lr = lane & 15, lq = lane >> 4;
-  const int TT = a.TP >> 4, MT = 2 * TT;
   const int q4 = blockIdx.x & 7, rest = blockIdx.x >> 3;
-  const int mt = rest % MT, bg = rest / MT;
-  const int g = bg % kHK, b = bg / kHK;
-  const int nsplit = a.S + a.NS;
-  const int row = mt * 16 + lr;
-  const int hh = mt / TT, i = (mt - hh * TT) * 16 + lr;
-  const size_t ml0 = (size_t)bg * nsplit * a.R16 + row;
-  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + (q4 * NT) * 256 + lane * 4;
-  float M = kNegBig, L = 0.f;
-  float acc[NT][4];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += CB) {
-    float2 ml[CB];
-    uint2 ov[CB][NT];
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      const int s = min(s0 + u, nsplit - 1);  // past the end: re-read the last split, skipped below
-      ml[u] = *reinterpret_cast<const float2*>(a.part_ml + (ml0 + (size_t)s * a.R16) * 2);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        ov[u][t] = *reinterpret_cast<const uint2*>(a.part_o + o0 + (size_t)s * MT * (16 * kD) + t * 256);
-    }
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      if (s0 + u < nsplit && ml[u].y > 0.f) {
-        const float Mn = fmaxf(M, ml[u].x);
-        const float so = exp2f(M - Mn), w = ml[u].y * exp2f(ml[u].x - Mn);
-        L = L * so + w;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          acc[t][0] = acc[t][0] * so + w * bf2f((uint16_t)(ov[u][t].x & 0xffffu));
-          acc[t][1] = acc[t][1] * so + w * bf2f((uint16_t)(ov[u][t].x >> 16));
-          acc[t][2] = acc[t][2] * so + w * bf2f((uint16_t)(ov[u][t].y & 0xffffu));
-          acc[t][3] = acc[t][3] * so + w * bf2f((uint16_t)(ov[u][t].y >> 16));
-        }
-        M = Mn;
-      }
-    }
-  }
-  if (i >= a.C) return;
-  const float inv = 1.0f / L;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int col = (kGroup * g + hh) * kD + (q4 * NT + t) * 16 + 4 * lq;
-    uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
-                                : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[t][0] * inv, acc[t][1] * inv),
-                                                pack2(acc[t][2] * inv, acc[t][3] * inv));
-  }
+  const int MT = 2 * (a.TP >> 4);
+  combine_unit(a, ctx, rest / MT, rest % MT, q4, threadIdx.x);
 }
 
 void attn_config(int B, int C, int P, AttnArgs& a) {
@@ -401,7 +408,7 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
   a.R16 = 2 * a.TP;
 }
 
-hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
+hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
   constexpr int NB = kAttnKps / KB;
   static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
   const dim3 grid(a.B * kHK * (a.S + a.NS));
@@ -409,8 +416,17 @@ hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
     k_attn_partial<true, NB><<<grid, dim3(512), 0, s>>>(a);
   else
     k_attn_partial<false, NB><<<grid, dim3(512), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
   k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 8), dim3(64), 0, s>>>(a, ctx);
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
+  const hipError_t e = launch_attn_partial(a, s);
+  return e != hipSuccess ? e : launch_attn_combine(a, ctx, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -119,7 +119,9 @@ struct AttnArgs {
 };
 constexpr int kAttnKps = 64;  // prefix keys per attention split (32 .. 128, multiple of 32)
 void attn_config(int B, int C, int P, AttnArgs& a);
-hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s);  // partial + combine
+hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
