@@ -174,6 +174,20 @@ __device__ __forceinline__ bf16x8 v_frag(const uint16_t* sV, int t, int lane) {
   return r;
 }
 
+// Work-groups are dealt to the 8 XCDs of the chip in turn (blockIdx % 8), and
+// each XCD has its own L2.  Work item lists ordered by (request, KV head) are
+// therefore split into 8 contiguous chunks, chunk x served by the
+// work-groups of XCD x, so the splits (and merge units) of one request / KV
+// head share one or two L2s: its queries are fetched into few L2s and its
+// partials merged where they were written.  Placement changes only where data
+// is cached, never the results.  Returns the work item of this work-group, or
+// -1 for a spare one (grid = 8 * ceil(items / 8)).
+__device__ __forceinline__ int xcd_chunked(int wg, int grid, int items) {
+  const int per = grid >> 3;
+  const int item = (wg & 7) * per + (wg >> 3);
+  return item < items ? item : -1;
+}
+
 // Merge of the split partials of one unit: 16 stacked rows (row tile mt) x
 // 32 dims (eighth q4 of the head dims) of request / KV head bg, in split
 // order with a running maximum.  One wave: lane (lr, lq) owns row lr and
@@ -248,8 +262,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   __shared__ uint32_t sMask[NB];
 
   const int nsplit = a.S + a.NS;
-  const int split = blockIdx.x % nsplit;
-  const int bg = blockIdx.x / nsplit;
+  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * nsplit);
+  if (item < 0) return;
+  const int split = item % nsplit;
+  const int bg = item / nsplit;
   const int g = bg % kHK, b = bg / kHK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -390,10 +406,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }  // active
 }
 
-// Separate merge kernel: one wave per (request, KV head, row tile, eighth).
+// Separate merge kernel: one wave per (request, KV head, row tile, eighth),
+// placed like the splits (xcd_chunked) so the partials are read from the L2
+// that received them.
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
-  const int q4 = blockIdx.x & 7, rest = blockIdx.x >> 3;
   const int MT = 2 * (a.TP >> 4);
+  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * MT * 8);
+  if (item < 0) return;
+  const int q4 = item & 7, rest = item >> 3;
   combine_unit(a, ctx, rest / MT, rest % MT, q4, threadIdx.x);
 }
 
@@ -411,7 +431,8 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
 hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
   constexpr int NB = kAttnKps / KB;
   static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
-  const dim3 grid(a.B * kHK * (a.S + a.NS));
+  const int items = a.B * kHK * (a.S + a.NS);
+  const dim3 grid(8 * ((items + 7) / 8));
   if (a.y)
     k_attn_partial<true, NB><<<grid, dim3(512), 0, s>>>(a);
   else
@@ -420,7 +441,7 @@ hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
-  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 8), dim3(64), 0, s>>>(a, ctx);
+  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 8), dim3(64), 0, s>>>(a, ctx);  // a multiple of 8
   return hipGetLastError();
 }
 
