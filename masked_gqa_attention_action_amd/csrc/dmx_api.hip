@@ -249,7 +249,8 @@ int enq_geglu(const dmx_bf16* xn2, const dmx_bf16* w_gu, const dmx_bf16* w_down,
 //                      bf16(x1 * (1 + scale2)) and row sums of squares of x1
 //   DMX_STAGE_GATEUP   gate-up GEMM with AdaRMS #2 fused + GEGLU
 //   DMX_STAGE_DOWN     down projection + gated residual: row-major x_out, its
-//                      tiled copy and row sums of squares, for the next layer
+//                      tiled copy (scaled by the next layer's 1 + scale1 when
+//                      that is known) and row sums of squares, for the next layer
 struct LayerCtx {
   const dmx_layer_weights* w;
   const dmx_prefix_kv* kv;
@@ -260,6 +261,8 @@ struct LayerCtx {
   const float *mod1, *mod2;
   void* ws;
   const WsLayout* L;
+  bool x_prescaled;          // the tiled x holds bf16(x * (1 + scale1)) already
+  const float* next_scale1;  // the next layer's modulation (its scale first), or null
 };
 
 int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
@@ -271,8 +274,9 @@ int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
   g.T = c.C;
   g.TP = L.TP;
   switch (stage) {
-    case DMX_STAGE_QKV:
-      gemm_config(GEMM_QKV1024_MOD, g);
+    case DMX_STAGE_QKV: {
+      const GemmKind kind = c.x_prescaled ? GEMM_QKV1024_MODPRE : GEMM_QKV1024_MOD;
+      gemm_config(kind, g);
       g.A = at<uint16_t>(ws, L.xp);
       g.nmod = c.mod1;
       g.ss_in = at<float>(ws, L.ss_b);
@@ -286,7 +290,8 @@ int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
       g.rope_base = 10000.0f;
       g.ss_q = at<float>(ws, L.ss_q);
       g.out_pk = at<uint16_t>(ws, L.vb);
-      return hip_check(launch_gemm(GEMM_QKV1024_MOD, g, s), "QKV GEMM launch");
+      return hip_check(launch_gemm(kind, g, s), "QKV GEMM launch");
+    }
     case DMX_STAGE_ATTN:
     case DMX_STAGE_COMBINE: {
       AttnArgs a = attn_args(L, ws);
@@ -336,6 +341,7 @@ int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
       g.resid_f32 = at<float>(ws, L.x1);
       g.ss_out = at<float>(ws, L.ss_b);
       g.ss_out_n = kSsParts;
+      g.xs_scale = c.next_scale1;
       return hip_check(launch_gemm(GEMM_DOWN_F32RES, g, s), "down projection launch");
   }
   return fail(DMX_ERR_INVALID_ARG, "unknown layer stage %d", stage);
@@ -360,7 +366,7 @@ int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf1
   const ModJob jobs[2] = {{w->w_mod1, w->b_mod1, cond, mod1}, {w->w_mod2, w->b_mod2, cond, mod2}};
   DMX_TRY(enq_mods(jobs, 2, B, s));
   DMX_TRY(enq_pack_input(x_in, B, C, ws, L, s));
-  const LayerCtx c{w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, &L};
+  const LayerCtx c{w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, &L, false, nullptr};
   return enq_layer_chain(c, s);
 }
 
@@ -605,9 +611,12 @@ static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) 
     // tiled x and its row statistics: a pack pass for the first layer of the
     // run, after that the down projection of the layer before
     if (st == 0) DMX_TRY(enq_pack_input(d->x, B, d->chunk, d->ws, L, s));
+    // inside a step, each down projection hands the next layer its input
+    // already scaled by that layer's 1 + scale1
     for (int l = 0; l < NL; ++l) {
       const dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
-      const LayerCtx c{&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1), d->ws, &L};
+      const LayerCtx c{&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1), d->ws, &L,
+                       l > 0, l + 1 < NL ? mod_of(l + 1, 0) : nullptr};
       DMX_TRY(enq_layer_chain(c, s));
     }
   }
@@ -631,7 +640,8 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
   hipStream_t s = (hipStream_t)stream;
   const dmx_prefix_kv kv{d->k_pre[layer], d->v_pre[layer], d->mask, d->p_bucket};
   const LayerCtx c{&d->layers[layer], &kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, layer, 0),
-                   stack_mod(d, L, layer, 1), d->ws, &L};
+                   stack_mod(d, L, layer, 1), d->ws, &L, layer > 0,
+                   layer + 1 < d->n_layers ? stack_mod(d, L, layer + 1, 0) : nullptr};
   for (int r = 0; r < reps; ++r) {
     if (stage == DMX_STAGE_MODS)
       DMX_TRY(enq_stack_mods(d, L, 0, s));

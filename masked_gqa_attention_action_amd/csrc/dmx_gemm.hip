@@ -98,7 +98,7 @@ __device__ __forceinline__ void epi_fetch(const GemmArgs& a, int prow, int n, Ep
     p.g[1] = *reinterpret_cast<const float4*>(gp + 4);
   }
   if (EPI == EPI_RESID_BB || EPI == EPI_RESID_BF) p.rb = *reinterpret_cast<const uint4*>(a.resid + lrow * a.ldo + n);
-  if (EPI == EPI_RESID_BF && a.xs_scale) {
+  if ((EPI == EPI_RESID_BF || EPI == EPI_RESID_FB) && a.xs_scale) {
     const float* sp = a.xs_scale + (size_t)b * a.gate_stride + n;
     p.sc[0] = *reinterpret_cast<const float4*>(sp);
     p.sc[1] = *reinterpret_cast<const float4*>(sp + 4);
@@ -173,8 +173,18 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& a, int prow, int n, c
     for (int i = 0; i < 8; ++i) v[i] = r[i] + g[i] * v[i];
     const uint4 hb = pack8(v);
     *reinterpret_cast<uint4*>(a.out_bf16 + lrow * a.ldo + n) = hb;
-    if (a.out_pk) *reinterpret_cast<uint4*>(a.out_pk + tile_off(prow, n, a.ldo)) = hb;
     unpack8(hb, seen);
+    if (a.out_pk) {  // the next layer's A operand: bf16(x) itself or bf16(bf16(x) * (1 + scale))
+      uint4 pk = hb;
+      if (a.xs_scale) {
+        float sc[8], xs[8];
+        f4x2(p.sc, sc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xs[i] = seen[i] * (1.0f + sc[i]);
+        pk = pack8(xs);
+      }
+      *reinterpret_cast<uint4*>(a.out_pk + tile_off(prow, n, a.ldo)) = pk;
+    }
   }
 }
 
@@ -470,6 +480,7 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
   switch (kind) {
     case GEMM_QKV1024: a.ntiles = kQKV / 16; a.K = kH; break;
     case GEMM_QKV1024_MOD: a.ntiles = kQKV / 32; a.K = kH; break;
+    case GEMM_QKV1024_MODPRE: a.ntiles = kQKV / 32; a.K = kH; break;
     case GEMM_QKV2560: a.ntiles = kQKV / 16; a.K = 2560; break;
     case GEMM_OPROJ: a.ntiles = kH / 16; a.K = kHQ * kD; break;
     case GEMM_OPROJ_F32: a.ntiles = kH / 16; a.K = kHQ * kD; break;
@@ -490,6 +501,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {
     case GEMM_QKV1024: DMX_GEMM(EPI_F32, 16, 4, 8, A_GLOBAL, 2, mb2); break;
     case GEMM_QKV1024_MOD: DMX_GEMM(EPI_QKV, 32, 4, 8, A_MOD, 2, nreq2); break;
+    case GEMM_QKV1024_MODPRE: DMX_GEMM(EPI_QKV, 32, 4, 8, A_MODPRE, 2, nreq2); break;
     case GEMM_QKV2560: DMX_GEMM(EPI_F32, 16, 4, 20, A_GLOBAL, 1, 4); break;
     case GEMM_OPROJ: DMX_GEMM(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 1, mb1); break;
     case GEMM_OPROJ_F32: DMX_GEMM(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 1, mb1); break;

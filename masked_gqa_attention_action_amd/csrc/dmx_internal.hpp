@@ -29,8 +29,9 @@ struct GemmArgs {
   int ss_in_n;        //   a multiple of 4 up to 64
   float* ss_out;      // EPI_RESID_BF / _FB: optional [M][ss_out_n] partials, one
   int ss_out_n;       //   per N-tile of 16 features (ntiles == ss_out_n)
-  const float* xs_scale;  // EPI_RESID_BF: out_pk = bf16(out * (1 + xs_scale[b][n])),
-                          //   row b at xs_scale + b * gate_stride (null: bf16(out))
+  const float* xs_scale;  // EPI_RESID_BF: out_pk = bf16(out * (1 + xs_scale[b][n]));
+                          // EPI_RESID_FB: out_pk = bf16(bf16(out) * (1 + xs_scale[b][n]));
+                          //   row b at xs_scale + b * gate_stride (null: no scaling)
   const uint16_t* W;  // tiled weights [N][K]
   int M, K;           // M = B * TP tiled rows
   int T, TP;          // tokens per request and their padded count
@@ -57,6 +58,7 @@ constexpr int kQkvTiles = 96;  // 32-feature tiles of the 12 q / k heads (8 per 
 enum GemmKind {
   GEMM_QKV1024 = 1,         // N = 4096, K = 1024, fp32 out, A given
   GEMM_QKV1024_MOD = 2,     // N = 4096 as rotation-pair tiles, AdaRMS of bf16 x fused, EPI_QKV
+  GEMM_QKV1024_MODPRE = 10, // as above with A already bf16(x * (1 + scale))
   GEMM_QKV2560 = 3,         // N = 4096, K = 2560, fp32 out
   GEMM_OPROJ = 4,           // N = 1024, K = 2048, gated residual (bf16 -> bf16)
   GEMM_OPROJ_F32 = 5,       // as GEMM_OPROJ, fp32 output (layer-internal residual)
