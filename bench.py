@@ -142,6 +142,24 @@ def time_stage(st, stage, n_layers, stream, reps):
     return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
 
 
+def time_replays(st, stream, warmup, reps):
+    """ms per replay of a captured stack graph, events on its stream."""
+    import torch
+    for _ in range(warmup):
+        st.replay(stream)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        st.replay(stream)
+    e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def cpu_baseline(wl, wbits, rq, conds, n_steps_sample):
     """Time the float64 oracle on the host for whole denoise steps (all layers)
     of the same workload; report ms per step."""
@@ -173,6 +191,7 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=16, help="denoise steps the oracle runs for the CPU baseline "
                                                              "(0: skip)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="replays per kernel for per-kernel timing (0: skip)")
+    ap.add_argument("--variants", type=int, default=1, help="also time the cached-modulation variants (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; --gpus must be 1", file=sys.stderr)
@@ -200,21 +219,35 @@ def main():
     st = dmx.Stack(wd, kp, vp, mask, cond, pos0, x)
     stream = torch.cuda.Stream()
     st.capture(stream)
-
-    for _ in range(args.warmup):
-        st.replay(stream)
-    stream.synchronize()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        st.replay(stream)
-    ev1.record(stream)
-    ev1.synchronize()
-    torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = time_replays(st, stream, args.warmup, args.steps)
     assert torch.isfinite(x.float()).all(), "non-finite activations"
+
+    # Reported beside the headline, never as it: the same step with the
+    # modulation vectors read from a table filled once per timestep schedule,
+    # and the whole denoise loop captured as one graph with that table.
+    variants = {}
+    if args.variants:
+        x.copy_(dev(rq.x[None]))
+        with torch.cuda.stream(stream):
+            tb = dmx.Stack(wd, kp, vp, mask, cond, pos0, x, mod_table=True, stream=stream)
+        tb.capture(stream)
+        variants["mod_table_step"] = {"ms_per_step": round(time_replays(tb, stream, args.warmup, args.steps), 4),
+                                      "note": "one step per replay, modulation vectors precomputed per schedule"}
+        tb.close()
+        x.copy_(dev(rq.x[None]))
+        cond_all = dev(conds[:, None, :])
+        with torch.cuda.stream(stream):
+            lp = dmx.Stack(wd, kp, vp, mask, cond_all, pos0, x, mod_table=True, stream=stream)
+        lp.capture(stream)
+        n = max(1, args.steps // wl.n_steps)
+        ms_loop = time_replays(lp, stream, max(1, args.warmup // wl.n_steps), n)
+        variants["mod_table_loop"] = {"ms_per_step": round(ms_loop / wl.n_steps, 4),
+                                      "note": f"whole {wl.n_steps}-step denoise loop per replay, modulation "
+                                              "vectors precomputed per schedule"}
+        lp.close()
+        assert torch.isfinite(x.float()).all(), "non-finite activations"
+        x.copy_(dev(rq.x[None]))
+        torch.cuda.synchronize()
 
     step_bytes = L * algorithmic_bytes_per_layer(B, C, P, visible)
     step_flops = L * layer_flops(B, C, visible)
@@ -268,6 +301,7 @@ def main():
         "step": {"algorithmic_bytes": step_bytes, "flops": step_flops, "achieved_gbs": round(step_gbs, 1),
                  "frac_of_hbm_peak": round(step_gbs / PEAK_HBM_GBS, 4)},
         "kernels": kernels,
+        "variants": variants,
     }
     if args.cpu_steps > 0:
         out["cpu_baseline"] = cpu_baseline(wl, wbits, rq, conds, args.cpu_steps)

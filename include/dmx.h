@@ -231,6 +231,14 @@ typedef struct dmx_stack_desc {
   dmx_bf16* x;                     /* device [batch][chunk][1024], updated in place */
   void* ws;                         /* >= dmx_stack_workspace_bytes(...) */
   size_t ws_bytes;
+  /* Optional device [n_steps][n_layers][2][batch][3072] fp32: the AdaRMS
+   * modulation vectors W_mod * cond[s][b] + b_mod of every step, layer and
+   * norm (index 0: the attention's, 1: the MLP's), as filled by
+   * dmx_stack_mod_table_fill.  The conditioning of a step depends on the
+   * timestep only, and the steps are fixed once a profile is captured ([Art]
+   * §4), so the table is computed once per schedule and reused by every
+   * request.  NULL: the vectors are computed from cond inside every step. */
+  const float* mod_table;
 } dmx_stack_desc;
 
 typedef struct dmx_graph dmx_graph;
@@ -239,6 +247,13 @@ typedef struct dmx_graph dmx_graph;
  * plus the modulation vectors of every layer of one step.  0 if unsupported
  * (n_layers above DMX_MAX_LAYERS included). */
 size_t dmx_stack_workspace_bytes(int32_t n_layers, int32_t batch, int32_t chunk, int32_t p_bucket);
+
+/* Bytes of the modulation table of a stack (0 if unsupported). */
+size_t dmx_stack_mod_table_bytes(int32_t n_layers, int32_t n_steps, int32_t batch);
+/* Fill `table` (>= dmx_stack_mod_table_bytes) with the modulation vectors of
+ * every step and layer of `d` from its cond buffer (d->mod_table is ignored).
+ * Enqueued on `stream`. */
+int dmx_stack_mod_table_fill(const dmx_stack_desc* d, float* table, void* stream);
 
 /* Eager run of the stack (same kernels as the graph). */
 int dmx_stack_forward(const dmx_stack_desc* d, void* stream);

@@ -35,7 +35,8 @@ EXPORTED = (
     "dmx_select_bucket", "dmx_workspace_bytes", "dmx_stack_workspace_bytes", "dmx_workspace_init", "dmx_pack_weight",
     "dmx_adarms_prenorm",
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
-    "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_stage_launch", "dmx_stack_graph_create", "dmx_graph_launch",
+    "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_stage_launch",
+    "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill", "dmx_stack_graph_create", "dmx_graph_launch",
     "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
 )
 
@@ -62,7 +63,8 @@ class StackDesc(ctypes.Structure):
                 ("layers", ctypes.POINTER(LayerWeights)),
                 ("k_pre", ctypes.POINTER(ctypes.c_void_p)), ("v_pre", ctypes.POINTER(ctypes.c_void_p)),
                 ("mask", ctypes.c_void_p), ("cond", ctypes.c_void_p), ("pos0", ctypes.c_void_p),
-                ("x", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+                ("x", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("mod_table", ctypes.c_void_p)]
 
 
 _lib = None
@@ -92,6 +94,8 @@ def lib():
                                           P, P, sz, P], ctypes.c_int),
             "dmx_stack_forward": ([ctypes.POINTER(StackDesc), P], ctypes.c_int),
             "dmx_stack_stage_launch": ([ctypes.POINTER(StackDesc), i32, i32, i32, P], ctypes.c_int),
+            "dmx_stack_mod_table_bytes": ([i32, i32, i32], sz),
+            "dmx_stack_mod_table_fill": ([ctypes.POINTER(StackDesc), P, P], ctypes.c_int),
             "dmx_stack_graph_create": ([ctypes.POINTER(StackDesc), P, ctypes.POINTER(P)], ctypes.c_int),
             "dmx_graph_launch": ([P, P], ctypes.c_int),
             "dmx_graph_destroy": ([P], None),
@@ -281,9 +285,14 @@ class Stack:
 
     layers: list of weight dicts; k_pre / v_pre: per-layer [B][4][P][256]
     tensors; mask [B][P] uint8; cond [n_steps][B][1024]; pos0 [B] int32;
-    x [B][C][1024] (updated in place by run / replay)."""
+    x [B][C][1024] (updated in place by run / replay).
 
-    def __init__(self, layers, k_pre, v_pre, mask, cond, pos0, x, ws=None):
+    mod_table=True computes the modulation vectors of every step and layer
+    once, from cond as it is at construction (or at the last
+    fill_mod_table()), and the runs read them instead of recomputing them in
+    every step."""
+
+    def __init__(self, layers, k_pre, v_pre, mask, cond, pos0, x, ws=None, mod_table=False, stream=None):
         self.n_layers = len(layers)
         self.n_steps, B, _ = cond.shape
         _, C, _ = x.shape
@@ -304,8 +313,20 @@ class Stack:
         _want(mask, (B, P), torch.uint8, "mask")
         self.desc = StackDesc(self.n_layers, self.n_steps, B, C, P, self._lw, self._kp, self._vp,
                               mask.data_ptr(), cond.data_ptr(), pos0.data_ptr(), x.data_ptr(),
-                              self.ws.data_ptr(), self.ws.numel())
+                              self.ws.data_ptr(), self.ws.numel(), None)
         self._graph = None
+        self.mod_table = None
+        if mod_table:
+            n = int(lib().dmx_stack_mod_table_bytes(self.n_layers, self.n_steps, B))
+            if n == 0:
+                raise DmxError(ERR_UNSUPPORTED, f"no modulation table for {self.n_layers} layers {self.n_steps} steps")
+            self.mod_table = torch.empty(n // 4, dtype=torch.float32, device=x.device)
+            self.fill_mod_table(stream)
+            self.desc.mod_table = self.mod_table.data_ptr()
+
+    def fill_mod_table(self, stream=None):
+        """(Re)compute the cached modulation vectors from the current cond."""
+        _check(lib().dmx_stack_mod_table_fill(ctypes.byref(self.desc), _p(self.mod_table), _stream(stream)))
 
     def run(self, stream=None):
         _check(lib().dmx_stack_forward(ctypes.byref(self.desc), _stream(stream)))

@@ -582,42 +582,65 @@ static int check_stack(const char* fn, const dmx_stack_desc* d, WsLayout& L) {
   DMX_REQUIRE_PTR(d->cond);
   DMX_REQUIRE_PTR(d->pos0);
   DMX_REQUIRE_PTR(d->x);
+  if (d->mod_table && !aligned16(d->mod_table))
+    return fail(DMX_ERR_MISALIGNED, "%s: mod_table is not 16-byte aligned", fn);
   return check_ws(fn, d->ws, d->ws_bytes, d->batch, d->chunk, d->p_bucket, L, d->n_layers);
 }
 
 // One pass of the stack.  Per step, one launch computes the modulation
 // vectors of every layer (they depend only on the step's conditioning), then
 // the layers run their fused chains.
-static float* stack_mod(const dmx_stack_desc* d, const WsLayout& L, int l, int which) {
-  return at<float>(d->ws, L.stack_mod) + ((size_t)l * 2 + which) * d->batch * 3 * kH;
+// modulation vectors of (step, layer, norm): the cached table, or the
+// workspace slot the current step's vectors are computed into
+static float* stack_mod(const dmx_stack_desc* d, const WsLayout& L, int st, int l, int which) {
+  const size_t vec = (size_t)d->batch * 3 * kH;
+  if (d->mod_table) return const_cast<float*>(d->mod_table) + (((size_t)st * d->n_layers + l) * 2 + which) * vec;
+  return at<float>(d->ws, L.stack_mod) + ((size_t)l * 2 + which) * vec;
 }
 
-// the modulation vectors of every layer for step st, in one launch
-static int enq_stack_mods(const dmx_stack_desc* d, const WsLayout& L, int st, hipStream_t s) {
+// the modulation vectors of every layer for step st, in one launch, into `out`
+// ([n_layers][2][batch][3072])
+static int enq_step_mods(const dmx_stack_desc* d, int st, float* out, hipStream_t s) {
   ModJob jobs[2 * DMX_MAX_LAYERS];
   const dmx_bf16* cond = d->cond + (size_t)st * d->batch * kH;
+  const size_t vec = (size_t)d->batch * 3 * kH;
   for (int l = 0; l < d->n_layers; ++l) {
-    jobs[2 * l] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, stack_mod(d, L, l, 0)};
-    jobs[2 * l + 1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, stack_mod(d, L, l, 1)};
+    jobs[2 * l] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, out + (size_t)(2 * l) * vec};
+    jobs[2 * l + 1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, out + (size_t)(2 * l + 1) * vec};
   }
   return enq_mods(jobs, 2 * d->n_layers, d->batch, s);
 }
 
+static int enq_stack_mods(const dmx_stack_desc* d, const WsLayout& L, int st, hipStream_t s) {
+  return enq_step_mods(d, st, at<float>(d->ws, L.stack_mod), s);
+}
+
+// Layer l of step st as the stack runs it.  Each down projection hands the
+// next layer its input already scaled by that layer's 1 + scale1 when the
+// next layer's modulation is known by then: inside a step always, across
+// steps with a cached table.  Only the first layer of a run (and, without a
+// table, of every step) scales its input itself.
+static LayerCtx stack_layer(const dmx_stack_desc* d, const WsLayout& L, const dmx_prefix_kv* kv, int st, int l) {
+  const bool table = d->mod_table != nullptr;
+  const float* next = nullptr;
+  if (l + 1 < d->n_layers)
+    next = stack_mod(d, L, st, l + 1, 0);
+  else if (table && st + 1 < d->n_steps)
+    next = stack_mod(d, L, st + 1, 0, 0);
+  const bool pre = l > 0 || (table && st > 0);
+  return LayerCtx{&d->layers[l], kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, st, l, 0),
+                  stack_mod(d, L, st, l, 1), d->ws, &L, pre, next};
+}
+
 static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) {
-  const int B = d->batch, NL = d->n_layers;
-  auto mod_of = [&](int l, int which) { return stack_mod(d, L, l, which); };
   for (int st = 0; st < d->n_steps; ++st) {
-    DMX_TRY(enq_stack_mods(d, L, st, s));
+    if (!d->mod_table) DMX_TRY(enq_stack_mods(d, L, st, s));
     // tiled x and its row statistics: a pack pass for the first layer of the
     // run, after that the down projection of the layer before
-    if (st == 0) DMX_TRY(enq_pack_input(d->x, B, d->chunk, d->ws, L, s));
-    // inside a step, each down projection hands the next layer its input
-    // already scaled by that layer's 1 + scale1
-    for (int l = 0; l < NL; ++l) {
+    if (st == 0) DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, d->ws, L, s));
+    for (int l = 0; l < d->n_layers; ++l) {
       const dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
-      const LayerCtx c{&d->layers[l], &kv, d->x, d->pos0, B, d->chunk, d->x, mod_of(l, 0), mod_of(l, 1), d->ws, &L,
-                       l > 0, l + 1 < NL ? mod_of(l + 1, 0) : nullptr};
-      DMX_TRY(enq_layer_chain(c, s));
+      DMX_TRY(enq_layer_chain(stack_layer(d, L, &kv, st, l), s));
     }
   }
   return DMX_OK;
@@ -639,9 +662,7 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
   if (reps < 1 || reps > 100000) return fail(DMX_ERR_INVALID_ARG, "%s: reps %d not in [1, 100000]", fn, reps);
   hipStream_t s = (hipStream_t)stream;
   const dmx_prefix_kv kv{d->k_pre[layer], d->v_pre[layer], d->mask, d->p_bucket};
-  const LayerCtx c{&d->layers[layer], &kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, layer, 0),
-                   stack_mod(d, L, layer, 1), d->ws, &L, layer > 0,
-                   layer + 1 < d->n_layers ? stack_mod(d, L, layer + 1, 0) : nullptr};
+  const LayerCtx c = stack_layer(d, L, &kv, 0, layer);
   for (int r = 0; r < reps; ++r) {
     if (stage == DMX_STAGE_MODS)
       DMX_TRY(enq_stack_mods(d, L, 0, s));
@@ -650,6 +671,24 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
     else
       DMX_TRY(enq_layer_stage(c, stage, s));
   }
+  return DMX_OK;
+}
+
+size_t dmx_stack_mod_table_bytes(int32_t n_layers, int32_t n_steps, int32_t batch) {
+  if (n_layers < 1 || n_layers > DMX_MAX_LAYERS || n_steps < 1 || n_steps > 1000 || batch < 1 ||
+      batch > DMX_MAX_BATCH)
+    return 0;
+  return (size_t)n_steps * n_layers * 2 * batch * 3 * kH * sizeof(float);
+}
+
+int dmx_stack_mod_table_fill(const dmx_stack_desc* d, float* table, void* stream) {
+  const char* fn = "dmx_stack_mod_table_fill";
+  WsLayout L;
+  DMX_TRY(check_stack(fn, d, L));
+  DMX_REQUIRE_PTR(table);
+  if (d->n_steps > 1000) return fail(DMX_ERR_UNSUPPORTED, "%s: more than 1000 steps", fn);
+  const size_t step = (size_t)d->n_layers * 2 * d->batch * 3 * kH;
+  for (int st = 0; st < d->n_steps; ++st) DMX_TRY(enq_step_mods(d, st, table + (size_t)st * step, (hipStream_t)stream));
   return DMX_OK;
 }
 

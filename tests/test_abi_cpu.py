@@ -54,6 +54,12 @@ def test_workspace_sizes(dmx):
     assert dmx.workspace_bytes(0, 50, 1024) == 0
     assert dmx.workspace_bytes(1, 0, 1024) == 0
     assert dmx.workspace_bytes(1, 50, -1) == 0
+    L = dmx.lib()
+    assert L.dmx_stack_mod_table_bytes(18, 10, 1) == 10 * 18 * 2 * 1 * 3 * 1024 * 4
+    assert L.dmx_stack_mod_table_bytes(18, 10, 4) == 4 * L.dmx_stack_mod_table_bytes(18, 10, 1)
+    assert L.dmx_stack_mod_table_bytes(0, 10, 1) == 0
+    assert L.dmx_stack_mod_table_bytes(18, 0, 1) == 0
+    assert L.dmx_stack_mod_table_bytes(18, 10, 0) == 0
 
 
 FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
@@ -95,6 +101,7 @@ def test_validation_errors_before_launch(dmx):
     assert b"overlaps" in L.dmx_last_error_string()
     g = ctypes.c_void_p()
     assert L.dmx_stack_graph_create(None, FAKE, ctypes.byref(g)) == dmx.ERR_INVALID_ARG
+    assert L.dmx_stack_mod_table_fill(None, FAKE, None) == dmx.ERR_INVALID_ARG
     assert L.dmx_graph_launch(None, None) == dmx.ERR_INVALID_ARG
     L.dmx_graph_destroy(None)
     for s in (0, 1, -1, -2, -3, -4, -5, -6, -7, -99):

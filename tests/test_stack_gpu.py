@@ -98,3 +98,44 @@ def test_stack_graph_matches_eager_and_oracle(stack_case):
         got = from_dev(probes[(s, l, "out")][0])
         gate(f"{c['name']} step {s} layer {l}", got, ref)
         delta_gate(f"{c['name']} step {s} layer {l} branch", got, ref, xin, rel=LAYER_BRANCH_REL)
+
+
+def test_stack_with_mod_table_matches_eager(stack_case):
+    """A cached modulation table (filled once per timestep schedule) gives the
+    same bits as computing the vectors inside every step, eager and replayed;
+    refilling it after cond changes follows the new cond."""
+    c = stack_case
+    dmx = c["dmx"]
+    x_eager, _ = eager_layers(c)
+    xs = c["x0"].clone()
+    st = dmx.Stack(c["wd"], c["kp"], c["vp"], c["mask"], c["cond"], c["pos0"], xs, mod_table=True)
+    n = int(dmx.lib().dmx_stack_mod_table_bytes(st.n_layers, st.n_steps, 1))
+    assert st.mod_table.numel() * 4 == n == st.n_steps * st.n_layers * 2 * 3 * dmx.H * 4
+    st.run()
+    torch.cuda.synchronize()
+    assert torch.equal(xs, x_eager), "stack with modulation table differs from layer-by-layer"
+
+    stream = torch.cuda.Stream()
+    st.capture(stream)
+    for rep in range(2):
+        xs.copy_(c["x0"])
+        torch.cuda.synchronize()
+        st.replay(stream)
+        stream.synchronize()
+        assert torch.equal(xs, x_eager), f"graph replay {rep} with modulation table differs"
+    st.close()
+
+    # a changed schedule: the table follows cond once refilled
+    cond2 = c["cond"].flip(0).contiguous()
+    xs2 = c["x0"].clone()
+    ref = dmx.Stack(c["wd"], c["kp"], c["vp"], c["mask"], cond2, c["pos0"], xs2)
+    ref.run()
+    c["cond"].copy_(cond2)
+    try:
+        st.fill_mod_table()
+        xs.copy_(c["x0"])
+        st.run()
+        torch.cuda.synchronize()
+    finally:
+        c["cond"].copy_(cond2.flip(0))
+    assert torch.equal(xs, xs2), "refilled modulation table does not follow the new cond"
