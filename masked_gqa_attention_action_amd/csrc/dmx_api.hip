@@ -55,7 +55,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // (for a stack) the modulation vectors of every layer of one step.  Rows of
 // the tiled / fp32 intermediates are tiled rows (each request padded to TP).
 struct WsLayout {
-  size_t mod1, mod2, apk, xp, raw, ss_q, vb, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
+  size_t mod1, mod2, apk, xp, raw, ss_q, qvb, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
   int TP;
   AttnArgs attn;
 };
@@ -78,7 +78,7 @@ bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
   L.xp = take(M * kH * 2);                  // tiled layer input
   L.raw = take(M * kQKV * 4);               // fp32 QKV projection (tiled in the fused layer)
   L.ss_q = take(M * kQkvTiles * 4);         // its q / k head sums of squares
-  L.vb = take(M * kHK * kD * 2);            // tiled bf16 v heads of the chunk
+  L.qvb = take(M * kQVB * 2);               // tiled bf16 q and v heads of the chunk
   L.ctx = take(M * kHQ * kD * 2);           // tiled attention output
   L.x1 = take(M * kH * 4);   // fp32 residual between the two halves of a layer
   L.x1s = take(M * kH * 2);  // tiled bf16(x1 * (1 + scale2)), the gate-up A operand
@@ -166,7 +166,7 @@ AttnArgs attn_args(const WsLayout& L, void* ws) {
   a.q = a.ks = a.vs = a.kp = a.vp = nullptr;
   a.y = nullptr;
   a.ss_q = nullptr;
-  a.vb = nullptr;
+  a.qvb = nullptr;
   a.mask = nullptr;
   a.part_o = at<uint16_t>(ws, L.part_o);
   a.part_ml = at<float>(ws, L.part_ml);
@@ -289,7 +289,7 @@ int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
       g.pos0 = c.pos0;
       g.rope_base = 10000.0f;
       g.ss_q = at<float>(ws, L.ss_q);
-      g.out_pk = at<uint16_t>(ws, L.vb);
+      g.out_pk = at<uint16_t>(ws, L.qvb);
       return hip_check(launch_gemm(kind, g, s), "QKV GEMM launch");
     }
     case DMX_STAGE_ATTN:
@@ -297,7 +297,7 @@ int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
       AttnArgs a = attn_args(L, ws);
       a.y = at<float>(ws, L.raw);
       a.ss_q = at<float>(ws, L.ss_q);
-      a.vb = at<uint16_t>(ws, L.vb);
+      a.qvb = at<uint16_t>(ws, L.qvb);
       a.kp = c.kv->k;
       a.vp = c.kv->v;
       a.mask = c.kv->mask;

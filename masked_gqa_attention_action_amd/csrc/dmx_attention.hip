@@ -47,41 +47,23 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 }  // namespace
 
-// Q fragments of one stacked query row from the tiled fp32 epilogue output:
-// lane (lr, lq) holds dims ks*32 + lq*8 + e (ks < 8, e < 8) of its row; each
-// load instruction of the wave reads 1 KB of contiguous memory.
-struct QRaw {
-  float4 x[8][2];
-  float4 ss[2];
-};
-
-__device__ __forceinline__ void q_load(const AttnArgs& a, int prow, int head, int lq, QRaw& q) {
+// Q fragments of one stacked query row from the tiled bf16 epilogue output
+// (rope((1 + w) * x), not yet divided by the row's rms): lane (lr, lq) holds
+// dims ks*32 + lq*8 + e (ks < 8, e < 8) of its row, which is the MFMA B
+// fragment as loaded; each load instruction of the wave reads 1 KB of
+// contiguous memory.  The head's 8 sums of squares come along: the query's
+// 1 / rms scales its logits instead of the operand.
+__device__ __forceinline__ void q_load(const AttnArgs& a, int prow, int head, int lq, bf16x8 qf[8], float4 ss[2]) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const float* src = a.y + tile_off_f32(prow, head * kD + ks * 32 + lq * 8, kQKV);
-    q.x[ks][0] = *reinterpret_cast<const float4*>(src);
-    q.x[ks][1] = *reinterpret_cast<const float4*>(src + 256);
-  }
-  const float* ss = a.ss_q + (size_t)prow * kQkvTiles + head * 8;
-  q.ss[0] = *reinterpret_cast<const float4*>(ss);
-  q.ss[1] = *reinterpret_cast<const float4*>(ss + 4);
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(a.qvb + tile_off(prow, head * kD + ks * 32 + lq * 8, kQVB));
+  const float* sp = a.ss_q + (size_t)prow * kQkvTiles + head * 8;
+  ss[0] = *reinterpret_cast<const float4*>(sp);
+  ss[1] = *reinterpret_cast<const float4*>(sp + 4);
 }
 
-__device__ __forceinline__ void q_finish(const QRaw& q, bool ok, bf16x8 qf[8]) {
-  const float t = ((q.ss[0].x + q.ss[0].y) + (q.ss[0].z + q.ss[0].w)) +
-                  ((q.ss[1].x + q.ss[1].y) + (q.ss[1].z + q.ss[1].w));
-  const float rn = 1.0f / sqrtf(t * (1.0f / kD) + kEps);
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const float v[8] = {q.x[ks][0].x, q.x[ks][0].y, q.x[ks][0].z, q.x[ks][0].w,
-                        q.x[ks][1].x, q.x[ks][1].y, q.x[ks][1].z, q.x[ks][1].w};
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const uint32_t p = ok ? pack2(v[e] * rn, v[e + 1] * rn) : 0u;
-      qf[ks][e] = (short)(p & 0xffffu);
-      qf[ks][e + 1] = (short)(p >> 16);
-    }
-  }
+__device__ __forceinline__ float q_rnorm(const float4 ss[2]) {
+  const float t = ((ss[0].x + ss[0].y) + (ss[0].z + ss[0].w)) + ((ss[1].x + ss[1].y) + (ss[1].z + ss[1].w));
+  return 1.0f / sqrtf(t * (1.0f / kD) + kEps);
 }
 
 // Suffix keys of one 32-key block from the epilogue output into LDS: thread
@@ -102,7 +84,7 @@ __device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int
     const float* kr = a.y + tile_off_f32(prow, (kHQ + g) * kD + c * 16 + h * 8, kQKV);
     r.k[2 * h] = *reinterpret_cast<const float4*>(kr);
     r.k[2 * h + 1] = *reinterpret_cast<const float4*>(kr + 256);
-    r.v[h] = *reinterpret_cast<const uint4*>(a.vb + tile_off(prow, g * kD + c * 16 + h * 8, kHK * kD));
+    r.v[h] = *reinterpret_cast<const uint4*>(a.qvb + tile_off(prow, (kHQ + g) * kD + c * 16 + h * 8, kQVB));
   }
   r.ss = c < 8 ? a.ss_q[(size_t)prow * kQkvTiles + (kHQ + g) * 8 + c] : 0.f;
 }
@@ -290,7 +272,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const bool qok = active && qi < a.C;
   KVRegs kv[NB];
   SufRaw sr;
-  QRaw qr;
+  float4 qss[2];
   bf16x8 qf[8];
   int mvis = 0;
   if (threadIdx.x < NB * KB && threadIdx.x < nkeys)
@@ -303,7 +285,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     suffix_load(a, b, g, key_lo, sr);  // one block
   }
   if (FUSED) {
-    q_load(a, b * a.TP + min(qi, a.C - 1), kGroup * g + hh, lq, qr);
+    q_load(a, b * a.TP + min(qi, a.C - 1), kGroup * g + hh, lq, qf, qss);
   } else {
     const uint16_t* qp = a.q + ((size_t)(b * a.C + min(qi, a.C - 1)) * kHQ + (kGroup * g + hh)) * kD + lq * 8;
 #pragma unroll
@@ -329,8 +311,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     else if (bi == 0)
       suffix_store(sr, vis, sK[0], sV[0]);
   }
-  if (FUSED) q_finish(qr, qok, qf);
-  else if (!qok) {
+  if (!qok) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = zero_bf16x8();
   }
@@ -342,7 +323,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
   for (int t = 0; t < 16; ++t) o[t] = zero_f32x4();
   float mrun = kNegBig, lrun = 0.f;
-  const float sl2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(head_dim)
+  // log2(e) / sqrt(head_dim), times the query row's 1 / rms in the fused path
+  const float sl2 = (1.4426950408889634f / 16.0f) * (FUSED ? q_rnorm(qss) : 1.0f);
 
 #pragma unroll
   for (int bi = 0; bi < NB; ++bi) {

@@ -408,17 +408,17 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
             hi[i] = x1 * cs + x0 * sn;
           }
         }
-        if (h < kHQ + kHK) {
+        if (h >= kHQ && h < kHQ + kHK) {  // k heads: fp32, scaled by 1 / rms when staged
           float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
           float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
           *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
           *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
           *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
           *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
-        } else {  // v heads: bf16, as the attention consumes them
-          const int fv = f - (kHQ + kHK) * kD;
-          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fv, kHK * kD)) = pack8(lo);
-          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fv + 128, kHK * kD)) = pack8(hi);
+        } else {  // q and v heads: bf16, as the attention's MFMA consumes them
+          const int fq = h < kHQ ? f : f - kHK * kD;
+          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq, kQVB)) = pack8(lo);
+          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq + 128, kQVB)) = pack8(hi);
         }
         sQ[r * 2 + (c0 >> 3)] = sq8;
       } else if (EPI == EPI_GEGLU) {

@@ -45,14 +45,17 @@ struct GemmArgs {
   int gate_stride;
   const uint16_t* resid;   // EPI_RESID_B*: bf16 residual, row-major
   const float* resid_f32;  // EPI_RESID_FB: fp32 residual [M][ldo]
-  // EPI_QKV: out_f32 is tiled fp32 [M][4096] (the v heads' columns unused), the
-  // v heads go to out_pk as tiled bf16 [M][1024]; ss_q [M][kQkvTiles] sums of squares
+  // EPI_QKV: the k heads go to out_f32, tiled fp32 [M][4096] (only the k
+  // heads' columns written); the q and v heads to out_pk, tiled bf16
+  // [M][kQVB] (q heads at columns 0 .. 2047, v heads after them);
+  // ss_q [M][kQkvTiles] sums of squares
   const uint16_t *qn_w, *kn_w;  // (1 + w) weights of the q / k heads, [256]
   const int32_t* pos0;          // token t of request b at position pos0[b] + t
   float rope_base;
   float* ss_q;
 };
 constexpr int kQkvTiles = 96;  // 32-feature tiles of the 12 q / k heads (8 per head)
+constexpr int kQVB = (kHQ + kHK) * kD;  // columns of the tiled bf16 q + v heads
 
 // Gemm shape presets (host picks one per projection).
 enum GemmKind {
@@ -102,12 +105,14 @@ hipError_t launch_qknorm_rope(const float* raw, const uint16_t* qn_w, const uint
 struct AttnArgs {
   const uint16_t *q, *ks, *vs, *kp, *vp;
   // fused path: when y != nullptr, q / ks / vs are ignored and built from the
-  // QKV epilogue's output: y tiled fp32 [B*TP][4096] (rope((1 + w) * x) for q,
-  // k heads, x for v heads) and ss_q [B*TP][96] (8 sums of squares of x per
-  // q / k head): q = y / sqrt(mean x^2 + eps).
+  // QKV epilogue's output: y tiled fp32 [B*TP][4096] (rope((1 + w) * x) for
+  // the k heads), qvb tiled bf16 [B*TP][kQVB] (the same for the q heads, x for
+  // the v heads) and ss_q [B*TP][96] (8 sums of squares of x per q / k head):
+  // k = y / sqrt(mean x^2 + eps), and the q heads' 1 / sqrt(mean x^2 + eps)
+  // scales the logits.
   const float* y;
   const float* ss_q;
-  const uint16_t* vb;  // fused path: the chunk's V heads, tiled bf16 [B*TP][1024]
+  const uint16_t* qvb;
   const uint8_t* mask;
   int B, C, P;
   int TP;       // padded chunk (tiled rows per request)
