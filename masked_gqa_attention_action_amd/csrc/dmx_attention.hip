@@ -171,14 +171,14 @@ __device__ __forceinline__ int xcd_chunked(int wg, int grid, int items) {
 }
 
 // Merge of the split partials of one unit: 16 stacked rows (row tile mt) x
-// 32 dims (eighth q4 of the head dims) of request / KV head bg, in split
-// order with a running maximum.  One wave: lane (lr, lq) owns row lr and
-// dims 16t + 4lq .. +3 of the eighth's 2 dim tiles t; all loads of a batch
-// of splits are in flight together, each instruction reading 512 contiguous
-// bytes.
-__device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, int bg, int mt, int q4, int lane) {
+// 16 dims (dim tile t) of request / KV head bg.  One wave: lane (lr, lq) owns
+// row lr and dims 16t + 4lq .. +3.  All loads of a batch of splits are in
+// flight together (each instruction reads 512 contiguous bytes); inside a
+// batch the row maximum is taken first, so every split costs one exp2 and one
+// multiply-add per output, in split order.  Batches after the first (prefixes
+// longer than CB splits) rescale what came before.
+__device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, int bg, int mt, int t, int lane) {
   constexpr int CB = 24;  // splits per batch of loads
-  constexpr int NT = 2;   // dim tiles per wave
   const int lr = lane & 15, lq = lane >> 4;
   const int TT = a.TP >> 4, MT = 2 * TT;
   const int g = bg % kHK, b = bg / kHK;
@@ -186,51 +186,43 @@ __device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, i
   const int row = mt * 16 + lr;
   const int hh = mt / TT, i = (mt - hh * TT) * 16 + lr;
   const size_t ml0 = (size_t)bg * nsplit * a.R16 + row;
-  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + (q4 * NT) * 256 + lane * 4;
+  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + t * 256 + lane * 4;
   float M = kNegBig, L = 0.f;
-  float acc[NT][4];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsplit; s0 += CB) {
     float2 ml[CB];
-    uint2 ov[CB][NT];
+    uint2 ov[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const int s = min(s0 + u, nsplit - 1);  // past the end: re-read the last split, skipped below
       ml[u] = *reinterpret_cast<const float2*>(a.part_ml + (ml0 + (size_t)s * a.R16) * 2);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        ov[u][t] = *reinterpret_cast<const uint2*>(a.part_o + o0 + (size_t)s * MT * (16 * kD) + t * 256);
+      ov[u] = *reinterpret_cast<const uint2*>(a.part_o + o0 + (size_t)s * MT * (16 * kD));
     }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (s0 + u < nsplit && ml[u].y > 0.f) Mb = fmaxf(Mb, ml[u].x);
+    const float so = exp2f(M - Mb);  // 0 before the first visible split, 1 if the max held
+    L *= so;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= so;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      if (s0 + u < nsplit && ml[u].y > 0.f) {
-        const float Mn = fmaxf(M, ml[u].x);
-        const float so = exp2f(M - Mn), w = ml[u].y * exp2f(ml[u].x - Mn);
-        L = L * so + w;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          acc[t][0] = acc[t][0] * so + w * bf2f((uint16_t)(ov[u][t].x & 0xffffu));
-          acc[t][1] = acc[t][1] * so + w * bf2f((uint16_t)(ov[u][t].x >> 16));
-          acc[t][2] = acc[t][2] * so + w * bf2f((uint16_t)(ov[u][t].y & 0xffffu));
-          acc[t][3] = acc[t][3] * so + w * bf2f((uint16_t)(ov[u][t].y >> 16));
-        }
-        M = Mn;
-      }
+      const float w = (s0 + u < nsplit && ml[u].y > 0.f) ? ml[u].y * exp2f(ml[u].x - Mb) : 0.f;
+      L += w;
+      acc[0] += w * bf2f((uint16_t)(ov[u].x & 0xffffu));
+      acc[1] += w * bf2f((uint16_t)(ov[u].x >> 16));
+      acc[2] += w * bf2f((uint16_t)(ov[u].y & 0xffffu));
+      acc[3] += w * bf2f((uint16_t)(ov[u].y >> 16));
     }
+    M = Mb;
   }
   if (i >= a.C) return;
   const float inv = 1.0f / L;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int col = (kGroup * g + hh) * kD + (q4 * NT + t) * 16 + 4 * lq;
-    uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
-                                : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[t][0] * inv, acc[t][1] * inv),
-                                                pack2(acc[t][2] * inv, acc[t][3] * inv));
-  }
+  const int col = (kGroup * g + hh) * kD + t * 16 + 4 * lq;
+  uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
+                              : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv));
 }
 
 // One split of one (request, KV head): every global load of the split (mask,
@@ -388,15 +380,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }  // active
 }
 
-// Separate merge kernel: one wave per (request, KV head, row tile, eighth),
-// placed like the splits (xcd_chunked) so the partials are read from the L2
-// that received them.
+// Separate merge kernel: one wave per (request, KV head, row tile, dim
+// tile), placed like the splits (xcd_chunked) so the partials are read from
+// the L2 that received them.
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
   const int MT = 2 * (a.TP >> 4);
-  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * MT * 8);
+  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * MT * 16);
   if (item < 0) return;
-  const int q4 = item & 7, rest = item >> 3;
-  combine_unit(a, ctx, rest / MT, rest % MT, q4, threadIdx.x);
+  const int t = item & 15, rest = item >> 4;
+  combine_unit(a, ctx, rest / MT, rest % MT, t, threadIdx.x);
 }
 
 void attn_config(int B, int C, int P, AttnArgs& a) {
@@ -423,7 +415,7 @@ hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
-  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 8), dim3(64), 0, s>>>(a, ctx);  // a multiple of 8
+  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 16), dim3(64), 0, s>>>(a, ctx);  // a multiple of 8
   return hipGetLastError();
 }
 
