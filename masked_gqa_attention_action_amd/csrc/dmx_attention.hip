@@ -42,6 +42,7 @@ constexpr int KB = 32;          // keys per block
 constexpr int KLD = kD + 8;     // K row stride in LDS (bf16): 528 B, 16 B past a bank period
 constexpr int VLD = kD + 16;    // V row stride in LDS (bf16): 544 B, 32 B past a bank period
 constexpr int kMaxNB = 4;       // blocks per split (upper bound)
+constexpr int kAttnHeadsPerWg = 1;  // query heads of a KV group per attention work-group
 constexpr float kNegBig = -1e30f;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -67,16 +68,17 @@ __device__ __forceinline__ float q_rnorm(const float4 ss[2]) {
 }
 
 // Suffix keys of one 32-key block from the epilogue output into LDS: thread
-// t (< 512) handles key j = t / 16 and the 16 dims (t % 16) * 16 .. +15 of
-// K (fp32, scaled by the key row's 1 / rms) and V (bf16 already).
+// t handles key j = t / 16 (+ 16 i for the i-th of its keys when the
+// work-group has 256 threads) and the 16 dims (t % 16) * 16 .. +15 of K
+// (fp32, scaled by the key row's 1 / rms) and V (bf16 already).
 struct SufRaw {
   float4 k[4];
   uint4 v[2];
   float ss;
 };
 
-__device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int kb0, SufRaw& r) {
-  const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
+__device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int kb0, int j, SufRaw& r) {
+  const int c = threadIdx.x & 15;
   const int key = min(kb0 + j, a.C - 1);  // rows past the chunk read a valid row and are zeroed later
   const int prow = b * a.TP + key;
 #pragma unroll
@@ -89,8 +91,8 @@ __device__ __forceinline__ void suffix_load(const AttnArgs& a, int b, int g, int
   r.ss = c < 8 ? a.ss_q[(size_t)prow * kQkvTiles + (kHQ + g) * 8 + c] : 0.f;
 }
 
-__device__ __forceinline__ void suffix_store(const SufRaw& r, uint32_t vis, uint16_t* sK, uint16_t* sV) {
-  const int j = threadIdx.x >> 4, c = threadIdx.x & 15;
+__device__ __forceinline__ void suffix_store(const SufRaw& r, uint32_t vis, int j, uint16_t* sK, uint16_t* sV) {
+  const int c = threadIdx.x & 15;
   const bool ok = (vis >> j) & 1u;
   const float t = group16_sum(r.ss);  // the 16 threads of key j form one DPP row
   const float rn = 1.0f / sqrtf(t * (1.0f / kD) + kEps);
@@ -105,18 +107,22 @@ __device__ __forceinline__ void suffix_store(const SufRaw& r, uint32_t vis, uint
   *reinterpret_cast<uint4*>(sV + j * VLD + c * 16 + 8) = keep_or_zero(ok, r.v[1]);
 }
 
-// K / V rows (bf16, from global) of one 32-key block: thread t owns 16-byte
-// chunks t and t + 512 of the 32 x 32 chunk grid.  Rows are read whether
-// visible or not (rows past the split's end read its last row); invisible rows
-// are replaced by zeros when staged, so their contents never reach the math.
+// K / V rows (bf16, from global) of one 32-key block: thread t of NTHR owns
+// 16-byte chunks t, t + NTHR, ... of the 32 x 32 chunk grid.  Rows are read
+// whether visible or not (rows past the split's end read its last row);
+// invisible rows are replaced by zeros when staged, so their contents never
+// reach the math.
+template <int NTHR>
 struct KVRegs {
-  uint4 k[2], v[2];
+  uint4 k[1024 / NTHR], v[1024 / NTHR];
 };
 
-__device__ __forceinline__ void kv_load(const uint16_t* Kb, const uint16_t* Vb, int kb0, int key_hi, KVRegs& r) {
+template <int NTHR>
+__device__ __forceinline__ void kv_load(const uint16_t* Kb, const uint16_t* Vb, int kb0, int key_hi,
+                                        KVRegs<NTHR>& r) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = threadIdx.x + h * 512;
+  for (int h = 0; h < 1024 / NTHR; ++h) {
+    const int c = threadIdx.x + h * NTHR;
     const int j = c >> 5, ch = c & 31;
     const size_t row = (size_t)min(kb0 + j, key_hi - 1);
     r.k[h] = *reinterpret_cast<const uint4*>(Kb + row * kD + ch * 8);
@@ -124,10 +130,11 @@ __device__ __forceinline__ void kv_load(const uint16_t* Kb, const uint16_t* Vb, 
   }
 }
 
-__device__ __forceinline__ void kv_store(const KVRegs& r, uint32_t vis, uint16_t* sK, uint16_t* sV) {
+template <int NTHR>
+__device__ __forceinline__ void kv_store(const KVRegs<NTHR>& r, uint32_t vis, uint16_t* sK, uint16_t* sV) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = threadIdx.x + h * 512;
+  for (int h = 0; h < 1024 / NTHR; ++h) {
+    const int c = threadIdx.x + h * NTHR;
     const int j = c >> 5, ch = c & 31;
     const bool ok = (vis >> j) & 1u;
     *reinterpret_cast<uint4*>(sK + j * KLD + ch * 8) = keep_or_zero(ok, r.k[h]);
@@ -225,21 +232,29 @@ __device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, i
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv));
 }
 
-// One split of one (request, KV head): every global load of the split (mask,
-// query rows, all K/V blocks or the raw suffix rows) is issued up front; the
-// blocks are then staged into LDS together and processed without further
-// work-group barriers.
-template <bool FUSED, int NB>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_partial(AttnArgs a) {
+// One split of one (request, KV head), for HPW of its query heads (HPW = 1:
+// one work-group per query head, 4 waves; 2: both heads, 8 waves): every
+// global load of the split (mask, query rows, all K/V blocks or the raw
+// suffix rows) is issued up front; the blocks are then staged into LDS
+// together and processed without further work-group barriers.  Work items
+// run (request, KV head, split, head), so the work-groups that share a
+// split's K/V rows sit on one XCD.
+template <bool FUSED, int NB, int HPW>
+__global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_partial(AttnArgs a) {
+  constexpr int NTHR = 256 * HPW;
+  constexpr int KPT = 512 / NTHR;  // suffix keys staged per thread
+  static_assert(HPW == 1 || HPW == kGroup, "one query head or the whole group per work-group");
   __shared__ __attribute__((aligned(16))) uint16_t sK[NB][KB * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NB][KB * VLD];
   __shared__ uint32_t sMask[NB];
 
   const int nsplit = a.S + a.NS;
-  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * nsplit);
+  const int per_split = kGroup / HPW;  // work-groups per split
+  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * nsplit * per_split);
   if (item < 0) return;
-  const int split = item % nsplit;
-  const int bg = item / nsplit;
+  const int hsel = item % per_split;  // first query head of this work-group within the group
+  const int split = (item / per_split) % nsplit;
+  const int bg = item / per_split / nsplit;
   const int g = bg % kHK, b = bg / kHK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
@@ -256,14 +271,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const bool from_global = !(FUSED && suffix);
 
   // ---- load phase: everything this WG reads from global memory
-  const int mt = wave;
-  const bool active = mt < MT;
+  const int mt = hsel * TT + wave;  // stacked row tile of this wave
+  const bool active = wave < HPW * TT;
   const int row = mt * 16 + lr;            // stacked row
   const int hh = active ? mt / TT : 0;     // head within the group
   const int qi = (mt - hh * TT) * 16 + lr; // token
   const bool qok = active && qi < a.C;
-  KVRegs kv[NB];
-  SufRaw sr;
+  KVRegs<NTHR> kv[NB];
+  SufRaw sr[KPT];
   float4 qss[2];
   bf16x8 qf[8];
   int mvis = 0;
@@ -274,7 +289,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int bi = 0; bi < NB; ++bi)
       if (bi < nblk) kv_load(Kb, Vb, key_lo + bi * KB, key_hi, kv[bi]);
   } else {
-    suffix_load(a, b, g, key_lo, sr);  // one block
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) suffix_load(a, b, g, key_lo, (threadIdx.x >> 4) + i * (NTHR / 16), sr[i]);
   }
   if (FUSED) {
     q_load(a, b * a.TP + min(qi, a.C - 1), kGroup * g + hh, lq, qf, qss);
@@ -300,8 +316,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     if (vis == 0u) continue;
     if (from_global)
       kv_store(kv[bi], vis, sK[bi], sV[bi]);
-    else if (bi == 0)
-      suffix_store(sr, vis, sK[0], sV[0]);
+    else if (bi == 0) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) suffix_store(sr[i], vis, (threadIdx.x >> 4) + i * (NTHR / 16), sK[0], sV[0]);
+    }
   }
   if (!qok) {
 #pragma unroll
@@ -404,13 +422,14 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
 
 hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
   constexpr int NB = kAttnKps / KB;
+  constexpr int HPW = kAttnHeadsPerWg;
   static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
-  const int items = a.B * kHK * (a.S + a.NS);
+  const int items = a.B * kHK * (a.S + a.NS) * (kGroup / HPW);
   const dim3 grid(8 * ((items + 7) / 8));
   if (a.y)
-    k_attn_partial<true, NB><<<grid, dim3(512), 0, s>>>(a);
+    k_attn_partial<true, NB, HPW><<<grid, dim3(256 * HPW), 0, s>>>(a);
   else
-    k_attn_partial<false, NB><<<grid, dim3(512), 0, s>>>(a);
+    k_attn_partial<false, NB, HPW><<<grid, dim3(256 * HPW), 0, s>>>(a);
   return hipGetLastError();
 }
 
