@@ -226,7 +226,8 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
                          : tile * NTT + nt;
     const uint16_t* wp = a.W + ((size_t)wt * kst + ks0) * 512 + lane * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) wf[ks][nt] = load_bf16x8(wp + ks * 512);
+    for (int ks = 0; ks < KSTEPS; ++ks)  // read once per launch: streaming loads
+      wf[ks][nt] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(wp + ks * 512));
   }
   __builtin_amdgcn_sched_barrier(0);
   if (QKV && threadIdx.x < 16) {
@@ -568,7 +569,8 @@ __global__ __launch_bounds__(256) void k_mod_multi(ModBatch mb) {
   bf16x8 wf[8];
   const uint16_t* wp = job.w + ((size_t)tile * (kH / 32) + wave * 8) * 512 + lane * 8;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) wf[ks] = load_bf16x8(wp + ks * 512);
+  for (int ks = 0; ks < 8; ++ks)  // read once per launch: streaming loads
+    wf[ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(wp + ks * 512));
   const uint16_t* cond = job.cond;
   for (int b0 = 0; b0 < mb.B; b0 += 16) {
     const int rows = min(16, mb.B - b0);
