@@ -28,9 +28,10 @@
 //   in LDS and their logits replaced by -inf (selection, never
 //   multiplication), so masked rows may hold anything, NaN included.
 // Each split writes (running max, running sum, output / sum) per row, the
-// outputs as 16 x 256 row tiles laid out by lane (every store instruction of a
-// wave covers 512 contiguous bytes); a combine kernel merges the S + NS
-// partials of each row in split order.
+// outputs as 16 x 256 row tiles, each row's 16 dims of a dim tile contiguous
+// (a store instruction of a wave covers 512 contiguous bytes; padded query
+// rows write nothing, so a tile's few valid rows touch few cache lines); a
+// combine kernel merges the S + NS partials of each row in split order.
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
 #include "dmx_tiles.hpp"
@@ -193,7 +194,8 @@ __device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, i
   const int row = mt * 16 + lr;
   const int hh = mt / TT, i = (mt - hh * TT) * 16 + lr;
   const size_t ml0 = (size_t)bg * nsplit * a.R16 + row;
-  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + t * 256 + lane * 4;
+  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + t * 256 + (lr * 4 + lq) * 4;
+  if (i >= a.C) return;  // padded row: nothing was written for it
   float M = kNegBig, L = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsplit; s0 += CB) {
@@ -224,7 +226,6 @@ __device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, i
     }
     M = Mb;
   }
-  if (i >= a.C) return;
   const float inv = 1.0f / L;
   const int col = (kGroup * g + hh) * kD + t * 16 + 4 * lq;
   uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col & ~7, kHQ * kD) + (col & 7)
@@ -384,17 +385,19 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2)
   }
 
   // this split's partial row: running max, running sum, output / sum; the
-  // outputs of row tile mt as [t][lane][4] (dims 16t + 4lq .. of row lr)
+  // outputs of row tile mt as [t][lr][lq][4] (dims 16t + 4lq .. of row lr)
   float l = lrun + __shfl_xor(lrun, 16, 64);
   l += __shfl_xor(l, 32, 64);
   const size_t pidx = (size_t)bg * nsplit + split;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  uint16_t* dst = a.part_o + (pidx * MT + mt) * (16 * kD) + lane * 4;
+  uint16_t* dst = a.part_o + (pidx * MT + mt) * (16 * kD) + (lr * 4 + lq) * 4;
+  if (qok) {  // padded query rows write nothing
 #pragma unroll
   for (int t = 0; t < 16; ++t)
     *reinterpret_cast<uint2*>(dst + t * 256) = make_uint2(pack2(o[t][0] * inv, o[t][1] * inv),
                                                           pack2(o[t][2] * inv, o[t][3] * inv));
   if (lq == 0) *reinterpret_cast<float2*>(a.part_ml + (pidx * a.R16 + row) * 2) = make_float2(mrun, l);
+  }
   }  // active
 }
 

@@ -121,7 +121,8 @@ struct AttnArgs {
   int NS;       // suffix splits (32 keys each)
   int kps;      // prefix keys per split (multiple of 32)
   int R16;      // stacked query rows (2 * C) rounded up to 16
-  uint16_t* part_o;  // [B][HK][S + NS][R16 / 16][16][64 lanes][4] bf16, normalised partial outputs
+  uint16_t* part_o;  // [B][HK][S + NS][R16 / 16][16 dim tiles][16 rows][4][4] bf16, normalised partial
+                     // outputs (dims 16t + 4q .. +3 of row r at [t][r][q]); padded rows never written
   float* part_ml;    // [B][HK][S + NS][R16][2] running max (log2 domain) and sum
 };
 constexpr int kAttnKps = 64;  // prefix keys per attention split (32 .. 128, multiple of 32)
