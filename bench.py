@@ -160,6 +160,89 @@ def time_replays(st, stream, warmup, reps):
     return e0.elapsed_time(e1) / reps
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def time_calls(fn, stream, reps=20, rounds=5):
+    """us per call of fn(stream), from graph replays of reps back-to-back
+    calls timed with events on the capture stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn(stream)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                fn(stream)
+        g.replay()
+        stream.synchronize()
+        best = []
+        for _ in range(rounds):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            best.append(e0.elapsed_time(e1) * 1e3 / reps)
+    del g
+    return float(np.median(best))
+
+
+def layer_case(name):
+    """One action-expert layer of a parity workload (eager path: modulation,
+    input pack and the six kernels), its us per layer and roofline fractions."""
+    import torch
+    import masked_gqa_attention_action_amd as dmx
+    from masked_gqa_attention_action_amd import synth
+    wl = synth.WORKLOADS[name]
+    B, C, P = wl.batch, wl.chunk, wl.p_bucket
+    w = dmx.pack_layer_weights({k: dev(v) for k, v in synth.layer_weights(wl.weight_seed(0)).items()})
+    rqs = [synth.make_request(wl.request_seed(b), C, P, wl.len_lo, wl.len_hi, 1, wl.hole_p) for b in range(B)]
+    x = dev(np.stack([r.x for r in rqs]))
+    cond = dev(np.stack([r.cond for r in rqs]))
+    kp = dev(np.stack([r.k_pre[0] for r in rqs]))
+    vp = dev(np.stack([r.v_pre[0] for r in rqs]))
+    mask = dev(np.stack([r.mask for r in rqs]), raw=True)
+    pos0 = dev(np.array([r.pos0 for r in rqs], np.int32), raw=True)
+    ws = dmx.new_workspace(B, C, P)
+    out = torch.empty_like(x)
+    us = time_calls(lambda s: dmx.suffix_layer_forward(w, kp, vp, mask, x, cond, pos0, ws, out=out, stream=s),
+                    torch.cuda.Stream())
+    assert torch.isfinite(out.float()).all(), "non-finite layer output"
+    visible = int(sum(int(r.mask.sum()) for r in rqs))
+    nbytes = algorithmic_bytes_per_layer(B, C, P, visible)
+    flops = layer_flops(B, C, visible)
+    return {"workload": wl.note, "us_per_layer": round(us, 2), "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "flops": flops,
+            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def prefix_qkv_case():
+    """Prefix-side QKV + QK-norm + RoPE at hidden 2560 over 2048 tokens, K/V
+    into a 2048-row cache: us per call against the bf16 MFMA peak."""
+    import torch
+    import masked_gqa_attention_action_amd as dmx
+    from masked_gqa_attention_action_amd import synth
+    T, hid = 2048, 2560
+    inp = synth.prefix_qkv_inputs(synth.BASE_SEED + 4000 + 77)
+    x = dev(inp["x"]).view(1, T, hid)
+    w = dmx.pack_weight(dev(inp["w_qkv"]))
+    qn, kn = dev(inp["q_norm"]), dev(inp["k_norm"])
+    pos = dev(np.zeros(1, np.int32), raw=True)
+    ws = dmx.new_workspace(1, T, 0)
+    kc = torch.empty((1, HK, T, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    us = time_calls(lambda s: dmx.qkv_qknorm_rope(x, w, qn, kn, pos, ws, k=kc, v=vc, kv_rows=T, stream=s),
+                    torch.cuda.Stream(), reps=10)
+    flops = 2 * T * hid * (HQ + 2 * HK) * D
+    nbytes = T * hid * 2 + (HQ + 2 * HK) * D * hid * 2 + T * (HQ + 2 * HK) * D * 2 + 2 * D * 2
+    return {"workload": "prefix QKV + QK-norm + RoPE, hidden 2560, 2048 tokens, K/V into the cache",
+            "us": round(us, 2), "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(wl, wbits, rq, conds, n_steps_sample):
     """Time the float64 oracle on the host for whole denoise steps (all layers)
     of the same workload; report ms per step."""
@@ -192,6 +275,8 @@ def main():
                                                              "(0: skip)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="replays per kernel for per-kernel timing (0: skip)")
     ap.add_argument("--variants", type=int, default=1, help="also time the cached-modulation variants (0: skip)")
+    ap.add_argument("--extras", type=int, default=1, help="also time single layers of the batched and long-prefix "
+                                                          "workloads and the prefix QKV (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; --gpus must be 1", file=sys.stderr)
@@ -231,7 +316,12 @@ def main():
         with torch.cuda.stream(stream):
             tb = dmx.Stack(wd, kp, vp, mask, cond, pos0, x, mod_table=True, stream=stream)
         tb.capture(stream)
-        variants["mod_table_step"] = {"ms_per_step": round(time_replays(tb, stream, args.warmup, args.steps), 4),
+        # no double credit: the modulation weights are not read in these steps
+        # (the table's two vectors per layer and request are)
+        tb_bytes = L * (algorithmic_bytes_per_layer(B, C, P, visible) - 2 * W_MOD + 2 * B * 3072 * 4)
+        ms_tb = time_replays(tb, stream, args.warmup, args.steps)
+        variants["mod_table_step"] = {"ms_per_step": round(ms_tb, 4), "algorithmic_bytes": tb_bytes,
+                                      "frac_of_hbm_peak": round(tb_bytes / (ms_tb * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                       "note": "one step per replay, modulation vectors precomputed per schedule"}
         tb.close()
         x.copy_(dev(rq.x[None]))
@@ -241,7 +331,9 @@ def main():
         lp.capture(stream)
         n = max(1, args.steps // wl.n_steps)
         ms_loop = time_replays(lp, stream, max(1, args.warmup // wl.n_steps), n)
-        variants["mod_table_loop"] = {"ms_per_step": round(ms_loop / wl.n_steps, 4),
+        ms_lp = ms_loop / wl.n_steps
+        variants["mod_table_loop"] = {"ms_per_step": round(ms_lp, 4), "algorithmic_bytes": tb_bytes,
+                                      "frac_of_hbm_peak": round(tb_bytes / (ms_lp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                       "note": f"whole {wl.n_steps}-step denoise loop per replay, modulation "
                                               "vectors precomputed per schedule"}
         lp.close()
@@ -266,6 +358,12 @@ def main():
                              "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if nbytes else None}
         torch.cuda.synchronize()
     st.close()
+    extras = {}
+    if args.extras:
+        for name in ("c2", "c4", "c5"):
+            extras[f"layer_{name}"] = layer_case(name)
+        extras["prefix_qkv_c4"] = prefix_qkv_case()
+        torch.cuda.synchronize()
     # a plain 256 MiB device copy: the reference dispatch for HBM byte counters
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -302,6 +400,7 @@ def main():
                  "frac_of_hbm_peak": round(step_gbs / PEAK_HBM_GBS, 4)},
         "kernels": kernels,
         "variants": variants,
+        "extras": extras,
     }
     if args.cpu_steps > 0:
         out["cpu_baseline"] = cpu_baseline(wl, wbits, rq, conds, args.cpu_steps)

@@ -272,7 +272,7 @@ void dmx_graph_destroy(dmx_graph* g);
  * changes the stack's state; others only rewrite workspace intermediates.
  * stage: one of DMX_STAGE_*; reps in [1, 100000]. */
 #define DMX_STAGE_MODS 0     /* modulation vectors of every layer (one launch per step) */
-#define DMX_STAGE_PACK 1     /* tiled copy + row statistics of the stack input */
+#define DMX_STAGE_PACK 1     /* tiled copy (scaled by 1 + scale1) + row statistics of the stack input */
 #define DMX_STAGE_QKV 2      /* QKV + AdaRMS + QK-norm weights + RoPE */
 #define DMX_STAGE_ATTN 3     /* masked GQA attention splits */
 #define DMX_STAGE_COMBINE 4  /* merge of the splits */

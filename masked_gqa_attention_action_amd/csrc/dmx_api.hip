@@ -261,7 +261,6 @@ struct LayerCtx {
   const float *mod1, *mod2;
   void* ws;
   const WsLayout* L;
-  bool x_prescaled;          // the tiled x holds bf16(x * (1 + scale1)) already
   const float* next_scale1;  // the next layer's modulation (its scale first), or null
 };
 
@@ -275,7 +274,7 @@ int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
   g.TP = L.TP;
   switch (stage) {
     case DMX_STAGE_QKV: {
-      const GemmKind kind = c.x_prescaled ? GEMM_QKV1024_MODPRE : GEMM_QKV1024_MOD;
+      const GemmKind kind = GEMM_QKV1024_MODPRE;  // the tiled x holds bf16(x * (1 + scale1))
       gemm_config(kind, g);
       g.A = at<uint16_t>(ws, L.xp);
       g.nmod = c.mod1;
@@ -352,9 +351,12 @@ int enq_layer_chain(const LayerCtx& c, hipStream_t s) {
   return DMX_OK;
 }
 
-// tiled copy and row statistics of a row-major layer input
-int enq_pack_input(const dmx_bf16* x, int B, int C, void* ws, const WsLayout& L, hipStream_t s) {
-  return hip_check(launch_pack_rows(x, B, C, L.TP, kH, at<uint16_t>(ws, L.xp), at<float>(ws, L.ss_b), s),
+// tiled copy of a row-major layer input, scaled by the layer's 1 + scale1
+// (mod1: the layer's modulation, scale first), and its row statistics
+int enq_pack_input(const dmx_bf16* x, int B, int C, const float* mod1, void* ws, const WsLayout& L,
+                   hipStream_t s) {
+  return hip_check(launch_pack_rows(x, B, C, L.TP, kH, at<uint16_t>(ws, L.xp), at<float>(ws, L.ss_b), s, mod1,
+                                    3 * kH),
                    "input pack launch");
 }
 
@@ -365,8 +367,8 @@ int enq_layer(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf1
   float* mod2 = at<float>(ws, L.mod2);
   const ModJob jobs[2] = {{w->w_mod1, w->b_mod1, cond, mod1}, {w->w_mod2, w->b_mod2, cond, mod2}};
   DMX_TRY(enq_mods(jobs, 2, B, s));
-  DMX_TRY(enq_pack_input(x_in, B, C, ws, L, s));
-  const LayerCtx c{w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, &L, false, nullptr};
+  DMX_TRY(enq_pack_input(x_in, B, C, mod1, ws, L, s));
+  const LayerCtx c{w, kv, x_in, pos0, B, C, x_out, mod1, mod2, ws, &L, nullptr};
   return enq_layer_chain(c, s);
 }
 
@@ -618,26 +620,26 @@ static int enq_stack_mods(const dmx_stack_desc* d, const WsLayout& L, int st, hi
 // Layer l of step st as the stack runs it.  Each down projection hands the
 // next layer its input already scaled by that layer's 1 + scale1 when the
 // next layer's modulation is known by then: inside a step always, across
-// steps with a cached table.  Only the first layer of a run (and, without a
-// table, of every step) scales its input itself.
+// steps with a cached table.
 static LayerCtx stack_layer(const dmx_stack_desc* d, const WsLayout& L, const dmx_prefix_kv* kv, int st, int l) {
-  const bool table = d->mod_table != nullptr;
   const float* next = nullptr;
   if (l + 1 < d->n_layers)
     next = stack_mod(d, L, st, l + 1, 0);
-  else if (table && st + 1 < d->n_steps)
+  else if (d->mod_table && st + 1 < d->n_steps)
     next = stack_mod(d, L, st + 1, 0, 0);
-  const bool pre = l > 0 || (table && st > 0);
   return LayerCtx{&d->layers[l], kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, st, l, 0),
-                  stack_mod(d, L, st, l, 1), d->ws, &L, pre, next};
+                  stack_mod(d, L, st, l, 1), d->ws, &L, next};
 }
 
 static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) {
   for (int st = 0; st < d->n_steps; ++st) {
     if (!d->mod_table) DMX_TRY(enq_stack_mods(d, L, st, s));
-    // tiled x and its row statistics: a pack pass for the first layer of the
-    // run, after that the down projection of the layer before
-    if (st == 0) DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, d->ws, L, s));
+    // the first layer's scaled tiled input and its row statistics: a pack
+    // pass at the start of the run, and of every step whose modulation was
+    // not known to the last down projection before it (no table); otherwise
+    // that down projection wrote them
+    if (st == 0 || !d->mod_table)
+      DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, stack_mod(d, L, st, 0, 0), d->ws, L, s));
     for (int l = 0; l < d->n_layers; ++l) {
       const dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
       DMX_TRY(enq_layer_chain(stack_layer(d, L, &kv, st, l), s));
@@ -667,7 +669,7 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
     if (stage == DMX_STAGE_MODS)
       DMX_TRY(enq_stack_mods(d, L, 0, s));
     else if (stage == DMX_STAGE_PACK)
-      DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, d->ws, L, s));
+      DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, stack_mod(d, L, 0, 0, 0), d->ws, L, s));
     else
       DMX_TRY(enq_layer_stage(c, stage, s));
   }

@@ -20,18 +20,16 @@
 //
 // A operand sources:
 //   A_GLOBAL   tiled bf16 rows (context, GEGLU hidden, normed inputs).
-//   A_MOD /    AdaRMS prenorm fused into the projection (OpenDM DM0.5
+//   A_MODPRE   AdaRMS prenorm fused into the projection (OpenDM DM0.5
 //              fast-stack article, §2.2, "Adarms 调制 prenorm"):
 //                xn W^T = r * ((x * (1 + scale)) W^T) + shift W^T,
-//              r = 1 / sqrt(mean x^2 + eps) per row.  The A operand is the raw
-//              bf16 residual row scaled by (1 + scale) (one bf16 rounding, as
-//              rounding xn would be); shift W^T is one extra MFMA tile whose
-//              row 0 is the shift vector; r comes from per-tile row sums of
-//              squares that the kernel producing x wrote, summed in a fixed
-//              order.
-//   A_MODPRE   as A_MOD with the A rows already bf16(x * (1 + scale)): the
-//              O-projection epilogue writes them from fp32 x1, so x1 is
-//              rounded once on its way into the gate-up projection.
+//              r = 1 / sqrt(mean x^2 + eps) per row.  The A rows arrive as
+//              bf16(x * (1 + scale)) (one bf16 rounding, as rounding xn would
+//              be), written by the kernel that produces x (the input pack, the
+//              O-projection epilogue from fp32 x1, the down epilogue for the
+//              next layer); shift W^T is one extra MFMA tile whose row 0 is
+//              the shift vector; r comes from per-tile row sums of squares of
+//              x that the same producer wrote, summed in a fixed order.
 // Epilogues (the same article's chaining of time modulation with GEGLU
 // gate-up and MLP down); every store moves 8 consecutive features:
 //   EPI_F32    raw fp32 store (QKV before QK-norm / RoPE)
@@ -192,8 +190,7 @@ template <int EPI, int NT, int NWAVES, int KSTEPS, int ASRC, int MT>
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_gemm(GemmArgs a) {
   constexpr int NTT = NT / 16;
   constexpr int KW = KSTEPS * 32;  // reduction elements per wave
-  constexpr bool MOD = ASRC != A_GLOBAL;   // AdaRMS fused: shift tile + row scale
-  constexpr bool SCALE = ASRC == A_MOD;    // ... and the (1 + scale) product on A
+  constexpr bool MOD = ASRC == A_MODPRE;   // AdaRMS fused: shift tile + row scale
   constexpr int MB = MT * 16;      // rows per block
   constexpr int RROWS = MB + (MOD ? 16 : 0);  // + the shift tile
   constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
@@ -205,7 +202,7 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
   static_assert(!MOD || NWAVES * KW == kH, "the modulated A operand spans one hidden row");
   __shared__ __attribute__((aligned(16))) float red[NWAVES * RROWS * NT];
   __shared__ float sq[SSQ ? MB * NOUT : 1];
-  __shared__ __attribute__((aligned(16))) float sS[SCALE ? kH : 4], sH[MOD ? kH : 4], sR[MOD ? MB : 1];
+  __shared__ __attribute__((aligned(16))) float sH[MOD ? kH : 4], sR[MOD ? MB : 1];
   __shared__ double sF[QKV ? 16 : 1];   // rotation frequencies of the tile (revolutions per position)
   __shared__ float sQ[QKV ? MB * 2 : 1];  // half-tile sums of squares
 
@@ -260,12 +257,11 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) av[ks][mt] = load_bf16x8(ap + ks * 512);
     }
-    float4 msc = make_float4(0.f, 0.f, 0.f, 0.f), msh = msc;
+    float4 msh = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 ssp[4];
     const int pos_b = QKV ? a.pos0[m0 / a.TP] : 0;
     if (MOD) {
       const float* mb = a.nmod + (size_t)(m0 / a.TP) * 3 * kH;
-      if (SCALE) msc = *reinterpret_cast<const float4*>(mb + threadIdx.x * 4);  // 256 threads x 4 = 1024
       msh = *reinterpret_cast<const float4*>(mb + kH + threadIdx.x * 4);
       // row statistics: thread (row rr, quarter qq) sums a quarter of the row's partials
       const int rr = threadIdx.x >> 2, qq = threadIdx.x & 3;
@@ -289,9 +285,6 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
     __builtin_amdgcn_sched_barrier(0);  // the whole block is in flight before any use
 
     if (MOD) {
-      if (SCALE)
-        reinterpret_cast<float4*>(sS)[threadIdx.x] =
-            make_float4(1.f + msc.x, 1.f + msc.y, 1.f + msc.z, 1.f + msc.w);
       reinterpret_cast<float4*>(sH)[threadIdx.x] = msh;
       float t = 0.f;
 #pragma unroll
@@ -301,26 +294,9 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       const int rr = threadIdx.x >> 2;
       if ((threadIdx.x & 3) == 0 && rr < MB) sR[rr] = 1.0f / sqrtf(t * (1.0f / kH) + kEps);
       __syncthreads();
-      // A <- bf16(x * (1 + scale)) (A_MOD); the shift tile's row 0 <- bf16(shift)
+      // the shift tile's row 0 <- bf16(shift)
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        if (SCALE) {
-          const float4 s0 = *reinterpret_cast<const float4*>(sS + k0 + ks * 32 + lk);
-          const float4 s1 = *reinterpret_cast<const float4*>(sS + k0 + ks * 32 + lk + 4);
-          const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            bf16x8 t8;
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const uint32_t p =
-                  pack2(bf2f((uint16_t)av[ks][mt][e]) * sv[e], bf2f((uint16_t)av[ks][mt][e + 1]) * sv[e + 1]);
-              t8[e] = (short)(p & 0xffffu);
-              t8[e + 1] = (short)(p >> 16);
-            }
-            av[ks][mt] = t8;
-          }
-        }
         bf16x8 hs = zero_bf16x8();
         if (lr == 0) {
           const float4 h0 = *reinterpret_cast<const float4*>(sH + k0 + ks * 32 + lk);
@@ -480,7 +456,6 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
 int gemm_config(GemmKind kind, GemmArgs& a) {
   switch (kind) {
     case GEMM_QKV1024: a.ntiles = kQKV / 16; a.K = kH; break;
-    case GEMM_QKV1024_MOD: a.ntiles = kQKV / 32; a.K = kH; break;
     case GEMM_QKV1024_MODPRE: a.ntiles = kQKV / 32; a.K = kH; break;
     case GEMM_QKV2560: a.ntiles = kQKV / 16; a.K = 2560; break;
     case GEMM_OPROJ: a.ntiles = kH / 16; a.K = kHQ * kD; break;
@@ -501,7 +476,6 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   const int nreq2 = std::min(8, (a.M / a.TP) * ((a.TP + 31) / 32));
   switch (kind) {
     case GEMM_QKV1024: DMX_GEMM(EPI_F32, 16, 4, 8, A_GLOBAL, 2, mb2); break;
-    case GEMM_QKV1024_MOD: DMX_GEMM(EPI_QKV, 32, 4, 8, A_MOD, 2, nreq2); break;
     case GEMM_QKV1024_MODPRE: DMX_GEMM(EPI_QKV, 32, 4, 8, A_MODPRE, 2, nreq2); break;
     case GEMM_QKV2560: DMX_GEMM(EPI_F32, 16, 4, 20, A_GLOBAL, 1, 4); break;
     case GEMM_OPROJ: DMX_GEMM(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 1, mb1); break;
@@ -518,9 +492,12 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
 // at tiled row b*TP + t).  One wave per row; lane j takes the 16-column
 // groups j, j + 64, ...  With ss != null (K = 1024) it also writes the row's
 // 64 sums of squares of 16 columns, summed in column order with every square
-// rounded before the add, exactly as the GEMM epilogues do.
+// rounded before the add, exactly as the GEMM epilogues do.  With scale !=
+// null (K = 1024) the tiled copy holds bf16(x * (1 + scale[b])) instead of x
+// (the A operand of an AdaRMS-fused projection), scale[b] at scale + b *
+// scale_stride; the sums of squares are always those of x.
 __global__ __launch_bounds__(256) void k_pack_rows(const uint16_t* x, int B, int T, int TP, int K, uint16_t* out,
-                                                   float* ss) {
+                                                   float* ss, const float* scale, int scale_stride) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63, m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= B * T) return;
@@ -530,10 +507,19 @@ __global__ __launch_bounds__(256) void k_pack_rows(const uint16_t* x, int B, int
   for (int j = lane; j < K / 16; j += 64) {
     const uint4 r0 = *reinterpret_cast<const uint4*>(src + j * 16);
     const uint4 r1 = *reinterpret_cast<const uint4*>(src + j * 16 + 8);
-    *reinterpret_cast<uint4*>(out + tile_off(prow, j * 16, K)) = r0;
-    *reinterpret_cast<uint4*>(out + tile_off(prow, j * 16 + 8, K)) = r1;
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    uint32_t o[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    if (scale) {
+      const float* sp = scale + (size_t)b * scale_stride + j * 16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float s0 = 1.f + sp[2 * i], s1 = 1.f + sp[2 * i + 1];
+        o[i] = pack2(bf2f((uint16_t)(w[i] & 0xffffu)) * s0, bf2f((uint16_t)(w[i] >> 16)) * s1);
+      }
+    }
+    *reinterpret_cast<uint4*>(out + tile_off(prow, j * 16, K)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(out + tile_off(prow, j * 16 + 8, K)) = make_uint4(o[4], o[5], o[6], o[7]);
     if (ss) {
-      const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -548,9 +534,9 @@ __global__ __launch_bounds__(256) void k_pack_rows(const uint16_t* x, int B, int
 }
 
 hipError_t launch_pack_rows(const uint16_t* x, int B, int T, int TP, int K, uint16_t* out, float* ss,
-                            hipStream_t s) {
+                            hipStream_t s, const float* scale, int scale_stride) {
   const int rows = B * T;
-  k_pack_rows<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(x, B, T, TP, K, out, ss);
+  k_pack_rows<<<dim3((rows + 3) / 4), dim3(256), 0, s>>>(x, B, T, TP, K, out, ss, scale, scale_stride);
   return hipGetLastError();
 }
 

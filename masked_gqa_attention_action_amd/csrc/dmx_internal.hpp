@@ -15,7 +15,7 @@ namespace dmx {
 enum Epi { EPI_F32 = 0, EPI_RESID_BB = 2, EPI_GEGLU = 3, EPI_RESID_BF = 4, EPI_RESID_FB = 5, EPI_QKV = 6 };
 
 // A-operand sources of the GEMM (see dmx_gemm.hip).
-enum ASrc { A_GLOBAL = 0, A_MOD = 1, A_MODPRE = 2 };
+enum ASrc { A_GLOBAL = 0, A_MODPRE = 2 };
 
 // Skinny GEMM y[m][n] = sum_k A[m][k] * W[n][k] with a fused epilogue.  A and W
 // are tiled (dmx_tiles.hpp); rows are tiled rows (request b, token t at
@@ -23,9 +23,9 @@ enum ASrc { A_GLOBAL = 0, A_MOD = 1, A_MODPRE = 2 };
 // bf16-residual epilogues) are indexed by b * T + t; fp32 intermediates and
 // out_f32 by the tiled row.
 struct GemmArgs {
-  const uint16_t* A;  // tiled bf16 [M][K]; A_MOD: x, A_MODPRE: bf16(x * (1 + scale))
-  const float* nmod;  // A_MOD*: modulation [B][3][1024] (scale | shift | gate)
-  const float* ss_in; // A_MOD*: row sums of squares of x, [M][ss_in_n] partials
+  const uint16_t* A;  // tiled bf16 [M][K]; A_MODPRE: bf16(x * (1 + scale))
+  const float* nmod;  // A_MODPRE: modulation [B][3][1024] (scale | shift | gate)
+  const float* ss_in; // A_MODPRE: row sums of squares of x, [M][ss_in_n] partials
   int ss_in_n;        //   a multiple of 4 up to 64
   float* ss_out;      // EPI_RESID_BF / _FB: optional [M][ss_out_n] partials, one
   int ss_out_n;       //   per N-tile of 16 features (ntiles == ss_out_n)
@@ -60,13 +60,12 @@ constexpr int kQVB = (kHQ + kHK) * kD;  // columns of the tiled bf16 q + v heads
 // Gemm shape presets (host picks one per projection).
 enum GemmKind {
   GEMM_QKV1024 = 1,         // N = 4096, K = 1024, fp32 out, A given
-  GEMM_QKV1024_MOD = 2,     // N = 4096 as rotation-pair tiles, AdaRMS of bf16 x fused, EPI_QKV
-  GEMM_QKV1024_MODPRE = 10, // as above with A already bf16(x * (1 + scale))
+  GEMM_QKV1024_MODPRE = 10, // rotation-pair tiles, AdaRMS fused (A = bf16(x * (1 + scale))), EPI_QKV
   GEMM_QKV2560 = 3,         // N = 4096, K = 2560, fp32 out
   GEMM_OPROJ = 4,           // N = 1024, K = 2048, gated residual (bf16 -> bf16)
   GEMM_OPROJ_F32 = 5,       // as GEMM_OPROJ, fp32 output (layer-internal residual)
   GEMM_GATEUP = 6,          // N = 2 x 4096, K = 1024, GEGLU, A given
-  GEMM_GATEUP_MOD = 7,      // as above with the AdaRMS prenorm of x1 fused
+  GEMM_GATEUP_MOD = 7,      // as above with the AdaRMS prenorm of x1 fused (A = bf16(x1 * (1 + scale)))
   GEMM_DOWN = 8,            // N = 1024, K = 4096, gated residual (bf16 -> bf16)
   GEMM_DOWN_F32RES = 9,     // as GEMM_DOWN, fp32 residual input
 };
@@ -78,7 +77,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s);
 // of the GEMM epilogues.
 constexpr int kSsParts = 1024 / 16;
 hipError_t launch_pack_rows(const uint16_t* x, int B, int T, int TP, int K, uint16_t* out, float* ss,
-                            hipStream_t s);
+                            hipStream_t s, const float* scale = nullptr, int scale_stride = 0);
 
 // Several modulation GEMVs in one launch: out_j[b] = W_j cond_j[b] + bias_j.
 struct ModJob {
