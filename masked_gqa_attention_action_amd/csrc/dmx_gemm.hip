@@ -186,6 +186,116 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& a, int prow, int n, c
   }
 }
 
+// Epilogue of one output tile (NT columns `tile`) over block rows m0 ..
+// m0 + nrows - 1, run by every thread of the work-group (it synchronises).
+// Rsum(r, c) is the projection sum of block row r and tile column c, Ssum(r,
+// c) the shift tile's sum for row r's request (MOD), both with their partial
+// sums added in one fixed order; sR[r] is the row's 1 / rms (MOD), sF the
+// tile's 16 rotation frequencies (QKV); sq / sQ are LDS scratch for nrows
+// rows.  pre0: the global operands of the thread's first task, if fetched.
+template <int EPI, int NT, bool MOD, class RF, class SF>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int tile, int m0, int nrows, RF Rsum, SF Ssum,
+                                              const float* sR, const double* sF, float* sq, float* sQ,
+                                              const EpiPre* pre0) {
+  constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
+  constexpr bool QKV = EPI == EPI_QKV;
+  constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;  // output features (pairs for QKV) per row
+  constexpr int OUTW = EPI == EPI_GEGLU ? 4 : 8;  // outputs per epilogue task
+  constexpr int TPR = NOUT / OUTW;                // epilogue tasks per row
+  for (int e = threadIdx.x; e < nrows * TPR; e += blockDim.x) {
+    const int r = e / TPR, c0 = (e - r * TPR) * OUTW;
+    if (!row_valid(m0 + r, a.T, a.TP)) continue;
+    const int n = QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0;
+    EpiPre cur;
+    if (pre0 && e == (int)threadIdx.x)
+      cur = *pre0;
+    else
+      epi_fetch<EPI>(a, m0 + r, n, cur);
+    float v[8], seen[8];
+    if (QKV) {
+      // 8 rotation pairs: first-half features f .. f+7 and partners f+128 ..
+      const int h = tile >> 3;  // head
+      const int f = n;
+      float lo[8], hi[8], sq8 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float tl = Rsum(r, c0 + i), th = Rsum(r, 16 + c0 + i);
+        if (MOD) {
+          const float sl = Ssum(r, c0 + i), sh = Ssum(r, 16 + c0 + i);
+          lo[i] = sR[r] * tl + sl;
+          hi[i] = sR[r] * th + sh;
+        } else {
+          lo[i] = tl;
+          hi[i] = th;
+        }
+        sq8 += lo[i] * lo[i] + hi[i] * hi[i];
+      }
+      if (h < kHQ + kHK) {
+        float wl[8], wh[8];
+        unpack8(cur.wl, wl);
+        unpack8(cur.wh, wh);
+        const int prow = m0 + r, b = prow / a.TP;
+        const double pos = (double)a.pos0[b] + (double)(prow - b * a.TP);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          double rev = pos * sF[c0 + i];
+          rev -= floor(rev);
+          const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+          const float x0 = lo[i] * (1.f + wl[i]), x1 = hi[i] * (1.f + wh[i]);
+          lo[i] = x0 * cs - x1 * sn;
+          hi[i] = x1 * cs + x0 * sn;
+        }
+      }
+      if (h >= kHQ && h < kHQ + kHK) {  // k heads: fp32, scaled by 1 / rms when staged
+        float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
+        float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
+        *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
+        *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
+      } else {  // q and v heads: bf16, as the attention's MFMA consumes them
+        const int fq = h < kHQ ? f : f - kHK * kD;
+        *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq, kQVB)) = pack8(lo);
+        *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq + 128, kQVB)) = pack8(hi);
+      }
+      sQ[r * 2 + (c0 >> 3)] = sq8;
+    } else if (EPI == EPI_GEGLU) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float g = Rsum(r, c0 + i), u = Rsum(r, 16 + c0 + i);
+        if (MOD) {
+          const float gs = Ssum(r, c0 + i), us = Ssum(r, 16 + c0 + i);
+          g = sR[r] * g + gs;
+          u = sR[r] * u + us;
+        }
+        v[i] = gelu_tanh(g) * u;
+      }
+      *reinterpret_cast<uint2*>(a.out_pk + tile_off(m0 + r, tile * 16 + (c0 & ~7), a.ldo) + (c0 & 7)) =
+          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float t = Rsum(r, c0 + i);
+        v[i] = MOD ? sR[r] * t + Ssum(r, c0 + i) : t;
+      }
+      epi_store8<EPI>(a, m0 + r, n, cur, v, seen);
+      if (SSQ) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sq[r * NOUT + c0 + i] = seen[i] * seen[i];
+      }
+    }
+  }
+  if (SSQ && a.ss_out) {
+    __syncthreads();
+    write_row_ssq<NOUT>(a, tile, m0, nrows, sq);
+  }
+  if (QKV && (tile >> 3) < kHQ + kHK) {
+    __syncthreads();
+    for (int r = threadIdx.x; r < nrows; r += blockDim.x)
+      if (row_valid(m0 + r, a.T, a.TP)) a.ss_q[(size_t)(m0 + r) * kQkvTiles + tile] = sQ[r * 2] + sQ[r * 2 + 1];
+  }
+}
+
 template <int EPI, int NT, int NWAVES, int KSTEPS, int ASRC, int MT>
 __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_gemm(GemmArgs a) {
   constexpr int NTT = NT / 16;
@@ -259,7 +369,6 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
     }
     float4 msh = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 ssp[4];
-    const int pos_b = QKV ? a.pos0[m0 / a.TP] : 0;
     if (MOD) {
       const float* mb = a.nmod + (size_t)(m0 / a.TP) * 3 * kH;
       msh = *reinterpret_cast<const float4*>(mb + kH + threadIdx.x * 4);
@@ -338,114 +447,21 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
       for (int nt = 0; nt < NTT; ++nt) red[(wave * RROWS + MB) * NT + nt * 16 + lr] = accs[nt][0];
     }
     __syncthreads();
-    const int nrows = mts * 16;
-    for (int e = threadIdx.x; e < nrows * TPR; e += NWAVES * 64) {
-      const int r = e / TPR, c0 = (e - r * TPR) * OUTW;
-      if (!row_valid(m0 + r, a.T, a.TP)) continue;
-      const int n = QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0;
-      EpiPre cur;
-      if (e == (int)threadIdx.x)
-        cur = pre;
-      else
-        epi_fetch<EPI>(a, m0 + r, n, cur);
-      float v[8], seen[8];
-      if (QKV) {
-        // 8 rotation pairs: first-half features f .. f+7 and partners f+128 ..
-        const int h = tile >> 3, jb = (tile & 7) * 16 + c0;  // head, dim in the first half
-        const int f = n;
-        float lo[8], hi[8], sq8 = 0.f;
+    tile_epilogue<EPI, NT, MOD>(
+        a, tile, m0, mts * 16,
+        [&](int r, int c) {
+          float t = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float tl = 0.f, th = 0.f, sl = 0.f, sh = 0.f;
+          for (int w = 0; w < NWAVES; ++w) t += red[(w * RROWS + r) * NT + c];
+          return t;
+        },
+        [&](int, int c) {
+          float t = 0.f;
 #pragma unroll
-          for (int w = 0; w < NWAVES; ++w) {
-            tl += red[(w * RROWS + r) * NT + c0 + i];
-            th += red[(w * RROWS + r) * NT + 16 + c0 + i];
-            if (MOD) {
-              sl += red[(w * RROWS + MB) * NT + c0 + i];
-              sh += red[(w * RROWS + MB) * NT + 16 + c0 + i];
-            }
-          }
-          lo[i] = MOD ? sR[r] * tl + sl : tl;
-          hi[i] = MOD ? sR[r] * th + sh : th;
-          sq8 += lo[i] * lo[i] + hi[i] * hi[i];
-        }
-        if (h < kHQ + kHK) {
-          float wl[8], wh[8];
-          unpack8(cur.wl, wl);
-          unpack8(cur.wh, wh);
-          const double pos = (double)pos_b + (double)((m0 + r) % a.TP);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            double rev = pos * sF[c0 + i];
-            rev -= floor(rev);
-            const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-            const float x0 = lo[i] * (1.f + wl[i]), x1 = hi[i] * (1.f + wh[i]);
-            lo[i] = x0 * cs - x1 * sn;
-            hi[i] = x1 * cs + x0 * sn;
-          }
-        }
-        if (h >= kHQ && h < kHQ + kHK) {  // k heads: fp32, scaled by 1 / rms when staged
-          float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
-          float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
-          *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
-          *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
-          *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
-          *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
-        } else {  // q and v heads: bf16, as the attention's MFMA consumes them
-          const int fq = h < kHQ ? f : f - kHK * kD;
-          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq, kQVB)) = pack8(lo);
-          *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq + 128, kQVB)) = pack8(hi);
-        }
-        sQ[r * 2 + (c0 >> 3)] = sq8;
-      } else if (EPI == EPI_GEGLU) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float g = 0.f, u = 0.f, gs = 0.f, us = 0.f;
-#pragma unroll
-          for (int w = 0; w < NWAVES; ++w) {
-            g += red[(w * RROWS + r) * NT + c0 + i];
-            u += red[(w * RROWS + r) * NT + 16 + c0 + i];
-            if (MOD) {
-              gs += red[(w * RROWS + MB) * NT + c0 + i];
-              us += red[(w * RROWS + MB) * NT + 16 + c0 + i];
-            }
-          }
-          if (MOD) {
-            g = sR[r] * g + gs;
-            u = sR[r] * u + us;
-          }
-          v[i] = gelu_tanh(g) * u;
-        }
-        *reinterpret_cast<uint2*>(a.out_pk + tile_off(m0 + r, tile * 16 + (c0 & ~7), a.ldo) + (c0 & 7)) =
-            make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float t = 0.f, ts = 0.f;
-#pragma unroll
-          for (int w = 0; w < NWAVES; ++w) {
-            t += red[(w * RROWS + r) * NT + c0 + i];
-            if (MOD) ts += red[(w * RROWS + MB) * NT + c0 + i];
-          }
-          v[i] = MOD ? sR[r] * t + ts : t;
-        }
-        epi_store8<EPI>(a, m0 + r, n, cur, v, seen);
-        if (SSQ) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sq[r * NOUT + c0 + i] = seen[i] * seen[i];
-        }
-      }
-    }
-    if (SSQ && a.ss_out) {
-      __syncthreads();
-      write_row_ssq<NOUT>(a, tile, m0, nrows, sq);
-    }
-    if (QKV && (tile >> 3) < kHQ + kHK) {
-      __syncthreads();
-      for (int r = threadIdx.x; r < nrows; r += blockDim.x)
-        if (row_valid(m0 + r, a.T, a.TP)) a.ss_q[(size_t)(m0 + r) * kQkvTiles + tile] = sQ[r * 2] + sQ[r * 2 + 1];
-    }
+          for (int w = 0; w < NWAVES; ++w) t += red[(w * RROWS + MB) * NT + c];
+          return t;
+        },
+        sR, sF, sq, sQ, &pre);
     __syncthreads();
   }
 }
