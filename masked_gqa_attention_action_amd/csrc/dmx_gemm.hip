@@ -202,15 +202,11 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int tile, int m
   constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;  // output features (pairs for QKV) per row
   constexpr int OUTW = EPI == EPI_GEGLU ? 4 : 8;  // outputs per epilogue task
   constexpr int TPR = NOUT / OUTW;                // epilogue tasks per row
-  for (int e = threadIdx.x; e < nrows * TPR; e += blockDim.x) {
+  // task e: row r = e / TPR, OUTW features from c0; the thread's first task
+  // is peeled so that the prefetched operands are used without a copy
+  auto task = [&](int e, const EpiPre& cur) {
     const int r = e / TPR, c0 = (e - r * TPR) * OUTW;
-    if (!row_valid(m0 + r, a.T, a.TP)) continue;
     const int n = QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0;
-    EpiPre cur;
-    if (pre0 && e == (int)threadIdx.x)
-      cur = *pre0;
-    else
-      epi_fetch<EPI>(a, m0 + r, n, cur);
     float v[8], seen[8];
     if (QKV) {
       // 8 rotation pairs: first-half features f .. f+7 and partners f+128 ..
@@ -284,6 +280,19 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int tile, int m
         for (int i = 0; i < 8; ++i) sq[r * NOUT + c0 + i] = seen[i] * seen[i];
       }
     }
+  };
+  auto task_row_ok = [&](int e) { return row_valid(m0 + e / TPR, a.T, a.TP); };
+  int e0 = threadIdx.x;
+  if (pre0) {
+    if (e0 < nrows * TPR && task_row_ok(e0)) task(e0, *pre0);
+    e0 += blockDim.x;
+  }
+  for (int e = e0; e < nrows * TPR; e += blockDim.x) {
+    if (!task_row_ok(e)) continue;
+    const int r = e / TPR, c0 = (e - r * TPR) * OUTW;
+    EpiPre cur;
+    epi_fetch<EPI>(a, m0 + r, QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0, cur);
+    task(e, cur);
   }
   if (SSQ && a.ss_out) {
     __syncthreads();
@@ -466,6 +475,195 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
+// Large-M projections (batches of requests, the prefix QKV over 2048
+// tokens): the same arithmetic as k_gemm, bit for bit, on a schedule that
+// keeps the MFMA units busy.  K is split into NR ranges of KSR 32-column steps
+// (k_gemm's waves); each range is accumulated from zero in step order by the
+// same MFMA, and the range sums are added in range order in LDS.  The shift
+// tile of the fused AdaRMS holds one row per request of the block.  The
+// epilogue is the same tile_epilogue, once per output tile of the block.
+// A work-group of 4 waves (2 x 2) owns BM rows x BNF 16-column fragments: wave
+// (wm, wn) the rows wm*WMT*16 .. and the fragments wn*WNF ..; every fragment is
+// loaded straight from the tiled operands into registers (one 1 KB load per
+// wave and fragment) one step ahead of its MFMAs.
+template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int WNF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_big(GemmArgs a) {
+  constexpr bool MOD = ASRC == A_MODPRE;
+  constexpr bool QKV = EPI == EPI_QKV;
+  constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
+  constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;
+  constexpr int NTT = NT / 16;       // fragments per output tile
+  constexpr int BM = 2 * WMT * 16;   // rows per block
+  constexpr int BNF = 2 * WNF;       // fragments per block
+  constexpr int BN = BNF * 16;       // columns per block
+  constexpr int NST = BNF / NTT;     // output tiles per block
+  constexpr int KS = NR * KSR;       // 32-column steps of K
+  constexpr int MAXREQ = BM / 16 + 1;  // requests a block can touch (at least 16 rows each)
+  constexpr int PD = 2;              // steps in flight per wave
+  static_assert(KSR % PD == 0 && BNF % NTT == 0, "block shape");
+  static_assert(!MOD || KS * 32 == kH, "the modulated A operand spans one hidden row");
+  __shared__ __attribute__((aligned(16))) float sTot[BM * BN];  // range sums [row][column]
+  __shared__ float sShift[MOD ? MAXREQ * BN : 1];               // shift sums [request][column]
+  __shared__ float sR[MOD ? BM : 1];
+  __shared__ double sF[QKV ? NST * 16 : 1];
+  __shared__ float sq[SSQ ? BM * NOUT : 1];
+  __shared__ float sQ[QKV ? BM * 2 : 1];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int m0 = blockIdx.y * BM;
+  const int nrows = min(BM, a.M - m0);
+  const int last_tile = a.M / 16 - 1;
+  const int b0 = m0 / a.TP;
+  const int nreq = MOD ? (m0 + nrows - 1) / a.TP - b0 + 1 : 0;
+  const bool shift_wave = MOD && wm == 0;
+
+  // operand base pointers (step 0) of this wave's fragments
+  const uint16_t* ap[WMT];
+  const uint16_t* wp[WNF];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i) {
+    const int mtile = min(m0 / 16 + wm * WMT + i, last_tile);  // rows past M re-read the last tile
+    ap[i] = a.A + (size_t)mtile * KS * 512 + lane * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < WNF; ++j) {
+    const int fj = wn * WNF + j, st = fj / NTT, nt = fj % NTT;
+    const int tile = blockIdx.x * NST + st;
+    const int wt = EPI == EPI_GEGLU ? (nt == 0 ? tile : a.wtile_up + tile)
+                   : QKV ? (tile >> 3) * 16 + nt * 8 + (tile & 7)
+                         : tile * NTT + nt;
+    wp[j] = a.W + (size_t)wt * KS * 512 + lane * 8;
+  }
+  // shift vector of request b0 + lr (lanes past the block's requests read
+  // request b0's and hold zeros); every wave loads it, so that all waves
+  // issue the same loads and the ring's waits stay exact
+  const bool h_ok = MOD && lr < nreq;
+  const float* hp = MOD ? a.nmod + (size_t)(b0 + (h_ok ? lr : 0)) * 3 * kH + kH + lq * 8 : nullptr;
+
+  // a ring of PD steps in flight per wave: step s lives in slot s % PD from
+  // PD steps before its MFMAs until they have run
+  bf16x8 Ab[PD][WMT], Wb[PD][WNF];
+  float4 Hb[PD][2];
+  auto load = [&](int ks, bf16x8* A, bf16x8* W, float4* Hs) {
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) A[i] = load_bf16x8(ap[i] + (size_t)ks * 512);
+#pragma unroll
+    for (int j = 0; j < WNF; ++j) W[j] = load_bf16x8(wp[j] + (size_t)ks * 512);  // shared by the row blocks
+    if (MOD) {
+      Hs[0] = *reinterpret_cast<const float4*>(hp + ks * 32);
+      Hs[1] = *reinterpret_cast<const float4*>(hp + ks * 32 + 4);
+    }
+  };
+  f32x4 acc[WMT][WNF], accs[WNF];
+  auto mma = [&](const bf16x8* A, const bf16x8* W, const float4* Hs) {
+    if (shift_wave) {
+      const float hv[8] = {Hs[0].x, Hs[0].y, Hs[0].z, Hs[0].w, Hs[1].x, Hs[1].y, Hs[1].z, Hs[1].w};
+      bf16x8 hs;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t p = h_ok ? pack2(hv[e], hv[e + 1]) : 0u;
+        hs[e] = (short)(p & 0xffffu);
+        hs[e + 1] = (short)(p >> 16);
+      }
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) accs[j] = mfma16(hs, W[j], accs[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < WMT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) acc[i][j] = mfma16(A[i], W[j], acc[i][j]);
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < WMT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) acc[i][j] = zero_f32x4();
+#pragma unroll
+    for (int j = 0; j < WNF; ++j) accs[j] = zero_f32x4();
+  };
+  // range r's sum into LDS: lane (lr, lq) holds rows 4 lq .. 4 lq + 3 of each tile, column lr
+  auto flush = [&](int r) {
+#pragma unroll
+    for (int i = 0; i < WMT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNF; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float* d = sTot + ((wm * WMT + i) * 16 + 4 * lq + e) * BN + (wn * WNF + j) * 16 + lr;
+          *d = (r == 0 ? 0.f : *d) + acc[i][j][e];
+        }
+    if (shift_wave) {
+#pragma unroll
+      for (int j = 0; j < WNF; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * lq + e < nreq) {
+            float* d = sShift + (4 * lq + e) * BN + (wn * WNF + j) * 16 + lr;
+            *d = (r == 0 ? 0.f : *d) + accs[j][e];
+          }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < PD; ++d) load(d, Ab[d], Wb[d], Hb[d]);
+  zero_acc();
+#pragma unroll 1
+  for (int s0 = 0; s0 < KS; s0 += PD) {
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+      const int ks = s0 + d;
+      mma(Ab[d], Wb[d], Hb[d]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the refill PD steps ahead of its use
+      load(min(ks + PD, KS - 1), Ab[d], Wb[d], Hb[d]);  // past the end: re-read the last step, unused
+      __builtin_amdgcn_sched_barrier(0);
+      if ((ks + 1) % KSR == 0) {  // end of a range
+        flush(ks / KSR);
+        zero_acc();
+      }
+    }
+  }
+
+  // row scales and rotation frequencies, as k_gemm computes them
+  if (MOD) {
+    for (int rb = 0; rb < BM; rb += 64) {
+      const int rr = rb + (threadIdx.x >> 2), qq = threadIdx.x & 3;
+      const int per = a.ss_in_n >> 2;
+      float4 ssp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ssp[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rr < nrows && row_valid(m0 + rr, a.T, a.TP)) {
+        const float* sp = a.ss_in + (size_t)(m0 + rr) * a.ss_in_n + qq * per;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i * 4 < per) ssp[i] = *reinterpret_cast<const float4*>(sp + i * 4);
+      }
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t += ssp[i].x + ssp[i].y + ssp[i].z + ssp[i].w;
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      if (qq == 0) sR[rr] = 1.0f / sqrtf(t * (1.0f / kH) + kEps);
+    }
+  }
+  if (QKV && threadIdx.x < NST * 16) {
+    const int tile = blockIdx.x * NST + (threadIdx.x >> 4);
+    const int j = (tile & 7) * 16 + (threadIdx.x & 15);
+    sF[threadIdx.x] = exp2(-(double)j / 128.0 * log2((double)a.rope_base)) * 0.15915494309189533577;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < NST; ++st) {
+    const int tile = blockIdx.x * NST + st;
+    tile_epilogue<EPI, NT, MOD>(
+        a, tile, m0, nrows, [&](int r, int c) { return sTot[r * BN + st * NT + c]; },
+        [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + st * NT + c]; }, sR, sF + st * 16, sq,
+        sQ, nullptr);
+    __syncthreads();
+  }
+}
+
 #define DMX_GEMM(EPI, NT, NW, KS, SRC, MT, GY) \
   k_gemm<EPI, NT, NW, KS, SRC, MT><<<dim3(a.ntiles, GY), dim3((NW) * 64), 0, s>>>(a)
 
@@ -484,7 +682,28 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
   return a.ntiles;
 }
 
+#define DMX_GEMM_BIG(EPI, NT, NR, KSR, SRC, WMT, WNF)                                              \
+  k_gemm_big<EPI, NT, NR, KSR, SRC, WMT, WNF>                                                        \
+      <<<dim3(a.ntiles * (NT) / (32 * (WNF)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(256), 0, s>>>(a)
+
+// Row count from which the large-M schedule (k_gemm_big) runs a projection.
+constexpr int kBigGemmRows = 256;
+
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
+  if (a.M >= kBigGemmRows) {
+    switch (kind) {
+      case GEMM_QKV1024: DMX_GEMM_BIG(EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4); break;
+      case GEMM_QKV1024_MODPRE: DMX_GEMM_BIG(EPI_QKV, 32, 4, 8, A_MODPRE, 4, 4); break;
+      case GEMM_QKV2560: DMX_GEMM_BIG(EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4); break;
+      case GEMM_OPROJ: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 2); break;
+      case GEMM_OPROJ_F32: DMX_GEMM_BIG(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 2); break;
+      case GEMM_GATEUP: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 4, 4); break;
+      case GEMM_GATEUP_MOD: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4); break;
+      case GEMM_DOWN: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 2, 2); break;
+      case GEMM_DOWN_F32RES: DMX_GEMM_BIG(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 2, 2); break;
+    }
+    return hipGetLastError();
+  }
   // row blocks: one per WG up to 4 (more blocks loop inside the WG)
   const int tiles = a.M / 16;
   const int mb1 = std::min(4, tiles), mb2 = std::min(4, (tiles + 1) / 2);

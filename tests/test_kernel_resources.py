@@ -25,7 +25,7 @@ def _report(src):
             name = m.group(1)
             kernels[name] = {}
             continue
-        m = re.search(r"remark: (ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill|VGPRs|AGPRs): (\d+)", line)
+        m = re.search(r"remark:\s+(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill|VGPRs|AGPRs): (\d+)", line)
         if m and name:
             kernels[name][m.group(1)] = int(m.group(2))
     return kernels

@@ -110,6 +110,32 @@ def test_qkv_prefix_hidden2560_into_cache():
     stage_gate("prefix v", from_dev(v[0][:, sample]), vr)
 
 
+def test_qkv_prefix_large_m_schedule_is_bit_identical():
+    """The 2048-token prefix QKV runs on the large-M GEMM schedule; 32 calls of
+    64 tokens (positions and cache rows offset) run on the skinny one.  Both
+    schedules add the same products in the same order, so every output bit
+    agrees."""
+    inp = synth.prefix_qkv_inputs(synth.BASE_SEED + 4000 + 78)
+    T, P, S = 2048, 2048, 64
+    x = to_dev(inp["x"]).view(1, T, 2560)
+    w, qn, kn = to_dev_w(inp["w_qkv"]), to_dev(inp["q_norm"]), to_dev(inp["k_norm"])
+    ws = dmx.new_workspace(1, T, 0)
+    pos = to_dev(np.zeros(1, dtype=np.int32), "raw")
+    q, k, v = dmx.qkv_qknorm_rope(x, w, qn, kn, pos, ws, kv_rows=P)
+    k2 = torch.empty_like(k)
+    v2 = torch.empty_like(v)
+    ws2 = dmx.new_workspace(1, S, 0)
+    qs = []
+    for c in range(T // S):
+        pc = to_dev(np.array([c * S], dtype=np.int32), "raw")
+        qc, _, _ = dmx.qkv_qknorm_rope(x[:, c * S:(c + 1) * S].contiguous(), w, qn, kn, pc, ws2, k=k2, v=v2,
+                                       kv_rows=P, kv_row0=c * S)
+        qs.append(qc)
+    torch.cuda.synchronize()
+    assert torch.equal(q, torch.cat(qs, dim=1))
+    assert torch.equal(k, k2) and torch.equal(v, v2)
+
+
 def test_qkv_writes_only_its_cache_rows():
     r = rng(210)
     T, P, row0 = 50, 1024, 1024 - 50 - 7
