@@ -502,7 +502,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int PD = 2;              // steps in flight per wave
   static_assert(KSR % PD == 0 && BNF % NTT == 0, "block shape");
   static_assert(!MOD || KS * 32 == kH, "the modulated A operand spans one hidden row");
-  __shared__ __attribute__((aligned(16))) float sTot[BM * BN];  // range sums [row][column]
+  constexpr int TLD = BN + 4;  // sTot row stride (floats): rows 4 banks apart
+  __shared__ __attribute__((aligned(16))) float sTot[BM * TLD];  // range sums [row][column]
   __shared__ float sShift[MOD ? MAXREQ * BN : 1];               // shift sums [request][column]
   __shared__ float sR[MOD ? BM : 1];
   __shared__ double sF[QKV ? NST * 16 : 1];
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int j = 0; j < WNF; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float* d = sTot + ((wm * WMT + i) * 16 + 4 * lq + e) * BN + (wn * WNF + j) * 16 + lr;
+          float* d = sTot + ((wm * WMT + i) * 16 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr;
           *d = (r == 0 ? 0.f : *d) + acc[i][j][e];
         }
     if (shift_wave) {
@@ -657,7 +658,246 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int st = 0; st < NST; ++st) {
     const int tile = blockIdx.x * NST + st;
     tile_epilogue<EPI, NT, MOD>(
-        a, tile, m0, nrows, [&](int r, int c) { return sTot[r * BN + st * NT + c]; },
+        a, tile, m0, nrows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
+        [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + st * NT + c]; }, sR, sF + st * 16, sq,
+        sQ, nullptr);
+    __syncthreads();
+  }
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// one 16-byte-per-lane load from global memory straight into LDS: lane i's
+// 16 bytes land at lds_dst + 16 i (lds_dst uniform across the wave)
+__device__ __forceinline__ void lds_copy16(const uint16_t* src, uint16_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+// work-group barrier that orders LDS traffic around it (no memory fence, so
+// loads into LDS that are still in flight are not waited for)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wide large-M projections (N >= 4096: QKV, gate-up, the prefix QKV), the
+// same arithmetic as k_gemm bit for bit, with the operands shared through
+// LDS.  A work-group of 8 waves (2 x 4; two per SIMD) owns BM rows x 256
+// columns.  Each 32-column step's operand fragments (BM/16 A tiles, 16 W
+// fragments, 1 KB each) are copied from HBM straight into an LDS stage by
+// loads that bypass registers (global_load_lds, 16 B per lane, so a wave's
+// fragment lands as one contiguous 1 KB block), four or five steps ahead of
+// their use; each wave reads its WMT A tiles and 4 W fragments of the next
+// step from LDS while the MFMAs of the current one run.  K is split into the same NR ranges of KSR
+// steps as the skinny kernel's waves; each range is accumulated from zero in
+// step order and the range sums are added in range order in registers.
+template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_lds(GemmArgs a) {
+  constexpr bool MOD = ASRC == A_MODPRE;
+  constexpr bool QKV = EPI == EPI_QKV;
+  constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
+  constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;
+  constexpr int WNF = 4;               // W fragments per wave
+  constexpr int BM = 2 * WMT * 16;     // rows per block
+  constexpr int BNF = 4 * WNF;         // fragments per block
+  constexpr int BN = BNF * 16;         // columns per block
+  constexpr int NTT = NT / 16, NST = BNF / NTT;
+  constexpr int KS = NR * KSR;
+  constexpr int AF = BM / 16;          // A tiles per step
+  constexpr int SF = AF + BNF;         // fragments per step
+  constexpr int DPW = SF / 8;          // fragments each wave copies per step
+  // a ring of STAGES steps, AHEAD = STAGES - 1 of them copied ahead: LDS
+  // latency times bandwidth needs about 100 KB in flight per CU
+  constexpr int STAGES = MOD ? 5 : 6, AHEAD = STAGES - 1;
+  constexpr int MAXREQ = BM / 16 + 1;
+  constexpr int STAGE_EL = SF * 512;   // bf16 elements per stage
+  constexpr int TLD = BN + 4;           // sTot row stride (floats): rows 4 banks apart
+  constexpr int RAW = (STAGES * STAGE_EL * 2 > BM * TLD * 4) ? STAGES * STAGE_EL * 2 : BM * TLD * 4;
+  static_assert(SF % 8 == 0 && BNF % NTT == 0 && KS % 2 == 0, "block shape");
+  static_assert(!MOD || KS * 32 == kH, "the modulated A operand spans one hidden row");
+  // the stages during the K loop, the range sums [row][column] after it
+  __shared__ __attribute__((aligned(16))) unsigned char smem[RAW];
+  __shared__ __attribute__((aligned(16))) uint16_t sHb[MOD ? MAXREQ * kH : 8];  // bf16 shift vectors
+  __shared__ float sShift[MOD ? MAXREQ * BN : 1];
+  __shared__ float sR[MOD ? BM : 1];
+  __shared__ double sF[QKV ? NST * 16 : 1];
+  __shared__ float sq[SSQ ? BM * NOUT : 1];
+  __shared__ float sQ[QKV ? BM * 2 : 1];
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
+  float* sTot = reinterpret_cast<float*>(smem);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int m0 = blockIdx.y * BM;
+  const int nrows = min(BM, a.M - m0);
+  const int last_tile = a.M / 16 - 1;
+  const int b0 = m0 / a.TP;
+  const int nreq = MOD ? (m0 + nrows - 1) / a.TP - b0 + 1 : 0;
+  const bool shift_wave = MOD && wm == 0;
+
+  if (MOD) {  // the block's shift vectors, rounded to bf16 as the shift tile holds them
+    for (int i = threadIdx.x; i < nreq * (kH / 2); i += blockDim.x) {
+      const int q = i / (kH / 2), k2 = (i - q * (kH / 2)) * 2;
+      const float* sh = a.nmod + (size_t)(b0 + q) * 3 * kH + kH + k2;
+      *reinterpret_cast<uint32_t*>(sHb + q * kH + k2) = pack2(sh[0], sh[1]);
+    }
+    __syncthreads();
+  }
+
+  // fragments this wave copies: f = wave * DPW + d (A tiles first, then W)
+  const uint16_t* gsrc[DPW];
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int f = wave * DPW + d;
+    if (f < AF) {
+      gsrc[d] = a.A + (size_t)min(m0 / 16 + f, last_tile) * KS * 512 + lane * 8;  // rows past M: last tile
+    } else {
+      const int fj = f - AF, st = fj / NTT, nt = fj % NTT;
+      const int tile = blockIdx.x * NST + st;
+      const int wt = EPI == EPI_GEGLU ? (nt == 0 ? tile : a.wtile_up + tile)
+                     : QKV ? (tile >> 3) * 16 + nt * 8 + (tile & 7)
+                           : tile * NTT + nt;
+      gsrc[d] = a.W + (size_t)wt * KS * 512 + lane * 8;
+    }
+  }
+  auto issue = [&](int ks) {
+    uint16_t* dst = stage + (ks % STAGES) * STAGE_EL;
+#pragma unroll
+    for (int d = 0; d < DPW; ++d)
+      lds_copy16(gsrc[d] + (size_t)ks * 512, dst + (wave * DPW + d) * 512);
+  };
+
+  f32x4 acc[WMT][WNF], tot[WMT][WNF], accs[WNF];
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNF; ++j) acc[i][j] = zero_f32x4();
+#pragma unroll
+  for (int j = 0; j < WNF; ++j) accs[j] = zero_f32x4();
+
+  // this wave's fragments of step ks from its stage (A tiles, W fragments,
+  // the shift row of each request for the shift waves)
+  auto read_frags = [&](int ks, bf16x8* af, bf16x8* wf, bf16x8& hs) {
+    const uint16_t* st = stage + (ks % STAGES) * STAGE_EL;
+#pragma unroll
+    for (int i = 0; i < WMT; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + (wm * WMT + i) * 512 + lane * 8);
+#pragma unroll
+    for (int j = 0; j < WNF; ++j)
+      wf[j] = *reinterpret_cast<const bf16x8*>(st + (AF + wn * WNF + j) * 512 + lane * 8);
+    if (shift_wave) hs = *reinterpret_cast<const bf16x8*>(sHb + (lr < nreq ? lr : 0) * kH + ks * 32 + lq * 8);
+  };
+  auto step_mma = [&](int ks, const bf16x8* af, const bf16x8* wf, bf16x8 hs) {
+    if (shift_wave) {
+      if (lr >= nreq) hs = zero_bf16x8();
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) accs[j] = mfma16(hs, wf[j], accs[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < WMT; ++i)
+#pragma unroll
+      for (int j = 0; j < WNF; ++j) acc[i][j] = mfma16(af[i], wf[j], acc[i][j]);
+    if ((ks + 1) % KSR == 0) {  // end of a range: add its sums in range order
+      const bool first = ks + 1 == KSR;
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNF; ++j) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tot[i][j][e] = (first ? 0.f : tot[i][j][e]) + acc[i][j][e];
+          acc[i][j] = zero_f32x4();
+        }
+      if (shift_wave) {  // the shift sums accumulate in LDS (sShift is not a stage)
+#pragma unroll
+        for (int j = 0; j < WNF; ++j) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * lq + e < nreq) {
+              float* d = sShift + (4 * lq + e) * BN + (wn * WNF + j) * 16 + lr;
+              *d = (first ? 0.f : *d) + accs[j][e];
+            }
+          accs[j] = zero_f32x4();
+        }
+      }
+    }
+  };
+
+  // Step ks: its fragments were read from LDS during step ks - 1.  Wait for
+  // step ks + 1's copies (own, then everyone's at the barrier, which also
+  // means every wave has consumed step ks - 1's fragments), refill step
+  // ks - 1's stage with step ks + AHEAD, read step ks + 1's fragments, then
+  // run step ks's MFMAs while those reads are in flight.
+#pragma unroll
+  for (int k = 0; k < AHEAD; ++k) issue(k);
+  wait_vmcnt<(AHEAD - 1) * DPW>();
+  lds_barrier();
+  bf16x8 af0[WMT], wf0[WNF], af1[WMT], wf1[WNF], hs0 = zero_bf16x8(), hs1 = zero_bf16x8();
+  read_frags(0, af0, wf0, hs0);
+#pragma unroll 1
+  for (int ks = 0; ks < KS; ks += 2) {
+    // even step ks (fragments in set 0), then odd step ks + 1 (set 1); KS is even
+    wait_vmcnt<(AHEAD - 2) * DPW>();
+    lds_barrier();
+    issue(min(ks + AHEAD, KS - 1));
+    read_frags(ks + 1, af1, wf1, hs1);
+    step_mma(ks, af0, wf0, hs0);
+    wait_vmcnt<(AHEAD - 2) * DPW>();
+    lds_barrier();
+    issue(min(ks + 1 + AHEAD, KS - 1));
+    read_frags(min(ks + 2, KS - 1), af0, wf0, hs0);  // past the end: a landed stage, unused
+    step_mma(ks + 1, af1, wf1, hs1);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every copy has landed and every stage read: the stages become sTot
+
+  // range sums into LDS: lane (lr, lq) holds rows 4 lq .. 4 lq + 3 of each tile, column lr
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNF; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sTot[((wm * WMT + i) * 16 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr] = tot[i][j][e];
+  // row scales and rotation frequencies, as k_gemm computes them
+  if (MOD) {
+    for (int rb = 0; rb < BM; rb += 128) {
+      const int rr = rb + (threadIdx.x >> 2), qq = threadIdx.x & 3;
+      const int per = a.ss_in_n >> 2;
+      float4 ssp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ssp[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rr < nrows && row_valid(m0 + rr, a.T, a.TP)) {
+        const float* sp = a.ss_in + (size_t)(m0 + rr) * a.ss_in_n + qq * per;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i * 4 < per) ssp[i] = *reinterpret_cast<const float4*>(sp + i * 4);
+      }
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t += ssp[i].x + ssp[i].y + ssp[i].z + ssp[i].w;
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      if (qq == 0 && rr < BM) sR[rr] = 1.0f / sqrtf(t * (1.0f / kH) + kEps);
+    }
+  }
+  if (QKV && threadIdx.x < NST * 16) {
+    const int tile = blockIdx.x * NST + (threadIdx.x >> 4);
+    const int j = (tile & 7) * 16 + (threadIdx.x & 15);
+    sF[threadIdx.x] = exp2(-(double)j / 128.0 * log2((double)a.rope_base)) * 0.15915494309189533577;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < NST; ++st) {
+    const int tile = blockIdx.x * NST + st;
+    tile_epilogue<EPI, NT, MOD>(
+        a, tile, m0, nrows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
         [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + st * NT + c]; }, sR, sF + st * 16, sq,
         sQ, nullptr);
     __syncthreads();
@@ -686,15 +926,22 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
   k_gemm_big<EPI, NT, NR, KSR, SRC, WMT, WNF>                                                        \
       <<<dim3(a.ntiles * (NT) / (32 * (WNF)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(256), 0, s>>>(a)
 
-// Row count from which the large-M schedule (k_gemm_big) runs a projection.
+#define DMX_GEMM_LDS(EPI, NT, NR, KSR, SRC, WMT)                                                    \
+  k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT>                                                           \
+      <<<dim3(a.ntiles * (NT) / 256, (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(512), 0, s>>>(a)
+
+// Row count from which the large-M schedules run a projection: k_gemm_lds
+// for the plain wide ones (the prefix QKV), k_gemm_big for the rest (the
+// AdaRMS-fused ones need their registers and LDS for the shift and epilogue;
+// measured faster there).
 constexpr int kBigGemmRows = 256;
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   if (a.M >= kBigGemmRows) {
     switch (kind) {
-      case GEMM_QKV1024: DMX_GEMM_BIG(EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4); break;
+      case GEMM_QKV1024: DMX_GEMM_LDS(EPI_F32, 16, 4, 8, A_GLOBAL, 4); break;
       case GEMM_QKV1024_MODPRE: DMX_GEMM_BIG(EPI_QKV, 32, 4, 8, A_MODPRE, 4, 4); break;
-      case GEMM_QKV2560: DMX_GEMM_BIG(EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4); break;
+      case GEMM_QKV2560: DMX_GEMM_LDS(EPI_F32, 16, 4, 20, A_GLOBAL, 4); break;
       case GEMM_OPROJ: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 2); break;
       case GEMM_OPROJ_F32: DMX_GEMM_BIG(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 2); break;
       case GEMM_GATEUP: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 4, 4); break;
