@@ -332,6 +332,26 @@ def test_layer_batched_equals_single_requests():
         assert torch.equal(batched[b], single[0])
 
 
+@pytest.mark.parametrize("B,C,P", [(20, 10, 576), (9, 40, 704), (5, 64, 768)])
+def test_layer_large_m_batches_equal_single_requests(B, C, P):
+    """Batches of 256+ padded rows run on the large-M GEMM schedules, whose
+    blocks hold several requests (padded to 16, 48 or 64 rows, so requests
+    straddle 128-row blocks) with one AdaRMS shift row each.  Every request
+    still gets the bits it gets alone on the skinny schedule, and the batch
+    passes the oracle gate on a sample of requests."""
+    wbits = synth.layer_weights(synth.BASE_SEED + 7000 + C)
+    reqs = [synth.make_request(synth.BASE_SEED + 7100 + 31 * C + b, C, P, P // 2, P, 1) for b in range(B)]
+    wd = device_weights(wbits)
+    batched = run_layer(wbits, reqs, wd)
+    for b in sorted({0, B // 2, B - 1}):
+        single = run_layer(wbits, [reqs[b]], wd)
+        assert torch.equal(batched[b], single[0]), f"request {b} of {B} (C={C})"
+    ow = oracle_weights(wbits)
+    rq = reqs[B - 1]
+    ref = orc.layer(f64(rq.x), f64(rq.cond), ow, f64(rq.k_pre[0]), f64(rq.v_pre[0]), rq.mask, rq.pos0)
+    gate(f"large-M batch B={B} C={C} request {B - 1}", from_dev(batched[B - 1]), ref)
+
+
 def test_layer_masked_rows_never_read():
     wl, wbits, reqs = layer_case("c4")
     wd = device_weights(wbits)
