@@ -65,6 +65,14 @@ def _load():
         lib.orc_geglu_mlp.restype = None
         lib.orc_layer.argtypes = [P] * 15 + [ctypes.c_int] * 7 + [i32, dbl, dbl] + [P] * 10
         lib.orc_layer.restype = None
+        lib.orc_rmsnorm.argtypes = [P, P, ctypes.c_int, ctypes.c_int, dbl, P]
+        lib.orc_rmsnorm.restype = None
+        lib.orc_image_merge.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P]
+        lib.orc_image_merge.restype = None
+        lib.orc_prefix_attention.argtypes = [P] * 4 + [ctypes.c_int] * 4 + [dbl, P]
+        lib.orc_prefix_attention.restype = None
+        lib.orc_prefix_layer.argtypes = [P] * 12 + [ctypes.c_int] * 6 + [dbl, dbl, P, P, P]
+        lib.orc_prefix_layer.restype = None
         _lib = lib
     return _lib
 
@@ -190,3 +198,56 @@ def layer(x, cond, w: dict, kp, vp, mask, pos0: int, hq=8, hk=4, d=256,
                       _ptr(mask), C, P, H, I_, hq, hk, d, int(pos0), float(base), float(eps),
                       _ptr(out), *[_ptr(a) for a in pp])
     return (out, pr) if probes else out
+
+
+# ----------------------------------------------------------------------------- prefix side
+def rmsnorm(x, w, eps=1e-6):
+    """Rows of x [T][H] RMS-normalised with the (1 + w) weight."""
+    x, w = _f64(x), _f64(w)
+    T, H = x.shape
+    y = np.empty((T, H))
+    _load().orc_rmsnorm(_ptr(x), _ptr(w), T, H, float(eps), _ptr(y))
+    return y
+
+
+def image_merge(tok, img, idx):
+    """tok [T][H], img [NI][H], idx [T] (row of img, or -1 for the text embedding)."""
+    tok, img = _f64(tok), _f64(img)
+    T, H = tok.shape
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32).reshape(T))
+    out = np.empty((T, H))
+    _load().orc_image_merge(_ptr(tok), _ptr(img), _ptr(idx), T, H, _ptr(out))
+    return out
+
+
+def prefix_attention(q, k, v, valid, scale=None):
+    """q [T][HQ][D]; k, v [HK][T][D]; valid [T] -> ctx [T][HQ][D] (prefix-causal mask)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, HQ_, D_ = q.shape
+    HK_ = k.shape[0]
+    valid = np.ascontiguousarray(np.asarray(valid, dtype=np.uint8).reshape(T))
+    if scale is None:
+        scale = 1.0 / np.sqrt(D_)
+    ctx = np.empty((T, HQ_, D_))
+    _load().orc_prefix_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(valid), T, HQ_, HK_, D_, float(scale), _ptr(ctx))
+    return ctx
+
+
+PREFIX_WEIGHTS = ("w_in", "w_qkv", "q_norm", "k_norm", "w_o", "w_post_attn", "w_pre_ffn", "w_gu", "w_down",
+                  "w_post_ffn")
+
+
+def prefix_layer(x, w: dict, valid, hq=8, hk=4, d=256, base=10000.0, eps=1e-6):
+    """One prefix decoder layer.  x [T][H]; w keyed by PREFIX_WEIGHTS; valid [T].
+    Returns (out [T][H], k [hk][T][d], v [hk][T][d])."""
+    x = _f64(x)
+    T, H = x.shape
+    ww = {k: _f64(w[k]) for k in PREFIX_WEIGHTS}
+    I_ = ww["w_down"].shape[1]
+    valid = np.ascontiguousarray(np.asarray(valid, dtype=np.uint8).reshape(T))
+    out = np.empty((T, H))
+    k = np.empty((hk, T, d))
+    v = np.empty((hk, T, d))
+    _load().orc_prefix_layer(_ptr(x), *[_ptr(ww[n]) for n in PREFIX_WEIGHTS], _ptr(valid), T, H, I_, hq, hk, d,
+                             float(base), float(eps), _ptr(out), _ptr(k), _ptr(v))
+    return out, k, v

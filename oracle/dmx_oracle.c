@@ -2,7 +2,8 @@
  * dmx oracle -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, obviously-correct CPU implementation (float64, nested loops)
- * of the action-expert ("suffix") layer forward that the HIP library computes.
+ * of the action-expert ("suffix") layer forward that the HIP library computes,
+ * and of the prefix (prefill) decoder layer that writes the KV cache it reads.
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
  * load this file's library.  It shares no code, header, table or constant with
  * the HIP path, and never calls into it.
@@ -365,5 +366,137 @@ void orc_layer(const double* x, const double* cond, const double* w_mod1,
   free(x1);
   free(xn2);
   free(mod2);
+  free(pos);
+}
+
+/* ---------------------------------------------------------------------------
+ * Prefix (prefill) side -- the Gemma3-4B decoder layer of the prefix path
+ * named in [Art §2.2]'s shape table (hidden 2560, intermediate 10240,
+ * head_dim 256, 8 Q / 4 KV heads) and its fusion list (image features merged
+ * into the input embeddings; QKV + QK-Norm + RoPE in one pass; norm after the
+ * attention, then the residual), with the prefix mask of [Art §2.3] (the
+ * prefix-causal mask mapping handed to FlexAttention).
+ * ------------------------------------------------------------------------- */
+
+/* RMS norm of each row with the (1 + w) weight convention:
+ *   y[t] = x[t] / sqrt(mean_j x[t][j]^2 + eps) * (1 + w). */
+void orc_rmsnorm(const double* x, const double* w, int T, int H, double eps, double* y) {
+  int t, j;
+  for (t = 0; t < T; ++t) {
+    double ss = 0.0, r;
+    for (j = 0; j < H; ++j) ss += x[(long)t * H + j] * x[(long)t * H + j];
+    r = 1.0 / sqrt(ss / H + eps);
+    for (j = 0; j < H; ++j) y[(long)t * H + j] = x[(long)t * H + j] * r * (1.0 + w[j]);
+  }
+}
+
+/* Image features merged into the input embeddings ([Art §2.2], prefix path):
+ * token t takes image-feature row idx[t] when idx[t] >= 0, else its own text
+ * embedding.  tok [T][H], img [NI][H], out [T][H]. */
+void orc_image_merge(const double* tok, const double* img, const int32_t* idx, int T, int H,
+                     double* out) {
+  int t, j;
+  for (t = 0; t < T; ++t) {
+    const double* src = idx[t] >= 0 ? img + (long)idx[t] * H : tok + (long)t * H;
+    for (j = 0; j < H; ++j) out[(long)t * H + j] = src[j];
+  }
+}
+
+/*
+ * Prefix attention ([Art §2.3]: FlexAttention with the prefix-causal mask
+ * mapping).  Reading: query token i sees key token j exactly when j <= i and
+ * token j is a valid prefix token (valid[j] != 0; the padding of a bucket is
+ * not).  GQA: query head h reads KV head h / (HQ/HK).  Two-pass softmax over
+ * that key set; a query with no visible key gets a zero output.
+ * q, ctx [T][HQ][D]; k, v [HK][T][D]; valid [T].
+ */
+void orc_prefix_attention(const double* q, const double* k, const double* v, const uint8_t* valid,
+                          int T, int HQ, int HK, int D, double scale, double* ctx) {
+  int group = HQ / HK;
+  long ih;
+#pragma omp parallel for schedule(dynamic)
+  for (ih = 0; ih < (long)T * HQ; ++ih) {
+    int i = (int)(ih / HQ), h = (int)(ih % HQ), g = h / group;
+    const double* qi = q + ((long)i * HQ + h) * D;
+    double* out = ctx + ((long)i * HQ + h) * D;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(i + 1));
+    double mx = 0.0, sum = 0.0;
+    int j, d, any = 0;
+    for (d = 0; d < D; ++d) out[d] = 0.0;
+    for (j = 0; j <= i; ++j) {
+      double dot = 0.0;
+      if (!valid[j]) continue;
+      for (d = 0; d < D; ++d) dot += qi[d] * k[((long)g * T + j) * D + d];
+      s[j] = dot * scale;
+      if (!any || s[j] > mx) mx = s[j];
+      any = 1;
+    }
+    if (any) {
+      for (j = 0; j <= i; ++j) {
+        if (!valid[j]) continue;
+        s[j] = exp(s[j] - mx);
+        sum += s[j];
+      }
+      for (j = 0; j <= i; ++j) {
+        if (!valid[j]) continue;
+        for (d = 0; d < D; ++d) out[d] += s[j] / sum * v[((long)g * T + j) * D + d];
+      }
+    }
+    free(s);
+  }
+}
+
+/*
+ * One prefix decoder layer for one request ([Art §2.2] prefix row of the shape
+ * table and fusion list; Gemma3-4B).  Reading (the pages name the pieces, the
+ * order follows the Gemma3 decoder they name):
+ *   xn  = rmsnorm(x; w_in)
+ *   q, k, v = QKV(xn) with QK-RMSNorm and RoPE at positions 0 .. T-1
+ *   ctx = prefix attention(q, k, v; valid), scale 1/sqrt(D)
+ *   x1  = x + rmsnorm(ctx W_o^T; w_post_attn)            (norm after attention, residual)
+ *   xn2 = rmsnorm(x1; w_pre_ffn)
+ *   hdn = gelu_tanh(xn2 W_g^T) * (xn2 W_u^T)             (W_gu rows: gate, then up)
+ *   out = x1 + rmsnorm(hdn W_d^T; w_post_ffn)
+ * k, v [HK][T][D] are the layer's KV cache (what the suffix reads).
+ * x, out [T][H]; valid [T].
+ */
+void orc_prefix_layer(const double* x, const double* w_in, const double* w_qkv, const double* qn_w,
+                      const double* kn_w, const double* w_o, const double* w_post_attn,
+                      const double* w_pre_ffn, const double* w_gu, const double* w_d,
+                      const double* w_post_ffn, const uint8_t* valid, int T, int H, int I, int HQ,
+                      int HK, int D, double base, double eps, double* out, double* k, double* v) {
+  size_t sH = (size_t)T * H, sQ = (size_t)T * HQ * D;
+  double* xn = (double*)malloc(sizeof(double) * sH);
+  double* q = (double*)malloc(sizeof(double) * sQ);
+  double* ctx = (double*)malloc(sizeof(double) * sQ);
+  double* a = (double*)malloc(sizeof(double) * sH);
+  double* x1 = (double*)malloc(sizeof(double) * sH);
+  double* gu = (double*)malloc(sizeof(double) * (size_t)T * 2 * I);
+  double* hdn = (double*)malloc(sizeof(double) * (size_t)T * I);
+  int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)T);
+  int t, n;
+  size_t z;
+  for (t = 0; t < T; ++t) pos[t] = t;
+  orc_rmsnorm(x, w_in, T, H, eps, xn);
+  orc_qkv_qknorm_rope(xn, w_qkv, qn_w, kn_w, T, H, HQ, HK, D, pos, base, eps, q, k, v);
+  orc_prefix_attention(q, k, v, valid, T, HQ, HK, D, 1.0 / sqrt((double)D), ctx);
+  orc_linear(ctx, w_o, T, HQ * D, H, a);
+  orc_rmsnorm(a, w_post_attn, T, H, eps, xn);
+  for (z = 0; z < sH; ++z) x1[z] = x[z] + xn[z];
+  orc_rmsnorm(x1, w_pre_ffn, T, H, eps, xn);
+  orc_linear(xn, w_gu, T, H, 2 * I, gu);
+  for (t = 0; t < T; ++t)
+    for (n = 0; n < I; ++n)
+      hdn[(long)t * I + n] = orc_gelu_tanh(gu[(long)t * 2 * I + n]) * gu[(long)t * 2 * I + I + n];
+  orc_linear(hdn, w_d, T, I, H, a);
+  orc_rmsnorm(a, w_post_ffn, T, H, eps, xn);
+  for (z = 0; z < sH; ++z) out[z] = x1[z] + xn[z];
+  free(xn);
+  free(q);
+  free(ctx);
+  free(a);
+  free(x1);
+  free(gu);
+  free(hdn);
   free(pos);
 }

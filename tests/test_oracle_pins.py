@@ -426,3 +426,118 @@ def test_layer_probes_are_consistent_with_stages():
     np.testing.assert_array_equal(mod1, p["mod1"])
     ctx = orc.attention(p["q"], p["ks"], p["vs"], kp, vp, mask)
     np.testing.assert_array_equal(ctx, p["ctx"])
+
+
+# ---------------------------------------------------------------- prefix side
+def test_rmsnorm_matches_torch_and_closed_form():
+    r = rng(60)
+    x, w = r.standard_normal((5, 24)), 0.3 * r.standard_normal(24)
+    ref = F.rms_norm(t64(x), (24,), weight=1.0 + t64(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(orc.rmsnorm(x, w), ref, rtol=1e-13, atol=1e-14)
+    # a constant row c: every element becomes c / sqrt(c^2 + eps) * (1 + w_j)
+    c = -2.5
+    y = orc.rmsnorm(np.full((1, 8), c), np.arange(8) / 10.0)
+    np.testing.assert_allclose(y[0], c / np.sqrt(c * c + 1e-6) * (1.0 + np.arange(8) / 10.0), rtol=1e-14)
+
+
+def test_image_merge_takes_image_rows_where_indexed():
+    r = rng(61)
+    tok, img = r.standard_normal((7, 5)), r.standard_normal((3, 5))
+    idx = np.array([-1, 0, 1, -1, 2, 2, -1], np.int32)
+    out = orc.image_merge(tok, img, idx)
+    for t in range(7):
+        np.testing.assert_array_equal(out[t], img[idx[t]] if idx[t] >= 0 else tok[t])
+    np.testing.assert_array_equal(orc.image_merge(tok, img, np.full(7, -1, np.int32)), tok)
+
+
+def _prefix_qkv(seed, T=11, hq=4, hk=2, d=8):
+    r = rng(seed)
+    return r.standard_normal((T, hq, d)), r.standard_normal((hk, T, d)), r.standard_normal((hk, T, d))
+
+
+def test_prefix_attention_all_valid_is_causal_sdpa():
+    q, k, v = _prefix_qkv(62)
+    T = q.shape[0]
+    ctx = orc.prefix_attention(q, k, v, np.ones(T, np.uint8))
+    ref = F.scaled_dot_product_attention(t64(q).permute(1, 0, 2).unsqueeze(0), t64(k).unsqueeze(0),
+                                         t64(v).unsqueeze(0), is_causal=True, enable_gqa=True)
+    np.testing.assert_allclose(ctx, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_prefix_attention_masked_keys_match_sdpa_and_edge_rows():
+    q, k, v = _prefix_qkv(63, T=13)
+    T, hq = q.shape[0], q.shape[1]
+    valid = np.ones(T, np.uint8)
+    valid[[0, 4, 5, 12]] = 0
+    ctx = orc.prefix_attention(q, k, v, valid)
+    allow = torch.tril(torch.ones(T, T, dtype=torch.bool)) & torch.from_numpy(valid != 0).unsqueeze(0)
+    rows = [i for i in range(T) if allow[i].any()]
+    ref = F.scaled_dot_product_attention(t64(q).permute(1, 0, 2).unsqueeze(0), t64(k).unsqueeze(0),
+                                         t64(v).unsqueeze(0), attn_mask=allow, enable_gqa=True)
+    ref = ref[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(ctx[rows], ref[rows], rtol=1e-12, atol=1e-13)
+    # token 0 is invalid and sees no key: zero output; token 1 sees only key 1: its value row
+    assert np.all(ctx[0] == 0.0)
+    for h in range(hq):
+        np.testing.assert_allclose(ctx[1, h], v[h // (hq // k.shape[0]), 1], rtol=1e-14)
+    # poisoned invisible keys change nothing
+    k2, v2 = k.copy(), v.copy()
+    k2[:, valid == 0] = np.nan
+    v2[:, valid == 0] = np.inf
+    np.testing.assert_array_equal(orc.prefix_attention(q, k2, v2, valid), ctx)
+
+
+def _tiny_prefix(seed, T=9, H=16, I_=24, hq=4, hk=2, d=8, std=0.3):
+    r = rng(seed)
+    w = {"w_in": std * r.standard_normal(H), "w_qkv": std * r.standard_normal(((hq + 2 * hk) * d, H)),
+         "q_norm": std * r.standard_normal(d), "k_norm": std * r.standard_normal(d),
+         "w_o": std * r.standard_normal((H, hq * d)), "w_post_attn": std * r.standard_normal(H),
+         "w_pre_ffn": std * r.standard_normal(H), "w_gu": std * r.standard_normal((2 * I_, H)),
+         "w_down": std * r.standard_normal((H, I_)), "w_post_ffn": std * r.standard_normal(H)}
+    x = r.standard_normal((T, H))
+    valid = np.ones(T, np.uint8)
+    valid[T - 2:] = 0
+    return w, x, valid, dict(hq=hq, hk=hk, d=d)
+
+
+def torch_prefix_layer(w, x, valid, hq, hk, d, base=10000.0, eps=1e-6):
+    """The prefix layer assembled from torch float64 library routines."""
+    W = {k: t64(v) for k, v in w.items()}
+    X = t64(x)
+    T, H = X.shape
+    xn = F.rms_norm(X, (H,), weight=1.0 + W["w_in"], eps=eps)
+    qkv = F.linear(xn, W["w_qkv"])
+    q = F.rms_norm(qkv[:, :hq * d].reshape(T, hq, d), (d,), weight=1.0 + W["q_norm"], eps=eps)
+    k = F.rms_norm(qkv[:, hq * d:(hq + hk) * d].reshape(T, hk, d), (d,), weight=1.0 + W["k_norm"], eps=eps)
+    v = qkv[:, (hq + hk) * d:].reshape(T, hk, d)
+    pos = torch.arange(T, dtype=torch.float64).reshape(T, 1, 1)
+    q, k = rope_complex(q, pos, base), rope_complex(k, pos, base)
+    allow = torch.tril(torch.ones(T, T, dtype=torch.bool)) & torch.from_numpy(valid != 0).unsqueeze(0)
+    att = F.scaled_dot_product_attention(q.permute(1, 0, 2).unsqueeze(0), k.permute(1, 0, 2).unsqueeze(0),
+                                         v.permute(1, 0, 2).unsqueeze(0), attn_mask=allow, enable_gqa=True)
+    ctx = att[0].permute(1, 0, 2).reshape(T, hq * d)
+    x1 = X + F.rms_norm(F.linear(ctx, W["w_o"]), (H,), weight=1.0 + W["w_post_attn"], eps=eps)
+    xn2 = F.rms_norm(x1, (H,), weight=1.0 + W["w_pre_ffn"], eps=eps)
+    I_ = W["w_down"].shape[1]
+    hdn = F.gelu(F.linear(xn2, W["w_gu"][:I_]), approximate="tanh") * F.linear(xn2, W["w_gu"][I_:])
+    out = x1 + F.rms_norm(F.linear(hdn, W["w_down"]), (H,), weight=1.0 + W["w_post_ffn"], eps=eps)
+    return out.numpy(), k.permute(1, 0, 2).numpy(), v.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("seed", [64, 65])
+def test_prefix_layer_matches_library_composition(seed):
+    w, x, valid, dims = _tiny_prefix(seed)
+    out, k, v = orc.prefix_layer(x, w, valid, **dims)
+    ref, rk, rv = torch_prefix_layer(w, x, valid, **dims)
+    rows = [0] + list(range(1, x.shape[0]))  # every row sees at least itself or key 0
+    np.testing.assert_allclose(out[rows], ref[rows], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(k, rk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(v, rv, rtol=1e-12, atol=1e-13)
+
+
+def test_prefix_layer_zero_projections_is_identity():
+    w, x, valid, dims = _tiny_prefix(66)
+    w["w_o"][:] = 0.0
+    w["w_down"][:] = 0.0
+    out, _, _ = orc.prefix_layer(x, w, valid, **dims)
+    np.testing.assert_array_equal(out, x)
