@@ -282,6 +282,69 @@ void dmx_graph_destroy(dmx_graph* g);
 int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage, int32_t reps, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Prefix (prefill) side: the Gemma3-4B decoder layer of the prefix path
+ * ([Art §2.2] shape table: hidden 2560, intermediate 10240, head_dim 256,
+ * 8 Q / 4 KV heads; its fusion list: image features merged into the input
+ * embeddings, QKV + QK-Norm + RoPE in one pass, a norm after the attention and
+ * the residual), with the prefix-causal mask of [Art §2.3].  One request. */
+#define DMX_PREFIX_INTER 10240
+
+/* Image features merged into the input embeddings ([Art §2.2], prefix path):
+ *   out[t] = img[idx[t]] if 0 <= idx[t] < n_img, tok[t] if idx[t] < 0, and a
+ *   zero row for an index past the image rows.
+ *   tok, out [tokens][hidden] bf16; img [n_img][hidden] bf16; idx [tokens]
+ *   int32 (device).  hidden % 8 == 0.  Enqueued on `stream`. */
+int dmx_image_merge(const dmx_bf16* tok, const dmx_bf16* img, const int32_t* idx, int32_t tokens,
+                    int32_t n_img, int32_t hidden, dmx_bf16* out, void* stream);
+
+/* Prefix attention ([Art §2.3]: the LLM attention under the prefix-causal
+ * mask mapping).  Query token i of head h reads key token j of KV head h / 2
+ * exactly when j <= i and valid[j] != 0 (bucket padding is not valid);
+ * softmax of q.k / 16 over that set; a query with no such key gets zeros.
+ *   q   [tokens][8][256] bf16 (normed and rotated, as dmx_qkv_qknorm_rope
+ *       writes it)
+ *   k, v [4][kv_rows][256] bf16: the layer's cache, tokens at rows 0 ..
+ *       tokens - 1 (kv_rows >= tokens); invalid rows are never read
+ *   valid [tokens] uint8 (device)
+ *   ctx [tokens][8][256] bf16 (out).  tokens <= DMX_MAX_PREFIX. */
+int dmx_prefix_attention(const dmx_bf16* q, const dmx_bf16* k, const dmx_bf16* v, const uint8_t* valid,
+                         int32_t tokens, int32_t kv_rows, dmx_bf16* ctx, void* stream);
+
+/* Weights of one prefix layer (device pointers; matrices tiled by
+ * dmx_pack_weight; norm weights use the (1 + w) convention). */
+typedef struct {
+  const dmx_bf16* w_in;         /* [2560] pre-attention norm */
+  const dmx_bf16* w_qkv;        /* [4096][2560] */
+  const dmx_bf16* q_norm;       /* [256] */
+  const dmx_bf16* k_norm;       /* [256] */
+  const dmx_bf16* w_o;          /* [2560][2048] */
+  const dmx_bf16* w_post_attn;  /* [2560] norm after the attention */
+  const dmx_bf16* w_pre_ffn;    /* [2560] norm before the MLP */
+  const dmx_bf16* w_gu;         /* [20480][2560]: gate rows, then up rows */
+  const dmx_bf16* w_down;       /* [2560][10240] */
+  const dmx_bf16* w_post_ffn;   /* [2560] norm after the MLP */
+} dmx_prefix_layer_weights;
+
+/* Workspace bytes of dmx_prefix_layer_forward for `tokens` tokens (0 if
+ * unsupported). */
+size_t dmx_prefix_workspace_bytes(int32_t tokens);
+
+/* One prefix decoder layer (reading of the pages' pieces in Gemma3 order):
+ *   xn  = rmsnorm(x_in; w_in)
+ *   q, k, v = QKV(xn) + QK-norm + RoPE at positions 0 .. tokens - 1; k and v
+ *             go to rows 0 .. tokens - 1 of k_cache / v_cache [4][kv_rows][256]
+ *   ctx = prefix attention (above) with `valid`
+ *   x1  = x_in + rmsnorm(ctx W_o^T; w_post_attn)
+ *   x_out = x1 + rmsnorm(GEGLU(rmsnorm(x1; w_pre_ffn)) W_down^T; w_post_ffn),
+ *           GEGLU(u) = gelu_tanh(u W_g^T) * (u W_up^T)
+ *   x_in, x_out [tokens][2560] bf16 (may not overlap); valid [tokens] uint8.
+ *   rmsnorm(u; w) = u / sqrt(mean u^2 + 1e-6) * (1 + w).
+ *   1 <= tokens <= kv_rows <= DMX_MAX_PREFIX.  All launches on `stream`. */
+int dmx_prefix_layer_forward(const dmx_prefix_layer_weights* w, const dmx_bf16* x_in, const uint8_t* valid,
+                             int32_t tokens, dmx_bf16* k_cache, dmx_bf16* v_cache, int32_t kv_rows,
+                             dmx_bf16* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 const char* dmx_status_string(int status);
 const char* dmx_last_error_string(void);
 

@@ -36,7 +36,8 @@ EXPORTED = (
     "dmx_adarms_prenorm",
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
     "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_stage_launch",
-    "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill", "dmx_stack_graph_create", "dmx_graph_launch",
+    "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill",
+    "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward", "dmx_stack_graph_create", "dmx_graph_launch",
     "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
 )
 
@@ -55,6 +56,16 @@ class LayerWeights(ctypes.Structure):
 class PrefixKV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("mask", ctypes.c_void_p),
                 ("p_bucket", ctypes.c_int32)]
+
+
+PREFIX_WEIGHTS = ("w_in", "w_qkv", "q_norm", "k_norm", "w_o", "w_post_attn", "w_pre_ffn", "w_gu", "w_down",
+                  "w_post_ffn")
+PREFIX_MATRICES = ("w_qkv", "w_o", "w_gu", "w_down")
+PREFIX_INTER = 10240
+
+
+class PrefixLayerWeights(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in PREFIX_WEIGHTS]
 
 
 class StackDesc(ctypes.Structure):
@@ -96,6 +107,11 @@ def lib():
             "dmx_stack_stage_launch": ([ctypes.POINTER(StackDesc), i32, i32, i32, P], ctypes.c_int),
             "dmx_stack_mod_table_bytes": ([i32, i32, i32], sz),
             "dmx_stack_mod_table_fill": ([ctypes.POINTER(StackDesc), P, P], ctypes.c_int),
+            "dmx_image_merge": ([P, P, P, i32, i32, i32, P, P], ctypes.c_int),
+            "dmx_prefix_attention": ([P, P, P, P, i32, i32, P, P], ctypes.c_int),
+            "dmx_prefix_workspace_bytes": ([i32], sz),
+            "dmx_prefix_layer_forward": ([ctypes.POINTER(PrefixLayerWeights), P, P, i32, P, P, i32, P, P, sz, P],
+                                         ctypes.c_int),
             "dmx_stack_graph_create": ([ctypes.POINTER(StackDesc), P, ctypes.POINTER(P)], ctypes.c_int),
             "dmx_graph_launch": ([P, P], ctypes.c_int),
             "dmx_graph_destroy": ([P], None),
@@ -358,3 +374,60 @@ class Stack:
             self.close()
         except Exception:
             pass
+
+
+# --------------------------------------------------------------------------- prefix (prefill) layer
+def image_merge(tok, img, idx, out=None, stream=None):
+    """tok [T][H] bf16, img [NI][H] bf16, idx [T] int32 -> [T][H] (image row idx[t], or tok[t] for -1)."""
+    T, Hd = tok.shape
+    _want(idx, (T,), torch.int32, "idx")
+    out = torch.empty_like(tok) if out is None else out
+    _check(lib().dmx_image_merge(_p(tok), _p(img) if img.numel() else None, _p(idx), T, img.shape[0], Hd, _p(out),
+                                 _stream(stream)))
+    return out
+
+
+def prefix_attention(q, k, v, valid, ctx=None, stream=None):
+    """q [T][8][256]; k, v [4][kv_rows][256]; valid [T] uint8 -> ctx [T][8][256]."""
+    T = q.shape[0]
+    kv_rows = k.shape[1]
+    _want(q, (T, HQ, D), torch.bfloat16, "q")
+    _want(k, (HK, kv_rows, D), torch.bfloat16, "k")
+    _want(v, (HK, kv_rows, D), torch.bfloat16, "v")
+    _want(valid, (T,), torch.uint8, "valid")
+    ctx = torch.empty_like(q) if ctx is None else ctx
+    _check(lib().dmx_prefix_attention(_p(q), _p(k), _p(v), _p(valid), T, kv_rows, _p(ctx), _stream(stream)))
+    return ctx
+
+
+def pack_prefix_weights(w: dict, stream=None) -> dict:
+    """Tile the matrices of a prefix-layer weight dict (vectors are kept)."""
+    return {k: pack_weight(v, stream) if k in PREFIX_MATRICES else v for k, v in w.items()}
+
+
+def new_prefix_workspace(tokens: int, device="cuda"):
+    n = int(lib().dmx_prefix_workspace_bytes(int(tokens)))
+    if n == 0:
+        raise DmxError(ERR_UNSUPPORTED, f"no prefix workspace for {tokens} tokens")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def prefix_layer_forward(w: dict, x, valid, k_cache, v_cache, ws=None, out=None, stream=None):
+    """One prefix decoder layer.  w: tiled weights keyed by PREFIX_WEIGHTS; x [T][2560];
+    valid [T] uint8; k_cache / v_cache [4][kv_rows][256] (rows 0 .. T-1 written)."""
+    T = x.shape[0]
+    kv_rows = k_cache.shape[1]
+    _want(x, (T, PREFIX_HIDDEN), torch.bfloat16, "x")
+    _want(valid, (T,), torch.uint8, "valid")
+    _want(k_cache, (HK, kv_rows, D), torch.bfloat16, "k_cache")
+    _want(v_cache, (HK, kv_rows, D), torch.bfloat16, "v_cache")
+    _want(w["w_qkv"], ((HQ + 2 * HK) * D, PREFIX_HIDDEN), torch.bfloat16, "w_qkv")
+    _want(w["w_o"], (PREFIX_HIDDEN, HQ * D), torch.bfloat16, "w_o")
+    _want(w["w_gu"], (2 * PREFIX_INTER, PREFIX_HIDDEN), torch.bfloat16, "w_gu")
+    _want(w["w_down"], (PREFIX_HIDDEN, PREFIX_INTER), torch.bfloat16, "w_down")
+    ws = new_prefix_workspace(T, x.device) if ws is None else ws
+    out = torch.empty_like(x) if out is None else out
+    pw = PrefixLayerWeights(*[w[k].data_ptr() for k in PREFIX_WEIGHTS])
+    _check(lib().dmx_prefix_layer_forward(ctypes.byref(pw), _p(x), _p(valid), T, _p(k_cache), _p(v_cache), kv_rows,
+                                          _p(out), _p(ws), ws.numel(), _stream(stream)))
+    return out

@@ -731,6 +731,165 @@ void dmx_graph_destroy(dmx_graph* g) {
   delete g;
 }
 
+// ---------------------------------------------------------------------------
+// Prefix (prefill) layer.  Workspace: the pieces of one layer at TP = tokens
+// padded to 16 rows (tiled activations, fp32 projection outputs).
+namespace {
+struct PrefixLayout {
+  size_t xn, raw, q, ctx, y, x1, xn2, h, pos, total;
+  int TP;
+};
+
+bool prefix_layout(int T, PrefixLayout& L) {
+  if (T < 1 || T > DMX_MAX_PREFIX) return false;
+  const size_t TP = padded_tokens(T);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  L.TP = (int)TP;
+  L.xn = take(TP * kPrefixHidden * 2);        // tiled rmsnorm(x; w_in)
+  L.raw = take(TP * kQKV * 4);                // fp32 QKV projection
+  L.q = take((size_t)T * kHQ * kD * 2);        // row-major q
+  L.ctx = take(TP * kHQ * kD * 2);            // tiled attention output
+  L.y = take(TP * kPrefixHidden * 4);         // fp32 O-projection / down output
+  L.x1 = take(TP * kPrefixHidden * 4);        // fp32 x1
+  L.xn2 = take(TP * kPrefixHidden * 2);       // tiled rmsnorm(x1; w_pre_ffn)
+  L.h = take(TP * kPrefixInter * 2);          // tiled GEGLU output
+  L.pos = take(16);                           // position of token 0 (zero)
+  L.total = off;
+  return true;
+}
+
+int check_prefix_weights(const char* fn, const dmx_prefix_layer_weights* w) {
+  if (w == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: weights struct is null", fn);
+  DMX_REQUIRE_PTR(w->w_in);
+  DMX_REQUIRE_PTR(w->w_qkv);
+  DMX_REQUIRE_PTR(w->q_norm);
+  DMX_REQUIRE_PTR(w->k_norm);
+  DMX_REQUIRE_PTR(w->w_o);
+  DMX_REQUIRE_PTR(w->w_post_attn);
+  DMX_REQUIRE_PTR(w->w_pre_ffn);
+  DMX_REQUIRE_PTR(w->w_gu);
+  DMX_REQUIRE_PTR(w->w_down);
+  DMX_REQUIRE_PTR(w->w_post_ffn);
+  return DMX_OK;
+}
+
+int enq_prefix_layer(const dmx_prefix_layer_weights* w, const dmx_bf16* x_in, const uint8_t* valid, int T,
+                     dmx_bf16* kc, dmx_bf16* vc, int kv_rows, dmx_bf16* x_out, void* ws, const PrefixLayout& L,
+                     hipStream_t s) {
+  uint16_t* xn = at<uint16_t>(ws, L.xn);
+  float* raw = at<float>(ws, L.raw);
+  uint16_t* q = at<uint16_t>(ws, L.q);
+  uint16_t* ctx = at<uint16_t>(ws, L.ctx);
+  float* y = at<float>(ws, L.y);
+  float* x1 = at<float>(ws, L.x1);
+  uint16_t* xn2 = at<uint16_t>(ws, L.xn2);
+  uint16_t* h = at<uint16_t>(ws, L.h);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  GemmArgs g = gemm_args();
+  g.M = L.TP;
+  g.T = T;
+  g.TP = L.TP;
+  // xn -> QKV (fp32) -> QK-norm + RoPE: q, and k / v into the cache
+  DMX_TRY(hip_check(launch_prefix_rmsnorm(x_in, w->w_in, T, xn, s), "prefix norm launch"));
+  DMX_TRY(hip_check(launch_fill_zero(pos, 16, s), "position fill"));
+  GemmArgs a = g;
+  gemm_config(GEMM_QKV2560, a);
+  a.A = xn;
+  a.W = w->w_qkv;
+  a.out_f32 = raw;
+  a.ldo = kQKV;
+  DMX_TRY(hip_check(launch_gemm(GEMM_QKV2560, a, s), "prefix QKV launch"));
+  DMX_TRY(hip_check(launch_qknorm_rope(raw, w->q_norm, w->k_norm, pos, 10000.0f, 1, T, L.TP, q, kc, vc, kv_rows, 0, s),
+                    "prefix QK-norm/RoPE launch"));
+  DMX_TRY(hip_check(launch_prefix_attention(q, kc, vc, valid, T, kv_rows, ctx, true, s), "prefix attention launch"));
+  // x1 = x + rmsnorm(ctx W_o^T); xn2 = rmsnorm(x1)
+  a = g;
+  gemm_config(GEMM_PRE_OPROJ, a);
+  a.A = ctx;
+  a.W = w->w_o;
+  a.out_f32 = y;
+  a.ldo = kPrefixHidden;
+  DMX_TRY(hip_check(launch_gemm(GEMM_PRE_OPROJ, a, s), "prefix O-projection launch"));
+  DMX_TRY(hip_check(launch_prefix_post_norm(y, nullptr, x_in, w->w_post_attn, w->w_pre_ffn, T, x1, xn2, nullptr, s),
+                    "prefix post-attention norm launch"));
+  // x_out = x1 + rmsnorm(GEGLU(xn2) W_down^T)
+  a = g;
+  gemm_config(GEMM_PRE_GATEUP, a);
+  a.A = xn2;
+  a.W = w->w_gu;
+  a.out_pk = h;
+  a.ldo = kPrefixInter;
+  DMX_TRY(hip_check(launch_gemm(GEMM_PRE_GATEUP, a, s), "prefix gate-up launch"));
+  a = g;
+  gemm_config(GEMM_PRE_DOWN, a);
+  a.A = h;
+  a.W = w->w_down;
+  a.out_f32 = y;
+  a.ldo = kPrefixHidden;
+  DMX_TRY(hip_check(launch_gemm(GEMM_PRE_DOWN, a, s), "prefix down launch"));
+  return hip_check(launch_prefix_post_norm(y, x1, nullptr, w->w_post_ffn, nullptr, T, nullptr, nullptr, x_out, s),
+                   "prefix post-MLP norm launch");
+}
+}  // namespace
+
+int dmx_image_merge(const dmx_bf16* tok, const dmx_bf16* img, const int32_t* idx, int32_t tokens, int32_t n_img,
+                    int32_t hidden, dmx_bf16* out, void* stream) {
+  const char* fn = "dmx_image_merge";
+  DMX_REQUIRE_PTR(tok);
+  DMX_REQUIRE_PTR(out);
+  if (idx == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: idx is null", fn);
+  if (tokens < 1 || hidden < 8 || hidden % 8 != 0 || n_img < 0 || (long)tokens * hidden > (1L << 31))
+    return fail(DMX_ERR_UNSUPPORTED, "%s: tokens %d / hidden %d / n_img %d unsupported", fn, tokens, hidden, n_img);
+  if (n_img > 0) DMX_REQUIRE_PTR(img);
+  return hip_check(launch_image_merge(tok, img, idx, tokens, n_img, hidden, out, (hipStream_t)stream),
+                   "image merge launch");
+}
+
+int dmx_prefix_attention(const dmx_bf16* q, const dmx_bf16* k, const dmx_bf16* v, const uint8_t* valid,
+                         int32_t tokens, int32_t kv_rows, dmx_bf16* ctx, void* stream) {
+  const char* fn = "dmx_prefix_attention";
+  DMX_REQUIRE_PTR(q);
+  DMX_REQUIRE_PTR(k);
+  DMX_REQUIRE_PTR(v);
+  DMX_REQUIRE_PTR(ctx);
+  if (valid == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: valid is null", fn);
+  if (tokens < 1 || tokens > DMX_MAX_PREFIX || kv_rows < tokens || kv_rows > DMX_MAX_PREFIX)
+    return fail(DMX_ERR_UNSUPPORTED, "%s: tokens %d / kv_rows %d unsupported", fn, tokens, kv_rows);
+  return hip_check(launch_prefix_attention(q, k, v, valid, tokens, kv_rows, ctx, false, (hipStream_t)stream),
+                   "prefix attention launch");
+}
+
+size_t dmx_prefix_workspace_bytes(int32_t tokens) {
+  PrefixLayout L;
+  return prefix_layout(tokens, L) ? L.total : 0;
+}
+
+int dmx_prefix_layer_forward(const dmx_prefix_layer_weights* w, const dmx_bf16* x_in, const uint8_t* valid,
+                             int32_t tokens, dmx_bf16* k_cache, dmx_bf16* v_cache, int32_t kv_rows, dmx_bf16* x_out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "dmx_prefix_layer_forward";
+  DMX_TRY(check_prefix_weights(fn, w));
+  DMX_REQUIRE_PTR(x_in);
+  DMX_REQUIRE_PTR(k_cache);
+  DMX_REQUIRE_PTR(v_cache);
+  DMX_REQUIRE_PTR(x_out);
+  if (valid == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: valid is null", fn);
+  PrefixLayout L;
+  if (!prefix_layout(tokens, L) || kv_rows < tokens || kv_rows > DMX_MAX_PREFIX)
+    return fail(DMX_ERR_UNSUPPORTED, "%s: tokens %d / kv_rows %d unsupported", fn, tokens, kv_rows);
+  if (x_in == x_out) return fail(DMX_ERR_INVALID_ARG, "%s: x_in and x_out overlap", fn);
+  if (ws == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: ws is null", fn);
+  if (!aligned16(ws)) return fail(DMX_ERR_MISALIGNED, "%s: ws is not 16-byte aligned", fn);
+  if (ws_bytes < L.total)
+    return fail(DMX_ERR_WORKSPACE, "%s: workspace %zu bytes, needs %zu", fn, ws_bytes, L.total);
+  return enq_prefix_layer(w, x_in, valid, tokens, k_cache, v_cache, kv_rows, x_out, ws, L, (hipStream_t)stream);
+}
+
 const char* dmx_status_string(int status) {
   switch (status) {
     case DMX_OK: return "ok";

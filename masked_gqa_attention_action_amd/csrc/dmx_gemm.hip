@@ -918,6 +918,9 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
     case GEMM_GATEUP_MOD: a.ntiles = kI / 16; a.K = kH; a.wtile_up = kI / 16; break;
     case GEMM_DOWN: a.ntiles = kH / 16; a.K = kI; break;
     case GEMM_DOWN_F32RES: a.ntiles = kH / 16; a.K = kI; break;
+    case GEMM_PRE_OPROJ: a.ntiles = kPrefixHidden / 16; a.K = kHQ * kD; break;
+    case GEMM_PRE_GATEUP: a.ntiles = kPrefixInter / 16; a.K = kPrefixHidden; a.wtile_up = kPrefixInter / 16; break;
+    case GEMM_PRE_DOWN: a.ntiles = kPrefixHidden / 16; a.K = kPrefixInter; break;
   }
   return a.ntiles;
 }
@@ -937,6 +940,12 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
 constexpr int kBigGemmRows = 256;
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
+  switch (kind) {  // prefix layer: the large-M schedule at every row count
+    case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 4, 16, A_GLOBAL, 4); return hipGetLastError();
+    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 20, A_GLOBAL, 4); return hipGetLastError();
+    case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 4, 80, A_GLOBAL, 4); return hipGetLastError();
+    default: break;
+  }
   if (a.M >= kBigGemmRows) {
     switch (kind) {
       case GEMM_QKV1024: DMX_GEMM_LDS(EPI_F32, 16, 4, 8, A_GLOBAL, 4); break;

@@ -68,6 +68,11 @@ enum GemmKind {
   GEMM_GATEUP_MOD = 7,      // as above with the AdaRMS prenorm of x1 fused (A = bf16(x1 * (1 + scale)))
   GEMM_DOWN = 8,            // N = 1024, K = 4096, gated residual (bf16 -> bf16)
   GEMM_DOWN_F32RES = 9,     // as GEMM_DOWN, fp32 residual input
+  // prefix (prefill) layer, hidden 2560, intermediate 10240; any row count
+  // runs on the large-M schedule
+  GEMM_PRE_OPROJ = 20,      // N = 2560, K = 2048, fp32 out
+  GEMM_PRE_GATEUP = 21,     // N = 2 x 10240, K = 2560, GEGLU (h tiled bf16)
+  GEMM_PRE_DOWN = 22,       // N = 2560, K = 10240, fp32 out
 };
 int gemm_config(GemmKind kind, GemmArgs& a);
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s);
@@ -129,6 +134,18 @@ void attn_config(int B, int C, int P, AttnArgs& a);
 hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s);  // partial + combine
 hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s);
+// prefix (prefill) layer pieces, hidden kPrefixHidden, one request
+constexpr int kPrefixHidden = 2560, kPrefixInter = 10240;
+hipError_t launch_prefix_rmsnorm(const uint16_t* x, const uint16_t* w, int T, uint16_t* out, hipStream_t s);
+hipError_t launch_prefix_post_norm(const float* y, const float* resid_f32, const uint16_t* resid_bf16,
+                                   const uint16_t* w_post, const uint16_t* w_next, int T, float* x1_out,
+                                   uint16_t* xn_tiled, uint16_t* out_bf16, hipStream_t s);
+hipError_t launch_image_merge(const uint16_t* tok, const uint16_t* img, const int32_t* idx, int T, int n_img,
+                              int hidden, uint16_t* out, hipStream_t s);
+// prefix attention of the prefill: q row-major [T][8][256]; k, v [4][kv_rows][256];
+// valid [T]; ctx tiled [TP][2048] (ctx_tiled) or row-major [T][8][256]
+hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,
+                                   int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, hipStream_t s);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 

@@ -197,3 +197,33 @@ def prefix_qkv_inputs(seed: int, tokens: int = 2048, hidden: int = 2560, hq=HQ, 
         "q_norm": _normal_bf16(rng, (d,), std),
         "k_norm": _normal_bf16(rng, (d,), std),
     }
+
+
+# --------------------------------------------------------------------------
+# prefix (prefill) layer inputs, Gemma3-4B shape of the prefix path
+# --------------------------------------------------------------------------
+PREFIX_H, PREFIX_I = 2560, 10240
+
+
+def prefix_layer_weights(seed: int, h=PREFIX_H, i=PREFIX_I, hq=HQ, hk=HK, d=D, std=WEIGHT_STD) -> dict:
+    """One prefix decoder layer's weights as bf16 bits: matrices N(0, std),
+    norm weights N(0, std) (the (1 + w) convention)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = {"w_in": (h,), "w_qkv": ((hq + 2 * hk) * d, h), "q_norm": (d,), "k_norm": (d,),
+              "w_o": (h, hq * d), "w_post_attn": (h,), "w_pre_ffn": (h,), "w_gu": (2 * i, h),
+              "w_down": (h, i), "w_post_ffn": (h,)}
+    return {k: _normal_bf16(rng, s, std) for k, s in shapes.items()}
+
+
+def prefix_inputs(seed: int, tokens: int, valid_len: int, hole_p: float = 0.0, h=PREFIX_H):
+    """Prefix-layer input rows x [tokens][h] ~ N(0, 1) (bf16 bits) and the key
+    validity [tokens] (uint8): tokens past valid_len are bucket padding, and a
+    fraction hole_p of the others are invisible too (token 0 stays valid)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _normal_bf16(rng, (tokens, h), 1.0)
+    valid = (np.arange(tokens) < valid_len).astype(np.uint8)
+    if hole_p > 0:
+        holes = rng.random(tokens) < hole_p
+        holes[0] = False
+        valid[holes] = 0
+    return x, valid
