@@ -244,6 +244,45 @@ def prefix_qkv_case():
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def prefix_layer_case(T=2048, valid_len=1936, hole_p=0.02):
+    """One prefix (prefill) decoder layer, hidden 2560 / intermediate 10240,
+    at the 2048-token bucket with padding and invisible tokens; and its
+    prefix-causal attention alone.  us per call against the bf16 MFMA peak
+    (the GEMMs dominate) and the HBM peak (weights, activations, K/V)."""
+    import torch
+    import masked_gqa_attention_action_amd as dmx
+    from masked_gqa_attention_action_amd import synth
+    PH, PI = 2560, 10240
+    wd = dmx.pack_prefix_weights({k: dev(v) for k, v in synth.prefix_layer_weights(synth.BASE_SEED + 9500).items()})
+    xb, valid_np = synth.prefix_inputs(synth.BASE_SEED + 9800, T, valid_len, hole_p)
+    x, valid = dev(xb), dev(valid_np, raw=True)
+    kc = torch.empty((HK, T, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    ws = dmx.new_prefix_workspace(T)
+    out = torch.empty_like(x)
+    us = time_calls(lambda s: dmx.prefix_layer_forward(wd, x, valid, kc, vc, ws=ws, out=out, stream=s),
+                    torch.cuda.Stream(), reps=5)
+    assert torch.isfinite(out.float()).all(), "non-finite prefix layer output"
+    # key j is visible to query i when j <= i and j is valid
+    pairs = int(np.cumsum(valid_np.astype(np.int64)).sum())
+    attn_flops = 4 * HQ * D * pairs
+    w_elems = (HQ + 2 * HK) * D * PH + PH * HQ * D + 2 * PI * PH + PH * PI
+    flops = 2 * T * w_elems + attn_flops
+    nbytes = w_elems * 2 + 5 * PH * 2 + 2 * T * PH * 2 + 2 * HK * T * D * 2
+    q = torch.randn((T, HQ, D), device="cuda").to(torch.bfloat16)
+    ctx = torch.empty_like(q)
+    us_attn = time_calls(lambda s: dmx.prefix_attention(q, kc, vc, valid, ctx=ctx, stream=s), torch.cuda.Stream())
+    attn_bytes = 2 * T * HQ * D * 2 + 2 * HK * T * D * 2 + T
+    return {"workload": f"prefix decoder layer, hidden 2560, {T} tokens ({int(valid_np.sum())} valid)",
+            "us": round(us, 2), "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "attention": {"us": round(us_attn, 2), "flops": attn_flops,
+                          "tflops": round(attn_flops / (us_attn * 1e-6) / 1e12, 1),
+                          "mfma_frac": round(attn_flops / (us_attn * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "algorithmic_bytes": attn_bytes}}
+
+
 def cpu_baseline(wl, wbits, rq, conds, n_steps_sample):
     """Time the float64 oracle on the host for whole denoise steps (all layers)
     of the same workload; report ms per step."""
@@ -364,6 +403,7 @@ def main():
         for name in ("c2", "c4", "c5"):
             extras[f"layer_{name}"] = layer_case(name)
         extras["prefix_qkv_c4"] = prefix_qkv_case()
+        extras["prefix_layer_2048"] = prefix_layer_case()
         torch.cuda.synchronize()
     # a plain 256 MiB device copy: the reference dispatch for HBM byte counters
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
