@@ -227,3 +227,32 @@ def prefix_inputs(seed: int, tokens: int, valid_len: int, hole_p: float = 0.0, h
         holes[0] = False
         valid[holes] = 0
     return x, valid
+
+
+# --------------------------------------------------------------------------
+# denoise sampler
+# --------------------------------------------------------------------------
+ACTION_DIM = 32
+
+
+def sampler_weights(seed: int, a=ACTION_DIM, h=H) -> dict:
+    """Sampler weights as bf16 bits, scaled so every stage sees O(1) values:
+    W_in [h][a] N(0, 1/a) (unit-variance noise in, O(1) rows out); the time
+    MLP's W_t1, W_t2 [h][h] N(0, 0.05^2) (conditioning of O(1), like the
+    layers' cond); the final modulation W_fmod [2h][h] N(0, 0.02^2) like the
+    layers' W_mod; W_out [a][h] N(0, 1/h) (O(1) velocity from a normalised
+    row); biases N(0, 0.02^2)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    spec = {"w_in": ((h, a), 1.0 / math.sqrt(a)), "b_in": ((h,), WEIGHT_STD),
+            "w_t1": ((h, h), 0.05), "b_t1": ((h,), WEIGHT_STD),
+            "w_t2": ((h, h), 0.05), "b_t2": ((h,), WEIGHT_STD),
+            "w_fmod": ((2 * h, h), WEIGHT_STD), "b_fmod": ((2 * h,), WEIGHT_STD),
+            "w_out": ((a, h), 1.0 / math.sqrt(h)), "b_out": ((a,), WEIGHT_STD)}
+    return {k: _normal_bf16(rng, s, std) for k, (s, std) in spec.items()}
+
+
+def sampler_noise(seed: int, batch: int, chunk: int, a=ACTION_DIM) -> np.ndarray:
+    """Initial action noise [batch][chunk][a], float32 N(0, 1) (the draw the
+    sampler starts from is an input of both sides)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.standard_normal((batch, chunk, a)).astype(np.float32)

@@ -73,6 +73,18 @@ def _load():
         lib.orc_prefix_attention.restype = None
         lib.orc_prefix_layer.argtypes = [P] * 12 + [ctypes.c_int] * 6 + [dbl, dbl, P, P, P]
         lib.orc_prefix_layer.restype = None
+        lib.orc_time_embedding.argtypes = [dbl, ctypes.c_int, P]
+        lib.orc_time_embedding.restype = None
+        lib.orc_swish.argtypes = [dbl]
+        lib.orc_swish.restype = dbl
+        lib.orc_time_mlp.argtypes = [P] * 5 + [ctypes.c_int, P]
+        lib.orc_time_mlp.restype = None
+        lib.orc_action_in.argtypes = [P, P, P] + [ctypes.c_int] * 3 + [P]
+        lib.orc_action_in.restype = None
+        lib.orc_final_velocity.argtypes = [P] * 6 + [ctypes.c_int] * 3 + [dbl, P]
+        lib.orc_final_velocity.restype = None
+        lib.orc_euler.argtypes = [P, P, ctypes.c_long, dbl]
+        lib.orc_euler.restype = None
         _lib = lib
     return _lib
 
@@ -251,3 +263,89 @@ def prefix_layer(x, w: dict, valid, hq=8, hk=4, d=256, base=10000.0, eps=1e-6):
     _load().orc_prefix_layer(_ptr(x), *[_ptr(ww[n]) for n in PREFIX_WEIGHTS], _ptr(valid), T, H, I_, hq, hk, d,
                              float(base), float(eps), _ptr(out), _ptr(k), _ptr(v))
     return out, k, v
+
+
+# ----------------------------------------------------------------------------- denoise sampler
+SAMPLER_WEIGHTS = ("w_in", "b_in", "w_t1", "b_t1", "w_t2", "b_t2", "w_fmod", "b_fmod", "w_out", "b_out")
+
+
+def step_time(k: int, n_steps: int) -> float:
+    """t_k = 1 - k / n: step 0 starts from noise at t = 1."""
+    return 1.0 - k / n_steps
+
+
+def time_embedding(t: float, h: int = 1024):
+    out = np.empty(h)
+    _load().orc_time_embedding(float(t), int(h), _ptr(out))
+    return out
+
+
+def swish(z: float) -> float:
+    return float(_load().orc_swish(float(z)))
+
+
+def time_mlp(temb, w1, b1, w2, b2):
+    """cond = swish(W2 swish(W1 temb + b1) + b2)."""
+    temb, w1, b1, w2, b2 = (_f64(a) for a in (temb, w1, b1, w2, b2))
+    H = temb.size
+    cond = np.empty(H)
+    _load().orc_time_mlp(_ptr(temb), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), H, _ptr(cond))
+    return cond
+
+
+def time_condition(t: float, sw: dict):
+    """Conditioning vector of diffusion time t from the sampler weights."""
+    H = sw["b_t1"].size
+    return time_mlp(time_embedding(t, H), sw["w_t1"], sw["b_t1"], sw["w_t2"], sw["b_t2"])
+
+
+def action_in(a, w_in, b_in):
+    """a [C][A] -> x [C][H] = a W_in^T + b_in."""
+    a, w_in, b_in = _f64(a), _f64(w_in), _f64(b_in)
+    C, A = a.shape
+    H = w_in.shape[0]
+    x = np.empty((C, H))
+    _load().orc_action_in(_ptr(a), _ptr(w_in), _ptr(b_in), C, A, H, _ptr(x))
+    return x
+
+
+def final_velocity(x, cond, w_f, b_f, w_out, b_out, eps=1e-6):
+    """Final AdaRMS norm of x [C][H] with [scale | shift] = W_f cond + b_f, then
+    v = xf W_out^T + b_out -> [C][A]."""
+    x, cond, w_f, b_f, w_out, b_out = (_f64(a) for a in (x, cond, w_f, b_f, w_out, b_out))
+    C, H = x.shape
+    A = w_out.shape[0]
+    v = np.empty((C, A))
+    _load().orc_final_velocity(_ptr(x), _ptr(cond), _ptr(w_f), _ptr(b_f), _ptr(w_out), _ptr(b_out), C, H, A,
+                               float(eps), _ptr(v))
+    return v
+
+
+def euler(a, v, dt: float):
+    a = _f64(a).copy()
+    v = _f64(v)
+    _load().orc_euler(_ptr(a), _ptr(v), a.size, float(dt))
+    return a
+
+
+def sampler_step(a, k: int, n_steps: int, sw: dict, layers, kps, vps, mask, pos0: int, **dims):
+    """One denoising step k of n for one request: a [C][A] -> (next a, v).
+    layers: per-layer weight dicts; kps / vps: per-layer [HK][P][D] caches;
+    dims: head counts / size passed to layer()."""
+    cond = time_condition(step_time(k, n_steps), sw)
+    x = action_in(a, sw["w_in"], sw["b_in"])
+    for w, kp, vp in zip(layers, kps, vps):
+        x = layer(x, cond, w, kp, vp, mask, pos0, **dims)
+    v = final_velocity(x, cond, sw["w_fmod"], sw["b_fmod"], sw["w_out"], sw["b_out"])
+    return euler(a, v, -1.0 / n_steps), v
+
+
+def sampler(noise, n_steps: int, sw: dict, layers, kps, vps, mask, pos0: int, **dims):
+    """The whole denoising run for one request from noise [C][A]; returns the
+    actions after every step, [n_steps][C][A]."""
+    a = _f64(noise)
+    traj = []
+    for k in range(n_steps):
+        a, _ = sampler_step(a, k, n_steps, sw, layers, kps, vps, mask, pos0, **dims)
+        traj.append(a)
+    return np.stack(traj)

@@ -3,7 +3,11 @@
  *
  * A plain, slow, obviously-correct CPU implementation (float64, nested loops)
  * of the action-expert ("suffix") layer forward that the HIP library computes,
- * and of the prefix (prefill) decoder layer that writes the KV cache it reads.
+ * of the prefix (prefill) decoder layer that writes the KV cache it reads, and
+ * of the denoise sampler around the layer stack (time conditioning, action
+ * projections, Euler steps; readings throughout, as the pages give no formula:
+ * parity of those readings is unpinned against the pages and pinned by
+ * closed forms and library routines only).
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
  * load this file's library.  It shares no code, header, table or constant with
  * the HIP path, and never calls into it.
@@ -499,4 +503,86 @@ void orc_prefix_layer(const double* x, const double* w_in, const double* w_qkv, 
   free(gu);
   free(hdn);
   free(pos);
+}
+
+/* ---------------------------------------------------------------------------
+ * Denoise sampler around the action-expert stack.  The pages describe the
+ * action chunk as decoded by diffusion in a fixed number of steps ([Art §1],
+ * [Art §4]; [Guide §2], the diffusion step count) and give none of the
+ * sampler's formulas.  Every step below is therefore a reading, the plainest
+ * one for a flow-matching action expert with AdaRMS time conditioning:
+ *   t_k = 1 - k / n, k = 0 .. n-1, from noise (t = 1) to data (t = 0);
+ *   temb(t)[i] = sin(1000 t w_i), temb(t)[H/2 + i] = cos(1000 t w_i),
+ *       w_i = 10000^(-i / (H/2));
+ *   cond(t) = swish(W_t2 swish(W_t1 temb(t) + b_t1) + b_t2),
+ *       swish(z) = z / (1 + exp(-z));
+ *   x = a W_in^T + b_in for each chunk token (action in-projection);
+ *   x <- the action-expert layers run with cond(t_k);
+ *   [scale | shift] = W_f cond + b_f, xf = x / sqrt(mean x^2 + eps) (1 + scale) + shift;
+ *   v = xf W_out^T + b_out (the velocity);
+ *   a <- a + dt v, dt = -1 / n (one Euler step of the flow ODE).
+ */
+
+/* temb(t), H values (sin half, then cos half). */
+void orc_time_embedding(double t, int H, double* out) {
+  int half = H / 2, i;
+  for (i = 0; i < half; ++i) {
+    double w = pow(10000.0, -(double)i / half);
+    out[i] = sin(1000.0 * t * w);
+    out[half + i] = cos(1000.0 * t * w);
+  }
+}
+
+double orc_swish(double z) { return z / (1.0 + exp(-z)); }
+
+/* cond = swish(W_t2 swish(W_t1 temb + b_t1) + b_t2); W_t1, W_t2 [H][H]. */
+void orc_time_mlp(const double* temb, const double* w1, const double* b1, const double* w2,
+                  const double* b2, int H, double* cond) {
+  double* h1 = (double*)malloc(sizeof(double) * (size_t)H);
+  int j;
+  orc_linear(temb, w1, 1, H, H, h1);
+  for (j = 0; j < H; ++j) h1[j] = orc_swish(h1[j] + b1[j]);
+  orc_linear(h1, w2, 1, H, H, cond);
+  for (j = 0; j < H; ++j) cond[j] = orc_swish(cond[j] + b2[j]);
+  free(h1);
+}
+
+/* x[c] = W_in a[c] + b_in; a [C][A], W_in [H][A] -> x [C][H]. */
+void orc_action_in(const double* a, const double* w_in, const double* b_in, int C, int A, int H,
+                   double* x) {
+  int c, j;
+  orc_linear(a, w_in, C, A, H, x);
+  for (c = 0; c < C; ++c)
+    for (j = 0; j < H; ++j) x[(long)c * H + j] += b_in[j];
+}
+
+/* Velocity of the chunk: the final AdaRMS norm (modulation [scale | shift] =
+ * W_f cond + b_f, W_f [2H][H]) of the expert's output x [C][H], then
+ * v = xf W_out^T + b_out, W_out [A][H] -> v [C][A]. */
+void orc_final_velocity(const double* x, const double* cond, const double* w_f, const double* b_f,
+                        const double* w_out, const double* b_out, int C, int H, int A, double eps,
+                        double* v) {
+  double* m = (double*)malloc(sizeof(double) * 2 * (size_t)H);
+  double* xf = (double*)malloc(sizeof(double) * (size_t)C * H);
+  int c, j;
+  orc_linear(cond, w_f, 1, H, 2 * H, m);
+  for (j = 0; j < 2 * H; ++j) m[j] += b_f[j];
+  for (c = 0; c < C; ++c) {
+    const double* xr = x + (long)c * H;
+    double ss = 0.0, r;
+    for (j = 0; j < H; ++j) ss += xr[j] * xr[j];
+    r = 1.0 / sqrt(ss / H + eps);
+    for (j = 0; j < H; ++j) xf[(long)c * H + j] = xr[j] * r * (1.0 + m[j]) + m[H + j];
+  }
+  orc_linear(xf, w_out, C, H, A, v);
+  for (c = 0; c < C; ++c)
+    for (j = 0; j < A; ++j) v[(long)c * A + j] += b_out[j];
+  free(m);
+  free(xf);
+}
+
+/* a <- a + dt v over n values (one Euler step). */
+void orc_euler(double* a, const double* v, long n, double dt) {
+  long i;
+  for (i = 0; i < n; ++i) a[i] += dt * v[i];
 }

@@ -541,3 +541,141 @@ def test_prefix_layer_zero_projections_is_identity():
     w["w_down"][:] = 0.0
     out, _, _ = orc.prefix_layer(x, w, valid, **dims)
     np.testing.assert_array_equal(out, x)
+
+
+# ---------------------------------------------------------------- denoise sampler
+def test_time_embedding_closed_forms():
+    H = 16
+    assert np.array_equal(orc.time_embedding(0.0, H), np.r_[np.zeros(8), np.ones(8)])
+    for t in (0.1, 0.37, 1.0):
+        e = orc.time_embedding(t, H)
+        np.testing.assert_allclose(e[:8] ** 2 + e[8:] ** 2, 1.0, rtol=1e-15)
+        # frequency 1 at i = 0, 10000^(-1/2) at i = H/4: angles 1000 t and 10 t
+        assert e[0] == pytest.approx(math.sin(1000.0 * t), abs=1e-12)
+        assert e[4] == pytest.approx(math.sin(10.0 * t), abs=1e-13)
+        assert e[12] == pytest.approx(math.cos(10.0 * t), abs=1e-13)
+        # frequencies fall geometrically: angle(i) / angle(i + 1) = 10000^(1/8)
+        assert e[8 + 7] == pytest.approx(math.cos(1000.0 * t * 10000.0 ** (-7 / 8)), abs=1e-13)
+
+
+def test_swish_matches_silu_and_identities():
+    z = np.linspace(-30.0, 30.0, 61) + 0.123
+    ref = F.silu(t64(z)).numpy()
+    np.testing.assert_allclose([orc.swish(v) for v in z], ref, rtol=1e-14, atol=1e-300)
+    for v in (0.3, 1.7, 5.0, 12.0):
+        assert orc.swish(v) - orc.swish(-v) == pytest.approx(v, rel=1e-14)  # z (s(z) + s(-z)) = z
+    assert orc.swish(0.0) == 0.0
+    assert orc.swish(math.log(3.0)) == pytest.approx(0.75 * math.log(3.0), rel=1e-15)  # sigmoid(ln 3) = 3/4
+
+
+def test_time_mlp_against_torch_and_permutation():
+    r = rng(70)
+    H = 12
+    w1, w2 = r.standard_normal((H, H)), r.standard_normal((H, H))
+    b1, b2 = r.standard_normal(H), r.standard_normal(H)
+    temb = r.standard_normal(H)
+    ref = F.silu(F.linear(F.silu(F.linear(t64(temb), t64(w1), t64(b1))), t64(w2), t64(b2))).numpy()
+    np.testing.assert_allclose(orc.time_mlp(temb, w1, b1, w2, b2), ref, rtol=1e-13, atol=1e-14)
+    # permutation weights (a 12-cycle, not an involution): row j picks temb[j + 1];
+    # a transposed operand would pick temb[j - 1]
+    P = np.zeros((H, H))
+    P[np.arange(H), (np.arange(H) + 1) % H] = 1.0
+    z = np.zeros(H)
+    cond = orc.time_mlp(temb, P, z, np.eye(H), z)
+    want = [orc.swish(orc.swish(temb[(j + 1) % H])) for j in range(H)]
+    np.testing.assert_allclose(cond, want, rtol=1e-15)
+    # zero second layer: the conditioning is swish of its bias, whatever the time
+    np.testing.assert_allclose(orc.time_mlp(temb, w1, b1, np.zeros((H, H)), b2), [orc.swish(v) for v in b2],
+                               rtol=1e-15)
+
+
+def test_action_in_one_hot_picks_a_column():
+    r = rng(71)
+    C, A, H = 3, 5, 7
+    w_in, b_in = r.standard_normal((H, A)), r.standard_normal(H)
+    a = np.zeros((C, A))
+    a[0, 2], a[1, 4] = 1.0, -2.0
+    x = orc.action_in(a, w_in, b_in)
+    np.testing.assert_allclose(x[0], w_in[:, 2] + b_in, rtol=1e-15)
+    np.testing.assert_allclose(x[1], -2.0 * w_in[:, 4] + b_in, rtol=1e-15)
+    assert np.array_equal(x[2], b_in)
+
+
+def test_final_velocity_against_torch_and_closed_forms():
+    r = rng(72)
+    C, H, A = 4, 8, 3
+    x, cond = r.standard_normal((C, H)), r.standard_normal(H)
+    w_f, b_f = r.standard_normal((2 * H, H)), r.standard_normal(2 * H)
+    w_out, b_out = r.standard_normal((A, H)), r.standard_normal(A)
+    m = F.linear(t64(cond), t64(w_f), t64(b_f))
+    xf = F.rms_norm(t64(x), (H,), eps=1e-6) * (1.0 + m[:H]) + m[H:]
+    ref = F.linear(xf, t64(w_out), t64(b_out)).numpy()
+    np.testing.assert_allclose(orc.final_velocity(x, cond, w_f, b_f, w_out, b_out), ref, rtol=1e-12, atol=1e-13)
+    # zero output weights: the bias on every token
+    v = orc.final_velocity(x, cond, w_f, b_f, np.zeros((A, H)), b_out)
+    assert np.array_equal(v, np.tile(b_out, (C, 1)))
+    # zero rows normalise to zero, so they carry the shift half only (the second H values)
+    zf = np.zeros((2 * H, H))
+    v = orc.final_velocity(np.zeros((2, H)), cond, zf, b_f, w_out, b_out)
+    np.testing.assert_allclose(v, np.tile(w_out @ b_f[H:] + b_out, (2, 1)), rtol=1e-14)
+    # a constant row c with the scale half only: c / sqrt(c^2 + eps) (1 + scale)
+    c, bs = -1.5, np.r_[b_f[:H], np.zeros(H)]
+    v = orc.final_velocity(np.full((1, H), c), cond, zf, bs, w_out, b_out)
+    np.testing.assert_allclose(v[0], w_out @ (c / math.sqrt(c * c + 1e-6) * (1.0 + b_f[:H])) + b_out, rtol=1e-13)
+    # with eps = 0 the velocity does not see the row's scale
+    v1 = orc.final_velocity(x, cond, w_f, b_f, w_out, b_out, eps=0.0)
+    v2 = orc.final_velocity(3.7 * x, cond, w_f, b_f, w_out, b_out, eps=0.0)
+    np.testing.assert_allclose(v1, v2, rtol=1e-13, atol=1e-13)
+
+
+def _tiny_sampler(seed, H=16, A=4):
+    r = rng(seed)
+    return {"w_in": r.standard_normal((H, A)), "b_in": 0.1 * r.standard_normal(H),
+            "w_t1": 0.3 * r.standard_normal((H, H)), "b_t1": 0.1 * r.standard_normal(H),
+            "w_t2": 0.3 * r.standard_normal((H, H)), "b_t2": 0.1 * r.standard_normal(H),
+            "w_fmod": 0.3 * r.standard_normal((2 * H, H)), "b_fmod": 0.1 * r.standard_normal(2 * H),
+            "w_out": r.standard_normal((A, H)), "b_out": r.standard_normal(A)}
+
+
+def _identity_layers(n, seed):
+    out = []
+    for i in range(n):
+        w, _, _, kp, vp, mask, dims = _tiny_layer(seed + i)
+        H = w["w_mod1"].shape[1]
+        for k in ("w_mod1", "w_mod2", "b_mod1", "b_mod2"):
+            w[k][2 * H:] = 0.0
+        out.append((w, kp, vp))
+    return out, mask, dims
+
+
+def test_sampler_constant_velocity_ends_at_noise_minus_bias():
+    """Zero output weights make v = b_out at every step; the n Euler steps of
+    dt = -1/n then move the noise by exactly -b_out, in equal steps."""
+    sw = _tiny_sampler(73)
+    sw["w_out"][:] = 0.0
+    lay, mask, dims = _identity_layers(2, 74)
+    noise = rng(75).standard_normal((3, 4))
+    n = 5
+    traj = orc.sampler(noise, n, sw, [w for w, _, _ in lay], [k for _, k, _ in lay], [v for _, _, v in lay],
+                       mask, 9, **dims)
+    for k in range(n):
+        np.testing.assert_allclose(traj[k], noise - (k + 1) / n * sw["b_out"], rtol=1e-14, atol=1e-14)
+
+
+def test_sampler_schedule_runs_from_time_one():
+    """With zero input weights and bias the expert sees zero rows, which the
+    final norm maps to its shift: v_k = W_out (W_f[H:] cond(t_k) + b_f[H:]) +
+    b_out.  Two steps must use t = 1 and t = 1/2, each with dt = -1/2."""
+    H = 16
+    sw = _tiny_sampler(76, H=H)
+    sw["w_in"][:] = 0.0
+    sw["b_in"][:] = 0.0
+    lay, mask, dims = _identity_layers(1, 77)
+    noise = rng(78).standard_normal((2, 4))
+    traj = orc.sampler(noise, 2, sw, [lay[0][0]], [lay[0][1]], [lay[0][2]], mask, 0, **dims)
+    prev = noise
+    for k, t in enumerate((1.0, 0.5)):
+        cond = orc.time_condition(t, sw)
+        v = sw["w_out"] @ (sw["w_fmod"][H:] @ cond + sw["b_fmod"][H:]) + sw["b_out"]
+        np.testing.assert_allclose(traj[k], prev - 0.5 * v, rtol=1e-12, atol=1e-12)
+        prev = traj[k]
