@@ -345,6 +345,66 @@ int dmx_prefix_layer_forward(const dmx_prefix_layer_weights* w, const dmx_bf16* 
                              dmx_bf16* x_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Denoise sampler around the action-expert stack.  The pages decode the
+ * action chunk by diffusion over a fixed number of steps ([Art §1], [Art §4];
+ * [Guide §2]: the diffusion step count, fixed once graphs are captured) and
+ * give no formula for the sampler; the readings implemented:
+ *   t_k   = 1 - k / n_steps, k = 0 .. n_steps - 1 (noise at t = 1)
+ *   temb  = [sin(1000 t w_i) | cos(1000 t w_i)], w_i = 10000^(-i / 512)
+ *   cond  = swish(W_t2 swish(W_t1 temb + b_t1) + b_t2), swish(z) = z / (1 + e^-z)
+ *   x     = W_in a + b_in for each chunk token (the stack's input)
+ *   x    <- the stack's layers with cond(t_k)
+ *   xf    = x / sqrt(mean x^2 + 1e-6) * (1 + scale) + shift,
+ *           [scale | shift] = W_fmod cond + b_fmod
+ *   v     = W_out xf + b_out;   a <- a - v / n_steps   (Euler step)
+ * Action dimension A: a multiple of 16 in [16, DMX_MAX_ACTION]. */
+#define DMX_MAX_ACTION 128
+#define DMX_MAX_STEPS 1000
+
+typedef struct dmx_sampler_weights {
+  int32_t action_dim;      /* A */
+  const dmx_bf16* w_in;    /* [1024][A] row-major */
+  const dmx_bf16* b_in;    /* [1024] */
+  const dmx_bf16* w_t1;    /* [1024][1024], tiled (dmx_pack_weight) */
+  const dmx_bf16* b_t1;    /* [1024] */
+  const dmx_bf16* w_t2;    /* [1024][1024], tiled */
+  const dmx_bf16* b_t2;    /* [1024] */
+  const dmx_bf16* w_fmod;  /* [2048][1024], tiled: scale rows, then shift rows */
+  const dmx_bf16* b_fmod;  /* [2048] */
+  const dmx_bf16* w_out;   /* [A][1024] row-major */
+  const dmx_bf16* b_out;   /* [A] */
+} dmx_sampler_weights;
+
+/* Bytes of a schedule buffer for n_steps steps (0 if unsupported). */
+size_t dmx_sampler_schedule_bytes(int32_t n_steps);
+
+/* The step-only part of a schedule, computed once per (weights, n_steps):
+ * cond[k][b] = cond(t_k) for every request b (bf16 [n_steps][batch][1024],
+ * the stack's conditioning buffer), and in `sched` the final norm's
+ * modulation of every step plus scratch.  Enqueued on `stream`. */
+int dmx_sampler_schedule_fill(const dmx_sampler_weights* w, int32_t n_steps, int32_t batch, dmx_bf16* cond,
+                              void* sched, size_t sched_bytes, void* stream);
+
+/* A denoising run: the stack (its cond holding the schedule's conditioning,
+ * n_steps equal to the schedule's; its x buffer receives each step's expert
+ * input and output) bracketed per step by the action in-projection and the
+ * final norm + out-projection + Euler update. */
+typedef struct dmx_sampler_desc {
+  const dmx_stack_desc* stack;
+  const dmx_sampler_weights* w;
+  const void* sched;      /* filled by dmx_sampler_schedule_fill for stack->n_steps */
+  size_t sched_bytes;
+  float* actions;         /* device [batch][chunk][A] fp32: the noise on entry, the denoised chunk after */
+  float* trajectory;      /* optional device [n_steps][batch][chunk][A]: actions after each step */
+} dmx_sampler_desc;
+
+/* Eager run (every kernel enqueued on `stream`). */
+int dmx_sampler_forward(const dmx_sampler_desc* d, void* stream);
+/* Capture the run on `stream` into a graph (nothing runs); replay with
+ * dmx_graph_launch after writing new noise / KV / mask into the buffers. */
+int dmx_sampler_graph_create(const dmx_sampler_desc* d, void* stream, dmx_graph** out);
+
+/* ------------------------------------------------------------------------ */
 const char* dmx_status_string(int status);
 const char* dmx_last_error_string(void);
 

@@ -37,8 +37,9 @@ EXPORTED = (
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
     "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_stage_launch",
     "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill",
-    "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward", "dmx_stack_graph_create", "dmx_graph_launch",
-    "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
+    "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward",
+    "dmx_sampler_schedule_bytes", "dmx_sampler_schedule_fill", "dmx_sampler_forward", "dmx_sampler_graph_create",
+    "dmx_stack_graph_create", "dmx_graph_launch", "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
 )
 
 
@@ -78,6 +79,20 @@ class StackDesc(ctypes.Structure):
                 ("mod_table", ctypes.c_void_p)]
 
 
+SAMPLER_WEIGHTS = ("w_in", "b_in", "w_t1", "b_t1", "w_t2", "b_t2", "w_fmod", "b_fmod", "w_out", "b_out")
+SAMPLER_MATRICES = ("w_t1", "w_t2", "w_fmod")  # tiled; w_in / w_out stay row-major
+
+
+class SamplerWeights(ctypes.Structure):
+    _fields_ = [("action_dim", ctypes.c_int32)] + [(k, ctypes.c_void_p) for k in SAMPLER_WEIGHTS]
+
+
+class SamplerDesc(ctypes.Structure):
+    _fields_ = [("stack", ctypes.POINTER(StackDesc)), ("w", ctypes.POINTER(SamplerWeights)),
+                ("sched", ctypes.c_void_p), ("sched_bytes", ctypes.c_size_t), ("actions", ctypes.c_void_p),
+                ("trajectory", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -113,6 +128,10 @@ def lib():
             "dmx_prefix_layer_forward": ([ctypes.POINTER(PrefixLayerWeights), P, P, i32, P, P, i32, P, P, sz, P],
                                          ctypes.c_int),
             "dmx_stack_graph_create": ([ctypes.POINTER(StackDesc), P, ctypes.POINTER(P)], ctypes.c_int),
+            "dmx_sampler_schedule_bytes": ([i32], sz),
+            "dmx_sampler_schedule_fill": ([ctypes.POINTER(SamplerWeights), i32, i32, P, P, sz, P], ctypes.c_int),
+            "dmx_sampler_forward": ([ctypes.POINTER(SamplerDesc), P], ctypes.c_int),
+            "dmx_sampler_graph_create": ([ctypes.POINTER(SamplerDesc), P, ctypes.POINTER(P)], ctypes.c_int),
             "dmx_graph_launch": ([P, P], ctypes.c_int),
             "dmx_graph_destroy": ([P], None),
             "dmx_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -431,3 +450,81 @@ def prefix_layer_forward(w: dict, x, valid, k_cache, v_cache, ws=None, out=None,
     _check(lib().dmx_prefix_layer_forward(ctypes.byref(pw), _p(x), _p(valid), T, _p(k_cache), _p(v_cache), kv_rows,
                                           _p(out), _p(ws), ws.numel(), _stream(stream)))
     return out
+
+
+# --------------------------------------------------------------------------- denoise sampler
+def pack_sampler_weights(w: dict, stream=None) -> dict:
+    """Tile the sampler's square / modulation matrices (w_in, w_out and the
+    biases are kept row-major)."""
+    return {k: pack_weight(v, stream) if k in SAMPLER_MATRICES else v for k, v in w.items()}
+
+
+class Sampler:
+    """Denoising runs over a Stack's buffers: per step the action
+    in-projection writes the stack's x, the layers run with the step's
+    conditioning, and the final norm + out-projection + Euler update advance
+    `actions` [B][C][A] (fp32, the noise on entry).  Building the sampler
+    writes the schedule's conditioning into the stack's cond buffer (and
+    refreshes its modulation table, if it has one).
+
+    sw: sampler weights from pack_sampler_weights; trajectory: optional
+    [n_steps][B][C][A] fp32 receiving the actions after every step."""
+
+    def __init__(self, stack: Stack, sw: dict, actions, trajectory=None, stream=None):
+        d = stack.desc
+        B, C, n = d.batch, d.chunk, d.n_steps
+        A = sw["w_out"].shape[0]
+        _want(sw["w_in"], (H, A), torch.bfloat16, "w_in")
+        _want(sw["w_t1"], (H, H), torch.bfloat16, "w_t1")
+        _want(sw["w_t2"], (H, H), torch.bfloat16, "w_t2")
+        _want(sw["w_fmod"], (2 * H, H), torch.bfloat16, "w_fmod")
+        _want(sw["w_out"], (A, H), torch.bfloat16, "w_out")
+        _want(actions, (B, C, A), torch.float32, "actions")
+        if trajectory is not None:
+            _want(trajectory, (n, B, C, A), torch.float32, "trajectory")
+        nb = int(lib().dmx_sampler_schedule_bytes(n))
+        if nb == 0:
+            raise DmxError(ERR_UNSUPPORTED, f"no sampler schedule for {n} steps")
+        self.stack = stack
+        self.sched = torch.empty(nb, dtype=torch.uint8, device=actions.device)
+        self._keep = (sw, actions, trajectory)
+        self._sw = SamplerWeights(A, *[sw[k].data_ptr() for k in SAMPLER_WEIGHTS])
+        self.desc = SamplerDesc(ctypes.pointer(stack.desc), ctypes.pointer(self._sw), self.sched.data_ptr(), nb,
+                                actions.data_ptr(), None if trajectory is None else trajectory.data_ptr())
+        self._graph = None
+        self.fill_schedule(stream)
+
+    def fill_schedule(self, stream=None):
+        """(Re)compute the step conditioning (into the stack's cond) and the
+        final norm's modulation from the sampler weights."""
+        d = self.stack.desc
+        _check(lib().dmx_sampler_schedule_fill(ctypes.byref(self._sw), d.n_steps, d.batch, ctypes.c_void_p(d.cond),
+                                               _p(self.sched), self.sched.numel(), _stream(stream)))
+        if self.stack.mod_table is not None:
+            self.stack.fill_mod_table(stream)
+
+    def run(self, stream=None):
+        _check(lib().dmx_sampler_forward(ctypes.byref(self.desc), _stream(stream)))
+
+    def capture(self, stream):
+        """Capture a whole denoising run into a hipGraph on a non-default stream."""
+        g = ctypes.c_void_p()
+        _check(lib().dmx_sampler_graph_create(ctypes.byref(self.desc), _stream(stream), ctypes.byref(g)))
+        self._graph = g
+        return self
+
+    def replay(self, stream=None):
+        if self._graph is None:
+            raise DmxError(ERR_INVALID_ARG, "replay() before capture()")
+        _check(lib().dmx_graph_launch(self._graph, _stream(stream)))
+
+    def close(self):
+        if self._graph is not None:
+            lib().dmx_graph_destroy(self._graph)
+            self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -621,32 +621,76 @@ static int enq_stack_mods(const dmx_stack_desc* d, const WsLayout& L, int st, hi
 // next layer its input already scaled by that layer's 1 + scale1 when the
 // next layer's modulation is known by then: inside a step always, across
 // steps with a cached table.
-static LayerCtx stack_layer(const dmx_stack_desc* d, const WsLayout& L, const dmx_prefix_kv* kv, int st, int l) {
+// chained: the next step's input is this step's output (a plain stack run);
+// otherwise each step's input is written anew (the sampler's in-projection).
+static LayerCtx stack_layer(const dmx_stack_desc* d, const WsLayout& L, const dmx_prefix_kv* kv, int st, int l,
+                            bool chained = true) {
   const float* next = nullptr;
   if (l + 1 < d->n_layers)
     next = stack_mod(d, L, st, l + 1, 0);
-  else if (d->mod_table && st + 1 < d->n_steps)
+  else if (chained && d->mod_table && st + 1 < d->n_steps)
     next = stack_mod(d, L, st + 1, 0, 0);
   return LayerCtx{&d->layers[l], kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, st, l, 0),
                   stack_mod(d, L, st, l, 1), d->ws, &L, next};
 }
 
-static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) {
+// The sampler's per-step work around the stack (null: a plain stack run).
+struct SamplerRun {
+  const dmx_sampler_weights* w;
+  const float* fmod;  // [n_steps][2048] final-norm modulation
+  float* actions;     // [batch * chunk][A]
+  float* traj;        // optional [n_steps][batch * chunk][A]
+};
+
+static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, const SamplerRun* smp = nullptr) {
+  const int rows = d->batch * d->chunk;
   for (int st = 0; st < d->n_steps; ++st) {
+    if (smp)
+      DMX_TRY(hip_check(launch_action_in(smp->actions, smp->w->w_in, smp->w->b_in, rows, smp->w->action_dim, d->x, s),
+                        "action in-projection launch"));
     if (!d->mod_table) DMX_TRY(enq_stack_mods(d, L, st, s));
     // the first layer's scaled tiled input and its row statistics: a pack
     // pass at the start of the run, and of every step whose modulation was
-    // not known to the last down projection before it (no table); otherwise
-    // that down projection wrote them
-    if (st == 0 || !d->mod_table)
+    // not known to the last down projection before it (no table) or whose
+    // input is new (sampler); otherwise that down projection wrote them
+    if (st == 0 || !d->mod_table || smp)
       DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, stack_mod(d, L, st, 0, 0), d->ws, L, s));
     for (int l = 0; l < d->n_layers; ++l) {
       const dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
-      DMX_TRY(enq_layer_chain(stack_layer(d, L, &kv, st, l), s));
+      DMX_TRY(enq_layer_chain(stack_layer(d, L, &kv, st, l, smp == nullptr), s));
+    }
+    if (smp) {
+      const int A = smp->w->action_dim;
+      float* traj = smp->traj ? smp->traj + (size_t)st * rows * A : nullptr;
+      DMX_TRY(hip_check(launch_final_velocity(d->x, smp->fmod + (size_t)st * 2 * kH, smp->w->w_out, smp->w->b_out,
+                                              rows, A, -1.0f / (float)d->n_steps, smp->actions, traj, s),
+                        "final velocity launch"));
     }
   }
   return DMX_OK;
 }
+
+// Capture what `enq` enqueues on `s` into an instantiated graph.
+}  // extern "C"
+template <typename F>
+static int capture_graph(hipStream_t s, dmx_graph** out, F&& enq) {
+  hipGraph_t g = nullptr;
+  int st = hip_check(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+  if (st == DMX_OK) {
+    st = enq();
+    const hipError_t ce = hipStreamEndCapture(s, &g);
+    if (st == DMX_OK) st = hip_check(ce, "hipStreamEndCapture");
+  }
+  hipGraphExec_t e = nullptr;
+  if (st == DMX_OK) st = hip_check(hipGraphInstantiate(&e, g, nullptr, nullptr, 0), "hipGraphInstantiate");
+  if (st != DMX_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  *out = new dmx_graph{g, e};
+  return DMX_OK;
+}
+extern "C" {
 
 int dmx_stack_forward(const dmx_stack_desc* d, void* stream) {
   WsLayout L;
@@ -702,21 +746,7 @@ int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** ou
   WsLayout L;
   DMX_TRY(check_stack(fn, d, L));
   hipStream_t s = (hipStream_t)stream;
-  hipGraph_t g = nullptr;
-  int st = hip_check(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
-  if (st == DMX_OK) {
-    st = enq_stack(d, L, s);
-    const hipError_t ce = hipStreamEndCapture(s, &g);
-    if (st == DMX_OK) st = hip_check(ce, "hipStreamEndCapture");
-  }
-  hipGraphExec_t e = nullptr;
-  if (st == DMX_OK) st = hip_check(hipGraphInstantiate(&e, g, nullptr, nullptr, 0), "hipGraphInstantiate");
-  if (st != DMX_OK) {
-    if (g) (void)hipGraphDestroy(g);
-    return st;
-  }
-  *out = new dmx_graph{g, e};
-  return DMX_OK;
+  return capture_graph(s, out, [&] { return enq_stack(d, L, s); });
 }
 
 int dmx_graph_launch(dmx_graph* g, void* stream) {
@@ -888,6 +918,112 @@ int dmx_prefix_layer_forward(const dmx_prefix_layer_weights* w, const dmx_bf16* 
   if (ws_bytes < L.total)
     return fail(DMX_ERR_WORKSPACE, "%s: workspace %zu bytes, needs %zu", fn, ws_bytes, L.total);
   return enq_prefix_layer(w, x_in, valid, tokens, k_cache, v_cache, kv_rows, x_out, ws, L, (hipStream_t)stream);
+}
+
+// ---- denoise sampler ---------------------------------------------------------
+// schedule buffer: final-norm modulation fp32 [n][2048], then bf16 scratch:
+// temb [n][1024] and the time MLP's hidden rows [n][1024]
+struct SchedLayout {
+  size_t fmod, temb, h1, total;
+};
+static SchedLayout sched_layout(int n) {
+  SchedLayout S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  S.fmod = take((size_t)n * 2 * kH * sizeof(float));
+  S.temb = take((size_t)n * kH * 2);
+  S.h1 = take((size_t)n * kH * 2);
+  S.total = off;
+  return S;
+}
+
+size_t dmx_sampler_schedule_bytes(int32_t n_steps) {
+  if (n_steps < 1 || n_steps > DMX_MAX_STEPS) return 0;
+  return sched_layout(n_steps).total;
+}
+
+static int check_sampler_weights(const char* fn, const dmx_sampler_weights* w) {
+  if (w == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: sampler weights struct is null", fn);
+  if (w->action_dim < 16 || w->action_dim > DMX_MAX_ACTION || w->action_dim % 16 != 0)
+    return fail(DMX_ERR_UNSUPPORTED, "%s: action_dim %d is not a multiple of 16 in [16, %d]", fn, w->action_dim,
+                DMX_MAX_ACTION);
+  DMX_REQUIRE_PTR(w->w_in);
+  DMX_REQUIRE_PTR(w->b_in);
+  DMX_REQUIRE_PTR(w->w_t1);
+  DMX_REQUIRE_PTR(w->b_t1);
+  DMX_REQUIRE_PTR(w->w_t2);
+  DMX_REQUIRE_PTR(w->b_t2);
+  DMX_REQUIRE_PTR(w->w_fmod);
+  DMX_REQUIRE_PTR(w->b_fmod);
+  DMX_REQUIRE_PTR(w->w_out);
+  DMX_REQUIRE_PTR(w->b_out);
+  return DMX_OK;
+}
+
+int dmx_sampler_schedule_fill(const dmx_sampler_weights* w, int32_t n_steps, int32_t batch, dmx_bf16* cond,
+                              void* sched, size_t sched_bytes, void* stream) {
+  const char* fn = "dmx_sampler_schedule_fill";
+  DMX_TRY(check_sampler_weights(fn, w));
+  if (n_steps < 1 || n_steps > DMX_MAX_STEPS)
+    return fail(DMX_ERR_INVALID_ARG, "%s: n_steps %d not in [1, %d]", fn, n_steps, DMX_MAX_STEPS);
+  if (batch < 1 || batch > DMX_MAX_BATCH)
+    return fail(DMX_ERR_INVALID_ARG, "%s: batch %d not in [1, %d]", fn, batch, DMX_MAX_BATCH);
+  DMX_REQUIRE_PTR(cond);
+  DMX_REQUIRE_PTR(sched);
+  const SchedLayout S = sched_layout(n_steps);
+  if (sched_bytes < S.total)
+    return fail(DMX_ERR_WORKSPACE, "%s: schedule buffer of %zu bytes, %zu needed", fn, sched_bytes, S.total);
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* temb = at<uint16_t>(sched, S.temb);
+  uint16_t* h1 = at<uint16_t>(sched, S.h1);
+  DMX_TRY(hip_check(launch_time_embed(n_steps, temb, s), "time embedding launch"));
+  DMX_TRY(hip_check(launch_gemv_rows(w->w_t1, w->b_t1, kH, true, temb, kH, n_steps, nullptr, 0, h1, 1, s),
+                    "time MLP launch"));
+  DMX_TRY(hip_check(launch_gemv_rows(w->w_t2, w->b_t2, kH, true, h1, kH, n_steps, nullptr, 0, cond, batch, s),
+                    "time MLP launch"));
+  return hip_check(launch_gemv_rows(w->w_fmod, w->b_fmod, 2 * kH, false, cond, batch * kH, n_steps,
+                                    at<float>(sched, S.fmod), 2 * kH, nullptr, 0, s),
+                   "final modulation launch");
+}
+
+static int check_sampler(const char* fn, const dmx_sampler_desc* d, WsLayout& L, SamplerRun& run) {
+  if (d == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: desc is null", fn);
+  DMX_TRY(check_stack(fn, d->stack, L));
+  DMX_TRY(check_sampler_weights(fn, d->w));
+  DMX_REQUIRE_PTR(d->sched);
+  DMX_REQUIRE_PTR(d->actions);
+  if (d->trajectory && !aligned16(d->trajectory))
+    return fail(DMX_ERR_MISALIGNED, "%s: trajectory is not 16-byte aligned", fn);
+  const SchedLayout S = sched_layout(d->stack->n_steps);
+  if (d->stack->n_steps > DMX_MAX_STEPS || d->sched_bytes < S.total)
+    return fail(DMX_ERR_WORKSPACE, "%s: schedule buffer of %zu bytes, %zu needed for %d steps", fn, d->sched_bytes,
+                S.total, d->stack->n_steps);
+  run = SamplerRun{d->w, at<float>(const_cast<void*>(d->sched), S.fmod), d->actions, d->trajectory};
+  return DMX_OK;
+}
+
+int dmx_sampler_forward(const dmx_sampler_desc* d, void* stream) {
+  const char* fn = "dmx_sampler_forward";
+  WsLayout L;
+  SamplerRun run;
+  DMX_TRY(check_sampler(fn, d, L, run));
+  return enq_stack(d->stack, L, (hipStream_t)stream, &run);
+}
+
+int dmx_sampler_graph_create(const dmx_sampler_desc* d, void* stream, dmx_graph** out) {
+  const char* fn = "dmx_sampler_graph_create";
+  if (out == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: out is null", fn);
+  *out = nullptr;
+  if (stream == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: capture needs a non-null stream", fn);
+  WsLayout L;
+  SamplerRun run;
+  DMX_TRY(check_sampler(fn, d, L, run));
+  hipStream_t s = (hipStream_t)stream;
+  return capture_graph(s, out, [&] { return enq_stack(d->stack, L, s, &run); });
 }
 
 const char* dmx_status_string(int status) {

@@ -147,6 +147,17 @@ hipError_t launch_image_merge(const uint16_t* tok, const uint16_t* img, const in
 hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,
                                    int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, hipStream_t s);
 
+// denoise sampler pieces
+constexpr int kMaxActionDim = 128;
+hipError_t launch_time_embed(int n_steps, uint16_t* temb, hipStream_t s);
+// y[r] = act(W x[r] + bias), W tiled [N][1024]; outputs as k_gemv_rows documents
+hipError_t launch_gemv_rows(const uint16_t* W, const uint16_t* bias, int N, bool swish, const uint16_t* x,
+                            int x_stride, int R, float* out_f32, int ldo, uint16_t* out_bf16, int rep, hipStream_t s);
+hipError_t launch_action_in(const float* a, const uint16_t* w_in, const uint16_t* b_in, int rows, int A, uint16_t* x,
+                            hipStream_t s);
+hipError_t launch_final_velocity(const uint16_t* x, const float* fmod, const uint16_t* w_out, const uint16_t* b_out,
+                                 int rows, int A, float dt, float* a, float* traj, hipStream_t s);
+
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace dmx

@@ -1,0 +1,168 @@
+// Denoise sampler kernels around the action-expert stack.  The pages describe
+// the action chunk as decoded by diffusion over a fixed number of steps
+// (OpenDM fast-stack article §1 and §4; DM05 inference guide §2, the
+// diffusion step count) but give no formula for the sampler.  The readings
+// implemented here:
+//   t_k = 1 - k / n;  temb(t) = [sin(1000 t w_i) | cos(1000 t w_i)],
+//   w_i = 10000^(-i / 512);  cond = swish(W_t2 swish(W_t1 temb + b_t1) + b_t2);
+//   x = W_in a + b_in per chunk token;  after the layers, the final AdaRMS
+//   norm with [scale | shift] = W_f cond + b_f, v = W_out xf + b_out, and the
+//   Euler step a <- a - v / n.
+// The schedule side (temb, time MLP, final modulation) depends on the step
+// only and runs once per schedule; the per-step side is two small kernels
+// around the stack: the action in-projection and the fused final norm +
+// out-projection + Euler update.
+#include "dmx_device.hpp"
+#include "dmx_internal.hpp"
+#include "dmx_tiles.hpp"
+
+namespace dmx {
+
+// temb of every step of an n-step schedule, bf16 [n][1024].  Angles and their
+// sine / cosine in double precision; one bf16 rounding at the end.
+__global__ __launch_bounds__(512) void k_time_embed(int n_steps, uint16_t* temb) {
+  const int s = blockIdx.x, i = threadIdx.x;
+  const double t = 1.0 - (double)s / n_steps;
+  const double ang = 1000.0 * t * pow(10000.0, -(double)i / (kH / 2));
+  temb[(size_t)s * kH + i] = f2bf((float)sin(ang));
+  temb[(size_t)s * kH + kH / 2 + i] = f2bf((float)cos(ang));
+}
+
+// Rows of a small batch through one linear layer:
+//   y[r][n] = act(W[n] . x[r] + bias[n]),  W tiled [N][1024], x bf16 rows
+// x_stride elements apart.  Work-group = 16 output features (N / 16 groups);
+// its 32 KB weight slab sits in registers while 16-row blocks of x stream by.
+// Outputs (each optional): fp32 [R][ldo]; bf16 [R * rep][N] with each row
+// written rep times (row r's copies at r * rep .. r * rep + rep - 1).
+template <bool SWISH>
+__global__ __launch_bounds__(256) void k_gemv_rows(const uint16_t* W, const uint16_t* bias, const uint16_t* x,
+                                                  int x_stride, int R, float* out_f32, int ldo, uint16_t* out_bf16,
+                                                  int rep) {
+  __shared__ float red[4][16 * 16];
+  const int tile = blockIdx.x, N = gridDim.x * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int k0 = wave * 256;
+  bf16x8 wf[8];
+  const uint16_t* wp = W + ((size_t)tile * (kH / 32) + wave * 8) * 512 + lane * 8;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) wf[ks] = load_bf16x8(wp + ks * 512);
+  for (int r0 = 0; r0 < R; r0 += 16) {
+    const int rows = min(16, R - r0);
+    f32x4 acc = zero_f32x4();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 av = lr < rows ? load_bf16x8(x + (size_t)(r0 + lr) * x_stride + k0 + ks * 32 + lk) : zero_bf16x8();
+      acc = mfma16(av, wf[ks], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][((lane >> 4) * 4 + r) * 16 + lr] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < rows * 16) {
+      const int r = threadIdx.x >> 4, c = threadIdx.x & 15, n = tile * 16 + c;
+      float v = red[0][r * 16 + c] + red[1][r * 16 + c] + red[2][r * 16 + c] + red[3][r * 16 + c] + bf2f(bias[n]);
+      if (SWISH) v = v / (1.0f + expf(-v));
+      if (out_f32) out_f32[(size_t)(r0 + r) * ldo + n] = v;
+      if (out_bf16) {
+        const uint16_t h = f2bf(v);
+        for (int i = 0; i < rep; ++i) out_bf16[((size_t)(r0 + r) * rep + i) * N + n] = h;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// x[row] = bf16(W_in a[row] + b_in): a fp32 [rows][A], W_in bf16 [1024][A]
+// row-major, x bf16 [rows][1024].  One work-group per token row, 4 features
+// per thread.
+__global__ __launch_bounds__(256) void k_action_in(const float* a, const uint16_t* w_in, const uint16_t* b_in, int A,
+                                                  uint16_t* x) {
+  __shared__ float sa[kMaxActionDim];
+  const int row = blockIdx.x;
+  if (threadIdx.x < A) sa[threadIdx.x] = a[(size_t)row * A + threadIdx.x];
+  __syncthreads();
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = threadIdx.x * 4 + i;
+    const uint16_t* wr = w_in + (size_t)n * A;
+    float acc = 0.f;
+    for (int j = 0; j < A; j += 8) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(wr + j);
+      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += bf2f((uint16_t)(w4[e] & 0xffffu)) * sa[j + 2 * e];
+        acc += bf2f((uint16_t)(w4[e] >> 16)) * sa[j + 2 * e + 1];
+      }
+    }
+    y[i] = acc + bf2f(b_in[n]);
+  }
+  *reinterpret_cast<uint2*>(x + (size_t)row * kH + threadIdx.x * 4) = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
+}
+
+// The step's velocity and Euler update for one token row:
+//   xf = x / sqrt(mean x^2 + eps) * (1 + scale) + shift   (fmod = [scale | shift])
+//   v  = W_out xf + b_out;  a += dt * v  (and traj = a when given)
+// x bf16 [rows][1024] (the stack's output), W_out bf16 [A][1024] row-major,
+// a / traj fp32 [rows][A].  One work-group per row, 4 features per thread.
+__global__ __launch_bounds__(256) void k_final_velocity(const uint16_t* x, const float* fmod, const uint16_t* w_out,
+                                                       const uint16_t* b_out, int A, float dt, float* a,
+                                                       float* traj) {
+  __shared__ float red[4][kMaxActionDim];
+  __shared__ float rss[4];
+  const int row = blockIdx.x, c = threadIdx.x * 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint2 raw = *reinterpret_cast<const uint2*>(x + (size_t)row * kH + c);
+  float v[4] = {bf2f((uint16_t)(raw.x & 0xffffu)), bf2f((uint16_t)(raw.x >> 16)), bf2f((uint16_t)(raw.y & 0xffffu)),
+                bf2f((uint16_t)(raw.y >> 16))};
+  const float ss = wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+  if (lane == 0) rss[wave] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((rss[0] + rss[1] + rss[2] + rss[3]) * (1.0f / kH) + kEps);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = v[i] * r * (1.f + fmod[c + i]) + fmod[kH + c + i];
+  for (int j = 0; j < A; ++j) {
+    const uint2 wr = *reinterpret_cast<const uint2*>(w_out + (size_t)j * kH + c);
+    float p = v[0] * bf2f((uint16_t)(wr.x & 0xffffu)) + v[1] * bf2f((uint16_t)(wr.x >> 16)) +
+              v[2] * bf2f((uint16_t)(wr.y & 0xffffu)) + v[3] * bf2f((uint16_t)(wr.y >> 16));
+    p = wave_sum(p);
+    if (lane == 0) red[wave][j] = p;
+  }
+  __syncthreads();
+  if (threadIdx.x < A) {
+    const int j = threadIdx.x;
+    const float vel = red[0][j] + red[1][j] + red[2][j] + red[3][j] + bf2f(b_out[j]);
+    const float an = a[(size_t)row * A + j] + dt * vel;
+    a[(size_t)row * A + j] = an;
+    if (traj) traj[(size_t)row * A + j] = an;
+  }
+}
+
+hipError_t launch_time_embed(int n_steps, uint16_t* temb, hipStream_t s) {
+  k_time_embed<<<dim3(n_steps), dim3(kH / 2), 0, s>>>(n_steps, temb);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_rows(const uint16_t* W, const uint16_t* bias, int N, bool swish, const uint16_t* x,
+                            int x_stride, int R, float* out_f32, int ldo, uint16_t* out_bf16, int rep, hipStream_t s) {
+  if (swish)
+    k_gemv_rows<true><<<dim3(N / 16), dim3(256), 0, s>>>(W, bias, x, x_stride, R, out_f32, ldo, out_bf16, rep);
+  else
+    k_gemv_rows<false><<<dim3(N / 16), dim3(256), 0, s>>>(W, bias, x, x_stride, R, out_f32, ldo, out_bf16, rep);
+  return hipGetLastError();
+}
+
+hipError_t launch_action_in(const float* a, const uint16_t* w_in, const uint16_t* b_in, int rows, int A, uint16_t* x,
+                            hipStream_t s) {
+  k_action_in<<<dim3(rows), dim3(256), 0, s>>>(a, w_in, b_in, A, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_final_velocity(const uint16_t* x, const float* fmod, const uint16_t* w_out, const uint16_t* b_out,
+                                 int rows, int A, float dt, float* a, float* traj, hipStream_t s) {
+  k_final_velocity<<<dim3(rows), dim3(256), 0, s>>>(x, fmod, w_out, b_out, A, dt, a, traj);
+  return hipGetLastError();
+}
+
+}  // namespace dmx

@@ -116,6 +116,19 @@ def test_validation_errors_before_launch(dmx):
                                       FAKE, 1 << 30, None) == dmx.ERR_UNSUPPORTED  # kv_rows < tokens
     assert L.dmx_prefix_layer_forward(ctypes.byref(pw), FAKE, FAKE, 8, FAKE, FAKE, 8, ctypes.c_void_p(0x20000),
                                       FAKE, 1024, None) == dmx.ERR_WORKSPACE
+    assert L.dmx_sampler_schedule_bytes(0) == 0 and L.dmx_sampler_schedule_bytes(1001) == 0
+    assert L.dmx_sampler_schedule_bytes(10) > L.dmx_sampler_schedule_bytes(1) > 0
+    sw = dmx.SamplerWeights(32, *([0x10000] * 10))
+    assert L.dmx_sampler_schedule_fill(None, 10, 1, FAKE, FAKE, 1 << 30, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_sampler_schedule_fill(ctypes.byref(sw), 0, 1, FAKE, FAKE, 1 << 30, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_sampler_schedule_fill(ctypes.byref(sw), 10, 0, FAKE, FAKE, 1 << 30, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_sampler_schedule_fill(ctypes.byref(sw), 10, 1, FAKE, FAKE, 64, None) == dmx.ERR_WORKSPACE
+    sw_bad = dmx.SamplerWeights(24, *([0x10000] * 10))
+    assert L.dmx_sampler_schedule_fill(ctypes.byref(sw_bad), 10, 1, FAKE, FAKE, 1 << 30, None) == dmx.ERR_UNSUPPORTED
+    sw_mis = dmx.SamplerWeights(32, *([0x10000] * 9 + [0x10008]))
+    assert L.dmx_sampler_schedule_fill(ctypes.byref(sw_mis), 10, 1, FAKE, FAKE, 1 << 30, None) == dmx.ERR_MISALIGNED
+    assert L.dmx_sampler_forward(None, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_sampler_graph_create(None, FAKE, ctypes.byref(g)) == dmx.ERR_INVALID_ARG
     assert L.dmx_graph_launch(None, None) == dmx.ERR_INVALID_ARG
     L.dmx_graph_destroy(None)
     for s in (0, 1, -1, -2, -3, -4, -5, -6, -7, -99):
