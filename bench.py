@@ -87,7 +87,8 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = ("dmx_attention.hip", "dmx_gemm.hip", "dmx_prefix.hip", "dmx_device.hpp", "dmx_internal.hpp",
+KERNEL_SOURCES = ("dmx_attention.hip", "dmx_gemm.hip", "dmx_prefix.hip", "dmx_sampler.hip", "dmx_device.hpp",
+                  "dmx_internal.hpp",
                   "dmx_tiles.hpp")
 
 
@@ -377,6 +378,27 @@ def main():
                                       "note": f"whole {wl.n_steps}-step denoise loop per replay, modulation "
                                               "vectors precomputed per schedule"}
         lp.close()
+        # the full sampler: per step the action in-projection, the stack (with
+        # the table) and the final norm + out-projection + Euler update
+        x.copy_(dev(rq.x[None]))
+        swd = dmx.pack_sampler_weights({k: dev(v) for k, v in synth.sampler_weights(wl.seed + 50).items()})
+        A = synth.ACTION_DIM
+        acts = torch.from_numpy(synth.sampler_noise(wl.seed + 60, B, C)).cuda()
+        cond_s = torch.empty_like(cond_all)
+        with torch.cuda.stream(stream):
+            sp_stack = dmx.Stack(wd, kp, vp, mask, cond_s, pos0, x, mod_table=True, stream=stream)
+            sp = dmx.Sampler(sp_stack, swd, acts, stream=stream)
+        sp.capture(stream)
+        ms_sp = time_replays(sp, stream, max(1, args.warmup // wl.n_steps), n) / wl.n_steps
+        assert torch.isfinite(acts).all(), "non-finite actions"
+        sp_bytes = tb_bytes + 2 * A * H * 2 + (H + A) * 2 + 2 * H * 4 + 2 * B * C * A * 4
+        variants["sampler_loop"] = {"ms_per_step": round(ms_sp, 4), "algorithmic_bytes": sp_bytes,
+                                    "frac_of_hbm_peak": round(sp_bytes / (ms_sp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                    "note": f"whole {wl.n_steps}-step sampler per replay: action in-projection, "
+                                            "stack with precomputed modulation, final norm + out-projection + "
+                                            "Euler update"}
+        sp.close()
+        sp_stack.close()
         assert torch.isfinite(x.float()).all(), "non-finite activations"
         x.copy_(dev(rq.x[None]))
         torch.cuda.synchronize()
