@@ -405,6 +405,47 @@ int dmx_sampler_forward(const dmx_sampler_desc* d, void* stream);
 int dmx_sampler_graph_create(const dmx_sampler_desc* d, void* stream, dmx_graph** out);
 
 /* ------------------------------------------------------------------------ */
+/* Lazily captured graph profiles ([Art §5] table, default backend): a
+ * request's prefix length is rounded up to a multiple of 16 tokens, and each
+ * such bucket (with the run's batch, chunk, steps and layers) is a profile.
+ * A profile's first call runs eager, its second call is captured into a graph
+ * (and runs), later calls replay that graph.  At most `capacity` (1 ..
+ * DMX_LAZY_MAX_PROFILES) profiles hold graphs.  A new profile beyond that
+ * either replaces the least recently used one (evict = 1) or runs eager
+ * without becoming a profile (evict = 0).  A profile whose buffers changed
+ * (another address in its descriptor) starts again from its first call. */
+#define DMX_LAZY_GRANULE 16
+#define DMX_LAZY_MAX_PROFILES 8
+#define DMX_ACTION_EAGER 0
+#define DMX_ACTION_CAPTURE 1
+#define DMX_ACTION_REPLAY 2
+
+/* Bucket of a prefix length: 16 * ceil(prefix_len / 16).  Negative status for
+ * prefix_len < 1 (DMX_ERR_INVALID_ARG) or above max_len
+ * (DMX_ERR_PREFIX_TOO_LONG). */
+int32_t dmx_lazy_bucket(int32_t prefix_len, int32_t max_len);
+
+typedef struct dmx_profile_cache dmx_profile_cache;
+int dmx_profile_cache_create(int32_t capacity, int32_t evict, dmx_profile_cache** out);
+void dmx_profile_cache_destroy(dmx_profile_cache* c);
+
+/* The policy alone (host only, enqueues nothing): the action for a call of
+ * profile `key` whose buffers hash to `fingerprint`, and the key of the
+ * profile it displaces (-1 if none; that profile's graph is destroyed).
+ * Updates the cache's bookkeeping exactly as a run would. */
+int dmx_profile_cache_plan(dmx_profile_cache* c, int64_t key, uint64_t fingerprint, int32_t* action,
+                           int64_t* evicted);
+/* Number of profiles held, and their keys from least to most recently used
+ * (keys: host array of at least DMX_LAZY_MAX_PROFILES, may be NULL). */
+int dmx_profile_cache_keys(const dmx_profile_cache* c, int64_t* keys);
+
+/* One denoising run of `d` through the cache: its profile key is (p_bucket,
+ * batch, chunk, n_steps, n_layers), its fingerprint the descriptor's buffer
+ * addresses.  *action (host, optional) receives what was done.  Capture and
+ * replay use `stream`, which must not be the null stream. */
+int dmx_profile_cache_run_sampler(dmx_profile_cache* c, const dmx_sampler_desc* d, void* stream, int32_t* action);
+
+/* ------------------------------------------------------------------------ */
 const char* dmx_status_string(int status);
 const char* dmx_last_error_string(void);
 

@@ -39,6 +39,8 @@ EXPORTED = (
     "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill",
     "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward",
     "dmx_sampler_schedule_bytes", "dmx_sampler_schedule_fill", "dmx_sampler_forward", "dmx_sampler_graph_create",
+    "dmx_lazy_bucket", "dmx_profile_cache_create", "dmx_profile_cache_destroy", "dmx_profile_cache_plan",
+    "dmx_profile_cache_keys", "dmx_profile_cache_run_sampler",
     "dmx_stack_graph_create", "dmx_graph_launch", "dmx_graph_destroy", "dmx_status_string", "dmx_last_error_string",
 )
 
@@ -132,6 +134,13 @@ def lib():
             "dmx_sampler_schedule_fill": ([ctypes.POINTER(SamplerWeights), i32, i32, P, P, sz, P], ctypes.c_int),
             "dmx_sampler_forward": ([ctypes.POINTER(SamplerDesc), P], ctypes.c_int),
             "dmx_sampler_graph_create": ([ctypes.POINTER(SamplerDesc), P, ctypes.POINTER(P)], ctypes.c_int),
+            "dmx_lazy_bucket": ([i32, i32], i32),
+            "dmx_profile_cache_create": ([i32, i32, ctypes.POINTER(P)], ctypes.c_int),
+            "dmx_profile_cache_destroy": ([P], None),
+            "dmx_profile_cache_plan": ([P, ctypes.c_int64, ctypes.c_uint64, ctypes.POINTER(i32),
+                                        ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+            "dmx_profile_cache_keys": ([P, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+            "dmx_profile_cache_run_sampler": ([P, ctypes.POINTER(SamplerDesc), P, ctypes.POINTER(i32)], ctypes.c_int),
             "dmx_graph_launch": ([P, P], ctypes.c_int),
             "dmx_graph_destroy": ([P], None),
             "dmx_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -522,6 +531,59 @@ class Sampler:
         if self._graph is not None:
             lib().dmx_graph_destroy(self._graph)
             self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# --------------------------------------------------------------------------- lazy graph profiles
+ACTION_EAGER, ACTION_CAPTURE, ACTION_REPLAY = 0, 1, 2
+LAZY_GRANULE, LAZY_MAX_PROFILES = 16, 8
+
+
+def lazy_bucket(prefix_len: int, max_len: int = 2048) -> int:
+    """16 * ceil(prefix_len / 16); raises for lengths outside [1, max_len]."""
+    return _check(int(lib().dmx_lazy_bucket(int(prefix_len), int(max_len))))
+
+
+class ProfileCache:
+    """At most `capacity` lazily captured graph profiles: a profile's first
+    call runs eager, its second is captured and run, later calls replay.
+    evict=True replaces the least recently used profile with a new one;
+    evict=False runs new profiles beyond capacity eager without keeping them."""
+
+    def __init__(self, capacity: int = LAZY_MAX_PROFILES, evict: bool = True):
+        h = ctypes.c_void_p()
+        _check(lib().dmx_profile_cache_create(int(capacity), int(bool(evict)), ctypes.byref(h)))
+        self._h = h
+
+    def plan(self, key: int, fingerprint: int = 0):
+        """The policy step alone: (action, evicted key or -1)."""
+        act, ev = ctypes.c_int32(-1), ctypes.c_int64(-2)
+        _check(lib().dmx_profile_cache_plan(self._h, int(key), int(fingerprint), ctypes.byref(act), ctypes.byref(ev)))
+        return int(act.value), int(ev.value)
+
+    def keys(self):
+        """Profile keys from least to most recently used."""
+        buf = (ctypes.c_int64 * LAZY_MAX_PROFILES)()
+        n = _check(lib().dmx_profile_cache_keys(self._h, buf))
+        return [int(buf[i]) for i in range(n)]
+
+    def run(self, sampler: "Sampler", stream) -> int:
+        """One denoising run of `sampler` through the cache on `stream` (not
+        the null stream); returns the action taken."""
+        act = ctypes.c_int32(-1)
+        _check(lib().dmx_profile_cache_run_sampler(self._h, ctypes.byref(sampler.desc), _stream(stream),
+                                                   ctypes.byref(act)))
+        return int(act.value)
+
+    def close(self):
+        if self._h:
+            lib().dmx_profile_cache_destroy(self._h)
+            self._h = None
 
     def __del__(self):
         try:

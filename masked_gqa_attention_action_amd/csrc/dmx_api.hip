@@ -1044,3 +1044,11 @@ const char* dmx_status_string(int status) {
 const char* dmx_last_error_string(void) { return g_last_error.c_str(); }
 
 }  // extern "C"
+
+// the error text of this thread, set by code outside this file
+namespace dmx {
+int set_last_error(int status, const char* msg) {
+  g_last_error = msg;
+  return status;
+}
+}  // namespace dmx

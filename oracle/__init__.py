@@ -349,3 +349,50 @@ def sampler(noise, n_steps: int, sw: dict, layers, kps, vps, mask, pos0: int, **
         a, _ = sampler_step(a, k, n_steps, sw, layers, kps, vps, mask, pos0, **dims)
         traj.append(a)
     return np.stack(traj)
+
+
+# ----------------------------------------------------------------------------- lazy graph profiles
+# The default backend's row of [Art §5]'s comparison table: prefix lengths
+# bucketed by 16 tokens, at most 8 profiles, a shape's first call eager and
+# its second captured.  A plain model of that policy in Python (host logic,
+# nothing numeric): a list of profiles ordered from least to most recently
+# used.
+EAGER, CAPTURE, REPLAY = 0, 1, 2
+
+
+def lazy_bucket(prefix_len: int, max_len: int):
+    """The 16-token bucket of a prefix length, or None outside [1, max_len]."""
+    if prefix_len < 1 or prefix_len > max_len:
+        return None
+    return -(-prefix_len // 16) * 16
+
+
+def lazy_profile_actions(calls, capacity: int = 8, evict: bool = True):
+    """calls: sequence of (key, fingerprint).  Returns the (action, evicted
+    key or -1) of every call and the final keys, least recently used first.
+    A profile counts its calls: the first runs eager, the second is captured,
+    the rest replay; other buffers (fingerprint) start the count again.  A new
+    key when `capacity` profiles exist replaces the least recently used one
+    (evict) or runs eager without being kept."""
+    order = []   # [key, fingerprint, calls], least recently used first
+    out = []
+    for key, fp in calls:
+        hit = [p for p in order if p[0] == key]
+        if hit:
+            p = hit[0]
+            order.remove(p)
+            order.append(p)
+            if p[1] != fp:
+                p[1], p[2] = fp, 0
+            p[2] += 1
+            out.append(((EAGER, CAPTURE)[p[2] - 1] if p[2] <= 2 else REPLAY, -1))
+            continue
+        evicted = -1
+        if len(order) == capacity:
+            if not evict:
+                out.append((EAGER, -1))
+                continue
+            evicted = order.pop(0)[0]
+        order.append([key, fp, 1])
+        out.append((EAGER, evicted))
+    return out, [p[0] for p in order]

@@ -11,6 +11,7 @@ import pytest
 from masked_gqa_attention_action_amd import build
 
 CSRC = os.path.join(os.path.dirname(build.__file__), "csrc")
+HOST_ONLY = ("dmx_api.hip", "dmx_profiles.hip")  # sources that define no kernel
 
 
 def _report(src):
@@ -34,7 +35,7 @@ def _report(src):
 @pytest.mark.parametrize("src", build.SOURCES)
 def test_no_private_memory(src):
     kernels = _report(src)
-    if src != "dmx_api.hip":
+    if src not in HOST_ONLY:
         assert kernels, f"no kernels reported for {src}"
     for name, r in kernels.items():
         assert r.get("ScratchSize [bytes/lane]", 0) == 0, (name, r)
