@@ -297,6 +297,10 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
 int dmx_image_merge(const dmx_bf16* tok, const dmx_bf16* img, const int32_t* idx, int32_t tokens,
                     int32_t n_img, int32_t hidden, dmx_bf16* out, void* stream);
 
+/* Workspace bytes of dmx_prefix_attention for `tokens` tokens (0 if
+ * unsupported): the partial outputs of query blocks whose keys are split. */
+size_t dmx_prefix_attention_workspace_bytes(int32_t tokens);
+
 /* Prefix attention ([Art §2.3]: the LLM attention under the prefix-causal
  * mask mapping).  Query token i of head h reads key token j of KV head h / 2
  * exactly when j <= i and valid[j] != 0 (bucket padding is not valid);
@@ -306,9 +310,11 @@ int dmx_image_merge(const dmx_bf16* tok, const dmx_bf16* img, const int32_t* idx
  *   k, v [4][kv_rows][256] bf16: the layer's cache, tokens at rows 0 ..
  *       tokens - 1 (kv_rows >= tokens); invalid rows are never read
  *   valid [tokens] uint8 (device)
- *   ctx [tokens][8][256] bf16 (out).  tokens <= DMX_MAX_PREFIX. */
+ *   ctx [tokens][8][256] bf16 (out).  tokens <= DMX_MAX_PREFIX.
+ *   ws: >= dmx_prefix_attention_workspace_bytes(tokens) bytes (caller-owned,
+ *   no initialisation). */
 int dmx_prefix_attention(const dmx_bf16* q, const dmx_bf16* k, const dmx_bf16* v, const uint8_t* valid,
-                         int32_t tokens, int32_t kv_rows, dmx_bf16* ctx, void* stream);
+                         int32_t tokens, int32_t kv_rows, dmx_bf16* ctx, void* ws, size_t ws_bytes, void* stream);
 
 /* Weights of one prefix layer (device pointers; matrices tiled by
  * dmx_pack_weight; norm weights use the (1 + w) convention). */

@@ -37,7 +37,7 @@ EXPORTED = (
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
     "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_stage_launch",
     "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill",
-    "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward",
+    "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_attention_workspace_bytes", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward",
     "dmx_sampler_schedule_bytes", "dmx_sampler_schedule_fill", "dmx_sampler_forward", "dmx_sampler_graph_create",
     "dmx_lazy_bucket", "dmx_profile_cache_create", "dmx_profile_cache_destroy", "dmx_profile_cache_plan",
     "dmx_profile_cache_keys", "dmx_profile_cache_run_sampler",
@@ -125,7 +125,8 @@ def lib():
             "dmx_stack_mod_table_bytes": ([i32, i32, i32], sz),
             "dmx_stack_mod_table_fill": ([ctypes.POINTER(StackDesc), P, P], ctypes.c_int),
             "dmx_image_merge": ([P, P, P, i32, i32, i32, P, P], ctypes.c_int),
-            "dmx_prefix_attention": ([P, P, P, P, i32, i32, P, P], ctypes.c_int),
+            "dmx_prefix_attention": ([P, P, P, P, i32, i32, P, P, sz, P], ctypes.c_int),
+            "dmx_prefix_attention_workspace_bytes": ([i32], sz),
             "dmx_prefix_workspace_bytes": ([i32], sz),
             "dmx_prefix_layer_forward": ([ctypes.POINTER(PrefixLayerWeights), P, P, i32, P, P, i32, P, P, sz, P],
                                          ctypes.c_int),
@@ -415,8 +416,9 @@ def image_merge(tok, img, idx, out=None, stream=None):
     return out
 
 
-def prefix_attention(q, k, v, valid, ctx=None, stream=None):
-    """q [T][8][256]; k, v [4][kv_rows][256]; valid [T] uint8 -> ctx [T][8][256]."""
+def prefix_attention(q, k, v, valid, ctx=None, ws=None, stream=None):
+    """q [T][8][256]; k, v [4][kv_rows][256]; valid [T] uint8 -> ctx [T][8][256].
+    ws: optional workspace of dmx_prefix_attention_workspace_bytes(T) bytes."""
     T = q.shape[0]
     kv_rows = k.shape[1]
     _want(q, (T, HQ, D), torch.bfloat16, "q")
@@ -424,7 +426,13 @@ def prefix_attention(q, k, v, valid, ctx=None, stream=None):
     _want(v, (HK, kv_rows, D), torch.bfloat16, "v")
     _want(valid, (T,), torch.uint8, "valid")
     ctx = torch.empty_like(q) if ctx is None else ctx
-    _check(lib().dmx_prefix_attention(_p(q), _p(k), _p(v), _p(valid), T, kv_rows, _p(ctx), _stream(stream)))
+    if ws is None:
+        n = int(lib().dmx_prefix_attention_workspace_bytes(T))
+        if n == 0:
+            raise DmxError(ERR_UNSUPPORTED, f"no prefix attention workspace for {T} tokens")
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(lib().dmx_prefix_attention(_p(q), _p(k), _p(v), _p(valid), T, kv_rows, _p(ctx), _p(ws), ws.numel(),
+                                      _stream(stream)))
     return ctx
 
 

@@ -766,7 +766,7 @@ void dmx_graph_destroy(dmx_graph* g) {
 // padded to 16 rows (tiled activations, fp32 projection outputs).
 namespace {
 struct PrefixLayout {
-  size_t xn, raw, q, ctx, y, x1, xn2, h, pos, total;
+  size_t xn, raw, q, ctx, y, x1, xn2, h, pos, attn, total;
   int TP;
 };
 
@@ -789,6 +789,7 @@ bool prefix_layout(int T, PrefixLayout& L) {
   L.xn2 = take(TP * kPrefixHidden * 2);       // tiled rmsnorm(x1; w_pre_ffn)
   L.h = take(TP * kPrefixInter * 2);          // tiled GEGLU output
   L.pos = take(16);                           // position of token 0 (zero)
+  L.attn = take(prefix_attention_ws_bytes(T));  // attention split partials
   L.total = off;
   return true;
 }
@@ -836,7 +837,7 @@ int enq_prefix_layer(const dmx_prefix_layer_weights* w, const dmx_bf16* x_in, co
   DMX_TRY(hip_check(launch_gemm(GEMM_QKV2560, a, s), "prefix QKV launch"));
   DMX_TRY(hip_check(launch_qknorm_rope(raw, w->q_norm, w->k_norm, pos, 10000.0f, 1, T, L.TP, q, kc, vc, kv_rows, 0, s),
                     "prefix QK-norm/RoPE launch"));
-  DMX_TRY(hip_check(launch_prefix_attention(q, kc, vc, valid, T, kv_rows, ctx, true, s), "prefix attention launch"));
+  DMX_TRY(hip_check(launch_prefix_attention(q, kc, vc, valid, T, kv_rows, ctx, true, at<void>(ws, L.attn), s), "prefix attention launch"));
   // x1 = x + rmsnorm(ctx W_o^T); xn2 = rmsnorm(x1)
   a = g;
   gemm_config(GEMM_PRE_OPROJ, a);
@@ -880,17 +881,26 @@ int dmx_image_merge(const dmx_bf16* tok, const dmx_bf16* img, const int32_t* idx
                    "image merge launch");
 }
 
+size_t dmx_prefix_attention_workspace_bytes(int32_t tokens) {
+  if (tokens < 1 || tokens > DMX_MAX_PREFIX) return 0;
+  return prefix_attention_ws_bytes(tokens) + 256;
+}
+
 int dmx_prefix_attention(const dmx_bf16* q, const dmx_bf16* k, const dmx_bf16* v, const uint8_t* valid,
-                         int32_t tokens, int32_t kv_rows, dmx_bf16* ctx, void* stream) {
+                         int32_t tokens, int32_t kv_rows, dmx_bf16* ctx, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "dmx_prefix_attention";
   DMX_REQUIRE_PTR(q);
   DMX_REQUIRE_PTR(k);
   DMX_REQUIRE_PTR(v);
   DMX_REQUIRE_PTR(ctx);
+  DMX_REQUIRE_PTR(ws);
   if (valid == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: valid is null", fn);
   if (tokens < 1 || tokens > DMX_MAX_PREFIX || kv_rows < tokens || kv_rows > DMX_MAX_PREFIX)
     return fail(DMX_ERR_UNSUPPORTED, "%s: tokens %d / kv_rows %d unsupported", fn, tokens, kv_rows);
-  return hip_check(launch_prefix_attention(q, k, v, valid, tokens, kv_rows, ctx, false, (hipStream_t)stream),
+  if (ws_bytes < prefix_attention_ws_bytes(tokens))
+    return fail(DMX_ERR_WORKSPACE, "%s: workspace %zu bytes, needs %zu", fn, ws_bytes,
+                prefix_attention_ws_bytes(tokens));
+  return hip_check(launch_prefix_attention(q, k, v, valid, tokens, kv_rows, ctx, false, ws, (hipStream_t)stream),
                    "prefix attention launch");
 }
 

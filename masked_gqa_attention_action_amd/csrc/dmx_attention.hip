@@ -447,131 +447,6 @@ hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefix attention of the prefill (OpenDM fast-stack article, §2.3: the LLM
-// attention with the prefix-causal mask mapping): query token i of head h
-// reads key tokens j <= i that are valid prefix tokens, from KV head h / 2 of
-// the layer's cache.  One work-group per (head, block of 64 query tokens);
-// wave w owns query rows 16w .. 16w + 15 of the block, one row per lane, with
-// the same transposed MFMA products and online softmax as the suffix splits.
-// Keys stream through LDS in blocks of 32 (double-buffered: the next block's
-// rows are in flight in registers while the current one is processed), up
-// to the block's last query row.  Blocks are dealt largest-first.
-template <bool CTX_TILED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_prefix_attn(
-    const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid, int T, int kv_rows,
-    uint16_t* ctx) {
-  constexpr int NTHR = 256;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KB * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][KB * VLD];
-  const int nqb = (T + 63) / 64;
-  const int h = blockIdx.x % kHQ, qb = nqb - 1 - blockIdx.x / kHQ;  // the longest key ranges first
-  const int g = h / kGroup;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
-  const int row = qb * 64 + wave * 16 + lr;  // this lane's query token
-  const int key_hi = min(T, qb * 64 + 64);   // keys past the block's last query are never visible
-  const int nkb = (key_hi + KB - 1) / KB;
-  const uint16_t* Kb = k + (size_t)g * kv_rows * kD;
-  const uint16_t* Vb = v + (size_t)g * kv_rows * kD;
-
-  bf16x8 qf[8];
-  const uint16_t* qp = q + ((size_t)min(row, T - 1) * kHQ + h) * kD + lq * 8;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = load_bf16x8(qp + ks * 32);
-
-  // validity of the 32 keys of block kb (the same word in every wave)
-  auto vis_of = [&](int kb) {
-    const int j = kb * KB + lane;
-    const bool ok = lane < KB && j < key_hi && valid[j] != 0;
-    return (uint32_t)__ballot(ok);
-  };
-  KVRegs<NTHR> kv;
-  kv_load(Kb, Vb, 0, key_hi, kv);
-  uint32_t vis = vis_of(0);
-
-  f32x4 o[16];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) o[t] = zero_f32x4();
-  float mrun = kNegBig, lrun = 0.f;
-  const float sl2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(head_dim)
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (vis) kv_store(kv, vis, sK[buf], sV[buf]);
-    __syncthreads();  // the block is staged; every wave is done with the block two back
-    const uint32_t cur = vis;
-    if (kb + 1 < nkb) {
-      kv_load(Kb, Vb, (kb + 1) * KB, key_hi, kv);
-      vis = vis_of(kb + 1);
-    }
-    if (cur == 0u) continue;  // uniform across the work-group
-    const int kb0 = kb * KB;
-    const uint16_t* bK = sK[buf];
-    f32x4 s0 = zero_f32x4(), s1 = zero_f32x4();
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(bK + lr * KLD + ks * 32 + lq * 8);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(bK + (16 + lr) * KLD + ks * 32 + lq * 8);
-      s0 = mfma16(k0, qf[ks], s0);
-      s1 = mfma16(k1, qf[ks], s1);
-    }
-    // s?[r] = S[row][key kb0 + 4lq + r (+16)]: visible when valid and not after the row
-    float x[8];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j0 = 4 * lq + r, j1 = 16 + 4 * lq + r;
-      x[r] = (((cur >> j0) & 1u) && kb0 + j0 <= row) ? s0[r] * sl2 : -INFINITY;
-      x[4 + r] = (((cur >> j1) & 1u) && kb0 + j1 <= row) ? s1[r] * sl2 : -INFINITY;
-      mloc = fmaxf(mloc, fmaxf(x[r], x[4 + r]));
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mnew = fmaxf(mrun, mloc);
-    const float alpha = exp2f(mrun - mnew);
-    mrun = mnew;
-    float psum = 0.f;
-    bf16x8 pf;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float p0 = exp2f(x[e] - mnew), p1 = exp2f(x[e + 1] - mnew);
-      psum += p0 + p1;
-      const uint32_t pk = pack2(p0, p1);
-      pf[e] = (short)(pk & 0xffffu);
-      pf[e + 1] = (short)(pk >> 16);
-    }
-    lrun = lrun * alpha + psum;
-    const uint16_t* bV = sV[buf];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      o[t] *= alpha;
-      o[t] = mfma16(v_frag(bV, t, lane), pf, o[t]);
-    }
-  }
-
-  float l = lrun + __shfl_xor(lrun, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (row >= T) return;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;  // no visible key: zero output
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int col = h * kD + t * 16 + 4 * lq;
-    uint16_t* dst = CTX_TILED ? ctx + tile_off(row, col & ~7, kHQ * kD) + (col & 7) : ctx + (size_t)row * kHQ * kD + col;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(o[t][0] * inv, o[t][1] * inv), pack2(o[t][2] * inv, o[t][3] * inv));
-  }
-}
-
-hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,
-                                   int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, hipStream_t s) {
-  const dim3 grid(kHQ * ((T + 63) / 64));
-  if (ctx_tiled)
-    k_prefix_attn<true><<<grid, dim3(256), 0, s>>>(q, k, v, valid, T, kv_rows, ctx);
-  else
-    k_prefix_attn<false><<<grid, dim3(256), 0, s>>>(q, k, v, valid, T, kv_rows, ctx);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // AdaRMS prenorm (fast-stack article §2.2, "Adarms 调制 prenorm"):
 // xn = x / sqrt(mean x^2 + eps) * (1 + scale[b]) + shift[b], one WG per row.
 // The input row is bf16 (layer input) or fp32 (the layer-internal residual).

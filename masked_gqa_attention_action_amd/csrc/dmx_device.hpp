@@ -107,4 +107,26 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// one 16-byte-per-lane load from global memory straight into LDS: lane i's
+// 16 bytes land at lds_dst + 16 i (lds_dst uniform across the wave)
+__device__ __forceinline__ void lds_copy16(const uint16_t* src, uint16_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+// work-group barrier that orders LDS traffic around it (no memory fence, so
+// loads into LDS that are still in flight are not waited for)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace dmx

@@ -143,9 +143,13 @@ hipError_t launch_prefix_post_norm(const float* y, const float* resid_f32, const
 hipError_t launch_image_merge(const uint16_t* tok, const uint16_t* img, const int32_t* idx, int T, int n_img,
                               int hidden, uint16_t* out, hipStream_t s);
 // prefix attention of the prefill: q row-major [T][8][256]; k, v [4][kv_rows][256];
-// valid [T]; ctx tiled [TP][2048] (ctx_tiled) or row-major [T][8][256]
+// valid [T]; ctx tiled [TP][2048] (ctx_tiled) or row-major [T][8][256]; ws of
+// prefix_attention_ws_bytes(T) bytes for the split partials
+constexpr int kPrefixAttnSplit = 16;  // key blocks of 32 per split
+int prefix_attn_items(int T, int sb);
+size_t prefix_attention_ws_bytes(int T);
 hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,
-                                   int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, hipStream_t s);
+                                   int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, void* ws, hipStream_t s);
 
 // denoise sampler pieces
 constexpr int kMaxActionDim = 128;

@@ -1,0 +1,430 @@
+// Prefix (prefill) attention on 32x32x16 MFMA.  Built with the compiler
+// option that keeps MFMA accumulators in VGPRs: the online softmax rescales
+// the 128 fp32 accumulators of every lane once per key block, which in AGPRs
+// costs a read and a write around every multiply.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "dmx_device.hpp"
+#include "dmx_internal.hpp"
+#include "dmx_tiles.hpp"
+
+namespace dmx {
+
+// ---------------------------------------------------------------------------
+// Prefix attention of the prefill (OpenDM fast-stack article, §2.3: the LLM
+// attention with the prefix-causal mask mapping): query token i of head h
+// reads key tokens j <= i that are valid prefix tokens, from KV head h / 2 of
+// the layer's cache.
+//
+// Work item = (KV head g, block of 64 query tokens, split of at most `sb`
+// key blocks of 32).  Its work-group of 4 waves holds both query heads of the
+// group: wave w takes head 2g + w/2 and query rows 32 (w % 2) .. +31 of the
+// block, so the four waves share one K/V stream.  Products run transposed on
+// 32x32x16 MFMA: S^T = K Q^T (Q^T in registers), O^T += V^T P^T (P^T never
+// leaves registers).  Lane l owns query row l % 32; its 16 logits per block
+// are keys 8 (r / 4) + 4 (l / 32) + r % 4.
+//
+// V^T comes from a transposed copy, [4][Tp / 32][256][32] (Tp = tokens
+// rounded up to 32: each key block's V^T one contiguous 16 KB run), that
+// k_prefix_vt writes with zeros for invisible keys: an MFMA operand needs its
+// 8 keys of one dimension contiguous.  K rows and V^T rows
+// are copied from HBM straight into a ring of LDS stages (global_load_lds,
+// 16 B per lane, STAGES - 1 blocks ahead); every read of a stage is then a
+// plain LDS load that the compiler can tell apart from the stages being
+// filled.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled
+// (K by key, V^T by dimension), so the fragment reads hit distinct banks.
+// Invisible keys' logits are masked by selection and their values are exact
+// zeros, so whatever the cache holds there cannot reach an output.
+//
+// Items are ordered by query block, longest key ranges first.  A query
+// block whose keys span several splits gets normalised partial outputs and
+// (max, sum) per split, merged by k_prefix_attn_merge; a single split writes
+// the context directly.
+namespace {
+constexpr float kNegBig = -1e30f;
+constexpr int kPaKB = 32;        // keys per block
+constexpr int kPaMaxSplit = 64;  // key blocks per split (upper bound)
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// K: 16-byte chunk c (of 32) of key row j sits at chunk c ^ swz_k(j);
+// V^T: chunk c (of 4, 8 keys each) of dimension row d at chunk c ^ swz_v(d)
+__device__ __forceinline__ int swz_k(int j) { return j & 15; }
+__device__ __forceinline__ int swz_v(int d) { return (d >> 2) & 3; }
+
+// query block qb, split index and key-block range of work item `item`
+// (items ordered by query block, longest first); false past the last item
+struct PaItem {
+  int qb, split, ns, first, kb_lo, kb_hi;
+};
+__host__ __device__ __forceinline__ bool pa_item(int item, int T, int sb, PaItem& it) {
+  const int nqb = (T + 63) / 64, nkb_all = (T + kPaKB - 1) / kPaKB;
+  int first = 0;
+  for (int qb = nqb - 1; qb >= 0; --qb) {
+    const int nkb = min(nkb_all, 2 * qb + 2);
+    const int ns = (nkb + sb - 1) / sb;
+    if (item < first + ns) {
+      it.qb = qb;
+      it.split = item - first;
+      it.ns = ns;
+      it.first = first;
+      it.kb_lo = it.split * sb;
+      it.kb_hi = min(it.kb_lo + sb, nkb);
+      return true;
+    }
+    first += ns;
+  }
+  return false;
+}
+}  // namespace
+
+int prefix_attn_items(int T, int sb) {
+  const int nqb = (T + 63) / 64, nkb_all = (T + kPaKB - 1) / kPaKB;
+  int n = 0;
+  for (int qb = 0; qb < nqb; ++qb) n += (min(nkb_all, 2 * qb + 2) + sb - 1) / sb;
+  return n;
+}
+
+// ctx element offset of (token, column col .. col+3) of the context
+template <bool CTX_TILED>
+__device__ __forceinline__ size_t ctx_off(int row, int col) {
+  return CTX_TILED ? tile_off(row, col & ~7, kHQ * kD) + (col & 7) : (size_t)row * kHQ * kD + col;
+}
+
+// vt[g][kb][d][.] = v[g][32 kb + j][d] for valid keys 32 kb + j < T, else 0.
+// Inside each block of 32 keys, 16-byte chunk c = 2m + h holds keys 16m + 4h
+// + e and 16m + 8 + 4h + e (e < 4): the 8 keys one lane of the P^T operand
+// holds, so one 16-byte read gives the matching V^T operand.  One work-group
+// per (block of 32 keys, KV head), staged through LDS.
+__global__ __launch_bounds__(256) void k_prefix_vt(const uint16_t* v, const uint8_t* valid, int T, int kv_rows,
+                                                  int Tp, uint16_t* vt) {
+  __shared__ uint16_t tile[kPaKB][kD + 2];
+  const int kb = blockIdx.x, g = blockIdx.y;
+  {
+    const int j = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 32;  // key row, 32 dims
+    const int key = kb * kPaKB + j;
+    const bool ok = key < T && valid[key] != 0;
+    const uint16_t* src = v + ((size_t)g * kv_rows + min(key, T - 1)) * kD + c0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 raw = ok ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[j][c0 + c * 8 + 2 * e] = (uint16_t)(w4[e] & 0xffffu);
+        tile[j][c0 + c * 8 + 2 * e + 1] = (uint16_t)(w4[e] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  const int d = threadIdx.x;  // one dimension row: the block's 32 keys, 64 bytes
+  uint16_t* dst = vt + (((size_t)g * (Tp / kPaKB) + kb) * kD + d) * kPaKB;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int k0 = 16 * (c >> 1) + 4 * (c & 1);  // keys k0 .. k0+3, then k0+8 .. k0+11
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ka = k0 + (e >> 1) * 8 + 2 * (e & 1);
+      w4[e] = (uint32_t)tile[ka][d] | ((uint32_t)tile[ka + 1][d] << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + c * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+}
+
+template <bool CTX_TILED>
+__global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+                                                    const uint8_t* valid, int T, int kv_rows, int Tp, int sb,
+                                                    int items, uint16_t* ctx, uint16_t* part_o, float* part_ml) {
+  constexpr int STAGES = 4, AHEAD = STAGES - 1;
+  constexpr int PIECES = 4;  // 1 KB pieces of K (and of V^T) each wave copies per block
+  // One array per stage, each holding a block's K rows and V^T rows, and
+  // the stage of every copy and read known at compile time: the compiler
+  // then sees that the stage being read is not one being filled (it tracks
+  // copies into LDS per array) and waits only where the code says so.
+  __shared__ __attribute__((aligned(16))) uint16_t sKV0[2][kPaKB * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV1[2][kPaKB * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV2[2][kPaKB * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV3[2][kPaKB * kD];
+  __shared__ uint32_t sVis[kPaMaxSplit + STAGES];
+  auto stage = [&](auto ST) -> uint16_t(*)[kPaKB * kD] {
+    constexpr int S = decltype(ST)::value;
+    if constexpr (S == 0) return sKV0;
+    else if constexpr (S == 1) return sKV1;
+    else if constexpr (S == 2) return sKV2;
+    else return sKV3;
+  };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = blockIdx.x % kHK, item = blockIdx.x / kHK;
+  PaItem it;
+  if (!pa_item(item, T, sb, it)) return;  // uniform per work-group
+  const int nblk = it.kb_hi - it.kb_lo;
+  // blocks run in groups of STAGES with no branch between them (a branch in
+  // the loop makes the compiler wait for every copy in flight); the padding
+  // blocks at the end have no visible key and add exactly nothing
+  const int npad = (nblk + STAGES - 1) / STAGES * STAGES;
+  const int hq = g * kGroup + (wave >> 1);
+  const int h = lane >> 5;
+  const int row = it.qb * 64 + (wave & 1) * 32 + (lane & 31);  // this lane's query token
+
+  // Q^T operand: lane l holds dims 16 s + 8 h .. +7 of its row, s < 16
+  bf16x8 qf[16];
+  const uint16_t* qp = q + ((size_t)min(row, T - 1) * kHQ + hq) * kD + 8 * h;
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) qf[s2] = load_bf16x8(qp + 16 * s2);
+  // visibility of the 32 keys of every block of the split (none in the
+  // padding blocks)
+  for (int i = wave; i < npad; i += 4) {
+    const int j = (it.kb_lo + i) * kPaKB + lane;
+    const bool ok = i < nblk && lane < kPaKB && j < T && valid[j] != 0;
+    const uint64_t b = __ballot(ok);
+    if (lane == 0) sVis[i] = (uint32_t)b;
+  }
+  // this wave's copy sources at the split's first block: K rows (a key past
+  // the tokens reads the last token's row; its logit is masked) and V^T rows
+  const uint16_t* ksrc[PIECES];
+  const uint16_t* vsrc[PIECES];
+#pragma unroll
+  for (int d = 0; d < PIECES; ++d) {
+    const int piece = wave * PIECES + d;
+    const int j = piece * 2 + (lane >> 5);  // K: key row of the block
+    ksrc[d] = k + ((size_t)g * kv_rows + it.kb_lo * kPaKB + j) * kD + (((lane & 31) ^ swz_k(j)) * 8);
+    const int dv = piece * 16 + (lane >> 2);  // V^T: dimension row
+    vsrc[d] = vt + (((size_t)g * (Tp / kPaKB) + it.kb_lo) * kD + dv) * kPaKB + (((lane & 3) ^ swz_v(dv)) * 8);
+  }
+  const int last_key_row = T - 1 - it.kb_lo * kPaKB;  // rows past it are clamped
+  wait_vmcnt<0>();
+  // consume the Q registers here: otherwise their loads may be scheduled past
+  // the wait above and the first MFMA of every block would wait for all the
+  // copies in flight
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) __asm__ volatile("" ::"v"(qf[s2]));
+  __syncthreads();
+
+  // block i of the split into stage ST (past the end: the last block again,
+  // into a stage that is never read, so every wave issues PIECES * 2 copies
+  // per call and the counter arithmetic stays uniform)
+  auto issue = [&](auto ST, int i) {
+    uint16_t(*b)[kPaKB * kD] = stage(ST);
+    const int ib = min(i, nblk - 1);
+#pragma unroll
+    for (int d = 0; d < PIECES; ++d) {
+      const int piece = wave * PIECES + d;
+      const int j = piece * 2 + (lane >> 5);
+      const int over = max(0, ib * kPaKB + j - last_key_row);  // rows past the tokens: the last one
+      lds_copy16(ksrc[d] + ((size_t)ib * kPaKB - over) * kD, &b[0][piece * 512]);
+      lds_copy16(vsrc[d] + (size_t)ib * kD * kPaKB, &b[1][piece * 512]);
+    }
+  };
+  issue(std::integral_constant<int, 0>{}, 0);
+  issue(std::integral_constant<int, 1>{}, 1);
+  issue(std::integral_constant<int, 2>{}, 2);
+
+  f32x16 o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float mrun = kNegBig, lrun = 0.f;
+  const float sl2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(head_dim)
+
+  // block ib, held in stage ST = ib % STAGES
+  auto body = [&](auto ST, int ib) {
+    constexpr int S = decltype(ST)::value;
+    wait_vmcnt<(AHEAD - 1) * PIECES * 2>();  // this wave's copies of block ib landed
+    lds_barrier();                           // everyone's have; stage (ib - 1) is free
+    issue(std::integral_constant<int, (S + AHEAD) % STAGES>{}, ib + AHEAD);
+    const int kb0 = (it.kb_lo + ib) * kPaKB;
+    const uint32_t vis = sVis[ib];
+    const uint16_t* bK = stage(ST)[0];
+    const uint16_t* bV = stage(ST)[1];
+
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    {
+      const int j = lane & 31;
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(bK + j * kD + (((2 * s2 + h) ^ swz_k(j)) * 8));
+        sacc = mfma32(kf, qf[s2], sacc);
+      }
+    }
+    float x[16];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+      x[r] = (((vis >> key) & 1u) && kb0 + key <= row) ? sacc[r] * sl2 : -INFINITY;
+      mloc = fmaxf(mloc, x[r]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(mrun, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // exp2(-inf) = 0 in hardware
+    mrun = mnew;
+    bf16x8 pf[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(x[r] - mnew), p1 = __builtin_amdgcn_exp2f(x[r + 1] - mnew);
+      psum += p0 + p1;
+      const uint32_t pk = pack2(p0, p1);
+      pf[r >> 3][r & 7] = (short)(pk & 0xffffu);
+      pf[r >> 3][(r & 7) + 1] = (short)(pk >> 16);
+    }
+    lrun = lrun * alpha + psum;
+    // unconditional (alpha = 1 leaves o as it is): see the loop comment
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    // V^T operand of dims 32 t + (l % 32): chunk 2m + h of the dimension's
+    // row holds keys 16 m + 4 h + e and 16 m + 8 + 4 h + e (e < 4), the key
+    // order of P^T's elements above
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int dv = 32 * t + (lane & 31);
+      const uint16_t* vrow = bV + dv * kPaKB;
+      const int sw = swz_v(dv);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + (((2 * m + h) ^ sw) * 8));
+        o[t] = mfma32(vf, pf[m], o[t]);
+      }
+    }
+  };
+#pragma unroll 1
+  for (int ib = 0; ib < npad; ib += STAGES) {
+    body(std::integral_constant<int, 0>{}, ib);
+    body(std::integral_constant<int, 1>{}, ib + 1);
+    body(std::integral_constant<int, 2>{}, ib + 2);
+    body(std::integral_constant<int, 3>{}, ib + 3);
+  }
+  wait_vmcnt<0>();  // the trailing copies (never read) are done before the work-group ends
+
+  const float l = lrun + __shfl_xor(lrun, 32, 64);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;  // no visible key: zero output
+  if (it.ns == 1) {
+    if (row >= T) return;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = hq * kD + 32 * t + 8 * q4 + 4 * h;
+        *reinterpret_cast<uint2*>(ctx + ctx_off<CTX_TILED>(row, col)) =
+            make_uint2(pack2(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv),
+                       pack2(o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv));
+      }
+    return;
+  }
+  // partial of this split: [g][item][wave][32 rows][256] bf16 normalised, and (max, sum)
+  const size_t pidx = ((size_t)g * items + item) * 4 + wave;
+  uint16_t* po = part_o + (pidx * 32 + (lane & 31)) * kD;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * t + 8 * q4 + 4 * h;
+      *reinterpret_cast<uint2*>(po + d) = make_uint2(pack2(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv),
+                                                     pack2(o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv));
+    }
+  if (lane < 32) *reinterpret_cast<float2*>(part_ml + (pidx * 32 + lane) * 2) = make_float2(mrun, l);
+}
+
+// Merge of the splits of one (KV head, query block, wave tile): for each of
+// the tile's 32 rows, M = max m_s, w_s = l_s 2^(m_s - M), out = sum_s w_s o_s /
+// sum_s w_s (zero when no split saw a visible key), in split order.  One
+// work-group of 256 threads per (g, query block, tile); 8 threads per row,
+// 32 dims each.  Query blocks with a single split return at once.
+template <bool CTX_TILED>
+__global__ __launch_bounds__(256) void k_prefix_attn_merge(int T, int sb, int items, const uint16_t* part_o,
+                                                          const float* part_ml, uint16_t* ctx) {
+  const int nqb = (T + 63) / 64;
+  const int tile = blockIdx.x & 3, g = (blockIdx.x >> 2) % kHK, qb = (blockIdx.x >> 2) / kHK;
+  if (qb >= nqb) return;
+  // the first item of query block qb
+  const int nkb_all = (T + kPaKB - 1) / kPaKB;
+  int first = 0;
+  for (int b = nqb - 1; b > qb; --b) first += (min(nkb_all, 2 * b + 2) + sb - 1) / sb;
+  const int ns = (min(nkb_all, 2 * qb + 2) + sb - 1) / sb;
+  if (ns == 1) return;
+  const int rr = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 32;
+  const int row = qb * 64 + (tile & 1) * 32 + rr;
+  if (row >= T) return;
+  const int hq = g * kGroup + (tile >> 1);
+  float M = kNegBig;
+  for (int s2 = 0; s2 < ns; ++s2) {
+    const size_t pidx = ((size_t)g * items + first + s2) * 4 + tile;
+    M = fmaxf(M, part_ml[(pidx * 32 + rr) * 2]);
+  }
+  float acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+  float L = 0.f;
+  for (int s2 = 0; s2 < ns; ++s2) {
+    const size_t pidx = ((size_t)g * items + first + s2) * 4 + tile;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (pidx * 32 + rr) * 2);
+    const float w = ml.y * exp2f(ml.x - M);
+    L += w;
+    const uint16_t* po = part_o + (pidx * 32 + rr) * kD + d0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(po + c * 8);
+      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[c * 8 + 2 * e] += w * bf2f((uint16_t)(wv[e] & 0xffffu));
+        acc[c * 8 + 2 * e + 1] += w * bf2f((uint16_t)(wv[e] >> 16));
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int col = hq * kD + d0 + 4 * c;
+    *reinterpret_cast<uint2*>(ctx + ctx_off<CTX_TILED>(row, col)) =
+        make_uint2(pack2(acc[4 * c] * inv, acc[4 * c + 1] * inv), pack2(acc[4 * c + 2] * inv, acc[4 * c + 3] * inv));
+  }
+}
+
+// workspace: V^T [4][256][Tp], then the split partials ([4][items][4][32][256]
+// bf16 and [4][items][4][32][2] fp32)
+static size_t vt_bytes(int T) { return (size_t)kHK * kD * ((T + kPaKB - 1) / kPaKB * kPaKB) * 2; }
+
+size_t prefix_attention_ws_bytes(int T) {
+  const int items = prefix_attn_items(T, kPrefixAttnSplit);
+  return vt_bytes(T) + (size_t)kHK * items * 4 * 32 * (kD * 2 + 2 * sizeof(float));
+}
+
+hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,
+                                   int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, void* ws, hipStream_t s) {
+  const int sb = kPrefixAttnSplit;
+  const int items = prefix_attn_items(T, sb);
+  const int Tp = (T + kPaKB - 1) / kPaKB * kPaKB;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(w);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(w + vt_bytes(T));
+  float* part_ml = reinterpret_cast<float*>(w + vt_bytes(T) + (size_t)kHK * items * 4 * 32 * kD * 2);
+  k_prefix_vt<<<dim3(Tp / kPaKB, kHK), dim3(256), 0, s>>>(v, valid, T, kv_rows, Tp, vt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(kHK * items);
+  if (ctx_tiled)
+    k_prefix_attn<true><<<grid, dim3(256), 0, s>>>(q, k, vt, valid, T, kv_rows, Tp, sb, items, ctx, part_o,
+                                                           part_ml);
+  else
+    k_prefix_attn<false><<<grid, dim3(256), 0, s>>>(q, k, vt, valid, T, kv_rows, Tp, sb, items, ctx, part_o,
+                                                            part_ml);
+  e = hipGetLastError();
+  if (e != hipSuccess || (T + kPaKB - 1) / kPaKB <= sb) return e;  // every query block in one split
+  const dim3 mgrid(4 * kHK * ((T + 63) / 64));
+  if (ctx_tiled)
+    k_prefix_attn_merge<true><<<mgrid, dim3(256), 0, s>>>(T, sb, items, part_o, part_ml, ctx);
+  else
+    k_prefix_attn_merge<false><<<mgrid, dim3(256), 0, s>>>(T, sb, items, part_o, part_ml, ctx);
+  return hipGetLastError();
+}
+
+}  // namespace dmx

@@ -104,9 +104,12 @@ def test_validation_errors_before_launch(dmx):
     assert L.dmx_stack_mod_table_fill(None, FAKE, None) == dmx.ERR_INVALID_ARG
     assert L.dmx_prefix_workspace_bytes(0) == 0 and L.dmx_prefix_workspace_bytes(5000) == 0
     assert L.dmx_prefix_workspace_bytes(2048) > L.dmx_prefix_workspace_bytes(96) > 0
-    assert L.dmx_prefix_attention(None, FAKE, FAKE, FAKE, 10, 10, FAKE, None) == dmx.ERR_INVALID_ARG
-    assert L.dmx_prefix_attention(FAKE, FAKE, FAKE, FAKE, 20, 10, FAKE, None) == dmx.ERR_UNSUPPORTED
-    assert L.dmx_prefix_attention(FAKE, FAKE, FAKE, None, 10, 10, FAKE, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_prefix_attention(None, FAKE, FAKE, FAKE, 10, 10, FAKE, FAKE, 1 << 30, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_prefix_attention(FAKE, FAKE, FAKE, FAKE, 20, 10, FAKE, FAKE, 1 << 30, None) == dmx.ERR_UNSUPPORTED
+    assert L.dmx_prefix_attention(FAKE, FAKE, FAKE, None, 10, 10, FAKE, FAKE, 1 << 30, None) == dmx.ERR_INVALID_ARG
+    assert L.dmx_prefix_attention(FAKE, FAKE, FAKE, FAKE, 2048, 2048, FAKE, FAKE, 1024, None) == dmx.ERR_WORKSPACE
+    assert L.dmx_prefix_attention_workspace_bytes(0) == 0
+    assert L.dmx_prefix_attention_workspace_bytes(2048) > L.dmx_prefix_attention_workspace_bytes(64) > 0
     assert L.dmx_image_merge(FAKE, FAKE, FAKE, 4, 2, 12, FAKE, None) == dmx.ERR_UNSUPPORTED
     assert L.dmx_image_merge(FAKE, FAKE, None, 4, 2, 16, FAKE, None) == dmx.ERR_INVALID_ARG
     assert L.dmx_prefix_layer_forward(None, FAKE, FAKE, 8, FAKE, FAKE, 8, FAKE, FAKE, 1 << 30,

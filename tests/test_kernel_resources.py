@@ -17,7 +17,7 @@ HOST_ONLY = ("dmx_api.hip", "dmx_profiles.hip")  # sources that define no kernel
 def _report(src):
     cmd = [build.hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
-           "-Rpass-analysis=kernel-resource-usage"]
+           "-Rpass-analysis=kernel-resource-usage"] + build.SOURCE_FLAGS.get(src, [])
     out = subprocess.run(cmd, capture_output=True, text=True, check=True).stderr
     kernels, name = {}, None
     for line in out.splitlines():
