@@ -87,7 +87,8 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = ("dmx_attention.hip", "dmx_gemm.hip", "dmx_prefix.hip", "dmx_sampler.hip", "dmx_device.hpp",
+KERNEL_SOURCES = ("dmx_attention.hip", "dmx_gemm.hip", "dmx_prefix.hip", "dmx_prefix_attn.hip", "dmx_sampler.hip",
+                  "dmx_device.hpp",
                   "dmx_internal.hpp",
                   "dmx_tiles.hpp")
 
