@@ -396,3 +396,26 @@ def lazy_profile_actions(calls, capacity: int = 8, evict: bool = True):
         order.append([key, fp, 1])
         out.append((EAGER, evicted))
     return out, [p[0] for p in order]
+
+
+def prefix_layer_rows(x, w: dict, valid, rows, hq=8, hk=4, d=256, base=10000.0, eps=1e-6):
+    """prefix_layer's output at the token rows `rows` only, plus the whole K/V
+    cache: every row's K and V (and the attention of the chosen rows over all
+    earlier rows) is still computed; the projections and MLP after the
+    attention run for the chosen rows only.  The same steps in the same
+    order as orc_prefix_layer, for token counts where the full layer is too
+    slow.  Returns (out [len(rows)][H], k [hk][T][d], v [hk][T][d])."""
+    x = _f64(x)
+    T, H = x.shape
+    ww = {kk: _f64(w[kk]) for kk in PREFIX_WEIGHTS}
+    rows = np.asarray(rows, dtype=np.int64)
+    xn = rmsnorm(x, ww["w_in"], eps)
+    q, k, v = qkv_qknorm_rope(xn, ww["w_qkv"], ww["q_norm"], ww["k_norm"], np.arange(T, dtype=np.int32), hq, hk, d,
+                              base, eps)
+    ctx = prefix_attention(q, k, v, valid)[rows].reshape(len(rows), hq * d)
+    x1 = x[rows] + rmsnorm(linear(ctx, ww["w_o"]), ww["w_post_attn"], eps)
+    gu = linear(rmsnorm(x1, ww["w_pre_ffn"], eps), ww["w_gu"])
+    I_ = gu.shape[1] // 2
+    hdn = np.vectorize(gelu_tanh)(gu[:, :I_]) * gu[:, I_:]
+    out = x1 + rmsnorm(linear(hdn, ww["w_down"]), ww["w_post_ffn"], eps)
+    return out, k, v

@@ -679,3 +679,23 @@ def test_sampler_schedule_runs_from_time_one():
         v = sw["w_out"] @ (sw["w_fmod"][H:] @ cond + sw["b_fmod"][H:]) + sw["b_out"]
         np.testing.assert_allclose(traj[k], prev - 0.5 * v, rtol=1e-12, atol=1e-12)
         prev = traj[k]
+
+
+def test_prefix_layer_rows_equals_full_layer():
+    """The row-sampled prefix layer (used at 2048 tokens) is the full layer's
+    output at those rows, K/V cache included."""
+    r = rng(80)
+    T, H, I_, hq, hk, d = 21, 16, 24, 4, 2, 8
+    w = {"w_in": 0.3 * r.standard_normal(H), "w_qkv": 0.3 * r.standard_normal(((hq + 2 * hk) * d, H)),
+         "q_norm": 0.3 * r.standard_normal(d), "k_norm": 0.3 * r.standard_normal(d),
+         "w_o": 0.3 * r.standard_normal((H, hq * d)), "w_post_attn": 0.3 * r.standard_normal(H),
+         "w_pre_ffn": 0.3 * r.standard_normal(H), "w_gu": 0.3 * r.standard_normal((2 * I_, H)),
+         "w_down": 0.3 * r.standard_normal((H, I_)), "w_post_ffn": 0.3 * r.standard_normal(H)}
+    x = r.standard_normal((T, H))
+    valid = (r.random(T) < 0.8).astype(np.uint8)
+    valid[0] = 1
+    full, k, v = orc.prefix_layer(x, w, valid, hq=hq, hk=hk, d=d)
+    rows = [0, 3, 7, 20]
+    out, k2, v2 = orc.prefix_layer_rows(x, w, valid, rows, hq=hq, hk=hk, d=d)
+    np.testing.assert_allclose(out, full[rows], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(k2, k) and np.array_equal(v2, v)

@@ -117,3 +117,27 @@ def test_prefix_layer_is_deterministic(prefix_weights):
     torch.cuda.synchronize()
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+def test_prefix_layer_2048_tokens_sampled_rows(prefix_weights):
+    """The benchmarked size: 2048 tokens (1936 valid, 2 % holes), the launch
+    the benchmark times.  Against the oracle on 24 sampled rows (first, last,
+    holes, padding, spread) and on the whole K/V cache."""
+    wbits, wd = prefix_weights
+    T = 2048
+    x, valid = synth.prefix_inputs(synth.BASE_SEED + 9900, T, 1936, 0.02)
+    kc = torch.full((4, T, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((4, T, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = dmx.prefix_layer_forward(wd, to_dev(x), to_dev(valid, "raw"), kc, vc)
+    torch.cuda.synchronize()
+    r = rng(11)
+    holes = np.flatnonzero(valid[:1936] == 0)
+    rows = sorted(set([0, 1, 63, 64, 1935, 1936, 2047] + [int(i) for i in holes[:3]] +
+                      [int(i) for i in r.integers(0, T, 14)]))
+    print(f"prefix layer T=2048: {int(valid.sum())} valid, rows {rows}", flush=True)
+    ref, rk, rv = orc.prefix_layer_rows(f64(x), {k: f64(v) for k, v in wbits.items()}, valid, rows)
+    got = from_dev(out)[rows]
+    stage_gate("prefix layer T=2048 rows", got, ref, rel=PREFIX_OUT_REL)
+    delta_gate("prefix layer T=2048 rows branch", got, ref, f64(x)[rows], rel=LAYER_BRANCH_REL)
+    stage_gate("prefix k cache T=2048", from_dev(kc), rk)
+    stage_gate("prefix v cache T=2048", from_dev(vc), rv)
