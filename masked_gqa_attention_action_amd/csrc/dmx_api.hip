@@ -645,15 +645,16 @@ struct SamplerRun {
 static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, const SamplerRun* smp = nullptr) {
   const int rows = d->batch * d->chunk;
   for (int st = 0; st < d->n_steps; ++st) {
-    if (smp)
+    // the sampler's first in-projection; later ones come with the step tail
+    if (smp && st == 0)
       DMX_TRY(hip_check(launch_action_in(smp->actions, smp->w->w_in, smp->w->b_in, rows, smp->w->action_dim, d->x, s),
                         "action in-projection launch"));
     if (!d->mod_table) DMX_TRY(enq_stack_mods(d, L, st, s));
     // the first layer's scaled tiled input and its row statistics: a pack
     // pass at the start of the run, and of every step whose modulation was
-    // not known to the last down projection before it (no table) or whose
-    // input is new (sampler); otherwise that down projection wrote them
-    if (st == 0 || !d->mod_table || smp)
+    // not known before it (no table); otherwise the last down projection
+    // (plain stack) or the step tail (sampler) wrote them
+    if (st == 0 || !d->mod_table)
       DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, stack_mod(d, L, st, 0, 0), d->ws, L, s));
     for (int l = 0; l < d->n_layers; ++l) {
       const dmx_prefix_kv kv{d->k_pre[l], d->v_pre[l], d->mask, d->p_bucket};
@@ -661,10 +662,20 @@ static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, 
     }
     if (smp) {
       const int A = smp->w->action_dim;
+      const float dt = -1.0f / (float)d->n_steps;
+      const float* fmod = smp->fmod + (size_t)st * 2 * kH;
       float* traj = smp->traj ? smp->traj + (size_t)st * rows * A : nullptr;
-      DMX_TRY(hip_check(launch_final_velocity(d->x, smp->fmod + (size_t)st * 2 * kH, smp->w->w_out, smp->w->b_out,
-                                              rows, A, -1.0f / (float)d->n_steps, smp->actions, traj, s),
-                        "final velocity launch"));
+      if (st + 1 < d->n_steps) {
+        const float* scale1 = d->mod_table ? stack_mod(d, L, st + 1, 0, 0) : nullptr;
+        DMX_TRY(hip_check(launch_step_tail(d->x, fmod, smp->w->w_out, smp->w->b_out, smp->w->w_in, smp->w->b_in, rows,
+                                           A, dt, smp->actions, traj, d->x, d->chunk, L.TP, scale1, 3 * kH,
+                                           at<uint16_t>(d->ws, L.xp), at<float>(d->ws, L.ss_b), s),
+                          "step tail launch"));
+      } else {
+        DMX_TRY(hip_check(launch_final_velocity(d->x, fmod, smp->w->w_out, smp->w->b_out, rows, A, dt, smp->actions,
+                                                traj, s),
+                          "final velocity launch"));
+      }
     }
   }
   return DMX_OK;

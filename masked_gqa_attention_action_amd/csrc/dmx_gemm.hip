@@ -935,6 +935,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
       case GEMM_GATEUP_MOD: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4); break;
       case GEMM_DOWN: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 2, 2); break;
       case GEMM_DOWN_F32RES: DMX_GEMM_BIG(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 2, 2); break;
+      default: break;  // the prefix kinds returned above
     }
     return hipGetLastError();
   }
@@ -953,6 +954,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
     case GEMM_GATEUP_MOD: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, nreq); break;
     case GEMM_DOWN: DMX_GEMM(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 1, mb1); break;
     case GEMM_DOWN_F32RES: DMX_GEMM(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 1, mb1); break;
+    default: break;
   }
   return hipGetLastError();
 }

@@ -161,6 +161,12 @@ hipError_t launch_action_in(const float* a, const uint16_t* w_in, const uint16_t
                             hipStream_t s);
 hipError_t launch_final_velocity(const uint16_t* x, const float* fmod, const uint16_t* w_out, const uint16_t* b_out,
                                  int rows, int A, float dt, float* a, float* traj, hipStream_t s);
+// final_velocity of one step + action_in of the next (+ its input pack when
+// scale1 is given): rows = B * T, the packed input at tiled rows b * TP + t
+hipError_t launch_step_tail(const uint16_t* x, const float* fmod, const uint16_t* w_out, const uint16_t* b_out,
+                            const uint16_t* w_in, const uint16_t* b_in, int rows, int A, float dt, float* a,
+                            float* traj, uint16_t* x_next, int T, int TP, const float* scale1, int scale_stride,
+                            uint16_t* xp, float* ss, hipStream_t s);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 

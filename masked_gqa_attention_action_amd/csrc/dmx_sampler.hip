@@ -9,9 +9,10 @@
 //   norm with [scale | shift] = W_f cond + b_f, v = W_out xf + b_out, and the
 //   Euler step a <- a - v / n.
 // The schedule side (temb, time MLP, final modulation) depends on the step
-// only and runs once per schedule; the per-step side is two small kernels
-// around the stack: the action in-projection and the fused final norm +
-// out-projection + Euler update.
+// only and runs once per schedule; per step, the stack is bracketed by the
+// action in-projection and the fused final norm + out-projection + Euler
+// update, the latter fused with the next step's in-projection (and its input
+// pack) between steps.
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
 #include "dmx_tiles.hpp"
@@ -137,6 +138,103 @@ __global__ __launch_bounds__(256) void k_final_velocity(const uint16_t* x, const
     a[(size_t)row * A + j] = an;
     if (traj) traj[(size_t)row * A + j] = an;
   }
+}
+
+// The end of step k and the start of step k + 1 for one token row, fused:
+// the final norm + out-projection + Euler update of k_final_velocity, then
+// x = bf16(W_in a + b_in) for the next step (k_action_in), and, when the next
+// step's first modulation is known (scale1 not null), the packed input the
+// first layer reads: bf16(x * (1 + scale1)) tiled at row prow and the 64
+// sums of squares of 16 columns of x, summed in column order as
+// k_pack_rows does.  One work-group per row, 4 features per thread.
+__global__ __launch_bounds__(256) void k_step_tail(const uint16_t* x, const float* fmod, const uint16_t* w_out,
+                                                  const uint16_t* b_out, const uint16_t* w_in, const uint16_t* b_in,
+                                                  int A, float dt, float* a, float* traj, uint16_t* x_next, int T,
+                                                  int TP, const float* scale1, int scale_stride, uint16_t* xp,
+                                                  float* ss) {
+  __shared__ float red[4][kMaxActionDim];
+  __shared__ float rss[4];
+  __shared__ float sa[kMaxActionDim];
+  __shared__ float sq[kH];
+  const int row = blockIdx.x, c = threadIdx.x * 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  {  // step k: velocity and Euler update (as k_final_velocity)
+    const uint2 raw = *reinterpret_cast<const uint2*>(x + (size_t)row * kH + c);
+    float v[4] = {bf2f((uint16_t)(raw.x & 0xffffu)), bf2f((uint16_t)(raw.x >> 16)),
+                  bf2f((uint16_t)(raw.y & 0xffffu)), bf2f((uint16_t)(raw.y >> 16))};
+    const float ssum = wave_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+    if (lane == 0) rss[wave] = ssum;
+    __syncthreads();
+    const float r = 1.0f / sqrtf((rss[0] + rss[1] + rss[2] + rss[3]) * (1.0f / kH) + kEps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = v[i] * r * (1.f + fmod[c + i]) + fmod[kH + c + i];
+    for (int j = 0; j < A; ++j) {
+      const uint2 wr = *reinterpret_cast<const uint2*>(w_out + (size_t)j * kH + c);
+      float p = v[0] * bf2f((uint16_t)(wr.x & 0xffffu)) + v[1] * bf2f((uint16_t)(wr.x >> 16)) +
+                v[2] * bf2f((uint16_t)(wr.y & 0xffffu)) + v[3] * bf2f((uint16_t)(wr.y >> 16));
+      p = wave_sum(p);
+      if (lane == 0) red[wave][j] = p;
+    }
+    __syncthreads();
+    if (threadIdx.x < A) {
+      const int j = threadIdx.x;
+      const float vel = red[0][j] + red[1][j] + red[2][j] + red[3][j] + bf2f(b_out[j]);
+      const float an = a[(size_t)row * A + j] + dt * vel;
+      a[(size_t)row * A + j] = an;
+      if (traj) traj[(size_t)row * A + j] = an;
+      sa[j] = an;
+    }
+    __syncthreads();
+  }
+  // step k + 1: the action in-projection (as k_action_in)
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = c + i;
+    const uint16_t* wr = w_in + (size_t)n * A;
+    float acc = 0.f;
+    for (int j = 0; j < A; j += 8) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(wr + j);
+      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += bf2f((uint16_t)(w4[e] & 0xffffu)) * sa[j + 2 * e];
+        acc += bf2f((uint16_t)(w4[e] >> 16)) * sa[j + 2 * e + 1];
+      }
+    }
+    y[i] = acc + bf2f(b_in[n]);
+  }
+  const uint32_t p01 = pack2(y[0], y[1]), p23 = pack2(y[2], y[3]);
+  *reinterpret_cast<uint2*>(x_next + (size_t)row * kH + c) = make_uint2(p01, p23);
+  if (!scale1) return;
+  {  // the packed input of the next step's first layer (as k_pack_rows, with
+     // its rounding: no fused multiply-adds)
+#pragma clang fp contract(off)
+    const int b = row / T, t = row - b * T, prow = b * TP + t;
+    const float xb[4] = {bf2f((uint16_t)(p01 & 0xffffu)), bf2f((uint16_t)(p01 >> 16)),
+                         bf2f((uint16_t)(p23 & 0xffffu)), bf2f((uint16_t)(p23 >> 16))};
+    const float* sp = scale1 + (size_t)b * scale_stride + c;
+    *reinterpret_cast<uint2*>(xp + tile_off(prow, c & ~7, kH) + (c & 7)) =
+        make_uint2(pack2(xb[0] * (1.f + sp[0]), xb[1] * (1.f + sp[1])),
+                   pack2(xb[2] * (1.f + sp[2]), xb[3] * (1.f + sp[3])));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sq[c + i] = xb[i] * xb[i];
+    __syncthreads();
+    if (threadIdx.x < kSsParts) {
+      float acc = 0.f;
+      for (int i = 0; i < 16; ++i) acc += sq[threadIdx.x * 16 + i];
+      ss[(size_t)prow * kSsParts + threadIdx.x] = acc;
+    }
+  }
+}
+
+hipError_t launch_step_tail(const uint16_t* x, const float* fmod, const uint16_t* w_out, const uint16_t* b_out,
+                            const uint16_t* w_in, const uint16_t* b_in, int rows, int A, float dt, float* a,
+                            float* traj, uint16_t* x_next, int T, int TP, const float* scale1, int scale_stride,
+                            uint16_t* xp, float* ss, hipStream_t s) {
+  k_step_tail<<<dim3(rows), dim3(256), 0, s>>>(x, fmod, w_out, b_out, w_in, b_in, A, dt, a, traj, x_next, T, TP,
+                                               scale1, scale_stride, xp, ss);
+  return hipGetLastError();
 }
 
 hipError_t launch_time_embed(int n_steps, uint16_t* temb, hipStream_t s) {
