@@ -13,14 +13,15 @@ from tests.helpers import device_weights, f64, oracle_weights, to_dev
 class Case:
     """Seeded inputs of one sampler run, on the device and for the oracle."""
 
-    def __init__(self, n_layers, n_steps, B, C, P, len_lo, len_hi, hole_p, seed, mod_table=False):
+    def __init__(self, n_layers, n_steps, B, C, P, len_lo, len_hi, hole_p, seed, mod_table=False,
+                 A=synth.ACTION_DIM):
         self.n_layers, self.n_steps, self.B, self.C, self.P = n_layers, n_steps, B, C, P
         wbits = [synth.layer_weights(seed + 100 + l) for l in range(n_layers)]
         self.rqs = [synth.make_request(seed + b, C, P, len_lo, len_hi, n_layers, hole_p) for b in range(B)]
-        self.swbits = synth.sampler_weights(seed + 500)
-        self.noise = synth.sampler_noise(seed + 600, B, C)
+        self.swbits = synth.sampler_weights(seed + 500, a=A)
+        self.noise = synth.sampler_noise(seed + 600, B, C, a=A)
         self.A = self.noise.shape[2]
-        print(f"sampler case: L={n_layers} steps={n_steps} B={B} C={C} P_b={P} "
+        print(f"sampler case: A={A} L={n_layers} steps={n_steps} B={B} C={C} P_b={P} "
               f"valid={[r.valid_len for r in self.rqs]} seed={seed}", flush=True)
         self.wbits = wbits
         self.wd = [device_weights(w) for w in wbits]

@@ -9,7 +9,9 @@ against the float64 oracle.
 - graph replay == eager run, bit for bit, also on new noise; with and without
   the modulation table, bit for bit;
 - a small run end to end against the oracle's free run (cosine);
-- the 18-layer, 10-step run at the P_b=896 bucket, every step teacher forced.
+- the 18-layer, 10-step run at the P_b=896 bucket, every step teacher forced;
+- action dimensions from 16 to 128 (one to four out-projection passes), every
+  step teacher forced, with and without the table bit for bit.
 """
 from __future__ import annotations
 
@@ -159,3 +161,24 @@ def test_full_size_steps_teacher_forced():
     sw, layers = c.oracle_inputs()
     worst = teacher_forced_steps(c, sw, layers)
     print(f"worst velocity ratio over the 10 steps: {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("A", [16, 48, 128])
+def test_action_dims(A):
+    """The velocity kernels are instantiated per action dimension: one pass
+    of 32 outputs (half idle at 16), two passes (the second half idle at 48),
+    four passes at 128; the in-projection's weights are preloaded up to 32."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = Case(2, 3, 2, 10, 576, 500, 576, 0.05, synth.BASE_SEED + 7400 + A, A=A)
+    c.sampler.run()
+    torch.cuda.synchronize()
+    sw, layers = c.oracle_inputs()
+    teacher_forced_steps(c, sw, layers)
+    t = Case(2, 3, 2, 10, 576, 500, 576, 0.05, synth.BASE_SEED + 7400 + A, mod_table=True, A=A)
+    t.sampler.run()
+    torch.cuda.synchronize()
+    assert torch.equal(t.traj, c.traj), "the cached table changes the run"
+    for x in (t, c):
+        x.sampler.close()
+        x.stack.close()
