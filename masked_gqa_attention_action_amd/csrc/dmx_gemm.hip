@@ -479,13 +479,13 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
 // tokens): the same arithmetic as k_gemm, bit for bit, on a schedule that
 // keeps the MFMA units busy.  K is split into NR ranges of KSR 32-column steps
 // (k_gemm's waves); each range is accumulated from zero in step order by the
-// same MFMA, and the range sums are added in range order in LDS.  The shift
+// same MFMA, and the range sums are added in range order.  The shift
 // tile of the fused AdaRMS holds one row per request of the block.  The
 // epilogue is the same tile_epilogue, once per output tile of the block.
 // A work-group of 4 waves (2 x 2) owns BM rows x BNF 16-column fragments: wave
 // (wm, wn) the rows wm*WMT*16 .. and the fragments wn*WNF ..; every fragment is
 // loaded straight from the tiled operands into registers (one 1 KB load per
-// wave and fragment) one step ahead of its MFMAs.
+// wave and fragment) PD steps ahead of its MFMAs.
 template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int WNF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_big(GemmArgs a) {
   constexpr bool MOD = ASRC == A_MODPRE;
@@ -499,7 +499,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NST = BNF / NTT;     // output tiles per block
   constexpr int KS = NR * KSR;       // 32-column steps of K
   constexpr int MAXREQ = BM / 16 + 1;  // requests a block can touch (at least 16 rows each)
-  constexpr int PD = 2;              // steps in flight per wave
+  // steps in flight per wave: 8 where the fragments are few (64 x 64 blocks,
+  // 32 KB per wave), else what the registers allow
+  constexpr int PD = WMT + WNF <= 4 ? 8 : 2;
   static_assert(KSR % PD == 0 && BNF % NTT == 0, "block shape");
   static_assert(!MOD || KS * 32 == kH, "the modulated A operand spans one hidden row");
   constexpr int TLD = BN + 4;  // sTot row stride (floats): rows 4 banks apart
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       Hs[1] = *reinterpret_cast<const float4*>(hp + ks * 32 + 4);
     }
   };
-  f32x4 acc[WMT][WNF], accs[WNF];
+  f32x4 acc[WMT][WNF], accs[WNF], tot[WMT][WNF];  // tot: the range sums so far
   auto mma = [&](const bf16x8* A, const bf16x8* W, const float4* Hs) {
     if (shift_wave) {
       const float hv[8] = {Hs[0].x, Hs[0].y, Hs[0].z, Hs[0].w, Hs[1].x, Hs[1].y, Hs[1].z, Hs[1].w};
@@ -584,7 +586,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int j = 0; j < WNF; ++j) accs[j] = zero_f32x4();
   };
-  // range r's sum into LDS: lane (lr, lq) holds rows 4 lq .. 4 lq + 3 of each tile, column lr
+  // range r's sum added to the total (in registers; the shift sums in LDS)
   auto flush = [&](int r) {
 #pragma unroll
     for (int i = 0; i < WMT; ++i)
@@ -592,8 +594,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int j = 0; j < WNF; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float* d = sTot + ((wm * WMT + i) * 16 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr;
-          *d = (r == 0 ? 0.f : *d) + acc[i][j][e];
+          tot[i][j][e] = (r == 0 ? 0.f : tot[i][j][e]) + acc[i][j][e];
         }
     if (shift_wave) {
 #pragma unroll
@@ -626,6 +627,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
+  // the total into LDS: lane (lr, lq) holds rows 4 lq .. 4 lq + 3 of each tile, column lr
+#pragma unroll
+  for (int i = 0; i < WMT; ++i)
+#pragma unroll
+    for (int j = 0; j < WNF; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sTot[((wm * WMT + i) * 16 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr] = tot[i][j][e];
   // row scales and rotation frequencies, as k_gemm computes them
   if (MOD) {
     for (int rb = 0; rb < BM; rb += 64) {
