@@ -43,7 +43,11 @@ constexpr int KB = 32;          // keys per block
 constexpr int KLD = kD + 8;     // K row stride in LDS (bf16): 528 B, 16 B past a bank period
 constexpr int VLD = kD + 16;    // V row stride in LDS (bf16): 544 B, 32 B past a bank period
 constexpr int kMaxNB = 4;       // blocks per split (upper bound)
-constexpr int kAttnHeadsPerWg = 1;  // query heads of a KV group per attention work-group
+// Query heads of a KV group per attention work-group: one (4 waves) while the
+// grid is small, both (8 waves, each K/V block read once for the pair) once
+// one-head work-groups would exceed two per CU (batches).  Each wave's rows
+// see the same blocks in the same order either way, so the outputs match.
+constexpr int kAttnPairFromWgs = 512;
 constexpr float kNegBig = -1e30f;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -423,9 +427,9 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
   a.R16 = 2 * a.TP;
 }
 
-hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
+template <int HPW>
+static void launch_partial_hpw(const AttnArgs& a, hipStream_t s) {
   constexpr int NB = kAttnKps / KB;
-  constexpr int HPW = kAttnHeadsPerWg;
   static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
   const int items = a.B * kHK * (a.S + a.NS) * (kGroup / HPW);
   const dim3 grid(8 * ((items + 7) / 8));
@@ -433,6 +437,13 @@ hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
     k_attn_partial<true, NB, HPW><<<grid, dim3(256 * HPW), 0, s>>>(a);
   else
     k_attn_partial<false, NB, HPW><<<grid, dim3(256 * HPW), 0, s>>>(a);
+}
+
+hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
+  if (a.B * kHK * (a.S + a.NS) * kGroup > kAttnPairFromWgs)
+    launch_partial_hpw<kGroup>(a, s);
+  else
+    launch_partial_hpw<1>(a, s);
   return hipGetLastError();
 }
 

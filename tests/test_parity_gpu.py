@@ -323,7 +323,9 @@ def test_layer_forward(wname):
 
 
 def test_layer_batched_equals_single_requests():
-    """A request's output does not depend on the other requests in the batch."""
+    """A request's output does not depend on the other requests in the batch
+    (four requests run the attention with both heads of a KV group per
+    work-group, one request with one head per work-group)."""
     wl, wbits, reqs = layer_case("c5")
     wd = device_weights(wbits)
     batched = run_layer(wbits, reqs[:4], wd)
