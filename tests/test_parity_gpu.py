@@ -224,6 +224,37 @@ def test_attention_edge_cases(B, C, P, kind):
     check_attention(kind, ctx, *inp)
 
 
+def test_attention_batched_edge_cases_equal_single_requests():
+    """Eight requests (the launch pairs the two query heads of a KV group in
+    one work-group at this grid size) mixing the degenerate masks: all
+    masked, one visible key, first and last only, ragged, full.  Each
+    request gets the bits it gets alone (one head per work-group) and passes
+    the oracle gate."""
+    B, C, P = 8, 50, 1024
+    r = rng(777)
+    masks = []
+    for b in range(B):
+        m = np.zeros(P, np.uint8)
+        kind = b % 5
+        if kind == 1:
+            m[P // 3 + b] = 1
+        elif kind == 2:
+            m[0] = 1
+            m[P - 1] = 1
+        elif kind == 3:
+            m[: P - 5 - 3 * b] = 1
+            m[r.integers(0, P, P // 7)] = 0
+        elif kind == 4:
+            m[:] = 1
+        masks.append(m)
+    inp = attn_inputs(778, B, C, P, masks)
+    ctx = run_attention(*inp)
+    check_attention("batched edge cases", ctx, *inp)
+    for b in range(B):
+        single = run_attention(*(x[b:b + 1] for x in inp))
+        assert torch.equal(ctx[b], single[0]), f"request {b} differs from its single-request run"
+
+
 @pytest.mark.parametrize("poison", [float("nan"), float("inf"), -float("inf"), 3e4, -3e4])
 def test_attention_masked_rows_never_read(poison):
     wl = synth.WORKLOADS["c4"]  # holes inside the valid range plus a masked tail
