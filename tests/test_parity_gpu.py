@@ -385,6 +385,24 @@ def test_layer_large_m_batches_equal_single_requests(B, C, P):
     gate(f"large-M batch B={B} C={C} request {B - 1}", from_dev(batched[B - 1]), ref)
 
 
+def test_layer_largest_shapes():
+    """16 requests at the 2048 bucket (the largest batch and prefix of the
+    workloads at once: large-M projections, the paired-head attention over
+    34 splits), the c4 mask rule with holes; requests 0, 7 and 15 against the
+    oracle, and request 15 bit-equal to its single-request run."""
+    wbits = synth.layer_weights(synth.BASE_SEED + 7700)
+    reqs = [synth.make_request(synth.BASE_SEED + 7800 + b, 50, 2048, 1900, 2048, 1, 0.05) for b in range(16)]
+    wd = device_weights(wbits)
+    out = run_layer(wbits, reqs, wd)
+    ow = oracle_weights(wbits)
+    for b in (0, 7, 15):
+        rq = reqs[b]
+        ref = orc.layer(f64(rq.x), f64(rq.cond), ow, f64(rq.k_pre[0]), f64(rq.v_pre[0]), rq.mask, rq.pos0)
+        gate(f"B=16 P_b=2048 layer[b={b}]", from_dev(out[b]), ref)
+    single = run_layer(wbits, [reqs[15]], wd)
+    assert torch.equal(out[15], single[0])
+
+
 def test_layer_masked_rows_never_read():
     wl, wbits, reqs = layer_case("c4")
     wd = device_weights(wbits)
