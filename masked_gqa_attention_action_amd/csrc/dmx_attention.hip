@@ -43,6 +43,12 @@ constexpr int KB = 32;          // keys per block
 constexpr int KLD = kD + 8;     // K row stride in LDS (bf16): 528 B, 16 B past a bank period
 constexpr int VLD = kD + 16;    // V row stride in LDS (bf16): 544 B, 32 B past a bank period
 constexpr int kMaxNB = 4;       // blocks per split (upper bound)
+// splits per batch of the combine's loads (upper bound: from 22 on the
+// compiler runs out of scalar registers for the load addresses)
+constexpr int kCombineMaxBatch = 21;
+#define DMX_COMBINE_BATCHES(X)                                                                      \
+  X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16) X(17) X(18) \
+  X(19) X(20) X(21)
 // Query heads of a KV group per attention work-group: one (4 waves) while the
 // grid is small, both (8 waves, each K/V block read once for the pair) once
 // one-head work-groups would exceed two per CU (batches).  Each wave's rows
@@ -189,8 +195,8 @@ __device__ __forceinline__ int xcd_chunked(int wg, int grid, int items) {
 // batch the row maximum is taken first, so every split costs one exp2 and one
 // multiply-add per output, in split order.  Batches after the first (prefixes
 // longer than CB splits) rescale what came before.
+template <int CB>  // splits per batch of loads
 __device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, int bg, int mt, int t, int lane) {
-  constexpr int CB = 24;  // splits per batch of loads
   const int lr = lane & 15, lq = lane >> 4;
   const int TT = a.TP >> 4, MT = 2 * TT;
   const int g = bg % kHK, b = bg / kHK;
@@ -408,12 +414,13 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2)
 // Separate merge kernel: one wave per (request, KV head, row tile, dim
 // tile), placed like the splits (xcd_chunked) so the partials are read from
 // the L2 that received them.
+template <int CB>
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
   const int MT = 2 * (a.TP >> 4);
   const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * MT * 16);
   if (item < 0) return;
   const int t = item & 15, rest = item >> 4;
-  combine_unit(a, ctx, rest / MT, rest % MT, t, threadIdx.x);
+  combine_unit<CB>(a, ctx, rest / MT, rest % MT, t, threadIdx.x);
 }
 
 void attn_config(int B, int C, int P, AttnArgs& a) {
@@ -448,7 +455,20 @@ hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s) {
-  k_attn_combine<<<dim3(a.B * kHK * (a.R16 / 16) * 16), dim3(64), 0, s>>>(a, ctx);  // a multiple of 8
+  // load batches of equal size, at most kCombineMaxBatch splits each: loads
+  // past the last split re-read it and are discarded, and each such wasted
+  // load measured ~2.5 us per 18-layer step, so the batch fits the count
+  const int nsplit = a.S + a.NS;
+  const int nbatch = (nsplit + kCombineMaxBatch - 1) / kCombineMaxBatch;
+  const int cb = (nsplit + nbatch - 1) / nbatch;
+  const dim3 grid(a.B * kHK * (a.R16 / 16) * 16);  // a multiple of 8
+  switch (cb) {
+#define DMX_CASE(N) \
+  case N: k_attn_combine<N><<<grid, dim3(64), 0, s>>>(a, ctx); break;
+    DMX_COMBINE_BATCHES(DMX_CASE)
+#undef DMX_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
