@@ -423,7 +423,7 @@ def main():
     st.close()
     extras = {}
     if args.extras:
-        for name in ("c2", "c4", "c5"):
+        for name in ("c1", "c2", "c4", "c5"):
             extras[f"layer_{name}"] = layer_case(name)
         extras["prefix_qkv_c4"] = prefix_qkv_case()
         extras["prefix_layer_2048"] = prefix_layer_case()

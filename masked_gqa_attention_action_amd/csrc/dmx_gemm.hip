@@ -951,16 +951,33 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   // row blocks: one per WG up to 4 (more blocks loop inside the WG)
   const int tiles = a.M / 16;
   const int mb1 = std::min(4, tiles), mb2 = std::min(4, (tiles + 1) / 2);
-  const int nreq = std::min(4, a.M / a.TP);  // MOD: blocks inside one request
+  // MOD kinds: blocks stay inside one request, so the row tiles per block
+  // follow the request's padded rows (TP / 16 = 1 .. 4): a block tile past
+  // the request would re-read the last one for nothing
+  const int nreq = std::min(4, a.M / a.TP);
+  const int tpr = a.TP / 16;  // row tiles per request
   const int nreq2 = std::min(8, (a.M / a.TP) * ((a.TP + 31) / 32));
+  const int nreq1 = std::min(8, (a.M / a.TP) * tpr);
   switch (kind) {
     case GEMM_QKV1024: DMX_GEMM(EPI_F32, 16, 4, 8, A_GLOBAL, 2, mb2); break;
-    case GEMM_QKV1024_MODPRE: DMX_GEMM(EPI_QKV, 32, 4, 8, A_MODPRE, 2, nreq2); break;
+    case GEMM_QKV1024_MODPRE:
+      if (tpr % 2 == 0)
+        DMX_GEMM(EPI_QKV, 32, 4, 8, A_MODPRE, 2, nreq2);
+      else
+        DMX_GEMM(EPI_QKV, 32, 4, 8, A_MODPRE, 1, nreq1);
+      break;
     case GEMM_QKV2560: DMX_GEMM(EPI_F32, 16, 4, 20, A_GLOBAL, 1, 4); break;
     case GEMM_OPROJ: DMX_GEMM(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 1, mb1); break;
     case GEMM_OPROJ_F32: DMX_GEMM(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 1, mb1); break;
     case GEMM_GATEUP: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 2, mb2); break;
-    case GEMM_GATEUP_MOD: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, nreq); break;
+    case GEMM_GATEUP_MOD:
+      switch (tpr) {
+        case 1: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_MODPRE, 1, nreq); break;
+        case 2: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_MODPRE, 2, nreq); break;
+        case 3: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_MODPRE, 3, nreq); break;
+        default: DMX_GEMM(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, nreq); break;
+      }
+      break;
     case GEMM_DOWN: DMX_GEMM(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 1, mb1); break;
     case GEMM_DOWN_F32RES: DMX_GEMM(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 1, mb1); break;
     default: break;
