@@ -49,15 +49,20 @@ def stage_bytes(stage, batch, chunk, p_bucket, visible, n_layers):
     """Algorithmic bytes of one launch of a stack kernel: the weights, KV rows
     and layer inputs / outputs that its operation must read or write (bf16
     activations).  Intermediates another fused design keeps on chip are not
-    counted; the attention combine therefore has none of its own."""
+    counted; the attention combine therefore has none of its own.  The step's
+    modulation launch computes layer 0's two vectors; every other layer's come
+    with the attention launch of the layer before it (averaged over the
+    layers here)."""
     import masked_gqa_attention_action_amd as dmx
     M = batch * chunk
     act = lambda n: M * n * 2
+    mods = 2 * W_MOD + batch * H * 2 + 2 * batch * 3072 * 4  # one layer's two vectors
     return {
-        dmx.STAGE_MODS: n_layers * 2 * W_MOD + batch * H * 2 + n_layers * 2 * batch * 3072 * 4,
+        dmx.STAGE_MODS: mods,
         dmx.STAGE_PACK: act(H) * 2,
         dmx.STAGE_QKV: W_QKV + act(H) + act(4096) + 2 * D * 2,
-        dmx.STAGE_ATTN: 2 * HK * D * 2 * visible + act(4096) + act(2048) + batch * p_bucket,
+        dmx.STAGE_ATTN: 2 * HK * D * 2 * visible + act(4096) + act(2048) + batch * p_bucket
+        + mods * (n_layers - 1) // n_layers,
         dmx.STAGE_COMBINE: 0,
         dmx.STAGE_OPROJ: W_O + act(2048) + 2 * act(H),
         dmx.STAGE_GATEUP: W_GU + act(H) + act(I),

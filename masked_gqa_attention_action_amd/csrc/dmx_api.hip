@@ -171,6 +171,7 @@ AttnArgs attn_args(const WsLayout& L, void* ws) {
   a.part_o = at<uint16_t>(ws, L.part_o);
   a.part_ml = at<float>(ws, L.part_ml);
   a.ctx_tiled = 0;
+  a.side_n = a.side_B = a.attn_grid = 0;
   return a;
 }
 
@@ -262,6 +263,8 @@ struct LayerCtx {
   void* ws;
   const WsLayout* L;
   const float* next_scale1;  // the next layer's modulation (its scale first), or null
+  ModJob side[2] = {};       // modulation GEMVs the attention launch runs on idle CUs
+  int side_n = 0;
 };
 
 int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
@@ -301,7 +304,12 @@ int enq_layer_stage(const LayerCtx& c, int stage, hipStream_t s) {
       a.vp = c.kv->v;
       a.mask = c.kv->mask;
       a.ctx_tiled = 1;
-      if (stage == DMX_STAGE_ATTN) return hip_check(launch_attn_partial(a, s), "attention launch");
+      if (stage == DMX_STAGE_ATTN) {
+        a.side_n = c.side_n;
+        a.side_B = c.B;
+        for (int j = 0; j < c.side_n; ++j) a.side[j] = c.side[j];
+        return hip_check(launch_attn_partial(a, s), "attention launch");
+      }
       return hip_check(launch_attn_combine(a, at<uint16_t>(ws, L.ctx), s), "attention combine launch");
     }
     case DMX_STAGE_OPROJ:  // x1 = x + gate1 * (ctx W_o^T)
@@ -613,8 +621,11 @@ static int enq_step_mods(const dmx_stack_desc* d, int st, float* out, hipStream_
   return enq_mods(jobs, 2 * d->n_layers, d->batch, s);
 }
 
-static int enq_stack_mods(const dmx_stack_desc* d, const WsLayout& L, int st, hipStream_t s) {
-  return enq_step_mods(d, st, at<float>(d->ws, L.stack_mod), s);
+// the two modulation GEMVs of layer l at step st, into the workspace slots
+static void layer_mod_jobs(const dmx_stack_desc* d, const WsLayout& L, int st, int l, ModJob jobs[2]) {
+  const dmx_bf16* cond = d->cond + (size_t)st * d->batch * kH;
+  jobs[0] = ModJob{d->layers[l].w_mod1, d->layers[l].b_mod1, cond, stack_mod(d, L, st, l, 0)};
+  jobs[1] = ModJob{d->layers[l].w_mod2, d->layers[l].b_mod2, cond, stack_mod(d, L, st, l, 1)};
 }
 
 // Layer l of step st as the stack runs it.  Each down projection hands the
@@ -630,8 +641,15 @@ static LayerCtx stack_layer(const dmx_stack_desc* d, const WsLayout& L, const dm
     next = stack_mod(d, L, st, l + 1, 0);
   else if (chained && d->mod_table && st + 1 < d->n_steps)
     next = stack_mod(d, L, st + 1, 0, 0);
-  return LayerCtx{&d->layers[l], kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, st, l, 0),
-                  stack_mod(d, L, st, l, 1), d->ws, &L, next};
+  LayerCtx c{&d->layers[l], kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, st, l, 0),
+             stack_mod(d, L, st, l, 1), d->ws, &L, next};
+  // without a table, the next layer's modulation vectors are computed by the
+  // attention launch of this one (its down projection reads the next scale)
+  if (!d->mod_table && l + 1 < d->n_layers) {
+    layer_mod_jobs(d, L, st, l + 1, c.side);
+    c.side_n = 2;
+  }
+  return c;
 }
 
 // The sampler's per-step work around the stack (null: a plain stack run).
@@ -649,7 +667,11 @@ static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, 
     if (smp && st == 0)
       DMX_TRY(hip_check(launch_action_in(smp->actions, smp->w->w_in, smp->w->b_in, rows, smp->w->action_dim, d->x, s),
                         "action in-projection launch"));
-    if (!d->mod_table) DMX_TRY(enq_stack_mods(d, L, st, s));
+    if (!d->mod_table) {  // layer 0's modulation; every later layer's comes with the attention before it
+      ModJob jobs[2];
+      layer_mod_jobs(d, L, st, 0, jobs);
+      DMX_TRY(enq_mods(jobs, 2, d->batch, s));
+    }
     // the first layer's scaled tiled input and its row statistics: a pack
     // pass at the start of the run, and of every step whose modulation was
     // not known before it (no table); otherwise the last down projection
@@ -721,8 +743,11 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
   const dmx_prefix_kv kv{d->k_pre[layer], d->v_pre[layer], d->mask, d->p_bucket};
   const LayerCtx c = stack_layer(d, L, &kv, 0, layer);
   for (int r = 0; r < reps; ++r) {
-    if (stage == DMX_STAGE_MODS)
-      DMX_TRY(enq_stack_mods(d, L, 0, s));
+    if (stage == DMX_STAGE_MODS) {  // what a step launches: layer 0's (later ones ride on the attention)
+      ModJob jobs[2];
+      layer_mod_jobs(d, L, 0, 0, jobs);
+      DMX_TRY(enq_mods(jobs, 2, d->batch, s));
+    }
     else if (stage == DMX_STAGE_PACK)
       DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, stack_mod(d, L, 0, 0, 0), d->ws, L, s));
     else

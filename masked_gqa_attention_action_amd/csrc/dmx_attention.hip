@@ -34,6 +34,7 @@
 // combine kernel merges the S + NS partials of each row in split order.
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
+#include "dmx_mod.hpp"
 #include "dmx_tiles.hpp"
 
 namespace dmx {
@@ -259,9 +260,19 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2)
   __shared__ __attribute__((aligned(16))) uint16_t sV[NB][KB * VLD];
   __shared__ uint32_t sMask[NB];
 
+  if constexpr (HPW == 1) {
+    if ((int)blockIdx.x >= a.attn_grid) {  // a modulation unit on a CU the splits leave idle
+      const int nside = gridDim.x - a.attn_grid;
+      for (int u = blockIdx.x - a.attn_grid; u < a.side_n * (3 * kH / 16); u += nside) {
+        const int j = u / (3 * kH / 16);
+        mod_unit(a.side[j], u - j * (3 * kH / 16), a.side_B, reinterpret_cast<float*>(&sK[0][0]));
+      }
+      return;
+    }
+  }
   const int nsplit = a.S + a.NS;
   const int per_split = kGroup / HPW;  // work-groups per split
-  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * nsplit * per_split);
+  const int item = xcd_chunked(blockIdx.x, a.attn_grid, a.B * kHK * nsplit * per_split);
   if (item < 0) return;
   const int hsel = item % per_split;  // first query head of this work-group within the group
   const int split = (item / per_split) % nsplit;
@@ -435,11 +446,12 @@ void attn_config(int B, int C, int P, AttnArgs& a) {
 }
 
 template <int HPW>
-static void launch_partial_hpw(const AttnArgs& a, hipStream_t s) {
+static void launch_partial_hpw(AttnArgs a, int side_wgs, hipStream_t s) {
   constexpr int NB = kAttnKps / KB;
   static_assert(NB <= kMaxNB && NB * KB == kAttnKps && NB >= 2, "keys per split");
   const int items = a.B * kHK * (a.S + a.NS) * (kGroup / HPW);
-  const dim3 grid(8 * ((items + 7) / 8));
+  a.attn_grid = 8 * ((items + 7) / 8);
+  const dim3 grid(a.attn_grid + side_wgs);
   if (a.y)
     k_attn_partial<true, NB, HPW><<<grid, dim3(256 * HPW), 0, s>>>(a);
   else
@@ -447,10 +459,20 @@ static void launch_partial_hpw(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
-  if (a.B * kHK * (a.S + a.NS) * kGroup > kAttnPairFromWgs)
-    launch_partial_hpw<kGroup>(a, s);
-  else
-    launch_partial_hpw<1>(a, s);
+  if (a.B * kHK * (a.S + a.NS) * kGroup > kAttnPairFromWgs) {
+    if (a.side_n > 0) {  // no idle CUs to fill: the modulation units in a launch of their own
+      ModBatch mb{};
+      mb.B = a.side_B;
+      mb.n = a.side_n;
+      for (int j = 0; j < a.side_n; ++j) mb.job[j] = a.side[j];
+      const hipError_t e = launch_mod_multi(mb, s);
+      if (e != hipSuccess) return e;
+    }
+    launch_partial_hpw<kGroup>(a, 0, s);
+  } else {
+    // two modulation units per extra work-group (one each, or three, measured slower)
+    launch_partial_hpw<1>(a, (a.side_n * (3 * kH / 16) + 1) / 2, s);
+  }
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@
 //   EPI_GEGLU  tile = 16 gate + 16 up features; h = gelu_tanh(gate) * up
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
+#include "dmx_mod.hpp"
 #include "dmx_tiles.hpp"
 
 #include <algorithm>
@@ -1044,36 +1045,8 @@ hipError_t launch_pack_rows(const uint16_t* x, int B, int T, int TP, int K, uint
 // front.
 __global__ __launch_bounds__(256) void k_mod_multi(ModBatch mb) {
   const int j = blockIdx.x / (3 * kH / 16), tile = blockIdx.x - j * (3 * kH / 16);
-  const ModJob& job = mb.job[j];
-  __shared__ float red[4][16 * 16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const int k0 = wave * 256;
-  bf16x8 wf[8];
-  const uint16_t* wp = job.w + ((size_t)tile * (kH / 32) + wave * 8) * 512 + lane * 8;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)  // read once per launch: streaming loads
-    wf[ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(wp + ks * 512));
-  const uint16_t* cond = job.cond;
-  for (int b0 = 0; b0 < mb.B; b0 += 16) {
-    const int rows = min(16, mb.B - b0);
-    f32x4 acc = zero_f32x4();
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 av = lr < rows ? load_bf16x8(cond + (size_t)(b0 + lr) * kH + k0 + ks * 32 + lk) : zero_bf16x8();
-      acc = mfma16(av, wf[ks], acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][((lane >> 4) * 4 + r) * 16 + lr] = acc[r];
-    __syncthreads();
-    if (threadIdx.x < rows * 16) {
-      const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
-      const float v = red[0][r * 16 + c] + red[1][r * 16 + c] + red[2][r * 16 + c] + red[3][r * 16 + c];
-      const int n = tile * 16 + c;
-      job.out[(size_t)(b0 + r) * 3 * kH + n] = v + bf2f(job.bias[n]);
-    }
-    __syncthreads();
-  }
+  __shared__ float red[4 * 256];
+  mod_unit(mb.job[j], tile, mb.B, red);
 }
 
 hipError_t launch_mod_multi(const ModBatch& mb, hipStream_t s) {

@@ -125,6 +125,12 @@ struct AttnArgs {
   int NS;       // suffix splits (32 keys each)
   int kps;      // prefix keys per split (multiple of 32)
   int R16;      // stacked query rows (2 * C) rounded up to 16
+  // optional work for the CUs the splits leave idle: the modulation GEMVs
+  // side[0 .. side_n) for side_B requests, in 16-feature units spread over
+  // the extra work-groups (blocks attn_grid .. of the partial launch)
+  ModJob side[2];
+  int side_n, side_B;
+  int attn_grid;  // work-groups of the splits (set by the launch)
   uint16_t* part_o;  // [B][HK][S + NS][R16 / 16][16 dim tiles][16 rows][4][4] bf16, normalised partial
                      // outputs (dims 16t + 4q .. +3 of row r at [t][r][q]); padded rows never written
   float* part_ml;    // [B][HK][S + NS][R16][2] running max (log2 domain) and sum
