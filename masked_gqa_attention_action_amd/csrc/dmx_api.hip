@@ -643,9 +643,10 @@ static LayerCtx stack_layer(const dmx_stack_desc* d, const WsLayout& L, const dm
     next = stack_mod(d, L, st + 1, 0, 0);
   LayerCtx c{&d->layers[l], kv, d->x, d->pos0, d->batch, d->chunk, d->x, stack_mod(d, L, st, l, 0),
              stack_mod(d, L, st, l, 1), d->ws, &L, next};
-  // without a table, the next layer's modulation vectors are computed by the
-  // attention launch of this one (its down projection reads the next scale)
-  if (!d->mod_table && l + 1 < d->n_layers) {
+  // without a table and with CUs the attention leaves idle, the next layer's
+  // modulation vectors are computed by the attention launch of this one (its
+  // down projection reads the next scale)
+  if (!d->mod_table && attn_has_idle_cus(L.attn) && l + 1 < d->n_layers) {
     layer_mod_jobs(d, L, st, l + 1, c.side);
     c.side_n = 2;
   }
@@ -667,10 +668,14 @@ static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, 
     if (smp && st == 0)
       DMX_TRY(hip_check(launch_action_in(smp->actions, smp->w->w_in, smp->w->b_in, rows, smp->w->action_dim, d->x, s),
                         "action in-projection launch"));
-    if (!d->mod_table) {  // layer 0's modulation; every later layer's comes with the attention before it
-      ModJob jobs[2];
-      layer_mod_jobs(d, L, st, 0, jobs);
-      DMX_TRY(enq_mods(jobs, 2, d->batch, s));
+    if (!d->mod_table) {
+      if (attn_has_idle_cus(L.attn)) {  // layer 0's; every later layer's comes with the attention before it
+        ModJob jobs[2];
+        layer_mod_jobs(d, L, st, 0, jobs);
+        DMX_TRY(enq_mods(jobs, 2, d->batch, s));
+      } else {  // no idle CUs (batches): every layer's in one launch
+        DMX_TRY(enq_step_mods(d, st, at<float>(d->ws, L.stack_mod), s));
+      }
     }
     // the first layer's scaled tiled input and its row statistics: a pack
     // pass at the start of the run, and of every step whose modulation was
@@ -743,10 +748,14 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
   const dmx_prefix_kv kv{d->k_pre[layer], d->v_pre[layer], d->mask, d->p_bucket};
   const LayerCtx c = stack_layer(d, L, &kv, 0, layer);
   for (int r = 0; r < reps; ++r) {
-    if (stage == DMX_STAGE_MODS) {  // what a step launches: layer 0's (later ones ride on the attention)
-      ModJob jobs[2];
-      layer_mod_jobs(d, L, 0, 0, jobs);
-      DMX_TRY(enq_mods(jobs, 2, d->batch, s));
+    if (stage == DMX_STAGE_MODS) {  // what a step launches
+      if (attn_has_idle_cus(L.attn)) {  // layer 0's (later ones ride on the attention)
+        ModJob jobs[2];
+        layer_mod_jobs(d, L, 0, 0, jobs);
+        DMX_TRY(enq_mods(jobs, 2, d->batch, s));
+      } else {
+        DMX_TRY(enq_step_mods(d, 0, at<float>(d->ws, L.stack_mod), s));
+      }
     }
     else if (stage == DMX_STAGE_PACK)
       DMX_TRY(enq_pack_input(d->x, d->batch, d->chunk, stack_mod(d, L, 0, 0, 0), d->ws, L, s));

@@ -458,8 +458,10 @@ static void launch_partial_hpw(AttnArgs a, int side_wgs, hipStream_t s) {
     k_attn_partial<false, NB, HPW><<<grid, dim3(256 * HPW), 0, s>>>(a);
 }
 
+bool attn_has_idle_cus(const AttnArgs& a) { return a.B * kHK * (a.S + a.NS) * kGroup <= kAttnPairFromWgs; }
+
 hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s) {
-  if (a.B * kHK * (a.S + a.NS) * kGroup > kAttnPairFromWgs) {
+  if (!attn_has_idle_cus(a)) {
     if (a.side_n > 0) {  // no idle CUs to fill: the modulation units in a launch of their own
       ModBatch mb{};
       mb.B = a.side_B;

@@ -139,6 +139,8 @@ constexpr int kAttnKps = 64;  // prefix keys per attention split (32 .. 128, mul
 void attn_config(int B, int C, int P, AttnArgs& a);
 hipError_t launch_attention(const AttnArgs& a, uint16_t* ctx, hipStream_t s);  // partial + combine
 hipError_t launch_attn_partial(const AttnArgs& a, hipStream_t s);
+// true when the split launch leaves CUs idle (one query head per work-group)
+bool attn_has_idle_cus(const AttnArgs& a);
 hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s);
 // prefix (prefill) layer pieces, hidden kPrefixHidden, one request
 constexpr int kPrefixHidden = 2560, kPrefixInter = 10240;

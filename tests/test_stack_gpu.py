@@ -139,3 +139,46 @@ def test_stack_with_mod_table_matches_eager(stack_case):
     finally:
         c["cond"].copy_(cond2.flip(0))
     assert torch.equal(xs, xs2), "refilled modulation table does not follow the new cond"
+
+
+@pytest.mark.parametrize("B,P", [(2, 576), (4, 1024)])
+def test_stack_batched_equals_layer_by_layer(B, P):
+    """A batched stack (3 layers x 2 steps) against the per-layer eager path,
+    bit for bit, eager and replayed.  At (2, 576) the attention leaves CUs
+    idle and computes each next layer's modulation vectors itself; at
+    (4, 1024) it pairs the heads of a KV group and every layer's vectors come
+    from one launch at the start of a step."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import masked_gqa_attention_action_amd as dmx
+    n_layers, n_steps, C = 3, 2, 50
+    wbits = [synth.layer_weights(synth.BASE_SEED + 7900 + l) for l in range(n_layers)]
+    rqs = [synth.make_request(synth.BASE_SEED + 7950 + b, C, P, P // 2, P, n_layers, 0.05) for b in range(B)]
+    wd = [device_weights(w) for w in wbits]
+    kp = [to_dev(np.stack([r.k_pre[l] for r in rqs])) for l in range(n_layers)]
+    vp = [to_dev(np.stack([r.v_pre[l] for r in rqs])) for l in range(n_layers)]
+    mask = to_dev(np.stack([r.mask for r in rqs]), "raw")
+    pos0 = to_dev(np.array([r.pos0 for r in rqs], np.int32), "raw")
+    conds = np.stack([np.stack([synth.time_embedding(t)] * B) for t in synth.step_times(n_steps)])
+    cond = to_dev(conds)
+    x0 = to_dev(np.stack([r.x for r in rqs]))
+    ws = dmx.new_workspace(B, C, P)
+    x = x0.clone()
+    for s in range(n_steps):
+        for l in range(n_layers):
+            x = dmx.suffix_layer_forward(wd[l], kp[l], vp[l], mask, x, cond[s], pos0, ws)
+    torch.cuda.synchronize()
+    xs = x0.clone()
+    st = dmx.Stack(wd, kp, vp, mask, cond, pos0, xs)
+    st.run()
+    torch.cuda.synchronize()
+    assert torch.equal(xs, x), "eager stack differs from the per-layer path"
+    stream = torch.cuda.Stream()
+    st.capture(stream)
+    for rep in range(2):
+        xs.copy_(x0)
+        torch.cuda.synchronize()
+        st.replay(stream)
+        stream.synchronize()
+        assert torch.equal(xs, x), f"replay {rep} differs from the per-layer path"
+    st.close()
