@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2)
   __shared__ uint32_t sMask[NB];
 
   if constexpr (HPW == 1) {
-    if ((int)blockIdx.x >= a.attn_grid) {  // a modulation unit on a CU the splits leave idle
+    if ((int)blockIdx.x >= a.attn_grid) {  // modulation units on the CUs the splits leave idle
       const int nside = gridDim.x - a.attn_grid;
       for (int u = blockIdx.x - a.attn_grid; u < a.side_n * (3 * kH / 16); u += nside) {
         const int j = u / (3 * kH / 16);
