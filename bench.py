@@ -92,10 +92,11 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = ("dmx_attention.hip", "dmx_gemm.hip", "dmx_prefix.hip", "dmx_prefix_attn.hip", "dmx_sampler.hip",
-                  "dmx_device.hpp",
-                  "dmx_internal.hpp",
-                  "dmx_tiles.hpp")
+# every kernel source and header of the library (device code included from any
+# header changes a kernel, so all of them decide whether a counter summary
+# still applies)
+KERNEL_SOURCES = tuple(sorted(n for n in os.listdir(os.path.join(ROOT, "masked_gqa_attention_action_amd", "csrc"))
+                              if n.endswith((".hip", ".hpp"))))
 
 
 def recorded_traffic(kernel_tag):

@@ -173,8 +173,11 @@ def _stream(stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _want(t, shape, dtype, name):
-    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+def _want(t, shape, dtype, name, device=True):
+    """Raise ValueError naming `name` unless t is a contiguous tensor of this
+    dtype and shape (and on a GPU, unless device=False)."""
+    if (t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous()
+            or (device and not t.is_cuda)):
         raise ValueError(f"{name}: expected contiguous cuda {dtype} {tuple(shape)}, got "
                          f"{t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} device={t.device}")
 
@@ -342,6 +345,12 @@ class Stack:
         self.n_steps, B, _ = cond.shape
         _, C, _ = x.shape
         P = mask.shape[1]
+        # the layers write x in place and read pos0 per request: both must
+        # match the batch that cond gives
+        _want(x, (B, C, H), torch.bfloat16, "x", device=False)
+        _want(pos0, (B,), torch.int32, "pos0", device=False)
+        _want(x, (B, C, H), torch.bfloat16, "x")
+        _want(pos0, (B,), torch.int32, "pos0")
         self._keep = (layers, k_pre, v_pre, mask, cond, pos0, x)
         if ws is None:
             n = int(lib().dmx_stack_workspace_bytes(self.n_layers, B, C, P))

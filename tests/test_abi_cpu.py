@@ -136,3 +136,20 @@ def test_validation_errors_before_launch(dmx):
     L.dmx_graph_destroy(None)
     for s in (0, 1, -1, -2, -3, -4, -5, -6, -7, -99):
         assert L.dmx_status_string(s)
+
+
+def test_stack_checks_x_and_pos0_against_the_batch(dmx):
+    """Stack() names x and pos0 when their shape or dtype does not match the
+    batch cond gives (the layers write x in place and read pos0 per request);
+    checked before anything touches a device."""
+    import torch
+    B, C, P = 2, 50, 64
+    cond = torch.zeros((3, B, 1024), dtype=torch.bfloat16)
+    mask = torch.zeros((B, P), dtype=torch.uint8)
+    pos0 = torch.zeros((B,), dtype=torch.int32)
+    x_short = torch.zeros((1, C, 1024), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"^x: expected .*\(2, 50, 1024\)"):
+        dmx.Stack([{}], [], [], mask, cond, pos0, x_short)
+    x = torch.zeros((B, C, 1024), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"^pos0: expected .*torch.int32 \(2,\)"):
+        dmx.Stack([{}], [], [], mask, cond, pos0.long(), x)
