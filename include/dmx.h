@@ -213,6 +213,27 @@ int dmx_suffix_layer_forward(const dmx_layer_weights* w, const dmx_prefix_kv* kv
                              const int32_t* pos0, int32_t batch, int32_t chunk,
                              dmx_bf16* x_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of dmx_suffix_layer_forward, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments and results as
+ * dmx_suffix_layer_forward (the same kernels, bit for bit), without `ws`: the
+ * layer's intermediates live in a fixed scratch array of
+ * DMX_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; nothing is allocated or freed by any call.
+ *   Limit: the sizes must fit the scratch, i.e. dmx_workspace_bytes(batch,
+ *   chunk, kv->p_bucket) <= DMX_NOALLOC_SCRATCH_BYTES (batch 1 with chunk <= 64
+ *   and p_bucket <= 2048 always does); larger sizes return DMX_ERR_WORKSPACE
+ *   and launch nothing.
+ *   All calls on one GPU share its scratch, which keeps the last call's
+ *   contents (nothing in it needs to start at zero): calls that overlap on one
+ *   GPU (other streams, other threads) race and give undefined results;
+ *   order them on one stream. */
+#define DMX_NOALLOC_SCRATCH_BYTES (12 * 1024 * 1024)
+int dmx_suffix_layer_forward_noalloc(const dmx_layer_weights* w, const dmx_prefix_kv* kv,
+                                     const dmx_bf16* x_in, const dmx_bf16* cond,
+                                     const int32_t* pos0, int32_t batch, int32_t chunk,
+                                     dmx_bf16* x_out, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* The action-expert stack of one denoising run, replayed from a per-bucket
  * hipGraph ([Art §3]: graphs captured once per prefix bucket, replayed per

@@ -35,7 +35,7 @@ EXPORTED = (
     "dmx_select_bucket", "dmx_workspace_bytes", "dmx_stack_workspace_bytes", "dmx_workspace_init", "dmx_pack_weight",
     "dmx_adarms_prenorm",
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
-    "dmx_suffix_layer_forward", "dmx_stack_forward", "dmx_stack_stage_launch",
+    "dmx_suffix_layer_forward", "dmx_suffix_layer_forward_noalloc", "dmx_stack_forward", "dmx_stack_stage_launch",
     "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill",
     "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_attention_workspace_bytes", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward",
     "dmx_sampler_schedule_bytes", "dmx_sampler_schedule_fill", "dmx_sampler_forward", "dmx_sampler_graph_create",
@@ -120,6 +120,8 @@ def lib():
             "dmx_geglu_mlp": ([P, P, P, P, P, i32, i32, P, P, sz, P], ctypes.c_int),
             "dmx_suffix_layer_forward": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, P, P, i32, i32,
                                           P, P, sz, P], ctypes.c_int),
+            "dmx_suffix_layer_forward_noalloc": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, P, P, i32,
+                                                  i32, P, P], ctypes.c_int),
             "dmx_stack_forward": ([ctypes.POINTER(StackDesc), P], ctypes.c_int),
             "dmx_stack_stage_launch": ([ctypes.POINTER(StackDesc), i32, i32, i32, P], ctypes.c_int),
             "dmx_stack_mod_table_bytes": ([i32, i32, i32], sz),
@@ -324,6 +326,29 @@ def suffix_layer_forward(w: dict, k_pre, v_pre, mask, x, cond, pos0, ws, out=Non
     kv = PrefixKV(k_pre.data_ptr(), v_pre.data_ptr(), mask.data_ptr(), P)
     _check(lib().dmx_suffix_layer_forward(ctypes.byref(lw), ctypes.byref(kv), _p(x), _p(cond), _p(pos0), B, C,
                                           _p(out), _p(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 12 * 1024 * 1024  # DMX_NOALLOC_SCRATCH_BYTES
+
+
+def suffix_layer_forward_noalloc(w: dict, k_pre, v_pre, mask, x, cond, pos0, out, stream=None):
+    """dmx_suffix_layer_forward_noalloc: the layer with the library's fixed
+    per-GPU scratch instead of a workspace (the caller passes only inputs and
+    the output, so nothing is allocated here either)."""
+    B, C, _ = x.shape
+    P = k_pre.shape[2]
+    _want(x, (B, C, H), torch.bfloat16, "x")
+    _want(out, (B, C, H), torch.bfloat16, "out")
+    _want(cond, (B, H), torch.bfloat16, "cond")
+    _want(pos0, (B,), torch.int32, "pos0")
+    _want(k_pre, (B, HK, P, D), torch.bfloat16, "k_pre")
+    _want(v_pre, (B, HK, P, D), torch.bfloat16, "v_pre")
+    _want(mask, (B, P), torch.uint8, "mask")
+    lw = layer_weights_struct(w)
+    kv = PrefixKV(k_pre.data_ptr(), v_pre.data_ptr(), mask.data_ptr(), P)
+    _check(lib().dmx_suffix_layer_forward_noalloc(ctypes.byref(lw), ctypes.byref(kv), _p(x), _p(cond), _p(pos0), B,
+                                                  C, _p(out), _stream(stream)))
     return out
 
 

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/dmx.h"
@@ -571,6 +572,77 @@ int dmx_suffix_layer_forward(const dmx_layer_weights* w, const dmx_prefix_kv* kv
   WsLayout L;
   DMX_TRY(check_ws(fn, ws, ws_bytes, batch, chunk, kv->p_bucket, L));
   return enq_layer(w, kv, x_in, cond, pos0, batch, chunk, x_out, ws, L, (hipStream_t)stream);
+}
+
+// ---- allocation-free layer call ---------------------------------------------
+}  // extern "C"
+
+// Scratch of dmx_suffix_layer_forward_noalloc: a file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends.  Its
+// name is a host-side stand-in in host code, never a device address: each
+// device's address is looked up once with hipGetSymbolAddress (with that
+// device current) and only that address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[DMX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// the device `stream` launches on (the current device for the null stream)
+int stream_device(hipStream_t s, int* dev) {
+  if (s == nullptr) return hip_check(hipGetDevice(dev), "hipGetDevice");
+  return hip_check(hipStreamGetDevice(s, dev), "hipStreamGetDevice");
+}
+
+// The scratch address on `dev`, looked up on the device's first call.
+int scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(DMX_ERR_UNSUPPORTED, "scratch: device %d beyond the %d supported", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    DMX_TRY(hip_check(hipGetDevice(&cur), "hipGetDevice"));
+    if (cur != dev) DMX_TRY(hip_check(hipSetDevice(dev), "hipSetDevice"));
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    DMX_TRY(hip_check(e, "hipGetSymbolAddress(scratch)"));
+    if (p == nullptr) return fail(DMX_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DMX_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dmx_suffix_layer_forward_noalloc(const dmx_layer_weights* w, const dmx_prefix_kv* kv, const dmx_bf16* x_in,
+                                     const dmx_bf16* cond, const int32_t* pos0, int32_t batch, int32_t chunk,
+                                     dmx_bf16* x_out, void* stream) {
+  const char* fn = "dmx_suffix_layer_forward_noalloc";
+  DMX_TRY(check_layer_weights(fn, w));
+  if (kv == nullptr) return fail(DMX_ERR_INVALID_ARG, "%s: kv struct is null", fn);
+  DMX_TRY(check_kv(fn, kv->k, kv->v, kv->mask, kv->p_bucket));
+  DMX_REQUIRE_PTR(x_in);
+  DMX_REQUIRE_PTR(cond);
+  DMX_REQUIRE_PTR(pos0);
+  DMX_REQUIRE_PTR(x_out);
+  DMX_TRY(check_bt(fn, batch, chunk, DMX_MAX_CHUNK));
+  WsLayout L;
+  if (!ws_layout(batch, chunk, kv->p_bucket, 0, L)) return fail(DMX_ERR_UNSUPPORTED, "%s: unsupported sizes", fn);
+  if (L.total > (size_t)DMX_NOALLOC_SCRATCH_BYTES)
+    return fail(DMX_ERR_WORKSPACE,
+                "%s: batch %d, chunk %d, p_bucket %d need %zu bytes of scratch, above the fixed %d "
+                "(use dmx_suffix_layer_forward with a workspace)",
+                fn, batch, chunk, kv->p_bucket, L.total, DMX_NOALLOC_SCRATCH_BYTES);
+  hipStream_t s = (hipStream_t)stream;
+  int dev = -1;
+  DMX_TRY(stream_device(s, &dev));
+  void* ws = nullptr;
+  DMX_TRY(scratch_on(dev, &ws));
+  return enq_layer(w, kv, x_in, cond, pos0, batch, chunk, x_out, ws, L, s);
 }
 
 // ---- stack and graphs -------------------------------------------------------

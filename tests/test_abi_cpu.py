@@ -138,6 +138,18 @@ def test_validation_errors_before_launch(dmx):
         assert L.dmx_status_string(s)
 
 
+def test_noalloc_layer_validates_before_any_device_call(dmx):
+    """The allocation-free layer call refuses null pointers and sizes beyond
+    its fixed scratch on the host, before it touches the device."""
+    L = dmx.lib()
+    lw = dmx.LayerWeights(*([0x10000] * 10))
+    assert L.dmx_suffix_layer_forward_noalloc(None, None, FAKE, FAKE, FAKE, 1, 50, FAKE, None) == dmx.ERR_INVALID_ARG
+    kv = dmx.PrefixKV(0x10000, 0x10000, 0x10000, 2048)
+    st = L.dmx_suffix_layer_forward_noalloc(ctypes.byref(lw), ctypes.byref(kv), FAKE, FAKE, FAKE, 2, 64, FAKE, None)
+    assert st == dmx.ERR_WORKSPACE and b"scratch" in L.dmx_last_error_string()
+    assert L.dmx_workspace_bytes(1, 64, 2048) <= dmx.NOALLOC_SCRATCH_BYTES < L.dmx_workspace_bytes(2, 64, 2048)
+
+
 def test_stack_checks_x_and_pos0_against_the_batch(dmx):
     """Stack() names x and pos0 when their shape or dtype does not match the
     batch cond gives (the layers write x in place and read pos0 per request);
