@@ -59,6 +59,7 @@ typedef uint16_t dmx_bf16;
 #define DMX_ERR_MISALIGNED (-5)
 #define DMX_ERR_WORKSPACE (-6)
 #define DMX_ERR_HIP (-7)
+#define DMX_ERR_SYNC (-8) /* a persistent step kernel gave up waiting (see dmx_stack_sync_check) */
 
 /* Fixed shapes of the suffix layer ([Art §2.2] shape table). */
 #define DMX_HIDDEN 1024
@@ -260,6 +261,22 @@ typedef struct dmx_stack_desc {
    * §4), so the table is computed once per schedule and reused by every
    * request.  NULL: the vectors are computed from cond inside every step. */
   const float* mod_table;
+  /* 0: every layer as its chain of stage kernels (any batch).
+   * 1: the persistent step kernel (batch 1, chunk <= 64, p_bucket <= 2048,
+   *    n_layers <= 32): the whole run in one launch of 256 co-resident
+   *    work-groups, one per CU, each XCC of the chip owning one query head
+   *    and 1/8 of the MLP, with every stage's weight slices prefetched while
+   *    the stage before finishes ([Art] §2.2: one large fused kernel instead
+   *    of many small ops).  Its summation order differs from the stage
+   *    kernels', so the two agree to the floating-point tolerance, not bit for
+   *    bit; each is deterministic.  Stages hand off through counters in the
+   *    workspace with bounded waits: a run that waits past its limit (work-
+   *    groups not all resident) stops early with an error word set, which
+   *    dmx_stack_sync_check reports. */
+  int32_t persistent;
+  /* Optional device [n_steps][n_layers][batch][chunk][1024] bf16: every
+   * layer's output (persistent mode only; NULL: none). */
+  dmx_bf16* layer_trace;
 } dmx_stack_desc;
 
 typedef struct dmx_graph dmx_graph;
@@ -278,7 +295,14 @@ int dmx_stack_mod_table_fill(const dmx_stack_desc* d, float* table, void* stream
 
 /* Eager run of the stack (same kernels as the graph). */
 int dmx_stack_forward(const dmx_stack_desc* d, void* stream);
-/* Capture the stack on `stream` into a graph (nothing runs).  *out (host). */
+/* Persistent mode: waits for `stream` and reads the run's error word.
+ * DMX_OK, or DMX_ERR_SYNC (the work-group and stage that gave up are in
+ * dmx_last_error_string) after which the hand-off counters are reset so the
+ * next run starts clean.  DMX_OK without doing anything in stage mode. */
+int dmx_stack_sync_check(const dmx_stack_desc* d, void* stream);
+/* Capture the stack on `stream` into a graph.  *out (host).  Nothing of the
+ * stack runs; in persistent mode the hand-off counters in the workspace are
+ * reset on `stream` before the capture. */
 int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** out);
 /* Replay a captured graph on `stream`. */
 int dmx_graph_launch(dmx_graph* g, void* stream);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libdmx.so")
 
 OK, FALLBACK_EAGER = 0, 1
 ERR_INVALID_ARG, ERR_BAD_BUCKETS, ERR_PREFIX_TOO_LONG = -1, -2, -3
-ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = -4, -5, -6, -7
+ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP, ERR_SYNC = -4, -5, -6, -7, -8
 
 H, I, D, HQ, HK = 1024, 4096, 256, 8, 4
 
@@ -35,7 +35,8 @@ EXPORTED = (
     "dmx_select_bucket", "dmx_workspace_bytes", "dmx_stack_workspace_bytes", "dmx_workspace_init", "dmx_pack_weight",
     "dmx_adarms_prenorm",
     "dmx_qkv_qknorm_rope", "dmx_suffix_attention", "dmx_oproj_gated_residual", "dmx_geglu_mlp",
-    "dmx_suffix_layer_forward", "dmx_suffix_layer_forward_noalloc", "dmx_stack_forward", "dmx_stack_stage_launch",
+    "dmx_suffix_layer_forward", "dmx_suffix_layer_forward_noalloc", "dmx_stack_forward", "dmx_stack_sync_check",
+    "dmx_stack_stage_launch",
     "dmx_stack_mod_table_bytes", "dmx_stack_mod_table_fill",
     "dmx_image_merge", "dmx_prefix_attention", "dmx_prefix_attention_workspace_bytes", "dmx_prefix_workspace_bytes", "dmx_prefix_layer_forward",
     "dmx_sampler_schedule_bytes", "dmx_sampler_schedule_fill", "dmx_sampler_forward", "dmx_sampler_graph_create",
@@ -78,7 +79,7 @@ class StackDesc(ctypes.Structure):
                 ("k_pre", ctypes.POINTER(ctypes.c_void_p)), ("v_pre", ctypes.POINTER(ctypes.c_void_p)),
                 ("mask", ctypes.c_void_p), ("cond", ctypes.c_void_p), ("pos0", ctypes.c_void_p),
                 ("x", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
-                ("mod_table", ctypes.c_void_p)]
+                ("mod_table", ctypes.c_void_p), ("persistent", ctypes.c_int32), ("layer_trace", ctypes.c_void_p)]
 
 
 SAMPLER_WEIGHTS = ("w_in", "b_in", "w_t1", "b_t1", "w_t2", "b_t2", "w_fmod", "b_fmod", "w_out", "b_out")
@@ -123,6 +124,7 @@ def lib():
             "dmx_suffix_layer_forward_noalloc": ([ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, P, P, i32,
                                                   i32, P, P], ctypes.c_int),
             "dmx_stack_forward": ([ctypes.POINTER(StackDesc), P], ctypes.c_int),
+            "dmx_stack_sync_check": ([ctypes.POINTER(StackDesc), P], ctypes.c_int),
             "dmx_stack_stage_launch": ([ctypes.POINTER(StackDesc), i32, i32, i32, P], ctypes.c_int),
             "dmx_stack_mod_table_bytes": ([i32, i32, i32], sz),
             "dmx_stack_mod_table_fill": ([ctypes.POINTER(StackDesc), P, P], ctypes.c_int),
@@ -363,9 +365,15 @@ class Stack:
     mod_table=True computes the modulation vectors of every step and layer
     once, from cond as it is at construction (or at the last
     fill_mod_table()), and the runs read them instead of recomputing them in
-    every step."""
+    every step.
 
-    def __init__(self, layers, k_pre, v_pre, mask, cond, pos0, x, ws=None, mod_table=False, stream=None):
+    persistent=True runs the whole stack as one persistent kernel (batch 1);
+    trace, an optional [n_steps][n_layers][B][C][1024] bf16 tensor, then
+    receives every layer's output.  sync_check() reports a persistent run
+    that gave up waiting."""
+
+    def __init__(self, layers, k_pre, v_pre, mask, cond, pos0, x, ws=None, mod_table=False, stream=None,
+                 persistent=False, trace=None):
         self.n_layers = len(layers)
         self.n_steps, B, _ = cond.shape
         _, C, _ = x.shape
@@ -390,9 +398,13 @@ class Stack:
         self._vp = (ctypes.c_void_p * self.n_layers)(*[t.data_ptr() for t in v_pre])
         _want(cond, (self.n_steps, B, H), torch.bfloat16, "cond")
         _want(mask, (B, P), torch.uint8, "mask")
+        if trace is not None:
+            _want(trace, (self.n_steps, self.n_layers, B, C, H), torch.bfloat16, "trace")
+        self.trace = trace
         self.desc = StackDesc(self.n_layers, self.n_steps, B, C, P, self._lw, self._kp, self._vp,
                               mask.data_ptr(), cond.data_ptr(), pos0.data_ptr(), x.data_ptr(),
-                              self.ws.data_ptr(), self.ws.numel(), None)
+                              self.ws.data_ptr(), self.ws.numel(), None, int(bool(persistent)),
+                              None if trace is None else trace.data_ptr())
         self._graph = None
         self.mod_table = None
         if mod_table:
@@ -409,6 +421,11 @@ class Stack:
 
     def run(self, stream=None):
         _check(lib().dmx_stack_forward(ctypes.byref(self.desc), _stream(stream)))
+
+    def sync_check(self, stream=None):
+        """Persistent mode: wait for the stream and raise if a run gave up
+        waiting (its hand-off counters are reset for the next run)."""
+        _check(lib().dmx_stack_sync_check(ctypes.byref(self.desc), _stream(stream)))
 
     def stage_launch(self, layer, stage, reps=1, stream=None):
         """reps back-to-back launches of one kernel of the stack (per-kernel timing)."""

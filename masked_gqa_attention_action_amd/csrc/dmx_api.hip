@@ -56,7 +56,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // (for a stack) the modulation vectors of every layer of one step.  Rows of
 // the tiled / fp32 intermediates are tiled rows (each request padded to TP).
 struct WsLayout {
-  size_t mod1, mod2, apk, xp, raw, ss_q, qvb, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, total;
+  size_t mod1, mod2, apk, xp, raw, ss_q, qvb, ctx, x1, x1s, h, part_o, part_ml, ss_a, ss_b, stack_mod, step, total;
+  bool has_step;  // the persistent step kernel's region (batch 1 stacks)
   int TP;
   AttnArgs attn;
 };
@@ -91,6 +92,8 @@ bool ws_layout(int B, int T, int P, int n_layers, WsLayout& L) {
   L.ss_a = take(M * kSsParts * 4);  // row sums of squares of x1, one per O-projection tile
   L.ss_b = take(M * kSsParts * 4);  // ... of a layer input (pack pass or the down tiles)
   L.stack_mod = take((size_t)n_layers * 2 * B * 3 * kH * 4);
+  L.has_step = n_layers > 0 && step_supported(B, T, P, n_layers);
+  L.step = L.has_step ? take(StepLayout::bytes(L.TP)) : 0;
   L.total = off;
   return true;
 }
@@ -666,7 +669,53 @@ static int check_stack(const char* fn, const dmx_stack_desc* d, WsLayout& L) {
   DMX_REQUIRE_PTR(d->x);
   if (d->mod_table && !aligned16(d->mod_table))
     return fail(DMX_ERR_MISALIGNED, "%s: mod_table is not 16-byte aligned", fn);
+  if (d->persistent != 0 && d->persistent != 1)
+    return fail(DMX_ERR_INVALID_ARG, "%s: persistent must be 0 or 1", fn);
+  if (d->layer_trace && !d->persistent)
+    return fail(DMX_ERR_UNSUPPORTED, "%s: layer_trace needs the persistent step kernel", fn);
+  if (d->layer_trace && !aligned16(d->layer_trace))
+    return fail(DMX_ERR_MISALIGNED, "%s: layer_trace is not 16-byte aligned", fn);
+  if (d->persistent) {
+    if (!step_supported(d->batch, d->chunk, d->p_bucket, d->n_layers))
+      return fail(DMX_ERR_UNSUPPORTED,
+                  "%s: the persistent step kernel runs batch 1, chunk <= 64, p_bucket <= 2048, <= %d layers", fn,
+                  kStepMaxLayers);
+    bool ok = false;
+    DMX_TRY(hip_check(step_occupancy_ok(padded_tokens(d->chunk), &ok), "occupancy query"));
+    if (!ok) return fail(DMX_ERR_UNSUPPORTED, "%s: 256 work-groups of the step kernel cannot be resident at once", fn);
+  }
   return check_ws(fn, d->ws, d->ws_bytes, d->batch, d->chunk, d->p_bucket, L, d->n_layers);
+}
+
+// The persistent step kernel: the whole run of a batch-1 stack in one launch.
+static int enq_stack_step(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) {
+  StepArgs a;
+  memset(&a, 0, sizeof a);
+  for (int l = 0; l < d->n_layers; ++l) {
+    const dmx_layer_weights& w = d->layers[l];
+    a.L[l] = StepLayer{w.w_mod1, w.b_mod1, w.w_qkv, w.q_norm, w.k_norm, w.w_o,
+                       w.w_mod2, w.b_mod2, w.w_gu,  w.w_down, d->k_pre[l], d->v_pre[l]};
+  }
+  a.cond = d->cond;
+  a.mask = d->mask;
+  a.pos0 = d->pos0;
+  a.x = d->x;
+  a.trace = d->layer_trace;
+  a.mod_table = d->mod_table;
+  a.ws = at<char>(d->ws, L.step);
+  a.n_layers = d->n_layers;
+  a.n_steps = d->n_steps;
+  a.C = d->chunk;
+  a.TP = L.TP;
+  a.P = d->p_bucket;
+  step_config(d->chunk, d->p_bucket, a.S, a.NS, a.kps);
+  a.rope_lb = log2(10000.0);
+  return hip_check(launch_step(a, s), "step kernel launch");
+}
+
+// zero the step kernel's hand-off counters and error word
+static int step_sync_reset(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s) {
+  return hip_check(launch_fill_zero(at<char>(d->ws, L.step), StepLayout::mods, s), "step counter reset");
 }
 
 // One pass of the stack.  Per step, one launch computes the modulation
@@ -734,6 +783,10 @@ struct SamplerRun {
 };
 
 static int enq_stack(const dmx_stack_desc* d, const WsLayout& L, hipStream_t s, const SamplerRun* smp = nullptr) {
+  if (d->persistent) {
+    if (smp) return fail(DMX_ERR_UNSUPPORTED, "the sampler runs the stack in stage mode (persistent = 0)");
+    return enq_stack_step(d, L, s);
+  }
   const int rows = d->batch * d->chunk;
   for (int st = 0; st < d->n_steps; ++st) {
     // the sampler's first in-projection; later ones come with the step tail
@@ -805,7 +858,25 @@ extern "C" {
 int dmx_stack_forward(const dmx_stack_desc* d, void* stream) {
   WsLayout L;
   DMX_TRY(check_stack("dmx_stack_forward", d, L));
+  if (d->persistent) DMX_TRY(step_sync_reset(d, L, (hipStream_t)stream));
   return enq_stack(d, L, (hipStream_t)stream);
+}
+
+int dmx_stack_sync_check(const dmx_stack_desc* d, void* stream) {
+  const char* fn = "dmx_stack_sync_check";
+  WsLayout L;
+  DMX_TRY(check_stack(fn, d, L));
+  if (!d->persistent) return DMX_OK;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t err = 0;
+  DMX_TRY(hip_check(hipStreamSynchronize(s), "hipStreamSynchronize"));
+  DMX_TRY(hip_check(hipMemcpy(&err, at<char>(d->ws, L.step) + StepLayout::err, 4, hipMemcpyDeviceToHost),
+                    "error word read"));
+  if (err == 0) return DMX_OK;
+  DMX_TRY(step_sync_reset(d, L, s));
+  DMX_TRY(hip_check(hipStreamSynchronize(s), "hipStreamSynchronize"));
+  return fail(DMX_ERR_SYNC, "%s: work-group %u gave up waiting at stage %u of the run (error word 0x%08x)", fn,
+              (err >> 20) & 0x7ffu, err & 0xfffffu, err);
 }
 
 int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage, int32_t reps, void* stream) {
@@ -816,6 +887,7 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
   if (stage < DMX_STAGE_MODS || stage > DMX_STAGE_DOWN)
     return fail(DMX_ERR_INVALID_ARG, "%s: unknown stage %d", fn, stage);
   if (reps < 1 || reps > 100000) return fail(DMX_ERR_INVALID_ARG, "%s: reps %d not in [1, 100000]", fn, reps);
+  if (d->persistent) return fail(DMX_ERR_UNSUPPORTED, "%s: the stage kernels belong to stage mode", fn);
   hipStream_t s = (hipStream_t)stream;
   const dmx_prefix_kv kv{d->k_pre[layer], d->v_pre[layer], d->mask, d->p_bucket};
   const LayerCtx c = stack_layer(d, L, &kv, 0, layer);
@@ -863,6 +935,7 @@ int dmx_stack_graph_create(const dmx_stack_desc* d, void* stream, dmx_graph** ou
   WsLayout L;
   DMX_TRY(check_stack(fn, d, L));
   hipStream_t s = (hipStream_t)stream;
+  if (d->persistent) DMX_TRY(step_sync_reset(d, L, s));
   return capture_graph(s, out, [&] { return enq_stack(d, L, s); });
 }
 
@@ -1164,6 +1237,7 @@ const char* dmx_status_string(int status) {
     case DMX_ERR_MISALIGNED: return "misaligned pointer";
     case DMX_ERR_WORKSPACE: return "workspace too small";
     case DMX_ERR_HIP: return "HIP runtime error";
+    case DMX_ERR_SYNC: return "persistent kernel gave up waiting";
     default: return "unknown status";
   }
 }

@@ -178,4 +178,59 @@ hipError_t launch_step_tail(const uint16_t* x, const float* fmod, const uint16_t
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// ---- persistent denoise-step kernel (batch 1; dmx_step.hip) ----------------
+constexpr int kStepMaxLayers = 32;
+constexpr int kStepMaxNB = 3;       // 32-key blocks per attention split
+constexpr int kStepMaxSplits = 32;  // attention splits per head (one per work-group of an XCC)
+constexpr int kStepModSlots = 4;    // ring of modulation vectors (linear layer index % 4)
+struct StepLayer {
+  const uint16_t *w_mod1, *b_mod1, *w_qkv, *q_norm, *k_norm, *w_o, *w_mod2, *b_mod2, *w_gu, *w_down, *k_pre, *v_pre;
+};
+// Byte layout of the step kernel's workspace for TP padded chunk rows (a
+// multiple of 16 up to 64), 256-byte aligned pieces.
+constexpr uint32_t step_align(uint32_t v) { return (v + 255u) & ~255u; }
+struct StepLayout {
+  static constexpr uint32_t al(uint32_t v) { return step_align(v); }
+  static constexpr uint32_t prog = 0;                                  // [256] counters, 128 B apart
+  static constexpr uint32_t err = prog + 256u * 128u;                  // error word
+  static constexpr uint32_t mods = err + 256u;                         // [kStepModSlots][2][3072] fp32
+  static constexpr uint32_t ypart = step_align(mods + kStepModSlots * 2u * 3072u * 4u);  // [8][4][64][64][4] fp32
+  static constexpr uint32_t y2part = ypart + 8u * 4u * 64u * 256u * 4u;
+  static constexpr uint32_t xcc = y2part + 8u * 4u * 64u * 256u * 4u;  // per-XCC buffers from here
+  // per-XCC buffers (offsets within an XCC's region)
+  static constexpr uint32_t xs(int) { return 0; }                               // tiled bf16 [TP][1024]
+  static constexpr uint32_t ssx(int TP) { return al(xs(TP) + TP * 1024u * 2u); }  // fp32 [TP][32]
+  static constexpr uint32_t qb(int TP) { return al(ssx(TP) + TP * 32u * 4u); }    // tiled bf16 [TP][256]
+  static constexpr uint32_t vb(int TP) { return al(qb(TP) + TP * 256u * 2u); }    // tiled bf16 [TP][256]
+  static constexpr uint32_t kf(int TP) { return al(vb(TP) + TP * 256u * 2u); }    // tiled fp32 [TP][256]
+  static constexpr uint32_t ssq(int TP) { return al(kf(TP) + TP * 256u * 4u); }   // fp32 [TP][16]
+  static constexpr uint32_t po(int TP) { return al(ssq(TP) + TP * 16u * 4u); }    // bf16 [32][4][16][256]
+  static constexpr uint32_t pml(int TP) { return al(po(TP) + kStepMaxSplits * 4u * 16u * 256u * 2u); }  // fp32 [32][64][2]
+  static constexpr uint32_t ctx(int TP) { return al(pml(TP) + kStepMaxSplits * 64u * 2u * 4u); }  // tiled bf16 [TP][256]
+  static constexpr uint32_t x1s(int TP) { return al(ctx(TP) + TP * 256u * 2u); }  // tiled bf16 [TP][1024]
+  static constexpr uint32_t ss1(int TP) { return al(x1s(TP) + TP * 1024u * 2u); } // fp32 [TP][32]
+  static constexpr uint32_t h(int TP) { return al(ss1(TP) + TP * 32u * 4u); }     // tiled bf16 [TP][512]
+  static constexpr uint32_t xcc_stride(int TP) { return al(h(TP) + TP * 512u * 2u); }
+  static constexpr size_t bytes(int TP) { return (size_t)xcc + 8u * (size_t)xcc_stride(TP); }
+};
+struct StepArgs {
+  StepLayer L[kStepMaxLayers];
+  const uint16_t* cond;      // [n_steps][1024]
+  const uint8_t* mask;       // [P]
+  const int32_t* pos0;       // [1]
+  uint16_t* x;               // [C][1024]: the input, replaced by the output
+  uint16_t* trace;           // optional [n_steps][n_layers][C][1024]: every layer's output
+  const float* mod_table;    // optional [n_steps][n_layers][2][3072]
+  char* ws;                  // the workspace (StepLayout)
+  int n_layers, n_steps, C, TP, P, S, NS, kps;
+  double rope_lb;            // log2 of the RoPE base
+};
+// attention split shape of the step kernel for chunk C and prefix P
+void step_config(int C, int P, int& S, int& NS, int& kps);
+bool step_supported(int B, int C, int P, int n_layers);
+hipError_t launch_step(const StepArgs& a, hipStream_t s);
+// whether 256 work-groups of the step kernel can be resident at once
+hipError_t step_occupancy_ok(int TP, bool* ok);
+
+
 }  // namespace dmx
