@@ -40,8 +40,10 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        # DMX_ORACLE_LIB names another build of the same source (the
+        # sanitizer build of the CPU tests); it is loaded as it is
+        path = os.environ.get("DMX_ORACLE_LIB") or build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32 = ctypes.c_int32
         dbl = ctypes.c_double

@@ -103,3 +103,24 @@ def device_weights(wbits: dict) -> dict:
 
 def oracle_weights(wbits: dict) -> dict:
     return {k: f64(v) for k, v in wbits.items()}
+
+
+def untile(flat_bits, rows, cols, dtype="bf16"):
+    """Row-major [rows][cols] float64 copy of a tiled activation buffer.
+
+    Tiled layout of the library (16 x 32 tiles of 512 elements): tile (rt, kt)
+    starts at element (rt * cols/32 + kt) * 512; inside it, the 8-element
+    chunk of row rt*16 + r, columns kt*32 + 8g .. +7 sits at (r + 16 g) * 8.
+    flat_bits: numpy uint16 (bf16 bits) of at least rows * cols elements."""
+    assert rows % 16 == 0 and cols % 32 == 0
+    a = np.asarray(flat_bits)[: rows * cols].reshape(rows // 16, cols // 32, 4, 16, 8)  # rt, kt, g, r, e
+    a = a.transpose(0, 3, 1, 2, 4).reshape(rows, cols)  # rt, r, kt, g, e
+    if dtype == "bf16":
+        return synth.bf16_to_f64(np.ascontiguousarray(a))
+    return a.astype(np.float64)
+
+
+def dev_bits(t) -> np.ndarray:
+    """The raw bytes of a device tensor as numpy uint16 (bf16 bit patterns)."""
+    import torch
+    return t.detach().view(torch.uint8).cpu().numpy().view(np.uint16)

@@ -15,7 +15,7 @@ import pytest
 
 import oracle as orc
 from masked_gqa_attention_action_amd import synth
-from tests.helpers import LAYER_BRANCH_REL, delta_gate, f64, from_dev, stage_gate, to_dev
+from tests.helpers import LAYER_BRANCH_REL, delta_gate, dev_bits, f64, from_dev, gate, stage_gate, to_dev, untile
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -104,6 +104,76 @@ def test_prefix_layer_against_oracle(prefix_weights, T, valid_len, hole_p):
     stage_gate(f"prefix k cache T={T}", from_dev(kc)[:, :T], rk)
     stage_gate(f"prefix v cache T={T}", from_dev(vc)[:, :T], rv)
     assert torch.isnan(kc[:, T:].float()).all(), "rows past the tokens were written"
+
+
+def prefix_ws_pieces(T):
+    """(TP, {name: (byte offset, bytes)}) of the pieces a prefix layer leaves in
+    its workspace, in the library's order, each 256-byte aligned: tiled
+    rmsnorm(x; w_in); the fp32 QKV projection [TP][4096]; row-major q
+    [T][8][256]; the tiled context [TP][2048]; the fp32 projection output
+    [TP][2560] (last written by the down projection); fp32 x1 [TP][2560];
+    tiled rmsnorm(x1; w_pre_ffn); the tiled GEGLU output [TP][10240]."""
+    TP = (T + 15) // 16 * 16
+    sizes = [("xn", TP * 2560 * 2), ("raw", TP * 4096 * 4), ("q", T * 8 * 256 * 2), ("ctx", TP * 2048 * 2),
+             ("y", TP * 2560 * 4), ("x1", TP * 2560 * 4), ("xn2", TP * 2560 * 2), ("h", TP * 10240 * 2)]
+    off, out = 0, {}
+    for name, n in sizes:
+        out[name] = (off, n)
+        off += (n + 255) // 256 * 256
+    return TP, out
+
+
+@pytest.mark.parametrize("T,valid_len,hole_p", [(96, 90, 0.0), (300, 280, 0.05)])
+def test_prefix_layer_each_stage_strict(prefix_weights, T, valid_len, hole_p):
+    """Every stage of the prefix layer at the strict gate, teacher forced: each
+    stage's oracle gets the GPU's own input to that stage (read from the
+    layer's workspace), so one stage's error cannot hide behind the whole
+    layer's looser output gate.  Stages: input norm; QKV projection; QK-norm +
+    RoPE (q, and k / v into the cache); prefix-causal attention; O-projection +
+    post-attention norm + residual (x1) and the pre-MLP norm; GEGLU; down
+    projection + post-MLP norm + residual (the output)."""
+    wbits, wd = prefix_weights
+    w = {k: f64(v) for k, v in wbits.items()}
+    x, valid = synth.prefix_inputs(synth.BASE_SEED + 9600 + T, T, valid_len, hole_p)
+    kv_rows = T + 16
+    kc = torch.full((4, kv_rows, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((4, kv_rows, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.full((int(dmx.lib().dmx_prefix_workspace_bytes(T)),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = dmx.prefix_layer_forward(wd, to_dev(x), to_dev(valid, "raw"), kc, vc, ws=ws)
+    torch.cuda.synchronize()
+    TP, pieces = prefix_ws_pieces(T)
+    assert ws.numel() >= pieces["h"][0] + pieces["h"][1]
+    wsb = ws.cpu().numpy()
+
+    def piece(name, dt):
+        o, n = pieces[name]
+        return wsb[o:o + n].view(dt)
+
+    xf = f64(x)
+    xn = untile(piece("xn", np.uint16), TP, 2560)[:T]
+    stage_gate(f"T={T} input norm", xn, orc.rmsnorm(xf, w["w_in"]))
+    raw = piece("raw", np.float32).reshape(TP, 4096)[:T].astype(np.float64)
+    gate(f"T={T} QKV projection", raw, orc.linear(xn, w["w_qkv"]))
+    rq, rk, rv = orc.qkv_qknorm_rope(xn, w["w_qkv"], w["q_norm"], w["k_norm"], np.arange(T), 8, 4, 256)
+    q = f64(piece("q", np.uint16).reshape(T, 8, 256))
+    stage_gate(f"T={T} QK-norm + RoPE q", q, rq)
+    k_gpu = f64(dev_bits(kc).reshape(4, kv_rows, 256))[:, :T]
+    v_gpu = f64(dev_bits(vc).reshape(4, kv_rows, 256))[:, :T]
+    stage_gate(f"T={T} QK-norm + RoPE k", k_gpu, rk)
+    stage_gate(f"T={T} v", v_gpu, rv)
+    ctx = untile(piece("ctx", np.uint16), TP, 2048)[:T]
+    stage_gate(f"T={T} attention", ctx, orc.prefix_attention(q, k_gpu, v_gpu, valid).reshape(T, 2048))
+    x1 = piece("x1", np.float32).reshape(TP, 2560)[:T].astype(np.float64)
+    gate(f"T={T} O-projection + post-norm + residual",
+         x1, xf + orc.rmsnorm(orc.linear(ctx, w["w_o"]), w["w_post_attn"]))
+    xn2 = untile(piece("xn2", np.uint16), TP, 2560)[:T]
+    stage_gate(f"T={T} pre-MLP norm", xn2, orc.rmsnorm(x1, w["w_pre_ffn"]))
+    _, rh = orc.geglu_mlp(xn2, w["w_gu"], w["w_down"], np.zeros(2560), np.zeros((T, 2560)))
+    h = untile(piece("h", np.uint16), TP, 10240)[:T]
+    stage_gate(f"T={T} GEGLU", h, rh)
+    ref_out = x1 + orc.rmsnorm(orc.linear(h, w["w_down"]), w["w_post_ffn"])
+    stage_gate(f"T={T} down + post-norm + residual", from_dev(out), ref_out)
+    delta_gate(f"T={T} down branch", from_dev(out), ref_out, x1, rel=LAYER_BRANCH_REL)
 
 
 def test_prefix_layer_is_deterministic(prefix_weights):
