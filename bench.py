@@ -9,10 +9,14 @@ GEGLU MLP) for one denoising step, replayed from a hipGraph captured for the
 embedding) are resident in HBM before timing starts.
 
 Per-kernel timing: every kernel of the step is also launched on its own,
-through dmx_stack_stage_launch, in a captured graph that runs it for all 18
-layers in stack order (so weights and KV stream as they do in the stack), and
-timed with events on the same stream.  The kernel with the largest share of
-the step is the "dominant" one whose roofline fraction is reported.
+through dmx_stack_stage_launch, in a captured graph that runs it once for
+each of the 64 layers of a timing stack (the step's 18 layers and copies of
+them at other addresses), timed with events on the same stream.  The 64
+layers' weights and KV exceed the 256 MB memory-side cache, so every launch
+streams its operands from HBM as in the step.  The kernel with the largest
+share of the step is the "dominant" one whose roofline fraction is reported.
+The single-layer and prefix timings rotate over copies of their operands for
+the same reason.
 
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -120,11 +124,30 @@ def recorded_traffic(kernel_tag):
         return None
 
 
+TIMING_LAYERS = 64  # layers of the per-kernel timing stack (DMX_MAX_LAYERS)
+
+
+def timing_stack(dmx, wd, kp, vp, mask, cond, pos0, x0, mod_table=False):
+    """A TIMING_LAYERS-layer stack over the step's layers and copies of them
+    (weights and KV at other addresses), run once so its workspace holds the
+    intermediates of a real pass."""
+    import torch
+    n = len(wd)
+    wdt = [wd[l] if l < n else {k: v.clone() for k, v in wd[l % n].items()} for l in range(TIMING_LAYERS)]
+    kpt = [kp[l] if l < n else kp[l % n].clone() for l in range(TIMING_LAYERS)]
+    vpt = [vp[l] if l < n else vp[l % n].clone() for l in range(TIMING_LAYERS)]
+    xt = x0.clone()
+    st = dmx.Stack(wdt, kpt, vpt, mask, cond, pos0, xt, mod_table=mod_table)
+    st.run()
+    torch.cuda.synchronize()
+    return st
+
+
 def time_stage(st, stage, n_layers, stream, reps):
     """Average launch duration (us) of one stack kernel: a captured graph runs
-    it once per layer in stack order (so each launch streams another layer's
-    weights and KV, as in the stack); replays are timed with events on the
-    same stream."""
+    it once per layer of the timing stack in stack order (each launch streams
+    another layer's weights and KV from HBM, as in the step); replays are
+    timed with events on the same stream."""
     import torch
     import masked_gqa_attention_action_amd as dmx
     g = torch.cuda.CUDAGraph()
@@ -170,19 +193,21 @@ def time_replays(st, stream, warmup, reps):
 
 
 PEAK_BF16_TFLOPS = 2500.0
+ROTATE, ROTATE_BYTES = 8, 512 << 20  # operand copies the single-call timings rotate over (at least)
 
 
 def time_calls(fn, stream, reps=20, rounds=5):
-    """us per call of fn(stream), from graph replays of reps back-to-back
-    calls timed with events on the capture stream."""
+    """us per call of fn(stream, i), from graph replays of reps back-to-back
+    calls (i = 0 .. reps - 1: the call's copy of its operands is i modulo the
+    number of copies) timed with events on the capture stream."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
-        fn(stream)
+        fn(stream, 0)
         stream.synchronize()
         with torch.cuda.graph(g, stream=stream):
-            for _ in range(reps):
-                fn(stream)
+            for i in range(reps):
+                fn(stream, i)
         g.replay()
         stream.synchronize()
         best = []
@@ -216,13 +241,21 @@ def layer_case(name):
     pos0 = dev(np.array([r.pos0 for r in rqs], np.int32), raw=True)
     ws = dmx.new_workspace(B, C, P)
     out = torch.empty_like(x)
-    us = time_calls(lambda s: dmx.suffix_layer_forward(w, kp, vp, mask, x, cond, pos0, ws, out=out, stream=s),
-                    torch.cuda.Stream())
+    # ROTATE copies of the weights and KV (>= 8, and >= 512 MB in all), so
+    # that no call finds its operands in the memory-side cache
+    per_copy = LAYER_WEIGHT_BYTES + kp.numel() * 4
+    n_copies = max(ROTATE, -(-ROTATE_BYTES // per_copy))
+    ops = [(w, kp, vp)] + [({k: v.clone() for k, v in w.items()}, kp.clone(), vp.clone()) for _ in range(n_copies - 1)]
+    us = time_calls(lambda s, i: dmx.suffix_layer_forward(ops[i % n_copies][0], ops[i % n_copies][1],
+                                                          ops[i % n_copies][2], mask, x, cond, pos0, ws, out=out,
+                                                          stream=s),
+                    torch.cuda.Stream(), reps=2 * n_copies)
     assert torch.isfinite(out.float()).all(), "non-finite layer output"
     visible = int(sum(int(r.mask.sum()) for r in rqs))
     nbytes = algorithmic_bytes_per_layer(B, C, P, visible)
     flops = layer_flops(B, C, visible)
-    return {"workload": wl.note, "us_per_layer": round(us, 2), "algorithmic_bytes": nbytes,
+    del ops
+    return {"workload": wl.note, "us_per_layer": round(us, 2), "operand_copies": n_copies, "algorithmic_bytes": nbytes,
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "flops": flops,
             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
@@ -242,12 +275,17 @@ def prefix_qkv_case():
     ws = dmx.new_workspace(1, T, 0)
     kc = torch.empty((1, HK, T, D), dtype=torch.bfloat16, device="cuda")
     vc = torch.empty_like(kc)
-    us = time_calls(lambda s: dmx.qkv_qknorm_rope(x, w, qn, kn, pos, ws, k=kc, v=vc, kv_rows=T, stream=s),
-                    torch.cuda.Stream(), reps=10)
+    per_copy = (x.numel() + w.numel() + 2 * kc.numel()) * 2
+    n = max(ROTATE, -(-ROTATE_BYTES // per_copy))
+    ops = [(x, w, kc, vc)] + [(x.clone(), w.clone(), torch.empty_like(kc), torch.empty_like(vc)) for _ in range(n - 1)]
+    us = time_calls(lambda s, i: dmx.qkv_qknorm_rope(ops[i % n][0], ops[i % n][1], qn, kn, pos, ws, k=ops[i % n][2],
+                                                     v=ops[i % n][3], kv_rows=T, stream=s),
+                    torch.cuda.Stream(), reps=2 * n)
+    del ops
     flops = 2 * T * hid * (HQ + 2 * HK) * D
     nbytes = T * hid * 2 + (HQ + 2 * HK) * D * hid * 2 + T * (HQ + 2 * HK) * D * 2 + 2 * D * 2
     return {"workload": "prefix QKV + QK-norm + RoPE, hidden 2560, 2048 tokens, K/V into the cache",
-            "us": round(us, 2), "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "us": round(us, 2), "operand_copies": n, "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_bytes": nbytes,
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
@@ -268,8 +306,13 @@ def prefix_layer_case(T=2048, valid_len=1936, hole_p=0.02):
     vc = torch.empty_like(kc)
     ws = dmx.new_prefix_workspace(T)
     out = torch.empty_like(x)
-    us = time_calls(lambda s: dmx.prefix_layer_forward(wd, x, valid, kc, vc, ws=ws, out=out, stream=s),
-                    torch.cuda.Stream(), reps=5)
+    per_copy = sum(v.numel() for v in wd.values()) * 2 + (x.numel() + 2 * kc.numel()) * 2
+    n = max(2, -(-ROTATE_BYTES // per_copy))
+    ops = [(wd, x, kc, vc)] + [({k: v.clone() for k, v in wd.items()}, x.clone(), torch.empty_like(kc),
+                                torch.empty_like(vc)) for _ in range(n - 1)]
+    us = time_calls(lambda s, i: dmx.prefix_layer_forward(ops[i % n][0], ops[i % n][1], valid, ops[i % n][2],
+                                                          ops[i % n][3], ws=ws, out=out, stream=s),
+                    torch.cuda.Stream(), reps=2 * n)
     assert torch.isfinite(out.float()).all(), "non-finite prefix layer output"
     # key j is visible to query i when j <= i and j is valid
     pairs = int(np.cumsum(valid_np.astype(np.int64)).sum())
@@ -279,10 +322,14 @@ def prefix_layer_case(T=2048, valid_len=1936, hole_p=0.02):
     nbytes = w_elems * 2 + 5 * PH * 2 + 2 * T * PH * 2 + 2 * HK * T * D * 2
     q = torch.randn((T, HQ, D), device="cuda").to(torch.bfloat16)
     ctx = torch.empty_like(q)
-    us_attn = time_calls(lambda s: dmx.prefix_attention(q, kc, vc, valid, ctx=ctx, stream=s), torch.cuda.Stream())
+    qs = [q] + [q.clone() for _ in range(n - 1)]
+    us_attn = time_calls(lambda s, i: dmx.prefix_attention(qs[i % n], ops[i % n][2], ops[i % n][3], valid, ctx=ctx,
+                                                           stream=s),
+                         torch.cuda.Stream(), reps=2 * n)
+    del ops, qs
     attn_bytes = 2 * T * HQ * D * 2 + 2 * HK * T * D * 2 + T
     return {"workload": f"prefix decoder layer, hidden 2560, {T} tokens ({int(valid_np.sum())} valid)",
-            "us": round(us, 2), "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "us": round(us, 2), "operand_copies": n, "flops": flops, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4), "algorithmic_bytes": nbytes,
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "attention": {"us": round(us_attn, 2), "flops": attn_flops,
@@ -291,26 +338,99 @@ def prefix_layer_case(T=2048, valid_len=1936, hole_p=0.02):
                           "algorithmic_bytes": attn_bytes}}
 
 
-def cpu_baseline(wl, wbits, rq, conds, n_steps_sample):
-    """Time the float64 oracle on the host for whole denoise steps (all layers)
-    of the same workload; report ms per step."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, wbits, rq, conds, n_steps_sample, n_layers_single):
+    """Time the float64 C oracle on the host: whole denoise steps (all layers)
+    of the same workload on every core, and a few layers on one thread
+    (scaled to a step); report ms per step."""
     import oracle as orc
     from masked_gqa_attention_action_amd import synth
-    threads = orc.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
     f = synth.bf16_to_f64
     ow = [{k: f(v) for k, v in w.items()} for w in wbits]
     kp = [f(rq.k_pre[l]) for l in range(wl.n_layers)]
     vp = [f(rq.v_pre[l]) for l in range(wl.n_layers)]
     cond = f(conds[0])
-    x = f(rq.x)
-    t0 = time.perf_counter()
-    for _ in range(n_steps_sample):
-        for l in range(wl.n_layers):
+
+    def run(n_layers):
+        x = f(rq.x)
+        t0 = time.perf_counter()
+        for i in range(n_layers):
+            l = i % wl.n_layers
             x = orc.layer(x, cond, ow[l], kp[l], vp[l], rq.mask, rq.pos0)
-    dt = time.perf_counter() - t0
-    return {"value": round(dt / n_steps_sample * 1e3, 2), "unit": "ms/step", "cores": threads, "kind": "oracle",
-            "sample": f"{n_steps_sample} whole denoise steps ({n_steps_sample * wl.n_layers} layer evaluations) of "
-                      f"the same workload by the float64 C oracle on {threads} threads, {dt:.1f} s wall"}
+        return time.perf_counter() - t0
+
+    threads = orc.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    dt = run(n_steps_sample * wl.n_layers)
+    out = {"value": round(dt / n_steps_sample * 1e3, 2), "unit": "ms/step", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{n_steps_sample} whole denoise steps ({n_steps_sample * wl.n_layers} layer evaluations) of "
+                     f"the same workload by the float64 C oracle on {threads} threads, {dt:.1f} s wall"}
+    if n_layers_single > 0:
+        orc.set_threads(1)
+        dt1 = run(n_layers_single)
+        orc.set_threads(threads)
+        out["single_thread"] = {
+            "value": round(dt1 / n_layers_single * wl.n_layers * 1e3, 1), "unit": "ms/step", "cores": 1,
+            "sample": f"{n_layers_single} layer evaluations on one thread, {dt1:.1f} s wall, scaled to "
+                      f"{wl.n_layers} layers"}
+    return out
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """GB/s of a plain device-to-device copy (bytes read + bytes written)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return round(gbs, 1)
+
+
+def stack_c3(dmx, reps=3):
+    """The 18-layer x 10-step stack at the P_b=896 bucket, chunk 50, captured
+    as one graph (the whole denoise loop per replay): ms per step."""
+    import torch
+    from masked_gqa_attention_action_amd import synth
+    wl = synth.WORKLOADS["c3"]
+    L = wl.n_layers
+    wbits = [synth.layer_weights(wl.weight_seed(l)) for l in range(L)]
+    rq = synth.make_request(wl.request_seed(0), wl.chunk, wl.p_bucket, wl.len_lo, wl.len_hi, L, wl.hole_p)
+    conds = np.stack([synth.time_embedding(t) for t in synth.step_times(wl.n_steps)])
+    wd = [dmx.pack_layer_weights({k: dev(v) for k, v in w.items()}) for w in wbits]
+    kp = [dev(rq.k_pre[l][None]) for l in range(L)]
+    vp = [dev(rq.v_pre[l][None]) for l in range(L)]
+    x0 = dev(rq.x[None])
+    x = x0.clone()
+    st = dmx.Stack(wd, kp, vp, dev(rq.mask[None], raw=True), dev(conds[:, None, :]),
+                   dev(np.array([rq.pos0], np.int32), raw=True), x)
+    stream = torch.cuda.Stream()
+    st.capture(stream)
+    ms = time_replays(st, stream, 1, reps) / wl.n_steps
+    assert torch.isfinite(x.float()).all(), "non-finite activations (c3)"
+    st.close()
+    visible = int(rq.mask.sum())
+    nbytes = L * algorithmic_bytes_per_layer(1, wl.chunk, wl.p_bucket, visible)
+    return {"workload": wl.note, "ms_per_step": round(ms, 4), "steps_per_replay": wl.n_steps,
+            "visible_prefix_rows": visible, "algorithmic_bytes_per_step": nbytes,
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def main():
@@ -319,8 +439,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="step1024")
-    ap.add_argument("--cpu-steps", type=int, default=16, help="denoise steps the oracle runs for the CPU baseline "
-                                                             "(0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=8, help="denoise steps the oracle runs for the CPU baseline "
+                                                            "on every core (0: skip the CPU baseline)")
+    ap.add_argument("--cpu-single-layers", type=int, default=4, help="layer evaluations the oracle runs on one "
+                                                                     "thread for the CPU baseline (0: skip)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="replays per kernel for per-kernel timing (0: skip)")
     ap.add_argument("--variants", type=int, default=1, help="also time the cached-modulation variants (0: skip)")
     ap.add_argument("--extras", type=int, default=1, help="also time single layers of the batched and long-prefix "
@@ -414,36 +536,63 @@ def main():
     step_flops = L * layer_flops(B, C, visible)
     step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # per-kernel timing (after the timed region) and the dominant kernel
+    # per-kernel timing (after the timed region) and the dominant kernel, on
+    # a 64-layer timing stack whose operands exceed the memory-side cache
     kernels = {}
+    st.close()
     if args.kernel_reps > 0:
+        tst = timing_stack(dmx, wd, kp, vp, mask, cond, pos0, x)
         for stage, name in enumerate(dmx.STAGE_NAMES):
-            us = time_stage(st, stage, L, stream, args.kernel_reps)
+            us = time_stage(tst, stage, TIMING_LAYERS, stream, args.kernel_reps)
             per_step = 1 if stage in (dmx.STAGE_MODS, dmx.STAGE_PACK) else L
             nbytes = stage_bytes(stage, B, C, P, visible, L)
             kernels[name] = {"us_per_launch": round(us, 3), "launches_per_step": per_step,
                              "share_of_step": round(us * per_step / (ms_step * 1e3), 4),
                              "algorithmic_bytes": nbytes,
                              "gbs": round(nbytes / (us * 1e-6) / 1e9, 1) if nbytes else None}
+        tst.close()
+        del tst
+        # the attention's own launch: with a modulation table the launch
+        # carries no modulation GEMVs on its idle CUs; the difference to the
+        # step's attention launch is what those GEMVs add
+        ttb = timing_stack(dmx, wd, kp, vp, mask, cond, pos0, x, mod_table=True)
+        us_own = time_stage(ttb, dmx.STAGE_ATTN, TIMING_LAYERS, stream, args.kernel_reps)
+        ttb.close()
+        del ttb
+        own_bytes = stage_bytes(dmx.STAGE_ATTN, B, C, P, visible, 1)  # no modulation weights
+        kernels["attention (own)"] = {
+            "us_per_launch": round(us_own, 3), "launches_per_step": L, "algorithmic_bytes": own_bytes,
+            "gbs": round(own_bytes / (us_own * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(own_bytes / (us_own * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "note": "the attention launch alone (modulation vectors from a table): KV, queries, suffix K/V, context"}
+        side = kernels["attention"]["algorithmic_bytes"] - own_bytes
+        extra = kernels["attention"]["us_per_launch"] - us_own
+        kernels["side modulation GEMVs"] = {
+            "us_added_per_launch": round(extra, 3), "algorithmic_bytes": side,
+            "note": "the next layer's two modulation GEMVs on the CUs the attention leaves idle: what they add to "
+                    "the attention launch"}
         torch.cuda.synchronize()
-    st.close()
     extras = {}
     if args.extras:
         for name in ("c1", "c2", "c4", "c5"):
             extras[f"layer_{name}"] = layer_case(name)
         extras["prefix_qkv_c4"] = prefix_qkv_case()
         extras["prefix_layer_2048"] = prefix_layer_case()
+        extras["stack_c3"] = stack_c3(dmx)
         torch.cuda.synchronize()
-    # a plain 256 MiB device copy: the reference dispatch for HBM byte counters
+    copy_gbs = copy_bandwidth()
+    # a plain 256 MiB device copy, the run's last: the reference dispatch for
+    # HBM byte counters
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
+    del src, dst
 
     roofline = {"bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": None,
-                "traffic": None}
+                "traffic": None, "measured_copy_gbs": copy_gbs}
     if kernels:
-        name = max(kernels, key=lambda k: kernels[k]["share_of_step"])
+        name = max((k for k in kernels if "share_of_step" in kernels[k]), key=lambda k: kernels[k]["share_of_step"])
         k = kernels[name]
         tag = name.replace(" ", "_").replace("+", "_")
         roofline.update({"kernel": name, "achieved": k["gbs"],
@@ -473,7 +622,7 @@ def main():
         "extras": extras,
     }
     if args.cpu_steps > 0:
-        out["cpu_baseline"] = cpu_baseline(wl, wbits, rq, conds, args.cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(wl, wbits, rq, conds, args.cpu_steps, args.cpu_single_layers)
     print(json.dumps(out), flush=True)
 
 

@@ -316,9 +316,10 @@ void dmx_graph_destroy(dmx_graph* g);
  * pass leaves in the workspace.  A stage that writes x (DMX_STAGE_DOWN)
  * changes the stack's state; others only rewrite workspace intermediates.
  * stage: one of DMX_STAGE_*; reps in [1, 100000]. */
-#define DMX_STAGE_MODS 0     /* modulation vectors of a step (one launch per step): layer 0's when the
-                                attention leaves CUs idle (each later layer's then come with the attention
-                                launch of the layer before it), else every layer's */
+#define DMX_STAGE_MODS 0     /* modulation vectors of a step (one launch per step): one layer's when the
+                                attention leaves CUs idle (a step launches layer 0's, each later layer's
+                                come with the attention launch of the layer before it; here: layer
+                                `layer`'s), else every layer's */
 #define DMX_STAGE_PACK 1     /* tiled copy (scaled by 1 + scale1) + row statistics of the stack input */
 #define DMX_STAGE_QKV 2      /* QKV + AdaRMS + QK-norm weights + RoPE */
 #define DMX_STAGE_ATTN 3     /* masked GQA attention splits (+ the next layer's modulation vectors, on the

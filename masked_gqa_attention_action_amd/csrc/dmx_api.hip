@@ -893,9 +893,9 @@ int dmx_stack_stage_launch(const dmx_stack_desc* d, int32_t layer, int32_t stage
   const LayerCtx c = stack_layer(d, L, &kv, 0, layer);
   for (int r = 0; r < reps; ++r) {
     if (stage == DMX_STAGE_MODS) {  // what a step launches
-      if (attn_has_idle_cus(L.attn)) {  // layer 0's (later ones ride on the attention)
+      if (attn_has_idle_cus(L.attn)) {  // one layer's two (a step: layer 0's; later ones ride on the attention)
         ModJob jobs[2];
-        layer_mod_jobs(d, L, 0, 0, jobs);
+        layer_mod_jobs(d, L, 0, layer, jobs);
         DMX_TRY(enq_mods(jobs, 2, d->batch, s));
       } else {
         DMX_TRY(enq_step_mods(d, 0, at<float>(d->ws, L.stack_mod), s));
