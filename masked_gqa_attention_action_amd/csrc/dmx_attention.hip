@@ -175,10 +175,11 @@ __device__ __forceinline__ bf16x8 v_frag(const uint16_t* sV, int t, int lane) {
   return r;
 }
 
-// Work-groups are dealt to the 8 XCDs of the chip in turn (blockIdx % 8), and
+// Work-groups are dealt to the 8 XCDs of the chip in turn (work-group w to
+// XCD (w + r) mod 8, with an offset r that the dispatches before set), and
 // each XCD has its own L2.  Work item lists ordered by (request, KV head) are
 // therefore split into 8 contiguous chunks, chunk x served by the
-// work-groups of XCD x, so the splits (and merge units) of one request / KV
+// work-groups w = x (mod 8), which share an XCD, so the splits (and merge units) of one request / KV
 // head share one or two L2s: its queries are fetched into few L2s and its
 // partials merged where they were written.  Placement changes only where data
 // is cached, never the results.  Returns the work item of this work-group, or

@@ -10,10 +10,12 @@
 // work-group keeps its weight slices for the next stage in flight while it
 // waits for that stage's inputs, so weight streaming overlaps the chain.
 //
-// Placement.  256 work-groups, one per CU; work-group w runs on XCC w % 8
-// (the dispatcher deals work-groups to the 8 XCCs in turn), and a hand-off
-// among the 32 work-groups of one XCC is several times cheaper than one that
-// crosses XCCs.  So XCC x owns query head x: it projects q head x and the
+// Placement.  256 work-groups, one per CU.  The dispatcher deals work-groups
+// to the 8 XCCs in turn: work-group w runs on XCC (w + r) mod 8, with an
+// offset r that the dispatches before set, so the 32 work-groups w = x
+// (mod 8) always share an XCC, and a hand-off among them (~1 us) is cheaper
+// than one that crosses XCCs (2.5 - 3 us).  Below, "XCC x" is that group of
+// work-groups.  XCC x owns query head x: it projects q head x and the
 // K/V head x / 2 of its group (the two XCCs of a group both compute it), runs
 // head x's attention over the prefix and chunk keys, merges the splits and
 // multiplies the context by head x's 256 columns of W_o.  The eight heads'
