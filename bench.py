@@ -494,6 +494,19 @@ def main():
                                       "frac_of_hbm_peak": round(tb_bytes / (ms_tb * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                       "note": "one step per replay, modulation vectors precomputed per schedule"}
         tb.close()
+        # the same step as one persistent kernel (batch 1: the whole stack in
+        # one launch, weights prefetched across its stage hand-offs)
+        x.copy_(dev(rq.x[None]))
+        ps = dmx.Stack(wd, kp, vp, mask, cond, pos0, x, persistent=True)
+        ps.capture(stream)
+        ms_ps = time_replays(ps, stream, args.warmup, args.steps)
+        ps.sync_check(stream)
+        assert torch.isfinite(x.float()).all(), "non-finite activations (persistent)"
+        step_b = L * algorithmic_bytes_per_layer(B, C, P, visible)
+        variants["persistent_step"] = {"ms_per_step": round(ms_ps, 4), "algorithmic_bytes": step_b,
+                                       "frac_of_hbm_peak": round(step_b / (ms_ps * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                       "note": "one step per replay as a single persistent kernel (k_step)"}
+        ps.close()
         # the whole denoise loop as one graph, the same work per step as the
         # headline (modulation vectors computed in every step, no table)
         x.copy_(dev(rq.x[None]))
