@@ -187,100 +187,127 @@ __device__ __forceinline__ void epi_store8(const GemmArgs& a, int prow, int n, c
   }
 }
 
+// Epilogue constants of an output tile: NOUT output features (pairs for QKV)
+// per row, OUTW of them per task, TPR tasks per row.
+template <int EPI, int NT>
+struct EpiShape {
+  static constexpr int NOUT = (EPI == EPI_GEGLU || EPI == EPI_QKV) ? 16 : NT;
+  static constexpr int OUTW = EPI == EPI_GEGLU ? 4 : 8;
+  static constexpr int TPR = NOUT / OUTW;
+};
+
+// First output feature of task column c0 of output tile `tile` (the
+// operand fetch and the stores address it).
+template <int EPI, int NT>
+__device__ __forceinline__ int epi_feature(int tile, int c0) {
+  return EPI == EPI_QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0;
+}
+
+// One epilogue task: block row r, OUTW features of output tile `tile` from
+// tile column c0.  Rsum(r, c) is the projection sum of block row r and tile
+// column c, Ssum(r, c) the shift tile's sum for row r's request (MOD), both
+// with their partial sums added in one fixed order; sR[r] is the row's 1 /
+// rms (MOD), sF the tile's 16 rotation frequencies (QKV); sq / sQ are the
+// tile's LDS scratch; cur holds the task's global operands (epi_fetch).
+template <int EPI, int NT, bool MOD, class RF, class SF>
+__device__ __forceinline__ void epi_task(const GemmArgs& a, int tile, int m0, int r, int c0, RF Rsum, SF Ssum,
+                                         const float* sR, const double* sF, float* sq, float* sQ,
+                                         const EpiPre& cur) {
+  constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
+  constexpr bool QKV = EPI == EPI_QKV;
+  constexpr int NOUT = EpiShape<EPI, NT>::NOUT;
+  const int n = epi_feature<EPI, NT>(tile, c0);
+  float v[8], seen[8];
+  if (QKV) {
+    // 8 rotation pairs: first-half features f .. f+7 and partners f+128 ..
+    const int h = tile >> 3;  // head
+    const int f = n;
+    float lo[8], hi[8], sq8 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float tl = Rsum(r, c0 + i), th = Rsum(r, 16 + c0 + i);
+      if (MOD) {
+        const float sl = Ssum(r, c0 + i), sh = Ssum(r, 16 + c0 + i);
+        lo[i] = sR[r] * tl + sl;
+        hi[i] = sR[r] * th + sh;
+      } else {
+        lo[i] = tl;
+        hi[i] = th;
+      }
+      sq8 += lo[i] * lo[i] + hi[i] * hi[i];
+    }
+    if (h < kHQ + kHK) {
+      float wl[8], wh[8];
+      unpack8(cur.wl, wl);
+      unpack8(cur.wh, wh);
+      const int prow = m0 + r, b = prow / a.TP;
+      const double pos = (double)a.pos0[b] + (double)(prow - b * a.TP);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        double rev = pos * sF[c0 + i];
+        rev -= floor(rev);
+        const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+        const float x0 = lo[i] * (1.f + wl[i]), x1 = hi[i] * (1.f + wh[i]);
+        lo[i] = x0 * cs - x1 * sn;
+        hi[i] = x1 * cs + x0 * sn;
+      }
+    }
+    if (h >= kHQ && h < kHQ + kHK) {  // k heads: fp32, scaled by 1 / rms when staged
+      float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
+      float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
+      *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+      *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
+      *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
+    } else {  // q and v heads: bf16, as the attention's MFMA consumes them
+      const int fq = h < kHQ ? f : f - kHK * kD;
+      *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq, kQVB)) = pack8(lo);
+      *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq + 128, kQVB)) = pack8(hi);
+    }
+    sQ[r * 2 + (c0 >> 3)] = sq8;
+  } else if (EPI == EPI_GEGLU) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float g = Rsum(r, c0 + i), u = Rsum(r, 16 + c0 + i);
+      if (MOD) {
+        const float gs = Ssum(r, c0 + i), us = Ssum(r, 16 + c0 + i);
+        g = sR[r] * g + gs;
+        u = sR[r] * u + us;
+      }
+      v[i] = gelu_tanh(g) * u;
+    }
+    *reinterpret_cast<uint2*>(a.out_pk + tile_off(m0 + r, tile * 16 + (c0 & ~7), a.ldo) + (c0 & 7)) =
+        make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = Rsum(r, c0 + i);
+      v[i] = MOD ? sR[r] * t + Ssum(r, c0 + i) : t;
+    }
+    epi_store8<EPI>(a, m0 + r, n, cur, v, seen);
+    if (SSQ) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sq[r * NOUT + c0 + i] = seen[i] * seen[i];
+    }
+  }
+}
+
 // Epilogue of one output tile (NT columns `tile`) over block rows m0 ..
 // m0 + nrows - 1, run by every thread of the work-group (it synchronises).
-// Rsum(r, c) is the projection sum of block row r and tile column c, Ssum(r,
-// c) the shift tile's sum for row r's request (MOD), both with their partial
-// sums added in one fixed order; sR[r] is the row's 1 / rms (MOD), sF the
-// tile's 16 rotation frequencies (QKV); sq / sQ are LDS scratch for nrows
-// rows.  pre0: the global operands of the thread's first task, if fetched.
+// Rsum, Ssum, sR, sF, sq and sQ as for epi_task (sq / sQ for nrows rows).
+// pre0: the global operands of the thread's first task, if fetched.
 template <int EPI, int NT, bool MOD, class RF, class SF>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int tile, int m0, int nrows, RF Rsum, SF Ssum,
                                               const float* sR, const double* sF, float* sq, float* sQ,
                                               const EpiPre* pre0) {
   constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
   constexpr bool QKV = EPI == EPI_QKV;
-  constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;  // output features (pairs for QKV) per row
-  constexpr int OUTW = EPI == EPI_GEGLU ? 4 : 8;  // outputs per epilogue task
-  constexpr int TPR = NOUT / OUTW;                // epilogue tasks per row
+  constexpr int NOUT = EpiShape<EPI, NT>::NOUT, OUTW = EpiShape<EPI, NT>::OUTW, TPR = EpiShape<EPI, NT>::TPR;
   // task e: row r = e / TPR, OUTW features from c0; the thread's first task
   // is peeled so that the prefetched operands are used without a copy
   auto task = [&](int e, const EpiPre& cur) {
     const int r = e / TPR, c0 = (e - r * TPR) * OUTW;
-    const int n = QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0;
-    float v[8], seen[8];
-    if (QKV) {
-      // 8 rotation pairs: first-half features f .. f+7 and partners f+128 ..
-      const int h = tile >> 3;  // head
-      const int f = n;
-      float lo[8], hi[8], sq8 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float tl = Rsum(r, c0 + i), th = Rsum(r, 16 + c0 + i);
-        if (MOD) {
-          const float sl = Ssum(r, c0 + i), sh = Ssum(r, 16 + c0 + i);
-          lo[i] = sR[r] * tl + sl;
-          hi[i] = sR[r] * th + sh;
-        } else {
-          lo[i] = tl;
-          hi[i] = th;
-        }
-        sq8 += lo[i] * lo[i] + hi[i] * hi[i];
-      }
-      if (h < kHQ + kHK) {
-        float wl[8], wh[8];
-        unpack8(cur.wl, wl);
-        unpack8(cur.wh, wh);
-        const int prow = m0 + r, b = prow / a.TP;
-        const double pos = (double)a.pos0[b] + (double)(prow - b * a.TP);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          double rev = pos * sF[c0 + i];
-          rev -= floor(rev);
-          const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-          const float x0 = lo[i] * (1.f + wl[i]), x1 = hi[i] * (1.f + wh[i]);
-          lo[i] = x0 * cs - x1 * sn;
-          hi[i] = x1 * cs + x0 * sn;
-        }
-      }
-      if (h >= kHQ && h < kHQ + kHK) {  // k heads: fp32, scaled by 1 / rms when staged
-        float* yo = a.out_f32 + tile_off_f32(m0 + r, f, kQKV);
-        float* yh = a.out_f32 + tile_off_f32(m0 + r, f + 128, kQKV);
-        *reinterpret_cast<float4*>(yo) = make_float4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<float4*>(yo + 256) = make_float4(lo[4], lo[5], lo[6], lo[7]);
-        *reinterpret_cast<float4*>(yh) = make_float4(hi[0], hi[1], hi[2], hi[3]);
-        *reinterpret_cast<float4*>(yh + 256) = make_float4(hi[4], hi[5], hi[6], hi[7]);
-      } else {  // q and v heads: bf16, as the attention's MFMA consumes them
-        const int fq = h < kHQ ? f : f - kHK * kD;
-        *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq, kQVB)) = pack8(lo);
-        *reinterpret_cast<uint4*>(a.out_pk + tile_off(m0 + r, fq + 128, kQVB)) = pack8(hi);
-      }
-      sQ[r * 2 + (c0 >> 3)] = sq8;
-    } else if (EPI == EPI_GEGLU) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float g = Rsum(r, c0 + i), u = Rsum(r, 16 + c0 + i);
-        if (MOD) {
-          const float gs = Ssum(r, c0 + i), us = Ssum(r, 16 + c0 + i);
-          g = sR[r] * g + gs;
-          u = sR[r] * u + us;
-        }
-        v[i] = gelu_tanh(g) * u;
-      }
-      *reinterpret_cast<uint2*>(a.out_pk + tile_off(m0 + r, tile * 16 + (c0 & ~7), a.ldo) + (c0 & 7)) =
-          make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float t = Rsum(r, c0 + i);
-        v[i] = MOD ? sR[r] * t + Ssum(r, c0 + i) : t;
-      }
-      epi_store8<EPI>(a, m0 + r, n, cur, v, seen);
-      if (SSQ) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sq[r * NOUT + c0 + i] = seen[i] * seen[i];
-      }
-    }
+    epi_task<EPI, NT, MOD>(a, tile, m0, r, c0, Rsum, Ssum, sR, sF, sq, sQ, cur);
   };
   auto task_row_ok = [&](int e) { return row_valid(m0 + e / TPR, a.T, a.TP); };
   int e0 = threadIdx.x;
@@ -292,7 +319,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int tile, int m
     if (!task_row_ok(e)) continue;
     const int r = e / TPR, c0 = (e - r * TPR) * OUTW;
     EpiPre cur;
-    epi_fetch<EPI>(a, m0 + r, QKV ? (tile >> 3) * kD + (tile & 7) * 16 + c0 : tile * NT + c0, cur);
+    epi_fetch<EPI>(a, m0 + r, epi_feature<EPI, NT>(tile, c0), cur);
     task(e, cur);
   }
   if (SSQ && a.ss_out) {
@@ -303,6 +330,60 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int tile, int m
     __syncthreads();
     for (int r = threadIdx.x; r < nrows; r += blockDim.x)
       if (row_valid(m0 + r, a.T, a.TP)) a.ss_q[(size_t)(m0 + r) * kQkvTiles + tile] = sQ[r * 2] + sQ[r * 2 + 1];
+  }
+}
+
+// Epilogue of the NST output tiles tile0 .. of a large-M block (rows m0 ..
+// m0 + nrows - 1, at most BM) in one pass: every task's global operands are
+// fetched first (TMAX tasks per thread at most), then the tasks run, with no
+// barrier between tiles; sq / sQ hold NST tiles' scratch (BM rows each).
+// Rsum(r, c) and Ssum(r, c) take the block column c.  The arithmetic of each
+// output is epi_task's, as in tile_epilogue.
+template <int EPI, int NT, int NST, int BM, int TMAX, bool MOD, class RF, class SF>
+__device__ __forceinline__ void block_epilogue(const GemmArgs& a, int tile0, int m0, int nrows, RF Rsum, SF Ssum,
+                                               const float* sR, const double* sF, float* sq, float* sQ) {
+  constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
+  constexpr bool QKV = EPI == EPI_QKV;
+  constexpr int NOUT = EpiShape<EPI, NT>::NOUT, OUTW = EpiShape<EPI, NT>::OUTW, TPR = EpiShape<EPI, NT>::TPR;
+  const int per_tile = nrows * TPR, ntask = NST * per_tile;
+  EpiPre pre[TMAX];
+  bool ok[TMAX];
+#pragma unroll
+  for (int k = 0; k < TMAX; ++k) {
+    const int e = threadIdx.x + k * blockDim.x;
+    const int st = e / per_tile, rc = e - st * per_tile, r = rc / TPR, c0 = (rc - r * TPR) * OUTW;
+    ok[k] = e < ntask && row_valid(m0 + r, a.T, a.TP);
+    if (ok[k]) epi_fetch<EPI>(a, m0 + r, epi_feature<EPI, NT>(tile0 + st, c0), pre[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < TMAX; ++k) {
+    if (!ok[k]) continue;
+    const int e = threadIdx.x + k * blockDim.x;
+    const int st = e / per_tile, rc = e - st * per_tile, r = rc / TPR, c0 = (rc - r * TPR) * OUTW;
+    epi_task<EPI, NT, MOD>(
+        a, tile0 + st, m0, r, c0, [&](int rr, int c) { return Rsum(rr, st * NT + c); },
+        [&](int rr, int c) { return Ssum(rr, st * NT + c); }, sR, sF + st * 16, sq + st * BM * NOUT,
+        sQ + st * BM * 2, pre[k]);
+  }
+  if (SSQ && a.ss_out) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < NST * nrows; i += blockDim.x) {
+      const int st = i / nrows, r = i - st * nrows;
+      if (!row_valid(m0 + r, a.T, a.TP)) continue;
+      const float* q = sq + st * BM * NOUT + r * NOUT;
+      float t = 0.f;
+#pragma unroll
+      for (int c = 0; c < NOUT; ++c) t += q[c];
+      a.ss_out[(size_t)(m0 + r) * a.ss_out_n + tile0 + st] = t;
+    }
+  }
+  if (QKV) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < NST * nrows; i += blockDim.x) {
+      const int st = i / nrows, r = i - st * nrows;
+      if (((tile0 + st) >> 3) < kHQ + kHK && row_valid(m0 + r, a.T, a.TP))
+        a.ss_q[(size_t)(m0 + r) * kQkvTiles + tile0 + st] = sQ[st * BM * 2 + r * 2] + sQ[st * BM * 2 + r * 2 + 1];
+    }
   }
 }
 
@@ -487,6 +568,55 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
 // (wm, wn) the rows wm*WMT*16 .. and the fragments wn*WNF ..; every fragment is
 // loaded straight from the tiled operands into registers (one 1 KB load per
 // wave and fragment) PD steps ahead of its MFMAs.
+// Row scales of a large-M block (AdaRMS: 1 / rms of each row, from the row's
+// sums-of-squares partials, summed as k_gemm sums them): thread (row rr,
+// quarter qq) of pass p handles row p * NTHR / 4 + rr.  row_ss_fetch issues
+// the loads (before the K loop, so that their latency hides behind its
+// operand loads), row_ss_store finishes the sums into sR.
+template <int BM, int NTHR>
+struct RowSS {
+  static constexpr int NP = (BM * 4 + NTHR - 1) / NTHR;  // passes
+  float4 v[NP][4];
+  __device__ __forceinline__ void fetch(const GemmArgs& a, int m0, int nrows) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int rr = p * (NTHR / 4) + (threadIdx.x >> 2), qq = threadIdx.x & 3;
+      const int per = a.ss_in_n >> 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[p][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rr < nrows && row_valid(m0 + rr, a.T, a.TP)) {
+        const float* sp = a.ss_in + (size_t)(m0 + rr) * a.ss_in_n + qq * per;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i * 4 < per) v[p][i] = *reinterpret_cast<const float4*>(sp + i * 4);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float* sR) const {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int rr = p * (NTHR / 4) + (threadIdx.x >> 2), qq = threadIdx.x & 3;
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t += v[p][i].x + v[p][i].y + v[p][i].z + v[p][i].w;
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      if (qq == 0 && rr < BM) sR[rr] = 1.0f / sqrtf(t * (1.0f / kH) + kEps);
+    }
+  }
+};
+
+// Rotation frequencies of the NST output tiles from tile0 (QKV), as k_gemm
+// computes them: revolutions per position of the tile's 16 first-half dims.
+template <int NST>
+__device__ __forceinline__ void rope_freqs(const GemmArgs& a, int tile0, double* sF) {
+  if (threadIdx.x < NST * 16) {
+    const int tile = tile0 + (threadIdx.x >> 4);
+    const int j = (tile & 7) * 16 + (threadIdx.x & 15);
+    sF[threadIdx.x] = exp2(-(double)j / 128.0 * log2((double)a.rope_base)) * 0.15915494309189533577;
+  }
+}
+
 template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int WNF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_big(GemmArgs a) {
   constexpr bool MOD = ASRC == A_MODPRE;
@@ -510,8 +640,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float sShift[MOD ? MAXREQ * BN : 1];               // shift sums [request][column]
   __shared__ float sR[MOD ? BM : 1];
   __shared__ double sF[QKV ? NST * 16 : 1];
-  __shared__ float sq[SSQ ? BM * NOUT : 1];
-  __shared__ float sQ[QKV ? BM * 2 : 1];
+  __shared__ float sq[SSQ ? NST * BM * NOUT : 1];
+  __shared__ float sQ[QKV ? NST * BM * 2 : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -609,8 +739,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  RowSS<BM, 256> rss;
+  if (MOD) rss.fetch(a, m0, nrows);
 #pragma unroll
   for (int d = 0; d < PD; ++d) load(d, Ab[d], Wb[d], Hb[d]);
+  if (MOD) rss.store(sR);  // read after the K loop's last barrier
+  if (QKV) rope_freqs<NST>(a, blockIdx.x * NST, sF);
   zero_acc();
 #pragma unroll 1
   for (int s0 = 0; s0 < KS; s0 += PD) {
@@ -636,109 +770,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         sTot[((wm * WMT + i) * 16 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr] = tot[i][j][e];
-  // row scales and rotation frequencies, as k_gemm computes them
-  if (MOD) {
-    for (int rb = 0; rb < BM; rb += 64) {
-      const int rr = rb + (threadIdx.x >> 2), qq = threadIdx.x & 3;
-      const int per = a.ss_in_n >> 2;
-      float4 ssp[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ssp[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (rr < nrows && row_valid(m0 + rr, a.T, a.TP)) {
-        const float* sp = a.ss_in + (size_t)(m0 + rr) * a.ss_in_n + qq * per;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i * 4 < per) ssp[i] = *reinterpret_cast<const float4*>(sp + i * 4);
-      }
-      float t = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t += ssp[i].x + ssp[i].y + ssp[i].z + ssp[i].w;
-      t += __shfl_xor(t, 1, 64);
-      t += __shfl_xor(t, 2, 64);
-      if (qq == 0) sR[rr] = 1.0f / sqrtf(t * (1.0f / kH) + kEps);
-    }
-  }
-  if (QKV && threadIdx.x < NST * 16) {
-    const int tile = blockIdx.x * NST + (threadIdx.x >> 4);
-    const int j = (tile & 7) * 16 + (threadIdx.x & 15);
-    sF[threadIdx.x] = exp2(-(double)j / 128.0 * log2((double)a.rope_base)) * 0.15915494309189533577;
-  }
   __syncthreads();
-#pragma unroll 1
-  for (int st = 0; st < NST; ++st) {
-    const int tile = blockIdx.x * NST + st;
-    tile_epilogue<EPI, NT, MOD>(
-        a, tile, m0, nrows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
-        [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + st * NT + c]; }, sR, sF + st * 16, sq,
-        sQ, nullptr);
-    __syncthreads();
-  }
+  constexpr int TMAX = (NST * BM * EpiShape<EPI, NT>::TPR + 255) / 256;
+  block_epilogue<EPI, NT, NST, BM, TMAX, MOD>(
+      a, blockIdx.x * NST, m0, nrows, [&](int r, int c) { return sTot[r * TLD + c]; },
+      [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + c]; }, sR, sF, sq, sQ);
 }
 
-// Wide large-M projections (N >= 4096: QKV, gate-up, the prefix QKV), the
-// same arithmetic as k_gemm bit for bit, with the operands shared through
-// LDS.  A work-group of 8 waves (2 x 4; two per SIMD) owns BM rows x 256
-// columns.  Each 32-column step's operand fragments (BM/16 A tiles, 16 W
+// Wide large-M projections, the same arithmetic as k_gemm bit for bit, with
+// the operands shared through LDS.  A work-group of 2 x NWN waves owns BM
+// rows x NWN * 64 columns (8 waves, two per SIMD, for 256 columns; 4 waves
+// for 128).  Each 32-column step's operand fragments (BM/16 A tiles, 4 NWN W
 // fragments, 1 KB each) are copied from HBM straight into an LDS stage by
 // loads that bypass registers (global_load_lds, 16 B per lane, so a wave's
-// fragment lands as one contiguous 1 KB block), four or five steps ahead of
+// fragment lands as one contiguous 1 KB block), STAGES - 1 steps ahead of
 // their use; each wave reads its WMT A tiles and 4 W fragments of the next
-// step from LDS while the MFMAs of the current one run.  K is split into the same NR ranges of KSR
-// steps as the skinny kernel's waves; each range is accumulated from zero in
-// step order and the range sums are added in range order in registers.
-template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_lds(GemmArgs a) {
+// step from LDS while the MFMAs of the current one run.  K is split into the
+// same NR ranges of KSR steps as the skinny kernel's waves; each range is
+// accumulated from zero in step order and the range sums are added in range
+// order in registers.
+template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int NWN, int STG>
+__global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN / 2, 2))) void k_gemm_lds(GemmArgs a) {
   constexpr bool MOD = ASRC == A_MODPRE;
   constexpr bool QKV = EPI == EPI_QKV;
   constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
   constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;
+  constexpr int NW = 2 * NWN;          // waves
   constexpr int WNF = 4;               // W fragments per wave
   constexpr int BM = 2 * WMT * 16;     // rows per block
-  constexpr int BNF = 4 * WNF;         // fragments per block
+  constexpr int BNF = NWN * WNF;       // fragments per block
   constexpr int BN = BNF * 16;         // columns per block
   constexpr int NTT = NT / 16, NST = BNF / NTT;
   constexpr int KS = NR * KSR;
   constexpr int AF = BM / 16;          // A tiles per step
   constexpr int SF = AF + BNF;         // fragments per step
-  constexpr int DPW = SF / 8;          // fragments each wave copies per step
+  constexpr int DPW = SF / NW;         // fragments each wave copies per step
   // a ring of STAGES steps, AHEAD = STAGES - 1 of them copied ahead: LDS
   // latency times bandwidth needs about 100 KB in flight per CU
-  constexpr int STAGES = MOD ? 5 : 6, AHEAD = STAGES - 1;
+  constexpr int STAGES = STG, AHEAD = STAGES - 1;
   constexpr int MAXREQ = BM / 16 + 1;
   constexpr int STAGE_EL = SF * 512;   // bf16 elements per stage
   constexpr int TLD = BN + 4;           // sTot row stride (floats): rows 4 banks apart
   constexpr int RAW = (STAGES * STAGE_EL * 2 > BM * TLD * 4) ? STAGES * STAGE_EL * 2 : BM * TLD * 4;
-  static_assert(SF % 8 == 0 && BNF % NTT == 0 && KS % 2 == 0, "block shape");
+  static_assert(SF % NW == 0 && BNF % NTT == 0 && KS % 2 == 0 && AHEAD * DPW < 64, "block shape");
   static_assert(!MOD || KS * 32 == kH, "the modulated A operand spans one hidden row");
-  // the stages during the K loop, the range sums [row][column] after it
-  __shared__ __attribute__((aligned(16))) unsigned char smem[RAW];
-  __shared__ __attribute__((aligned(16))) uint16_t sHb[MOD ? MAXREQ * kH : 8];  // bf16 shift vectors
-  __shared__ float sShift[MOD ? MAXREQ * BN : 1];
-  __shared__ float sR[MOD ? BM : 1];
-  __shared__ double sF[QKV ? NST * 16 : 1];
-  __shared__ float sq[SSQ ? BM * NOUT : 1];
-  __shared__ float sQ[QKV ? BM * 2 : 1];
+  // One LDS array for everything: the stages during the K loop (the range
+  // sums [row][column] after it), then the bf16 shift vectors, the shift
+  // sums [request][column], the row scales, the rotation frequencies and the
+  // epilogue's sums of squares.  With several LDS arrays the compiler makes
+  // every LDS read of the loop wait for all copies in flight; the loop's
+  // explicit waits and barriers order the copies and the reads instead.
+  constexpr int O_HB = RAW;
+  constexpr int O_SHIFT = O_HB + (MOD ? MAXREQ * kH * 2 : 0);
+  constexpr int O_R = O_SHIFT + (MOD ? MAXREQ * BN * 4 : 0);
+  constexpr int O_F = (O_R + (MOD ? BM * 4 : 0) + 7) & ~7;
+  constexpr int O_Q2 = O_F + (QKV ? NST * 16 * 8 : 0);
+  constexpr int O_Q = O_Q2 + (SSQ ? BM * NOUT * 4 : 0);
+  constexpr int LDS_BYTES = O_Q + (QKV ? BM * 2 * 4 : 0);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
   float* sTot = reinterpret_cast<float*>(smem);
+  uint16_t* sHb = reinterpret_cast<uint16_t*>(smem + O_HB);
+  float* sShift = reinterpret_cast<float*>(smem + O_SHIFT);
+  float* sR = reinterpret_cast<float*>(smem + O_R);
+  double* sF = reinterpret_cast<double*>(smem + O_F);
+  float* sq = reinterpret_cast<float*>(smem + O_Q2);
+  float* sQ = reinterpret_cast<float*>(smem + O_Q);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int lr = lane & 15, lq = lane >> 4;
+  const int cblk = blockIdx.x;  // column block
   const int m0 = blockIdx.y * BM;
   const int nrows = min(BM, a.M - m0);
   const int last_tile = a.M / 16 - 1;
   const int b0 = m0 / a.TP;
   const int nreq = MOD ? (m0 + nrows - 1) / a.TP - b0 + 1 : 0;
-  const bool shift_wave = MOD && wm == 0;
-
-  if (MOD) {  // the block's shift vectors, rounded to bf16 as the shift tile holds them
-    for (int i = threadIdx.x; i < nreq * (kH / 2); i += blockDim.x) {
-      const int q = i / (kH / 2), k2 = (i - q * (kH / 2)) * 2;
-      const float* sh = a.nmod + (size_t)(b0 + q) * 3 * kH + kH + k2;
-      *reinterpret_cast<uint32_t*>(sHb + q * kH + k2) = pack2(sh[0], sh[1]);
-    }
-    __syncthreads();
-  }
 
   // fragments this wave copies: f = wave * DPW + d (A tiles first, then W)
   const uint16_t* gsrc[DPW];
@@ -749,7 +856,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       gsrc[d] = a.A + (size_t)min(m0 / 16 + f, last_tile) * KS * 512 + lane * 8;  // rows past M: last tile
     } else {
       const int fj = f - AF, st = fj / NTT, nt = fj % NTT;
-      const int tile = blockIdx.x * NST + st;
+      const int tile = cblk * NST + st;
       const int wt = EPI == EPI_GEGLU ? (nt == 0 ? tile : a.wtile_up + tile)
                      : QKV ? (tile >> 3) * 16 + nt * 8 + (tile & 7)
                            : tile * NTT + nt;
@@ -763,7 +870,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       lds_copy16(gsrc[d] + (size_t)ks * 512, dst + (wave * DPW + d) * 512);
   };
 
-  f32x4 acc[WMT][WNF], tot[WMT][WNF], accs[WNF];
+  // accs / stot: the shift tile's sums of this wave's W fragments (range,
+  // total); every wave runs them, so that the loop has no branch (with one,
+  // the compiler waits for every LDS read in flight before the MFMAs); the
+  // waves of row half 0 keep theirs
+  f32x4 acc[WMT][WNF], tot[WMT][WNF], accs[WNF], stot[WNF];
 #pragma unroll
   for (int i = 0; i < WMT; ++i)
 #pragma unroll
@@ -772,7 +883,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int j = 0; j < WNF; ++j) accs[j] = zero_f32x4();
 
   // this wave's fragments of step ks from its stage (A tiles, W fragments,
-  // the shift row of each request for the shift waves)
+  // the shift row of each request; lanes past the block's requests read
+  // request 0's and zero it)
   auto read_frags = [&](int ks, bf16x8* af, bf16x8* wf, bf16x8& hs) {
     const uint16_t* st = stage + (ks % STAGES) * STAGE_EL;
 #pragma unroll
@@ -780,13 +892,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int j = 0; j < WNF; ++j)
       wf[j] = *reinterpret_cast<const bf16x8*>(st + (AF + wn * WNF + j) * 512 + lane * 8);
-    if (shift_wave) hs = *reinterpret_cast<const bf16x8*>(sHb + (lr < nreq ? lr : 0) * kH + ks * 32 + lq * 8);
+    if (MOD) hs = *reinterpret_cast<const bf16x8*>(sHb + (lr < nreq ? lr : 0) * kH + ks * 32 + lq * 8);
   };
   auto step_mma = [&](int ks, const bf16x8* af, const bf16x8* wf, bf16x8 hs) {
-    if (shift_wave) {
-      if (lr >= nreq) hs = zero_bf16x8();
+    if (MOD) {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, keep_or_zero(lr < nreq, __builtin_bit_cast(uint4, hs)));
 #pragma unroll
-      for (int j = 0; j < WNF; ++j) accs[j] = mfma16(hs, wf[j], accs[j]);
+      for (int j = 0; j < WNF; ++j) accs[j] = mfma16(h, wf[j], accs[j]);
     }
 #pragma unroll
     for (int i = 0; i < WMT; ++i)
@@ -802,15 +914,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int e = 0; e < 4; ++e) tot[i][j][e] = (first ? 0.f : tot[i][j][e]) + acc[i][j][e];
           acc[i][j] = zero_f32x4();
         }
-      if (shift_wave) {  // the shift sums accumulate in LDS (sShift is not a stage)
+      if (MOD) {
 #pragma unroll
         for (int j = 0; j < WNF; ++j) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * lq + e < nreq) {
-              float* d = sShift + (4 * lq + e) * BN + (wn * WNF + j) * 16 + lr;
-              *d = (first ? 0.f : *d) + accs[j][e];
-            }
+          for (int e = 0; e < 4; ++e) stot[j][e] = (first ? 0.f : stot[j][e]) + accs[j][e];
           accs[j] = zero_f32x4();
         }
       }
@@ -822,8 +930,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // means every wave has consumed step ks - 1's fragments), refill step
   // ks - 1's stage with step ks + AHEAD, read step ks + 1's fragments, then
   // run step ks's MFMAs while those reads are in flight.
+  // set-up inputs first (the block's shift vectors, the rows' sums-of-squares
+  // partials), then the first copies, then the set-up: its loads land while
+  // the copies are in flight
+  constexpr int NTHR = NW * 64;
+  constexpr int SHP = (MAXREQ * (kH / 2) + NTHR - 1) / NTHR;  // shift pairs per thread
+  float2 shv[MOD ? SHP : 1];
+  RowSS<BM, NTHR> rss;
+  if (MOD) {
+#pragma unroll
+    for (int k = 0; k < SHP; ++k) {
+      const int i = threadIdx.x + k * NTHR, q = i / (kH / 2), k2 = (i - q * (kH / 2)) * 2;
+      shv[k] = q < nreq ? *reinterpret_cast<const float2*>(a.nmod + (size_t)(b0 + q) * 3 * kH + kH + k2)
+                        : make_float2(0.f, 0.f);
+    }
+    rss.fetch(a, m0, nrows);
+  }
 #pragma unroll
   for (int k = 0; k < AHEAD; ++k) issue(k);
+  if (MOD) {  // the shift vectors rounded to bf16, as the shift tile holds them
+#pragma unroll
+    for (int k = 0; k < SHP; ++k) {
+      const int i = threadIdx.x + k * NTHR, q = i / (kH / 2), k2 = (i - q * (kH / 2)) * 2;
+      if (q < nreq) *reinterpret_cast<uint32_t*>(sHb + q * kH + k2) = pack2(shv[k].x, shv[k].y);
+    }
+    rss.store(sR);
+  }
+  if (QKV) rope_freqs<NST>(a, cblk * NST, sF);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the set-up's LDS writes are done before the barrier
   wait_vmcnt<(AHEAD - 1) * DPW>();
   lds_barrier();
   bf16x8 af0[WMT], wf0[WNF], af1[WMT], wf1[WNF], hs0 = zero_bf16x8(), hs1 = zero_bf16x8();
@@ -853,37 +987,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         sTot[((wm * WMT + i) * 16 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr] = tot[i][j][e];
-  // row scales and rotation frequencies, as k_gemm computes them
-  if (MOD) {
-    for (int rb = 0; rb < BM; rb += 128) {
-      const int rr = rb + (threadIdx.x >> 2), qq = threadIdx.x & 3;
-      const int per = a.ss_in_n >> 2;
-      float4 ssp[4];
+  // the shift sums [request][column], lane (lr, lq) holding requests 4 lq .. 4 lq + 3
+  if (MOD && wm == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ssp[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (rr < nrows && row_valid(m0 + rr, a.T, a.TP)) {
-        const float* sp = a.ss_in + (size_t)(m0 + rr) * a.ss_in_n + qq * per;
+    for (int j = 0; j < WNF; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (i * 4 < per) ssp[i] = *reinterpret_cast<const float4*>(sp + i * 4);
-      }
-      float t = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t += ssp[i].x + ssp[i].y + ssp[i].z + ssp[i].w;
-      t += __shfl_xor(t, 1, 64);
-      t += __shfl_xor(t, 2, 64);
-      if (qq == 0 && rr < BM) sR[rr] = 1.0f / sqrtf(t * (1.0f / kH) + kEps);
-    }
-  }
-  if (QKV && threadIdx.x < NST * 16) {
-    const int tile = blockIdx.x * NST + (threadIdx.x >> 4);
-    const int j = (tile & 7) * 16 + (threadIdx.x & 15);
-    sF[threadIdx.x] = exp2(-(double)j / 128.0 * log2((double)a.rope_base)) * 0.15915494309189533577;
+      for (int e = 0; e < 4; ++e)
+        if (4 * lq + e < nreq) sShift[(4 * lq + e) * BN + (wn * WNF + j) * 16 + lr] = stot[j][e];
   }
   __syncthreads();
 #pragma unroll 1
-  for (int st = 0; st < NST; ++st) {
-    const int tile = blockIdx.x * NST + st;
+  for (int st = 0; st < NST; ++st) {  // (one pass over all tiles, as k_gemm_big does, measured no faster here)
+    const int tile = cblk * NST + st;
     tile_epilogue<EPI, NT, MOD>(
         a, tile, m0, nrows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
         [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + st * NT + c]; }, sR, sF + st * 16, sq,
@@ -917,32 +1032,33 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
   k_gemm_big<EPI, NT, NR, KSR, SRC, WMT, WNF>                                                        \
       <<<dim3(a.ntiles * (NT) / (32 * (WNF)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(256), 0, s>>>(a)
 
-#define DMX_GEMM_LDS(EPI, NT, NR, KSR, SRC, WMT)                                                    \
-  k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT>                                                           \
-      <<<dim3(a.ntiles * (NT) / 256, (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(512), 0, s>>>(a)
+#define DMX_GEMM_LDS(EPI, NT, NR, KSR, SRC, WMT, NWN, STG)                                          \
+  k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT, NWN, STG>                                                  \
+      <<<dim3(a.ntiles * (NT) / (64 * (NWN)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(128 * (NWN)), 0, s>>>(a)
 
 // Row count from which the large-M schedules run a projection: k_gemm_lds
-// for the plain wide ones (the prefix QKV), k_gemm_big for the rest (the
-// AdaRMS-fused ones need their registers and LDS for the shift and epilogue;
-// measured faster there).
+// for the plain wide ones (the prefix QKV) and the AdaRMS-fused gate-up,
+// k_gemm_big for the rest (the fused QKV measured faster there at 1024 rows,
+// 25.6 vs 26.0 us with 4-wave LDS blocks of 128 x 128; the 1024-column
+// projections have too few 128-column blocks to fill the chip).
 constexpr int kBigGemmRows = 256;
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {  // prefix layer: the large-M schedule at every row count
-    case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 4, 16, A_GLOBAL, 4); return hipGetLastError();
-    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 20, A_GLOBAL, 4); return hipGetLastError();
-    case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 4, 80, A_GLOBAL, 4); return hipGetLastError();
+    case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 4, 16, A_GLOBAL, 4, 4, 6); return hipGetLastError();
+    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 20, A_GLOBAL, 4, 4, 6); return hipGetLastError();
+    case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 4, 80, A_GLOBAL, 4, 4, 6); return hipGetLastError();
     default: break;
   }
   if (a.M >= kBigGemmRows) {
     switch (kind) {
-      case GEMM_QKV1024: DMX_GEMM_LDS(EPI_F32, 16, 4, 8, A_GLOBAL, 4); break;
+      case GEMM_QKV1024: DMX_GEMM_LDS(EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4, 6); break;
       case GEMM_QKV1024_MODPRE: DMX_GEMM_BIG(EPI_QKV, 32, 4, 8, A_MODPRE, 4, 4); break;
-      case GEMM_QKV2560: DMX_GEMM_LDS(EPI_F32, 16, 4, 20, A_GLOBAL, 4); break;
+      case GEMM_QKV2560: DMX_GEMM_LDS(EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4, 6); break;
       case GEMM_OPROJ: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 2); break;
       case GEMM_OPROJ_F32: DMX_GEMM_BIG(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 2); break;
       case GEMM_GATEUP: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 4, 4); break;
-      case GEMM_GATEUP_MOD: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4); break;
+      case GEMM_GATEUP_MOD: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4, 5); break;
       case GEMM_DOWN: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 2, 2); break;
       case GEMM_DOWN_F32RES: DMX_GEMM_BIG(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 2, 2); break;
       default: break;  // the prefix kinds returned above
