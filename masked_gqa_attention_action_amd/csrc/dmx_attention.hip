@@ -304,9 +304,15 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2)
   SufRaw sr[KPT];
   float4 qss[2];
   bf16x8 qf[8];
-  int mvis = 0;
-  if (threadIdx.x < NB * KB && threadIdx.x < nkeys)
-    mvis = suffix || a.mask[(size_t)b * a.P + key_lo + threadIdx.x] != 0;
+  // the key's mask byte: loaded first, tested only once every load is in
+  // flight (testing it at once would hold the K/V loads behind its latency).
+  // The load is unconditional (threads without a prefix key read a byte of
+  // the queries and ignore it): a conditional one leaves a copy of its
+  // result at the branch's end that waits for it just the same.
+  const bool mkey = threadIdx.x < NB * KB && threadIdx.x < nkeys;
+  const uint8_t* mp = (mkey && !suffix) ? a.mask + (size_t)b * a.P + key_lo + threadIdx.x
+                                        : reinterpret_cast<const uint8_t*>(FUSED ? a.qvb : a.q);
+  const int mraw = *mp;
   if (from_global) {
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
@@ -325,6 +331,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2)
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- compute phase
+  int mr = mraw;
+  asm volatile("" : "+v"(mr));  // the byte stays live on both split kinds (its register is not reused early)
+  const int mvis = mkey && (suffix || mr != 0);
   if (wave < (NB * KB) / 64) {  // visibility words: bit j of word bi = key bi * 32 + j
     const uint64_t bal = __ballot(mvis);
     if (lane == 0) sMask[2 * wave] = (uint32_t)bal;
