@@ -811,7 +811,14 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
   constexpr int MAXREQ = BM / 16 + 1;
   constexpr int STAGE_EL = SF * 512;   // bf16 elements per stage
   constexpr int TLD = BN + 4;           // sTot row stride (floats): rows 4 banks apart
-  constexpr int RAW = (STAGES * STAGE_EL * 2 > BM * TLD * 4) ? STAGES * STAGE_EL * 2 : BM * TLD * 4;
+  // the epilogue runs in passes of EPH rows (one row half of the waves each
+  // when the block has more than 128 rows), their sums staged in sTot
+  constexpr int EPH = BM > 128 ? BM / 2 : BM;
+  constexpr int RAW = (STAGES * STAGE_EL * 2 > EPH * TLD * 4) ? STAGES * STAGE_EL * 2 : EPH * TLD * 4;
+  // NR == 1: one range, accumulated straight through K (the projections
+  // that always run this schedule, so no other schedule's sum order binds)
+  constexpr bool RANGES = NR > 1;
+  static_assert(RANGES || !MOD, "the AdaRMS-fused projections follow the skinny kernel's ranges");
   static_assert(SF % NW == 0 && BNF % NTT == 0 && KS % 2 == 0 && AHEAD * DPW < 64, "block shape");
   static_assert(!MOD || KS * 32 == kH, "the modulated A operand spans one hidden row");
   // One LDS array for everything: the stages during the K loop (the range
@@ -904,7 +911,7 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
     for (int i = 0; i < WMT; ++i)
 #pragma unroll
       for (int j = 0; j < WNF; ++j) acc[i][j] = mfma16(af[i], wf[j], acc[i][j]);
-    if ((ks + 1) % KSR == 0) {  // end of a range: add its sums in range order
+    if (RANGES && (ks + 1) % KSR == 0) {  // end of a range: add its sums in range order
       const bool first = ks + 1 == KSR;
 #pragma unroll
       for (int i = 0; i < WMT; ++i)
@@ -979,14 +986,6 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
   wait_vmcnt<0>();
   __syncthreads();  // every copy has landed and every stage read: the stages become sTot
 
-  // range sums into LDS: lane (lr, lq) holds rows 4 lq .. 4 lq + 3 of each tile, column lr
-#pragma unroll
-  for (int i = 0; i < WMT; ++i)
-#pragma unroll
-    for (int j = 0; j < WNF; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sTot[((wm * WMT + i) * 16 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr] = tot[i][j][e];
   // the shift sums [request][column], lane (lr, lq) holding requests 4 lq .. 4 lq + 3
   if (MOD && wm == 0) {
 #pragma unroll
@@ -995,15 +994,31 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
       for (int e = 0; e < 4; ++e)
         if (4 * lq + e < nreq) sShift[(4 * lq + e) * BN + (wn * WNF + j) * 16 + lr] = stot[j][e];
   }
-  __syncthreads();
 #pragma unroll 1
-  for (int st = 0; st < NST; ++st) {  // (one pass over all tiles, as k_gemm_big does, measured no faster here)
-    const int tile = cblk * NST + st;
-    tile_epilogue<EPI, NT, MOD>(
-        a, tile, m0, nrows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
-        [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + st * NT + c]; }, sR, sF + st * 16, sq,
-        sQ, nullptr);
+  for (int p0 = 0; p0 < BM; p0 += EPH) {
+    // the pass's sums into LDS: lane (lr, lq) holds rows 4 lq .. 4 lq + 3 of each tile, column lr
+    if (wm * WMT * 16 >= p0 && wm * WMT * 16 < p0 + EPH) {
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNF; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sTot[((wm * WMT + i) * 16 - p0 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr] =
+                RANGES ? tot[i][j][e] : acc[i][j][e];
+    }
     __syncthreads();
+    const int prows = min(EPH, nrows - p0);
+#pragma unroll 1
+    for (int st = 0; st < NST; ++st) {  // (one pass over all tiles, as k_gemm_big does, measured no faster here)
+      const int tile = cblk * NST + st;
+      if (prows > 0)
+        tile_epilogue<EPI, NT, MOD>(
+            a, tile, m0 + p0, prows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
+            [&](int r, int c) { return sShift[((m0 + p0 + r) / a.TP - b0) * BN + st * NT + c]; },
+            sR + p0, sF + st * 16, sq, sQ, nullptr);
+      __syncthreads();
+    }
   }
 }
 
@@ -1046,7 +1061,7 @@ constexpr int kBigGemmRows = 256;
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   switch (kind) {  // prefix layer: the large-M schedule at every row count
     case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 4, 16, A_GLOBAL, 4, 4, 6); return hipGetLastError();
-    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 20, A_GLOBAL, 4, 4, 6); return hipGetLastError();
+    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 8, 4, 4); return hipGetLastError();
     case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 4, 80, A_GLOBAL, 4, 4, 6); return hipGetLastError();
     default: break;
   }
