@@ -245,6 +245,65 @@ __device__ __forceinline__ void combine_unit(const AttnArgs& a, uint16_t* ctx, i
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv));
 }
 
+// The same merge with 8 dims per lane (two 4-dim chunks of the partial
+// layout: one 16-byte load per split): lanes 0-31 take dim tile 2 tp, lanes
+// 32-63 dim tile 2 tp + 1; lane (lr, hq) owns row lr and dims 16 t + 8 hq ..
+// +7.  Every output goes through exactly combine_unit's operations, so the
+// two forms give the same bits; this one runs for batches (half the waves,
+// twice the bytes per load).
+template <int CB>
+__device__ __forceinline__ void combine_unit8(const AttnArgs& a, uint16_t* ctx, int bg, int mt, int tp, int lane) {
+  const int lr = lane & 15, hq = (lane >> 4) & 1, t = 2 * tp + (lane >> 5);
+  const int TT = a.TP >> 4, MT = 2 * TT;
+  const int g = bg % kHK, b = bg / kHK;
+  const int nsplit = a.S + a.NS;
+  const int row = mt * 16 + lr;
+  const int hh = mt / TT, i = (mt - hh * TT) * 16 + lr;
+  const size_t ml0 = (size_t)bg * nsplit * a.R16 + row;
+  const size_t o0 = ((size_t)bg * nsplit * MT + mt) * (16 * kD) + t * 256 + (lr * 4 + 2 * hq) * 4;
+  if (i >= a.C) return;  // padded row: nothing was written for it
+  float M = kNegBig, L = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += CB) {
+    float2 ml[CB];
+    uint4 ov[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int s = min(s0 + u, nsplit - 1);  // past the end: re-read the last split, skipped below
+      ml[u] = *reinterpret_cast<const float2*>(a.part_ml + (ml0 + (size_t)s * a.R16) * 2);
+      ov[u] = *reinterpret_cast<const uint4*>(a.part_o + o0 + (size_t)s * MT * (16 * kD));
+    }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (s0 + u < nsplit && ml[u].y > 0.f) Mb = fmaxf(Mb, ml[u].x);
+    const float so = exp2f(M - Mb);  // 0 before the first visible split, 1 if the max held
+    L *= so;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= so;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float w = (s0 + u < nsplit && ml[u].y > 0.f) ? ml[u].y * exp2f(ml[u].x - Mb) : 0.f;
+      L += w;
+      const uint32_t wd[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += w * bf2f((uint16_t)(wd[q] & 0xffffu));
+        acc[2 * q + 1] += w * bf2f((uint16_t)(wd[q] >> 16));
+      }
+    }
+    M = Mb;
+  }
+  const float inv = 1.0f / L;
+  const int col = (kGroup * g + hh) * kD + t * 16 + 8 * hq;
+  uint16_t* dst = a.ctx_tiled ? ctx + tile_off(b * a.TP + i, col, kHQ * kD)
+                              : ctx + (size_t)(b * a.C + i) * kHQ * kD + col;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv),
+                                              pack2(acc[4] * inv, acc[5] * inv), pack2(acc[6] * inv, acc[7] * inv));
+}
+
 // One split of one (request, KV head), for HPW of its query heads (HPW = 1:
 // one work-group per query head, 4 waves; 2: both heads, 8 waves): every
 // global load of the split (mask, query rows, all K/V blocks or the raw
@@ -435,13 +494,17 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(1, 2)
 // Separate merge kernel: one wave per (request, KV head, row tile, dim
 // tile), placed like the splits (xcd_chunked) so the partials are read from
 // the L2 that received them.
-template <int CB>
+template <int CB, bool WIDE>
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a, uint16_t* ctx) {
   const int MT = 2 * (a.TP >> 4);
-  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * MT * 16);
+  constexpr int UPM = WIDE ? 8 : 16;  // waves per (request, KV head, row tile)
+  const int item = xcd_chunked(blockIdx.x, gridDim.x, a.B * kHK * MT * UPM);
   if (item < 0) return;
-  const int t = item & 15, rest = item >> 4;
-  combine_unit<CB>(a, ctx, rest / MT, rest % MT, t, threadIdx.x);
+  const int t = item % UPM, rest = item / UPM;
+  if (WIDE)
+    combine_unit8<CB>(a, ctx, rest / MT, rest % MT, t, threadIdx.x);
+  else
+    combine_unit<CB>(a, ctx, rest / MT, rest % MT, t, threadIdx.x);
 }
 
 void attn_config(int B, int C, int P, AttnArgs& a) {
@@ -495,10 +558,18 @@ hipError_t launch_attn_combine(const AttnArgs& a, uint16_t* ctx, hipStream_t s) 
   const int nsplit = a.S + a.NS;
   const int nbatch = (nsplit + kCombineMaxBatch - 1) / kCombineMaxBatch;
   const int cb = (nsplit + nbatch - 1) / nbatch;
-  const dim3 grid(a.B * kHK * (a.R16 / 16) * 16);  // a multiple of 8
+  // batches: 8 dims per lane (16-byte loads, half the waves); one request:
+  // 4 dims per lane (more waves in flight for its few rows)
+  const bool wide = a.B > 1;
+  const dim3 grid(a.B * kHK * (a.R16 / 16) * (wide ? 8 : 16));  // a multiple of 8
   switch (cb) {
-#define DMX_CASE(N) \
-  case N: k_attn_combine<N><<<grid, dim3(64), 0, s>>>(a, ctx); break;
+#define DMX_CASE(N)                                                  \
+  case N:                                                            \
+    if (wide)                                                        \
+      k_attn_combine<N, true><<<grid, dim3(64), 0, s>>>(a, ctx);     \
+    else                                                             \
+      k_attn_combine<N, false><<<grid, dim3(64), 0, s>>>(a, ctx);    \
+    break;
     DMX_COMBINE_BATCHES(DMX_CASE)
 #undef DMX_CASE
     default: return hipErrorInvalidValue;
