@@ -557,22 +557,11 @@ __global__ __launch_bounds__(NWAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
-// Large-M projections (batches of requests, the prefix QKV over 2048
-// tokens): the same arithmetic as k_gemm, bit for bit, on a schedule that
-// keeps the MFMA units busy.  K is split into NR ranges of KSR 32-column steps
-// (k_gemm's waves); each range is accumulated from zero in step order by the
-// same MFMA, and the range sums are added in range order.  The shift
-// tile of the fused AdaRMS holds one row per request of the block.  The
-// epilogue is the same tile_epilogue, once per output tile of the block.
-// A work-group of 4 waves (2 x 2) owns BM rows x BNF 16-column fragments: wave
-// (wm, wn) the rows wm*WMT*16 .. and the fragments wn*WNF ..; every fragment is
-// loaded straight from the tiled operands into registers (one 1 KB load per
-// wave and fragment) PD steps ahead of its MFMAs.
 // Row scales of a large-M block (AdaRMS: 1 / rms of each row, from the row's
 // sums-of-squares partials, summed as k_gemm sums them): thread (row rr,
-// quarter qq) of pass p handles row p * NTHR / 4 + rr.  row_ss_fetch issues
-// the loads (before the K loop, so that their latency hides behind its
-// operand loads), row_ss_store finishes the sums into sR.
+// quarter qq) of pass p handles row p * NTHR / 4 + rr.  fetch issues the
+// loads (before the K loop, so that their latency hides behind its operand
+// loads), store finishes the sums into sR.
 template <int BM, int NTHR>
 struct RowSS {
   static constexpr int NP = (BM * 4 + NTHR - 1) / NTHR;  // passes
@@ -617,6 +606,17 @@ __device__ __forceinline__ void rope_freqs(const GemmArgs& a, int tile0, double*
   }
 }
 
+// Large-M projections (batches of requests, the prefix QKV over 2048
+// tokens): the same arithmetic as k_gemm, bit for bit, on a schedule that
+// keeps the MFMA units busy.  K is split into NR ranges of KSR 32-column steps
+// (k_gemm's waves); each range is accumulated from zero in step order by the
+// same MFMA, and the range sums are added in range order.  The shift
+// tile of the fused AdaRMS holds one row per request of the block.  The
+// epilogue is the same tile_epilogue, once per output tile of the block.
+// A work-group of 4 waves (2 x 2) owns BM rows x BNF 16-column fragments: wave
+// (wm, wn) the rows wm*WMT*16 .. and the fragments wn*WNF ..; every fragment is
+// loaded straight from the tiled operands into registers (one 1 KB load per
+// wave and fragment) PD steps ahead of its MFMAs.
 template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int WNF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_big(GemmArgs a) {
   constexpr bool MOD = ASRC == A_MODPRE;
