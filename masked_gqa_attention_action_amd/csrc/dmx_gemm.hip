@@ -789,22 +789,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // same NR ranges of KSR steps as the skinny kernel's waves; each range is
 // accumulated from zero in step order and the range sums are added in range
 // order in registers.
-template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int NWN, int STG>
-__global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN / 2, 2))) void k_gemm_lds(GemmArgs a) {
+// KG > 1 (blocks too few or too small to keep 8 waves per CU busy): KG
+// groups of 2 x NWN waves share the block, group g running ranges
+// g NR / KG .. with a stage ring of its own, in the same barriers; every
+// group keeps its range sums apart (in the accumulators if it has one), and
+// after the loop group 0 adds them all in range order (the other groups'
+// through LDS), EPH rows at a time.
+template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int NWN, int STG, int KG>
+__global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(NWN * KG / 2, 2))) void k_gemm_lds(
+    GemmArgs a) {
   constexpr bool MOD = ASRC == A_MODPRE;
   constexpr bool QKV = EPI == EPI_QKV;
   constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
   constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;
-  constexpr int NW = 2 * NWN;          // waves
+  constexpr int NWG = 2 * NWN;         // waves per K group
+  constexpr int NW = NWG * KG;         // waves
   constexpr int WNF = 4;               // W fragments per wave
   constexpr int BM = 2 * WMT * 16;     // rows per block
   constexpr int BNF = NWN * WNF;       // fragments per block
   constexpr int BN = BNF * 16;         // columns per block
   constexpr int NTT = NT / 16, NST = BNF / NTT;
   constexpr int KS = NR * KSR;
+  constexpr int NRG = NR / KG;         // ranges per K group
+  constexpr int KSG = NRG * KSR;       // steps per K group
   constexpr int AF = BM / 16;          // A tiles per step
   constexpr int SF = AF + BNF;         // fragments per step
-  constexpr int DPW = SF / NW;         // fragments each wave copies per step
+  constexpr int DPW = SF / NWG;        // fragments each wave copies per step
   // a ring of STAGES steps, AHEAD = STAGES - 1 of them copied ahead: LDS
   // latency times bandwidth needs about 100 KB in flight per CU
   constexpr int STAGES = STG, AHEAD = STAGES - 1;
@@ -814,12 +824,21 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
   // the epilogue runs in passes of EPH rows (one row half of the waves each
   // when the block has more than 128 rows), their sums staged in sTot
   constexpr int EPH = BM > 128 ? BM / 2 : BM;
-  constexpr int RAW = (STAGES * STAGE_EL * 2 > EPH * TLD * 4) ? STAGES * STAGE_EL * 2 : EPH * TLD * 4;
+  // the other groups' range sums [group - 1][range][row][column] after the
+  // loop (sTot behind them)
+  constexpr int XCH = (KG - 1) * NRG * EPH * TLD * 4;
+  constexpr int RING = KG * STAGES * STAGE_EL * 2;
+  // after the loop: the exchanged sums, sTot and (K groups) the epilogue's
+  // sums of squares of every output tile of the block
+  constexpr int SQB = SSQ ? (KG > 1 ? NST : 1) * BM * NOUT * 4 : 0;
+  constexpr int POST = XCH + EPH * TLD * 4 + (KG > 1 ? SQB : 0);
+  constexpr int RAW = RING > POST ? RING : POST;
   // NR == 1: one range, accumulated straight through K (the projections
   // that always run this schedule, so no other schedule's sum order binds)
   constexpr bool RANGES = NR > 1;
   static_assert(RANGES || !MOD, "the AdaRMS-fused projections follow the skinny kernel's ranges");
-  static_assert(SF % NW == 0 && BNF % NTT == 0 && KS % 2 == 0 && AHEAD * DPW < 64, "block shape");
+  static_assert(KG == 1 || (!MOD && !QKV && RANGES && NR % KG == 0), "K groups: plain projections");
+  static_assert(SF % NWG == 0 && BNF % NTT == 0 && KSG % 2 == 0 && AHEAD <= KSG && AHEAD * DPW < 64, "block shape");
   static_assert(!MOD || KS * 32 == kH, "the modulated A operand spans one hidden row");
   // One LDS array for everything: the stages during the K loop (the range
   // sums [row][column] after it), then the bf16 shift vectors, the shift
@@ -831,12 +850,13 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
   constexpr int O_SHIFT = O_HB + (MOD ? MAXREQ * kH * 2 : 0);
   constexpr int O_R = O_SHIFT + (MOD ? MAXREQ * BN * 4 : 0);
   constexpr int O_F = (O_R + (MOD ? BM * 4 : 0) + 7) & ~7;
-  constexpr int O_Q2 = O_F + (QKV ? NST * 16 * 8 : 0);
-  constexpr int O_Q = O_Q2 + (SSQ ? BM * NOUT * 4 : 0);
+  constexpr int O_Q2 = KG > 1 ? XCH + EPH * TLD * 4 : O_F + (QKV ? NST * 16 * 8 : 0);
+  constexpr int O_Q = KG > 1 ? O_F : O_Q2 + SQB;
   constexpr int LDS_BYTES = O_Q + (QKV ? BM * 2 * 4 : 0);
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
-  float* sTot = reinterpret_cast<float*>(smem);
+  float* sTot = reinterpret_cast<float*>(smem + XCH);
+  float* sX = reinterpret_cast<float*>(smem);
   uint16_t* sHb = reinterpret_cast<uint16_t*>(smem + O_HB);
   float* sShift = reinterpret_cast<float*>(smem + O_SHIFT);
   float* sR = reinterpret_cast<float*>(smem + O_R);
@@ -845,20 +865,32 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
   float* sQ = reinterpret_cast<float*>(smem + O_Q);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / NWN, wn = wave % NWN;
+  const int g = wave / NWG, wig = wave % NWG;  // K group, wave in the group
+  const int wm = wig / NWN, wn = wig % NWN;
   const int lr = lane & 15, lq = lane >> 4;
-  const int cblk = blockIdx.x;  // column block
-  const int m0 = blockIdx.y * BM;
+  // K groups: the blocks of linear id i mod 8 (one XCD's, the dispatcher
+  // deals work-groups round robin) form a sub-grid of a quarter of the row
+  // blocks by half the column blocks, so that their operands meet in that
+  // XCD's L2
+  int cb = blockIdx.x, rb = blockIdx.y;
+  if (KG > 1 && gridDim.y % 4 == 0 && gridDim.x % 2 == 0) {
+    const int L = blockIdx.y * gridDim.x + blockIdx.x, x8 = L & 7, sl = L >> 3, cbw = gridDim.x / 2;
+    rb = (x8 >> 1) * (gridDim.y / 4) + sl / cbw;
+    cb = (x8 & 1) * cbw + sl % cbw;
+  }
+  const int cblk = cb;  // column block
+  const int m0 = rb * BM;
   const int nrows = min(BM, a.M - m0);
   const int last_tile = a.M / 16 - 1;
   const int b0 = m0 / a.TP;
   const int nreq = MOD ? (m0 + nrows - 1) / a.TP - b0 + 1 : 0;
 
-  // fragments this wave copies: f = wave * DPW + d (A tiles first, then W)
+  // fragments this wave copies: f = wig * DPW + d (A tiles first, then W),
+  // from the group's first step on
   const uint16_t* gsrc[DPW];
 #pragma unroll
   for (int d = 0; d < DPW; ++d) {
-    const int f = wave * DPW + d;
+    const int f = wig * DPW + d;
     if (f < AF) {
       gsrc[d] = a.A + (size_t)min(m0 / 16 + f, last_tile) * KS * 512 + lane * 8;  // rows past M: last tile
     } else {
@@ -869,19 +901,22 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
                            : tile * NTT + nt;
       gsrc[d] = a.W + (size_t)wt * KS * 512 + lane * 8;
     }
+    gsrc[d] += (size_t)g * KSG * 512;
   }
+  uint16_t* const ring = stage + g * STAGES * STAGE_EL;  // the group's stages
   auto issue = [&](int ks) {
-    uint16_t* dst = stage + (ks % STAGES) * STAGE_EL;
+    uint16_t* dst = ring + (ks % STAGES) * STAGE_EL;
 #pragma unroll
     for (int d = 0; d < DPW; ++d)
-      lds_copy16(gsrc[d] + (size_t)ks * 512, dst + (wave * DPW + d) * 512);
+      lds_copy16(gsrc[d] + (size_t)ks * 512, dst + (wig * DPW + d) * 512);
   };
 
   // accs / stot: the shift tile's sums of this wave's W fragments (range,
   // total); every wave runs them, so that the loop has no branch (with one,
   // the compiler waits for every LDS read in flight before the MFMAs); the
   // waves of row half 0 keep theirs
-  f32x4 acc[WMT][WNF], tot[WMT][WNF], accs[WNF], stot[WNF];
+  // rs (K groups): the group's range sums, range q of the group in rs[q]
+  f32x4 acc[WMT][WNF], tot[WMT][WNF], accs[WNF], stot[WNF], rs[KG > 1 && NRG > 1 ? NRG : 1][WMT][WNF];
 #pragma unroll
   for (int i = 0; i < WMT; ++i)
 #pragma unroll
@@ -893,7 +928,7 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
   // the shift row of each request; lanes past the block's requests read
   // request 0's and zero it)
   auto read_frags = [&](int ks, bf16x8* af, bf16x8* wf, bf16x8& hs) {
-    const uint16_t* st = stage + (ks % STAGES) * STAGE_EL;
+    const uint16_t* st = ring + (ks % STAGES) * STAGE_EL;
 #pragma unroll
     for (int i = 0; i < WMT; ++i) af[i] = *reinterpret_cast<const bf16x8*>(st + (wm * WMT + i) * 512 + lane * 8);
 #pragma unroll
@@ -911,7 +946,21 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
     for (int i = 0; i < WMT; ++i)
 #pragma unroll
       for (int j = 0; j < WNF; ++j) acc[i][j] = mfma16(af[i], wf[j], acc[i][j]);
-    if (RANGES && (ks + 1) % KSR == 0) {  // end of a range: add its sums in range order
+    if (KG > 1 && NRG > 1 && (ks + 1) % KSR == 0) {  // end of a range: its sums kept apart
+#pragma unroll
+      for (int q = 0; q + 1 < NRG; ++q)
+#pragma unroll
+        for (int i = 0; i < WMT; ++i)
+#pragma unroll
+          for (int j = 0; j < WNF; ++j) rs[q][i][j] = rs[q + 1][i][j];
+#pragma unroll
+      for (int i = 0; i < WMT; ++i)
+#pragma unroll
+        for (int j = 0; j < WNF; ++j) {
+          rs[NRG - 1][i][j] = acc[i][j];
+          acc[i][j] = zero_f32x4();
+        }
+    } else if (KG == 1 && RANGES && (ks + 1) % KSR == 0) {  // end of a range: add its sums in range order
       const bool first = ks + 1 == KSR;
 #pragma unroll
       for (int i = 0; i < WMT; ++i)
@@ -970,21 +1019,91 @@ __global__ __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(NWN /
   bf16x8 af0[WMT], wf0[WNF], af1[WMT], wf1[WNF], hs0 = zero_bf16x8(), hs1 = zero_bf16x8();
   read_frags(0, af0, wf0, hs0);
 #pragma unroll 1
-  for (int ks = 0; ks < KS; ks += 2) {
-    // even step ks (fragments in set 0), then odd step ks + 1 (set 1); KS is even
+  for (int ks = 0; ks < KSG; ks += 2) {
+    // even step ks (fragments in set 0), then odd step ks + 1 (set 1); KSG is even
     wait_vmcnt<(AHEAD - 2) * DPW>();
     lds_barrier();
-    issue(min(ks + AHEAD, KS - 1));
+    issue(min(ks + AHEAD, KSG - 1));
     read_frags(ks + 1, af1, wf1, hs1);
     step_mma(ks, af0, wf0, hs0);
     wait_vmcnt<(AHEAD - 2) * DPW>();
     lds_barrier();
-    issue(min(ks + 1 + AHEAD, KS - 1));
-    read_frags(min(ks + 2, KS - 1), af0, wf0, hs0);  // past the end: a landed stage, unused
+    issue(min(ks + 1 + AHEAD, KSG - 1));
+    read_frags(min(ks + 2, KSG - 1), af0, wf0, hs0);  // past the end: a landed stage, unused
     step_mma(ks + 1, af1, wf1, hs1);
   }
   wait_vmcnt<0>();
   __syncthreads();  // every copy has landed and every stage read: the stages become sTot
+
+  if (KG > 1) {
+    // per epilogue pass of EPH rows: the other groups' range sums of the
+    // pass's rows into LDS, then group 0 adds every range in range order
+    // (0 + r0, + r1, ...) into sTot; a group with one range holds it in acc
+    auto rsum = [&](int q, int i, int j) -> const f32x4& { return NRG == 1 ? acc[i][j] : rs[q][i][j]; };
+#pragma unroll 1
+    for (int p0 = 0; p0 < BM; p0 += EPH) {
+      const bool in_pass = wm * WMT * 16 >= p0 && wm * WMT * 16 < p0 + EPH;
+      auto xidx = [&](int gq, int i, int j, int e) {
+        return (gq * EPH + (wm * WMT + i) * 16 - p0 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr;
+      };
+      if (g > 0 && in_pass) {
+#pragma unroll
+        for (int q = 0; q < NRG; ++q)
+#pragma unroll
+          for (int i = 0; i < WMT; ++i)
+#pragma unroll
+            for (int j = 0; j < WNF; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sX[xidx((g - 1) * NRG + q, i, j, e)] = rsum(q, i, j)[e];
+      }
+      __syncthreads();
+      if (g == 0 && in_pass) {
+#pragma unroll
+        for (int i = 0; i < WMT; ++i)
+#pragma unroll
+          for (int j = 0; j < WNF; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              tot[i][j][e] = 0.f + rsum(0, i, j)[e];
+#pragma unroll
+              for (int q = 1; q < NRG; ++q) tot[i][j][e] += rsum(q, i, j)[e];
+            }
+#pragma unroll
+        for (int gq = 0; gq < (KG - 1) * NRG; ++gq)
+#pragma unroll
+          for (int i = 0; i < WMT; ++i)
+#pragma unroll
+            for (int j = 0; j < WNF; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) tot[i][j][e] += sX[xidx(gq, i, j, e)];
+#pragma unroll
+        for (int i = 0; i < WMT; ++i)
+#pragma unroll
+          for (int j = 0; j < WNF; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sTot[((wm * WMT + i) * 16 - p0 + 4 * lq + e) * TLD + (wn * WNF + j) * 16 + lr] = tot[i][j][e];
+      }
+      __syncthreads();
+      const int prows = min(EPH, nrows - p0);
+      if (EPH == BM) {  // one pass: every output tile's operands fetched first
+        constexpr int TMAX = (NST * EPH * EpiShape<EPI, NT>::TPR + NW * 64 - 1) / (NW * 64);
+        block_epilogue<EPI, NT, NST, EPH, TMAX, false>(
+            a, cblk * NST, m0, nrows, [&](int r, int c) { return sTot[r * TLD + c]; },
+            [&](int, int) { return 0.f; }, sR, sF, sq, sQ);
+      } else {
+#pragma unroll 1
+        for (int st = 0; st < NST; ++st) {
+          if (prows > 0)
+            tile_epilogue<EPI, NT, false>(
+                a, cblk * NST + st, m0 + p0, prows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
+                [&](int, int) { return 0.f; }, sR, sF, sq, sQ, nullptr);
+          __syncthreads();
+        }
+      }
+    }
+    return;
+  }
 
   // the shift sums [request][column], lane (lr, lq) holding requests 4 lq .. 4 lq + 3
   if (MOD && wm == 0) {
@@ -1047,35 +1166,40 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
   k_gemm_big<EPI, NT, NR, KSR, SRC, WMT, WNF>                                                        \
       <<<dim3(a.ntiles * (NT) / (32 * (WNF)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(256), 0, s>>>(a)
 
-#define DMX_GEMM_LDS(EPI, NT, NR, KSR, SRC, WMT, NWN, STG)                                          \
-  k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT, NWN, STG>                                                  \
-      <<<dim3(a.ntiles * (NT) / (64 * (NWN)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(128 * (NWN)), 0, s>>>(a)
+#define DMX_GEMM_LDS(EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG)                                     \
+  k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG>                                              \
+      <<<dim3(a.ntiles * (NT) / (64 * (NWN)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(128 * (NWN) * (KG)), 0, \
+         s>>>(a)
 
 // Row count from which the large-M schedules run a projection: k_gemm_lds
-// for the plain wide ones (the prefix QKV) and the AdaRMS-fused gate-up,
-// k_gemm_big for the rest (the fused QKV measured faster there at 1024 rows,
-// 25.6 vs 26.0 us with 4-wave LDS blocks of 128 x 128; the 1024-column
-// projections have too few 128-column blocks to fill the chip).
+// for the plain wide ones (the prefix QKV), the AdaRMS-fused gate-up and the
+// 1024-column projections (64 x 64 blocks, 256 for 1024 rows, each shared by
+// 4 K groups of 2 waves), k_gemm_big for the fused QKV (measured faster there
+// at 1024 rows, 25.6 vs 26.0 us with 4-wave LDS blocks of 128 x 128) and the
+// plain gate-up.
 constexpr int kBigGemmRows = 256;
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
-  switch (kind) {  // prefix layer: the large-M schedule at every row count
-    case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 4, 16, A_GLOBAL, 4, 4, 6); return hipGetLastError();
-    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 8, 4, 4); return hipGetLastError();
-    case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 4, 80, A_GLOBAL, 4, 4, 6); return hipGetLastError();
+  // prefix layer: the large-M schedule at every row count; the 2560-column
+  // projections on 192 x 128 blocks in 2 K groups (220 blocks for 2048 rows,
+  // where 128 x 256 blocks leave 96 CUs idle)
+  switch (kind) {
+    case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 2, 32, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
+    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 8, 4, 4, 1); return hipGetLastError();
+    case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 2, 160, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
     default: break;
   }
   if (a.M >= kBigGemmRows) {
     switch (kind) {
-      case GEMM_QKV1024: DMX_GEMM_LDS(EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4, 6); break;
+      case GEMM_QKV1024: DMX_GEMM_LDS(EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4, 6, 1); break;
       case GEMM_QKV1024_MODPRE: DMX_GEMM_BIG(EPI_QKV, 32, 4, 8, A_MODPRE, 4, 4); break;
-      case GEMM_QKV2560: DMX_GEMM_LDS(EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4, 6); break;
-      case GEMM_OPROJ: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 2); break;
-      case GEMM_OPROJ_F32: DMX_GEMM_BIG(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 2); break;
+      case GEMM_QKV2560: DMX_GEMM_LDS(EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4, 6, 1); break;
+      case GEMM_OPROJ: DMX_GEMM_LDS(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
+      case GEMM_OPROJ_F32: DMX_GEMM_LDS(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
       case GEMM_GATEUP: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 4, 4); break;
-      case GEMM_GATEUP_MOD: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4, 5); break;
-      case GEMM_DOWN: DMX_GEMM_BIG(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 2, 2); break;
-      case GEMM_DOWN_F32RES: DMX_GEMM_BIG(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 2, 2); break;
+      case GEMM_GATEUP_MOD: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4, 5, 1); break;
+      case GEMM_DOWN: DMX_GEMM_LDS(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 2, 1, 4, 4); break;
+      case GEMM_DOWN_F32RES: DMX_GEMM_LDS(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 2, 1, 4, 4); break;
       default: break;  // the prefix kinds returned above
     }
     return hipGetLastError();
