@@ -878,7 +878,8 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
     rb = (x8 >> 1) * (gridDim.y / 4) + sl / cbw;
     cb = (x8 & 1) * cbw + sl % cbw;
   }
-  const int cblk = cb;  // column block
+  const int cblk = cb;  // column block (of this launch's columns)
+  const int tile0 = a.tile0 + cblk * NST;  // the block's first output tile
   const int m0 = rb * BM;
   const int nrows = min(BM, a.M - m0);
   const int last_tile = a.M / 16 - 1;
@@ -895,7 +896,7 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
       gsrc[d] = a.A + (size_t)min(m0 / 16 + f, last_tile) * KS * 512 + lane * 8;  // rows past M: last tile
     } else {
       const int fj = f - AF, st = fj / NTT, nt = fj % NTT;
-      const int tile = cblk * NST + st;
+      const int tile = tile0 + st;
       const int wt = EPI == EPI_GEGLU ? (nt == 0 ? tile : a.wtile_up + tile)
                      : QKV ? (tile >> 3) * 16 + nt * 8 + (tile & 7)
                            : tile * NTT + nt;
@@ -1012,7 +1013,7 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
     }
     rss.store(sR);
   }
-  if (QKV) rope_freqs<NST>(a, cblk * NST, sF);
+  if (QKV) rope_freqs<NST>(a, tile0, sF);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the set-up's LDS writes are done before the barrier
   wait_vmcnt<(AHEAD - 1) * DPW>();
   lds_barrier();
@@ -1089,14 +1090,14 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
       if (EPH == BM) {  // one pass: every output tile's operands fetched first
         constexpr int TMAX = (NST * EPH * EpiShape<EPI, NT>::TPR + NW * 64 - 1) / (NW * 64);
         block_epilogue<EPI, NT, NST, EPH, TMAX, false>(
-            a, cblk * NST, m0, nrows, [&](int r, int c) { return sTot[r * TLD + c]; },
+            a, tile0, m0, nrows, [&](int r, int c) { return sTot[r * TLD + c]; },
             [&](int, int) { return 0.f; }, sR, sF, sq, sQ);
       } else {
 #pragma unroll 1
         for (int st = 0; st < NST; ++st) {
           if (prows > 0)
             tile_epilogue<EPI, NT, false>(
-                a, cblk * NST + st, m0 + p0, prows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
+                a, tile0 + st, m0 + p0, prows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
                 [&](int, int) { return 0.f; }, sR, sF, sq, sQ, nullptr);
           __syncthreads();
         }
@@ -1130,7 +1131,7 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
     const int prows = min(EPH, nrows - p0);
 #pragma unroll 1
     for (int st = 0; st < NST; ++st) {  // (one pass over all tiles, as k_gemm_big does, measured no faster here)
-      const int tile = cblk * NST + st;
+      const int tile = tile0 + st;
       if (prows > 0)
         tile_epilogue<EPI, NT, MOD>(
             a, tile, m0 + p0, prows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
@@ -1185,7 +1186,26 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   // where 128 x 256 blocks leave 96 CUs idle)
   switch (kind) {
     case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 2, 32, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
-    case GEMM_PRE_GATEUP: DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 8, 4, 4, 1); return hipGetLastError();
+    case GEMM_PRE_GATEUP: {
+      // 256 x 256 blocks; where they would run 2.5 or 1.25 rounds over the
+      // CUs (1024 or 2048 rows), the last 128 tiles run in a launch of their
+      // own as 128 x 256 blocks, one round of blocks with 3/4 the bytes
+      // (the prefix layer 532 -> 519 us at 2048 tokens; 524 with 256 x 128)
+      const int gy = (a.M + 255) / 256, tail = (gy == 4 || gy == 8) ? 128 : 0;
+      GemmArgs b = a;
+      b.ntiles = a.ntiles - tail;
+      {
+        const GemmArgs& a = b;
+        DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 8, 4, 4, 1);
+      }
+      if (tail) {
+        b.tile0 = b.ntiles;
+        b.ntiles = tail;
+        const GemmArgs& a = b;
+        DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 4, 4, 4, 1);
+      }
+      return hipGetLastError();
+    }
     case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 2, 160, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
     default: break;
   }

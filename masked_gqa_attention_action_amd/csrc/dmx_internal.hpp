@@ -36,6 +36,7 @@ struct GemmArgs {
   int M, K;           // M = B * TP tiled rows
   int T, TP;          // tokens per request and their padded count
   int ntiles;         // grid.x = ntiles work-groups
+  int tile0;          // k_gemm_lds: the launch's first output tile (its grid covers tiles tile0 ..)
   int wtile_up;       // GEGLU: weight tile of the first "up" feature
   float* out_f32;     // EPI_F32 / EPI_RESID_BF output [M][ldo]
   uint16_t* out_bf16; // EPI_RESID_BB / EPI_RESID_FB row-major output
