@@ -777,6 +777,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + c]; }, sR, sF, sq, sQ);
 }
 
+// Block (column cb, row rb) of work-group blockIdx when the grid is dealt to
+// XCDs in compact pieces.  The dispatcher deals work-groups round robin, so
+// the work-groups of linear id = k mod 8 share XCD k's L2; they take the k-th
+// eighth of the blocks in strip order (strips of W column blocks, left to
+// right, each row by row), so that each XCD fetches a few row blocks of A and
+// W column blocks instead of most of both.
+__device__ __forceinline__ void xcd_block(int W, int& cb, int& rb) {
+  const int gx = gridDim.x, gy = gridDim.y, n = gx * gy;
+  const int L = blockIdx.y * gx + blockIdx.x, k = L & 7, sl = L >> 3;
+  const int idx = k * (n >> 3) + min(k, n & 7) + sl;  // class k holds n / 8 (+ 1 for k < n % 8) blocks
+  const int nfull = gx / W, per = gy * W;              // whole strips, blocks per whole strip
+  const int st = idx / per;
+  if (st < nfull) {
+    const int p = idx - st * per;
+    rb = p / W;
+    cb = st * W + p % W;
+  } else {  // the narrower last strip
+    const int w2 = gx - nfull * W, p = idx - nfull * per;
+    rb = p / w2;
+    cb = nfull * W + p % w2;
+  }
+}
+
 // Wide large-M projections, the same arithmetic as k_gemm bit for bit, with
 // the operands shared through LDS.  A work-group of 2 x NWN waves owns BM
 // rows x NWN * 64 columns (8 waves, two per SIMD, for 256 columns; 4 waves
@@ -868,16 +891,8 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
   const int g = wave / NWG, wig = wave % NWG;  // K group, wave in the group
   const int wm = wig / NWN, wn = wig % NWN;
   const int lr = lane & 15, lq = lane >> 4;
-  // K groups: the blocks of linear id i mod 8 (one XCD's, the dispatcher
-  // deals work-groups round robin) form a sub-grid of a quarter of the row
-  // blocks by half the column blocks, so that their operands meet in that
-  // XCD's L2
   int cb = blockIdx.x, rb = blockIdx.y;
-  if (KG > 1 && gridDim.y % 4 == 0 && gridDim.x % 2 == 0) {
-    const int L = blockIdx.y * gridDim.x + blockIdx.x, x8 = L & 7, sl = L >> 3, cbw = gridDim.x / 2;
-    rb = (x8 >> 1) * (gridDim.y / 4) + sl / cbw;
-    cb = (x8 & 1) * cbw + sl % cbw;
-  }
+  if (a.xcd_strip > 0) xcd_block(a.xcd_strip, cb, rb);
   const int cblk = cb;  // column block (of this launch's columns)
   const int tile0 = a.tile0 + cblk * NST;  // the block's first output tile
   const int m0 = rb * BM;
@@ -1167,10 +1182,15 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
   k_gemm_big<EPI, NT, NR, KSR, SRC, WMT, WNF>                                                        \
       <<<dim3(a.ntiles * (NT) / (32 * (WNF)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(256), 0, s>>>(a)
 
-#define DMX_GEMM_LDS(EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG)                                     \
-  k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG>                                              \
-      <<<dim3(a.ntiles * (NT) / (64 * (NWN)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(128 * (NWN) * (KG)), 0, \
-         s>>>(a)
+// XS: strips of XS column blocks dealt to XCDs (xcd_block), 0 for the plain grid
+#define DMX_GEMM_LDS(XS, EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG)                                 \
+  do {                                                                                              \
+    GemmArgs b_ = a;                                                                                \
+    b_.xcd_strip = (XS);                                                                            \
+    k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG>                                            \
+        <<<dim3(b_.ntiles * (NT) / (64 * (NWN)), (b_.M + 32 * (WMT) - 1) / (32 * (WMT))),          \
+           dim3(128 * (NWN) * (KG)), 0, s>>>(b_);                                                   \
+  } while (0)
 
 // Row count from which the large-M schedules run a projection: k_gemm_lds
 // for the plain wide ones (the prefix QKV), the AdaRMS-fused gate-up and the
@@ -1185,7 +1205,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   // projections on 192 x 128 blocks in 2 K groups (220 blocks for 2048 rows,
   // where 128 x 256 blocks leave 96 CUs idle)
   switch (kind) {
-    case GEMM_PRE_OPROJ: DMX_GEMM_LDS(EPI_F32, 16, 2, 32, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
+    case GEMM_PRE_OPROJ: DMX_GEMM_LDS(5, EPI_F32, 16, 2, 32, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
     case GEMM_PRE_GATEUP: {
       // 256 x 256 blocks; where they would run 2.5 or 1.25 rounds over the
       // CUs (1024 or 2048 rows), the last 128 tiles run in a launch of their
@@ -1196,30 +1216,30 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
       b.ntiles = a.ntiles - tail;
       {
         const GemmArgs& a = b;
-        DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 8, 4, 4, 1);
+        DMX_GEMM_LDS(0, EPI_GEGLU, 32, 1, 80, A_GLOBAL, 8, 4, 4, 1);
       }
       if (tail) {
         b.tile0 = b.ntiles;
         b.ntiles = tail;
         const GemmArgs& a = b;
-        DMX_GEMM_LDS(EPI_GEGLU, 32, 1, 80, A_GLOBAL, 4, 4, 4, 1);
+        DMX_GEMM_LDS(4, EPI_GEGLU, 32, 1, 80, A_GLOBAL, 4, 4, 4, 1);
       }
       return hipGetLastError();
     }
-    case GEMM_PRE_DOWN: DMX_GEMM_LDS(EPI_F32, 16, 2, 160, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
+    case GEMM_PRE_DOWN: DMX_GEMM_LDS(5, EPI_F32, 16, 2, 160, A_GLOBAL, 6, 2, 4, 2); return hipGetLastError();
     default: break;
   }
   if (a.M >= kBigGemmRows) {
     switch (kind) {
-      case GEMM_QKV1024: DMX_GEMM_LDS(EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4, 6, 1); break;
+      case GEMM_QKV1024: DMX_GEMM_LDS(0, EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4, 6, 1); break;
       case GEMM_QKV1024_MODPRE: DMX_GEMM_BIG(EPI_QKV, 32, 4, 8, A_MODPRE, 4, 4); break;
-      case GEMM_QKV2560: DMX_GEMM_LDS(EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4, 6, 1); break;
-      case GEMM_OPROJ: DMX_GEMM_LDS(EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
-      case GEMM_OPROJ_F32: DMX_GEMM_LDS(EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
+      case GEMM_QKV2560: DMX_GEMM_LDS(4, EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4, 6, 1); break;
+      case GEMM_OPROJ: DMX_GEMM_LDS(8, EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
+      case GEMM_OPROJ_F32: DMX_GEMM_LDS(8, EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
       case GEMM_GATEUP: DMX_GEMM_BIG(EPI_GEGLU, 32, 4, 8, A_GLOBAL, 4, 4); break;
-      case GEMM_GATEUP_MOD: DMX_GEMM_LDS(EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4, 5, 1); break;
-      case GEMM_DOWN: DMX_GEMM_LDS(EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 2, 1, 4, 4); break;
-      case GEMM_DOWN_F32RES: DMX_GEMM_LDS(EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 2, 1, 4, 4); break;
+      case GEMM_GATEUP_MOD: DMX_GEMM_LDS(0, EPI_GEGLU, 32, 4, 8, A_MODPRE, 4, 4, 5, 1); break;
+      case GEMM_DOWN: DMX_GEMM_LDS(8, EPI_RESID_BB, 16, 8, 16, A_GLOBAL, 2, 1, 4, 4); break;
+      case GEMM_DOWN_F32RES: DMX_GEMM_LDS(8, EPI_RESID_FB, 16, 8, 16, A_GLOBAL, 2, 1, 4, 4); break;
       default: break;  // the prefix kinds returned above
     }
     return hipGetLastError();

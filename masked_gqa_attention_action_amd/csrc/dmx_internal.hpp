@@ -37,6 +37,7 @@ struct GemmArgs {
   int T, TP;          // tokens per request and their padded count
   int ntiles;         // grid.x = ntiles work-groups
   int tile0;          // k_gemm_lds: the launch's first output tile (its grid covers tiles tile0 ..)
+  int xcd_strip;      // k_gemm_lds: blocks dealt to XCDs in strips of this many column blocks (0: plain grid)
   int wtile_up;       // GEGLU: weight tile of the first "up" feature
   float* out_f32;     // EPI_F32 / EPI_RESID_BF output [M][ldo]
   uint16_t* out_bf16; // EPI_RESID_BB / EPI_RESID_FB row-major output
