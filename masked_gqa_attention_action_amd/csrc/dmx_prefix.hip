@@ -4,8 +4,11 @@
 // after the attention followed by the residual; the layer is the Gemma3-4B
 // decoder the table names): RMS norms with the (1 + w) weight, the residual
 // adds around them, and the image-feature merge.  Rows are tokens of one
-// request; hidden 2560.  One work-group of 320 threads per row, each thread
-// owning 8 consecutive features (16-byte loads).
+// request; hidden 2560.  The norms take 8 rows per work-group, one per wave,
+// each lane owning 5 pieces of 8 consecutive features (16-byte loads): the
+// 16-byte pieces they write into the tiled layout then fill whole 128-byte
+// lines (8 rows of one 32-column step) inside one work-group, where one row
+// per work-group left every line to be merged from 8 work-groups.
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
 #include "dmx_tiles.hpp"
@@ -14,8 +17,9 @@ namespace dmx {
 
 namespace {
 constexpr int kPH = kPrefixHidden;
-constexpr int kPThreads = kPH / 8;  // 320
-static_assert(kPThreads % 64 == 0, "whole waves");
+constexpr int kNormRows = 8;           // rows (waves) per work-group
+constexpr int kPieces = kPH / 8 / 64;  // 8-feature pieces per lane: 5
+static_assert(kPieces * 8 * 64 == kPH, "whole pieces");
 
 __device__ __forceinline__ void ld8(const uint16_t* p, float v[8]) {
   const uint4 r = *reinterpret_cast<const uint4*>(p);
@@ -36,68 +40,89 @@ __device__ __forceinline__ uint4 pk8(const float v[8]) {
   return make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
 }
 
-// 1 / rms of a row whose 8 values per thread are v (sum over the work-group)
-__device__ __forceinline__ float row_rscale(const float v[8], float* red) {
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
-  ss = wave_sum(ss);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();  // red is free again
-  if ((threadIdx.x & 63) == 0) red[wave] = ss;
-  __syncthreads();
+// 1 / rms of the wave's row, lane l holding features (64 p + l) * 8 .. + 7 in
+// v[p]: each piece's squares summed in order, each piece summed over the
+// wave (lane 0's sum: the rotating reduction rounds differently per lane),
+// the piece sums added in piece order
+__device__ __forceinline__ float row_rscale(const float v[kPieces][8]) {
   float t = 0.f;
 #pragma unroll
-  for (int w = 0; w < kPThreads / 64; ++w) t += red[w];
+  for (int p = 0; p < kPieces; ++p) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[p][i] * v[p][i];
+    t += __shfl(wave_sum(ss), 0, 64);
+  }
   return 1.0f / sqrtf(t * (1.0f / kPH) + kEps);
 }
 }  // namespace
 
 // xn = rmsnorm(x; w) of row-major bf16 rows, written tiled (a GEMM's A operand)
-__global__ __launch_bounds__(kPThreads) void k_prefix_rmsnorm(const uint16_t* x, const uint16_t* w, uint16_t* out) {
-  __shared__ float red[kPThreads / 64];
-  const int t = blockIdx.x, c = threadIdx.x * 8;
-  float v[8], wv[8];
-  ld8(x + (size_t)t * kPH + c, v);
-  ld8(w + c, wv);
-  const float r = row_rscale(v, red);
+__global__ __launch_bounds__(64 * kNormRows) void k_prefix_rmsnorm(const uint16_t* x, const uint16_t* w, int T,
+                                                                   uint16_t* out) {
+  const int lane = threadIdx.x & 63, t = blockIdx.x * kNormRows + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[kPieces][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = v[i] * r * (1.f + wv[i]);
-  *reinterpret_cast<uint4*>(out + tile_off(t, c, kPH)) = pk8(v);
+  for (int p = 0; p < kPieces; ++p) ld8(x + (size_t)t * kPH + (p * 64 + lane) * 8, v[p]);
+  const float r = row_rscale(v);
+#pragma unroll
+  for (int p = 0; p < kPieces; ++p) {
+    const int c = (p * 64 + lane) * 8;
+    float wv[8];
+    ld8(w + c, wv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[p][i] = v[p][i] * r * (1.f + wv[i]);
+    *reinterpret_cast<uint4*>(out + tile_off(t, c, kPH)) = pk8(v[p]);
+  }
 }
 
 // x1 = resid + rmsnorm(y; w_post) for projection rows y (fp32, row-major by
 // tiled row).  resid is fp32 (x1 of the same layer) or, when resid_f32 is
 // null, the bf16 row-major layer input.  Outputs (each optional): x1 in fp32,
 // rmsnorm(x1; w_next) tiled bf16, bf16(x1) row-major.
-__global__ __launch_bounds__(kPThreads) void k_prefix_post_norm(const float* y, const float* resid_f32,
-                                                               const uint16_t* resid_bf16, const uint16_t* w_post,
-                                                               const uint16_t* w_next, float* x1_out,
-                                                               uint16_t* xn_tiled, uint16_t* out_bf16) {
-  __shared__ float red[kPThreads / 64];
-  const int t = blockIdx.x, c = threadIdx.x * 8;
-  float v[8], wv[8], rs[8];
-  ld8(y + (size_t)t * kPH + c, v);
-  ld8(w_post + c, wv);
-  if (resid_f32)
-    ld8(resid_f32 + (size_t)t * kPH + c, rs);
-  else
-    ld8(resid_bf16 + (size_t)t * kPH + c, rs);
-  const float r = row_rscale(v, red);
+__global__ __launch_bounds__(64 * kNormRows) void k_prefix_post_norm(const float* y, const float* resid_f32,
+                                                                     const uint16_t* resid_bf16, const uint16_t* w_post,
+                                                                     const uint16_t* w_next, int T, float* x1_out,
+                                                                     uint16_t* xn_tiled, uint16_t* out_bf16) {
+  const int lane = threadIdx.x & 63, t = blockIdx.x * kNormRows + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[kPieces][8], rs[kPieces][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = rs[i] + v[i] * r * (1.f + wv[i]);
-  if (x1_out) {
-    *reinterpret_cast<float4*>(x1_out + (size_t)t * kPH + c) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(x1_out + (size_t)t * kPH + c + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  for (int p = 0; p < kPieces; ++p) {
+    const size_t o = (size_t)t * kPH + (p * 64 + lane) * 8;
+    ld8(y + o, v[p]);
+    if (resid_f32)
+      ld8(resid_f32 + o, rs[p]);
+    else
+      ld8(resid_bf16 + o, rs[p]);
   }
-  if (out_bf16) *reinterpret_cast<uint4*>(out_bf16 + (size_t)t * kPH + c) = pk8(v);
-  if (w_next) {
-    float xn[8];
-    ld8(w_next + c, wv);
-    const float r2 = row_rscale(v, red);
+  const float r = row_rscale(v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xn[i] = v[i] * r2 * (1.f + wv[i]);
-    *reinterpret_cast<uint4*>(xn_tiled + tile_off(t, c, kPH)) = pk8(xn);
+  for (int p = 0; p < kPieces; ++p) {
+    const int c = (p * 64 + lane) * 8;
+    float wv[8];
+    ld8(w_post + c, wv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[p][i] = rs[p][i] + v[p][i] * r * (1.f + wv[i]);
+    const size_t o = (size_t)t * kPH + c;
+    if (x1_out) {
+      *reinterpret_cast<float4*>(x1_out + o) = make_float4(v[p][0], v[p][1], v[p][2], v[p][3]);
+      *reinterpret_cast<float4*>(x1_out + o + 4) = make_float4(v[p][4], v[p][5], v[p][6], v[p][7]);
+    }
+    if (out_bf16) *reinterpret_cast<uint4*>(out_bf16 + o) = pk8(v[p]);
+  }
+  if (w_next) {
+    const float r2 = row_rscale(v);
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+      const int c = (p * 64 + lane) * 8;
+      float wv[8], xn[8];
+      ld8(w_next + c, wv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xn[i] = v[p][i] * r2 * (1.f + wv[i]);
+      *reinterpret_cast<uint4*>(xn_tiled + tile_off(t, c, kPH)) = pk8(xn);
+    }
   }
 }
 
@@ -119,15 +144,15 @@ __global__ __launch_bounds__(256) void k_image_merge(const uint16_t* tok, const 
 }
 
 hipError_t launch_prefix_rmsnorm(const uint16_t* x, const uint16_t* w, int T, uint16_t* out, hipStream_t s) {
-  k_prefix_rmsnorm<<<dim3(T), dim3(kPThreads), 0, s>>>(x, w, out);
+  k_prefix_rmsnorm<<<dim3((T + kNormRows - 1) / kNormRows), dim3(64 * kNormRows), 0, s>>>(x, w, T, out);
   return hipGetLastError();
 }
 
 hipError_t launch_prefix_post_norm(const float* y, const float* resid_f32, const uint16_t* resid_bf16,
                                    const uint16_t* w_post, const uint16_t* w_next, int T, float* x1_out,
                                    uint16_t* xn_tiled, uint16_t* out_bf16, hipStream_t s) {
-  k_prefix_post_norm<<<dim3(T), dim3(kPThreads), 0, s>>>(y, resid_f32, resid_bf16, w_post, w_next, x1_out,
-                                                        xn_tiled, out_bf16);
+  k_prefix_post_norm<<<dim3((T + kNormRows - 1) / kNormRows), dim3(64 * kNormRows), 0, s>>>(
+      y, resid_f32, resid_bf16, w_post, w_next, T, x1_out, xn_tiled, out_bf16);
   return hipGetLastError();
 }
 
