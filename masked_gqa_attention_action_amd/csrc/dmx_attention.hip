@@ -655,15 +655,32 @@ __global__ __launch_bounds__(256) void k_qknorm_rope(const float* raw, const uin
     sincosf((float)th, &sn[e], &cs[e]);
   }
   const float* src = raw + (size_t)(b * TP + t) * kQKV;
+  // every load of the token first (its 12 q / k heads, 4 v heads, the norm weights)
+  float2 los[kHQ + kHK], his[kHQ + kHK];
+  float4 xv[kHK];
+#pragma unroll
+  for (int h = 0; h < kHQ + kHK; ++h) {
+    los[h] = *reinterpret_cast<const float2*>(src + h * kD + 2 * lane);
+    his[h] = *reinterpret_cast<const float2*>(src + h * kD + 128 + 2 * lane);
+  }
+#pragma unroll
+  for (int hv = 0; hv < kHK; ++hv) xv[hv] = *reinterpret_cast<const float4*>(src + (kHQ + kHK + hv) * kD + 4 * lane);
+  float wq[4], wk[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = (e >> 1) * 128 + 2 * lane + (e & 1);
+    wq[e] = 1.f + bf2f(qn_w[j]);
+    wk[e] = 1.f + bf2f(kn_w[j]);
+  }
+#pragma unroll
   for (int h = 0; h < kHQ + kHK; ++h) {
     const bool isq = h < kHQ;
-    const uint16_t* wn = isq ? qn_w : kn_w;
-    const float2 lo = *reinterpret_cast<const float2*>(src + h * kD + 2 * lane);
-    const float2 hi = *reinterpret_cast<const float2*>(src + h * kD + 128 + 2 * lane);
+    const float* wn = isq ? wq : wk;
+    const float2 lo = los[h], hi = his[h];
     const float ss = wave_sum(lo.x * lo.x + lo.y * lo.y + hi.x * hi.x + hi.y * hi.y);
     const float r = 1.0f / sqrtf(ss * (1.0f / kD) + kEps);
-    const float a0 = lo.x * r * (1.f + bf2f(wn[2 * lane])), a1 = lo.y * r * (1.f + bf2f(wn[2 * lane + 1]));
-    const float c0 = hi.x * r * (1.f + bf2f(wn[128 + 2 * lane])), c1 = hi.y * r * (1.f + bf2f(wn[129 + 2 * lane]));
+    const float a0 = lo.x * r * wn[0], a1 = lo.y * r * wn[1];
+    const float c0 = hi.x * r * wn[2], c1 = hi.y * r * wn[3];
     const uint32_t outlo = pack2(a0 * cs[0] - c0 * sn[0], a1 * cs[1] - c1 * sn[1]);
     const uint32_t outhi = pack2(c0 * cs[0] + a0 * sn[0], c1 * cs[1] + a1 * sn[1]);
     uint16_t* dst = isq ? q + ((size_t)m * kHQ + h) * kD
@@ -671,8 +688,9 @@ __global__ __launch_bounds__(256) void k_qknorm_rope(const float* raw, const uin
     *reinterpret_cast<uint32_t*>(dst + 2 * lane) = outlo;
     *reinterpret_cast<uint32_t*>(dst + 128 + 2 * lane) = outhi;
   }
+#pragma unroll
   for (int hv = 0; hv < kHK; ++hv) {
-    const float4 x4 = *reinterpret_cast<const float4*>(src + (kHQ + kHK + hv) * kD + 4 * lane);
+    const float4 x4 = xv[hv];
     uint2 o;
     o.x = pack2(x4.x, x4.y);
     o.y = pack2(x4.z, x4.w);
