@@ -368,14 +368,15 @@ def test_layer_batched_equals_single_requests():
 def test_layer_large_m_batches_equal_single_requests(B, C, P):
     """Batches of 256+ padded rows run on the large-M GEMM schedules, whose
     blocks hold several requests (padded to 16, 48 or 64 rows, so requests
-    straddle 128-row blocks) with one AdaRMS shift row each.  Every request
-    still gets the bits it gets alone on the skinny schedule, and the batch
-    passes the oracle gate on a sample of requests."""
+    straddle 128-row blocks) with one AdaRMS shift row each, and grids whose
+    blocks do not split evenly over the XCDs.  Every request still gets the
+    bits it gets alone on the skinny schedule, and the batch passes the
+    oracle gate on a sample of requests."""
     wbits = synth.layer_weights(synth.BASE_SEED + 7000 + C)
     reqs = [synth.make_request(synth.BASE_SEED + 7100 + 31 * C + b, C, P, P // 2, P, 1) for b in range(B)]
     wd = device_weights(wbits)
     batched = run_layer(wbits, reqs, wd)
-    for b in sorted({0, B // 2, B - 1}):
+    for b in range(B):
         single = run_layer(wbits, [reqs[b]], wd)
         assert torch.equal(batched[b], single[0]), f"request {b} of {B} (C={C})"
     ow = oracle_weights(wbits)

@@ -191,8 +191,10 @@ def test_prefix_layer_is_deterministic(prefix_weights):
 
 def test_prefix_layer_2048_tokens_sampled_rows(prefix_weights):
     """The benchmarked size: 2048 tokens (1936 valid, 2 % holes), the launch
-    the benchmark times.  Against the oracle on 24 sampled rows (first, last,
-    holes, padding, spread) and on the whole K/V cache."""
+    the benchmark times.  Against the oracle on sampled rows (first, last,
+    holes, padding, spread, and one in every 128 rows, so that every row
+    block of every projection's grid is checked over all its columns) and on
+    the whole K/V cache."""
     wbits, wd = prefix_weights
     T = 2048
     x, valid = synth.prefix_inputs(synth.BASE_SEED + 9900, T, 1936, 0.02)
@@ -203,7 +205,7 @@ def test_prefix_layer_2048_tokens_sampled_rows(prefix_weights):
     r = rng(11)
     holes = np.flatnonzero(valid[:1936] == 0)
     rows = sorted(set([0, 1, 63, 64, 1935, 1936, 2047] + [int(i) for i in holes[:3]] +
-                      [int(i) for i in r.integers(0, T, 14)]))
+                      [int(i) for i in r.integers(0, T, 14)] + [128 * i + 77 for i in range(T // 128)]))
     print(f"prefix layer T=2048: {int(valid.sum())} valid, rows {rows}", flush=True)
     ref, rk, rv = orc.prefix_layer_rows(f64(x), {k: f64(v) for k, v in wbits.items()}, valid, rows)
     got = from_dev(out)[rows]
