@@ -82,13 +82,6 @@ __device__ __forceinline__ float dpp_f(float v) {
 }
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
-__device__ __forceinline__ float group16_max(float v) {
-  v = fmaxf(v, dpp_f<kRowRor1>(v));
-  v = fmaxf(v, dpp_f<kRowRor2>(v));
-  v = fmaxf(v, dpp_f<kRowRor4>(v));
-  v = fmaxf(v, dpp_f<kRowRor8>(v));
-  return v;
-}
 __device__ __forceinline__ float group16_sum(float v) {
   v += dpp_f<kRowRor1>(v);
   v += dpp_f<kRowRor2>(v);

@@ -65,12 +65,6 @@ __device__ __forceinline__ void write_row_ssq(const GemmArgs& a, int tile, int m
   }
 }
 
-__device__ __forceinline__ void ld8f(const float* p, float v[8]) {
-  const float4 x = *reinterpret_cast<const float4*>(p);
-  const float4 y = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-  v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-}
 __device__ __forceinline__ void st8f(float* p, const float v[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -801,34 +795,34 @@ __device__ __forceinline__ void xcd_block(int W, int& cb, int& rb) {
 }
 
 // Wide large-M projections, the same arithmetic as k_gemm bit for bit, with
-// the operands shared through LDS.  A work-group of 2 x NWN waves owns BM
-// rows x NWN * 64 columns (8 waves, two per SIMD, for 256 columns; 4 waves
-// for 128).  Each 32-column step's operand fragments (BM/16 A tiles, 4 NWN W
-// fragments, 1 KB each) are copied from HBM straight into an LDS stage by
-// loads that bypass registers (global_load_lds, 16 B per lane, so a wave's
-// fragment lands as one contiguous 1 KB block), STAGES - 1 steps ahead of
-// their use; each wave reads its WMT A tiles and 4 W fragments of the next
-// step from LDS while the MFMAs of the current one run.  K is split into the
-// same NR ranges of KSR steps as the skinny kernel's waves; each range is
-// accumulated from zero in step order and the range sums are added in range
-// order in registers.
+// the operands shared through LDS.  A work-group of NWM x NWN waves owns BM =
+// NWM * WMT * 16 rows x NWN * 64 columns (8 waves, two per SIMD: 2 x 4 for
+// 256 columns, 4 x 2 for 128).  Each 32-column step's operand fragments
+// (BM/16 A tiles, 4 NWN W fragments, 1 KB each) are copied from HBM straight
+// into an LDS stage by loads that bypass registers (global_load_lds, 16 B per
+// lane, so a wave's fragment lands as one contiguous 1 KB block), STAGES - 1
+// steps ahead of their use; each wave reads its WMT A tiles and 4 W fragments
+// of the next step from LDS while the MFMAs of the current one run.  K is
+// split into the same NR ranges of KSR steps as the skinny kernel's waves;
+// each range is accumulated from zero in step order and the range sums are
+// added in range order in registers.
 // KG > 1 (blocks too few or too small to keep 8 waves per CU busy): KG
-// groups of 2 x NWN waves share the block, group g running ranges
+// groups of NWM x NWN waves share the block, group g running ranges
 // g NR / KG .. with a stage ring of its own, in the same barriers; every
 // group keeps its range sums apart (in the accumulators if it has one), and
 // after the loop group 0 adds them all in range order (the other groups'
 // through LDS), EPH rows at a time.
-template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int NWN, int STG, int KG>
-__global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(NWN * KG / 2, 2))) void k_gemm_lds(
+template <int EPI, int NT, int NR, int KSR, int ASRC, int WMT, int NWN, int STG, int KG, int NWM>
+__global__ __launch_bounds__(64 * NWM * NWN * KG) __attribute__((amdgpu_waves_per_eu(NWM * NWN * KG / 4, 2))) void k_gemm_lds(
     GemmArgs a) {
   constexpr bool MOD = ASRC == A_MODPRE;
   constexpr bool QKV = EPI == EPI_QKV;
   constexpr bool SSQ = EPI == EPI_RESID_BF || EPI == EPI_RESID_FB;
   constexpr int NOUT = (EPI == EPI_GEGLU || QKV) ? 16 : NT;
-  constexpr int NWG = 2 * NWN;         // waves per K group
+  constexpr int NWG = NWM * NWN;       // waves per K group (NWM along M, NWN along N)
   constexpr int NW = NWG * KG;         // waves
   constexpr int WNF = 4;               // W fragments per wave
-  constexpr int BM = 2 * WMT * 16;     // rows per block
+  constexpr int BM = NWM * WMT * 16;   // rows per block
   constexpr int BNF = NWN * WNF;       // fragments per block
   constexpr int BN = BNF * 16;         // columns per block
   constexpr int NTT = NT / 16, NST = BNF / NTT;
@@ -875,7 +869,7 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
   constexpr int O_F = (O_R + (MOD ? BM * 4 : 0) + 7) & ~7;
   constexpr int O_Q2 = KG > 1 ? XCH + EPH * TLD * 4 : O_F + (QKV ? NST * 16 * 8 : 0);
   constexpr int O_Q = KG > 1 ? O_F : O_Q2 + SQB;
-  constexpr int LDS_BYTES = O_Q + (QKV ? BM * 2 * 4 : 0);
+  constexpr int LDS_BYTES = O_Q + (QKV ? NST * BM * 2 * 4 : 0);  // sQ: every tile's (one-pass epilogue)
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
   float* sTot = reinterpret_cast<float*>(smem + XCH);
@@ -1144,15 +1138,25 @@ __global__ __launch_bounds__(128 * NWN * KG) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
     const int prows = min(EPH, nrows - p0);
+    if constexpr (QKV && EPH == BM) {
+      // the rotation epilogue in one pass over the block's tiles, every
+      // task's operands fetched first (as k_gemm_big runs it; the fused
+      // gate-up measured no faster this way, 27.9 vs 27.4 us)
+      constexpr int TMAX = (NST * BM * EpiShape<EPI, NT>::TPR + NW * 64 - 1) / (NW * 64);
+      block_epilogue<EPI, NT, NST, BM, TMAX, MOD>(
+          a, tile0, m0, nrows, [&](int r, int c) { return sTot[r * TLD + c]; },
+          [&](int r, int c) { return sShift[((m0 + r) / a.TP - b0) * BN + c]; }, sR, sF, sq, sQ);
+    } else {
 #pragma unroll 1
-    for (int st = 0; st < NST; ++st) {  // (one pass over all tiles, as k_gemm_big does, measured no faster here)
-      const int tile = tile0 + st;
-      if (prows > 0)
-        tile_epilogue<EPI, NT, MOD>(
-            a, tile, m0 + p0, prows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
-            [&](int r, int c) { return sShift[((m0 + p0 + r) / a.TP - b0) * BN + st * NT + c]; },
-            sR + p0, sF + st * 16, sq, sQ, nullptr);
-      __syncthreads();
+      for (int st = 0; st < NST; ++st) {  // (one pass over all tiles measured no faster for these)
+        const int tile = tile0 + st;
+        if (prows > 0)
+          tile_epilogue<EPI, NT, MOD>(
+              a, tile, m0 + p0, prows, [&](int r, int c) { return sTot[r * TLD + st * NT + c]; },
+              [&](int r, int c) { return sShift[((m0 + p0 + r) / a.TP - b0) * BN + st * NT + c]; },
+              sR + p0, sF + st * 16, sq, sQ, nullptr);
+        __syncthreads();
+      }
     }
   }
 }
@@ -1183,21 +1187,24 @@ int gemm_config(GemmKind kind, GemmArgs& a) {
       <<<dim3(a.ntiles * (NT) / (32 * (WNF)), (a.M + 32 * (WMT) - 1) / (32 * (WMT))), dim3(256), 0, s>>>(a)
 
 // XS: strips of XS column blocks dealt to XCDs (xcd_block), 0 for the plain grid
-#define DMX_GEMM_LDS(XS, EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG)                                 \
+#define DMX_GEMM_LDS_W(XS, EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG, NWM)                          \
   do {                                                                                              \
     GemmArgs b_ = a;                                                                                \
     b_.xcd_strip = (XS);                                                                            \
-    k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG>                                            \
-        <<<dim3(b_.ntiles * (NT) / (64 * (NWN)), (b_.M + 32 * (WMT) - 1) / (32 * (WMT))),          \
-           dim3(128 * (NWN) * (KG)), 0, s>>>(b_);                                                   \
+    k_gemm_lds<EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG, NWM>                                       \
+        <<<dim3(b_.ntiles * (NT) / (64 * (NWN)), (b_.M + 16 * (NWM) * (WMT) - 1) / (16 * (NWM) * (WMT))), \
+           dim3(64 * (NWM) * (NWN) * (KG)), 0, s>>>(b_);                                            \
   } while (0)
+// two waves along M
+#define DMX_GEMM_LDS(XS, EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG) \
+  DMX_GEMM_LDS_W(XS, EPI, NT, NR, KSR, SRC, WMT, NWN, STG, KG, 2)
 
 // Row count from which the large-M schedules run a projection: k_gemm_lds
-// for the plain wide ones (the prefix QKV), the AdaRMS-fused gate-up and the
-// 1024-column projections (64 x 64 blocks, 256 for 1024 rows, each shared by
-// 4 K groups of 2 waves), k_gemm_big for the fused QKV (measured faster there
-// at 1024 rows, 25.6 vs 26.0 us with 4-wave LDS blocks of 128 x 128) and the
-// plain gate-up.
+// for the plain wide ones (the prefix QKV), the AdaRMS-fused gate-up, the
+// AdaRMS-fused QKV (128 x 128 blocks of 8 waves, 4 along M: 21.6 us at 1024
+// rows against 25.6 on k_gemm_big) and the 1024-column projections (64 x 64
+// blocks, 256 for 1024 rows, each shared by 4 K groups of 2 waves);
+// k_gemm_big for the plain gate-up.
 constexpr int kBigGemmRows = 256;
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
@@ -1232,7 +1239,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& a, hipStream_t s) {
   if (a.M >= kBigGemmRows) {
     switch (kind) {
       case GEMM_QKV1024: DMX_GEMM_LDS(0, EPI_F32, 16, 4, 8, A_GLOBAL, 4, 4, 6, 1); break;
-      case GEMM_QKV1024_MODPRE: DMX_GEMM_BIG(EPI_QKV, 32, 4, 8, A_MODPRE, 4, 4); break;
+      case GEMM_QKV1024_MODPRE: DMX_GEMM_LDS_W(0, EPI_QKV, 32, 4, 8, A_MODPRE, 2, 2, 8, 1, 4); break;
       case GEMM_QKV2560: DMX_GEMM_LDS(4, EPI_F32, 16, 4, 20, A_GLOBAL, 4, 4, 6, 1); break;
       case GEMM_OPROJ: DMX_GEMM_LDS(8, EPI_RESID_BB, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
       case GEMM_OPROJ_F32: DMX_GEMM_LDS(8, EPI_RESID_BF, 16, 8, 8, A_GLOBAL, 2, 1, 4, 4); break;
