@@ -24,14 +24,15 @@ namespace dmx {
 // block, so the four waves share one K/V stream.  Products run transposed on
 // 32x32x16 MFMA: S^T = K Q^T (Q^T in registers), O^T += V^T P^T (P^T never
 // leaves registers).  Lane l owns query row l % 32; its 16 logits per block
-// are keys 8 (r / 4) + 4 (l / 32) + r % 4.
+// are keys 8 (r / 4) + 4 (l / 32) + r % 4.  The online softmax takes two
+// blocks (64 keys) per round.
 //
 // V^T comes from a transposed copy, [4][Tp / 32][256][32] (Tp = tokens
 // rounded up to 32: each key block's V^T one contiguous 16 KB run), that
 // k_prefix_vt writes with zeros for invisible keys: an MFMA operand needs its
 // 8 keys of one dimension contiguous.  K rows and V^T rows
 // are copied from HBM straight into a ring of LDS stages (global_load_lds,
-// 16 B per lane, STAGES - 1 blocks ahead); every read of a stage is then a
+// 16 B per lane, one pair of blocks ahead); every read of a stage is then a
 // plain LDS load that the compiler can tell apart from the stages being
 // filled.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled
 // (K by key, V^T by dimension), so the fragment reads hit distinct banks.
@@ -55,6 +56,24 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // V^T: chunk c (of 4, 8 keys each) of dimension row d at chunk c ^ swz_v(d)
 __device__ __forceinline__ int swz_k(int j) { return j & 15; }
 __device__ __forceinline__ int swz_v(int d) { return (d >> 2) & 3; }
+
+// Scheduling of a run of N LDS fragment reads each feeding one MFMA, in
+// program order: kAhead reads, then MFMA / read pairs, then the last kAhead
+// MFMAs, so that reads stay in flight under the MFMAs instead of each
+// waiting for its own.
+constexpr int kAhead = 4;
+template <int N>
+__device__ __forceinline__ void pipeline_reads() {
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+#pragma unroll
+  for (int i = 0; i < N - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
 
 // query block qb, split index and key-block range of work item `item`
 // (items ordered by query block, longest first); false past the last item
@@ -140,7 +159,7 @@ template <bool CTX_TILED>
 __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                                                     const uint8_t* valid, int T, int kv_rows, int Tp, int sb,
                                                     int items, uint16_t* ctx, uint16_t* part_o, float* part_ml) {
-  constexpr int STAGES = 4, AHEAD = STAGES - 1;
+  constexpr int STAGES = 4;  // two pairs of blocks: one being read, one loading
   constexpr int PIECES = 4;  // 1 KB pieces of K (and of V^T) each wave copies per block
   // One array per stage, each holding a block's K rows and V^T rows, and
   // the stage of every copy and read known at compile time: the compiler
@@ -222,7 +241,6 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
   };
   issue(std::integral_constant<int, 0>{}, 0);
   issue(std::integral_constant<int, 1>{}, 1);
-  issue(std::integral_constant<int, 2>{}, 2);
 
   f32x16 o[8];
 #pragma unroll
@@ -232,50 +250,92 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
   float mrun = kNegBig, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(head_dim)
 
-  // block ib, held in stage ST = ib % STAGES
-  auto body = [&](auto ST, int ib) {
-    constexpr int S = decltype(ST)::value;
-    wait_vmcnt<(AHEAD - 1) * PIECES * 2>();  // this wave's copies of block ib landed
-    lds_barrier();                           // everyone's have; stage (ib - 1) is free
-    issue(std::integral_constant<int, (S + AHEAD) % STAGES>{}, ib + AHEAD);
-    const int kb0 = (it.kb_lo + ib) * kPaKB;
-    const uint32_t vis = sVis[ib];
-    const uint16_t* bK = stage(ST)[0];
-    const uint16_t* bV = stage(ST)[1];
+  // LDS element offsets of this lane's fragment reads inside a stage.  K:
+  // chunk 2 s2 + h of key row j sits at chunk 16 (s2 / 8) + ((2 (s2 % 8) + h)
+  // ^ swz_k(j)) (the swizzle is below 16), so eight offsets serve all 16
+  // steps.  V^T: dimension row 32 t + l % 32 has swz_v = (l % 32 / 4) % 4 for
+  // every t, so two offsets (m = 0, 1) serve all 8 dimension tiles.
+  // Byte offsets; each round re-reads them through an empty asm statement,
+  // so the compiler forms every address as offset + immediate at its read
+  // instead of keeping one hoisted address per read live across the loop.
+  int koff[8], voff[2];
+  {
+    const int j = lane & 31;
+#pragma unroll
+    for (int lo = 0; lo < 8; ++lo) koff[lo] = 2 * (j * kD + ((2 * lo + h) ^ swz_k(j)) * 8);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) voff[m] = 2 * (j * kPaKB + ((2 * m + h) ^ swz_v(j)) * 8);
+  }
 
-    f32x16 sacc;
+  // Blocks ib and ib + 1, held in stages SA = ib % STAGES and SB = SA + 1,
+  // in one softmax round of 64 keys: one maximum, one rescale of the
+  // accumulators and one barrier per pair.  The pair's copies are the only
+  // ones in flight when the round starts; the next pair goes into the
+  // stages the previous round read (free once every wave is past the
+  // barrier), so one pair is always loading under the current one.
+  auto pair = [&](auto SA, auto SB, int ib) {
+    constexpr int A = decltype(SA)::value, B = decltype(SB)::value;
+    wait_vmcnt<0>();  // this wave's copies of blocks ib, ib + 1 landed
+    lds_barrier();    // everyone's have; the previous pair's stages are free
+    issue(std::integral_constant<int, (A + 2) % STAGES>{}, ib + 2);
+    issue(std::integral_constant<int, (B + 2) % STAGES>{}, ib + 3);
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before the round's reads
+    const char* bK[2] = {reinterpret_cast<const char*>(stage(SA)[0]), reinterpret_cast<const char*>(stage(SB)[0])};
+    const char* bV[2] = {reinterpret_cast<const char*>(stage(SA)[1]), reinterpret_cast<const char*>(stage(SB)[1])};
+    __asm__ volatile("" : "+v"(koff[0]), "+v"(koff[1]), "+v"(koff[2]), "+v"(koff[3]), "+v"(koff[4]), "+v"(koff[5]),
+                     "+v"(koff[6]), "+v"(koff[7]), "+v"(voff[0]), "+v"(voff[1]));
+
+    f32x16 sacc[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[u][r] = 0.f;
     {
-      const int j = lane & 31;
+      // K fragment (s2, u) at byte koff[s2 % 8] + 256 (s2 / 8); the two blocks'
+      // chains alternate, and each read is issued kAhead MFMAs early
+      bf16x8 kf[32];
 #pragma unroll
-      for (int s2 = 0; s2 < 16; ++s2) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(bK + j * kD + (((2 * s2 + h) ^ swz_k(j)) * 8));
-        sacc = mfma32(kf, qf[s2], sacc);
-      }
+      for (int i = 0; i < 32; ++i)
+        kf[i] = *reinterpret_cast<const bf16x8*>(bK[i & 1] + koff[(i >> 1) & 7] + 256 * (i >> 4));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sacc[i & 1] = mfma32(kf[i], qf[i >> 1], sacc[i & 1]);
+      pipeline_reads<32>();
     }
-    float x[16];
+    // key `key` of block u is read when its bit is set in the block's
+    // visibility and key <= row - kb0 (causal); the logit of any other key is
+    // replaced, bit for bit, by -inf (a select by bit mask: whatever the
+    // cache holds there, NaN included, cannot pass)
+    float x[2][16];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-      x[r] = (((vis >> key) & 1u) && kb0 + key <= row) ? sacc[r] * sl2 : -INFINITY;
-      mloc = fmaxf(mloc, x[r]);
+    for (int u = 0; u < 2; ++u) {
+      const int lim = row - (it.kb_lo + ib + u) * kPaKB;
+      const uint32_t causal = lim >= kPaKB - 1 ? 0xffffffffu : lim < 0 ? 0u : (2u << lim) - 1u;
+      const uint32_t keep = sVis[ib + u] & causal;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+        const uint32_t sel = (uint32_t)((int32_t)(keep << (31 - key)) >> 31);  // all ones when kept
+        x[u][r] = __uint_as_float((__float_as_uint(sacc[u][r] * sl2) & sel) | (__float_as_uint(-INFINITY) & ~sel));
+        mloc = fmaxf(mloc, x[u][r]);
+      }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     const float mnew = fmaxf(mrun, mloc);
     const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // exp2(-inf) = 0 in hardware
     mrun = mnew;
-    bf16x8 pf[2];
+    bf16x8 pf[2][2];
     float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[r] - mnew), p1 = __builtin_amdgcn_exp2f(x[r + 1] - mnew);
-      psum += p0 + p1;
-      const uint32_t pk = pack2(p0, p1);
-      pf[r >> 3][r & 7] = (short)(pk & 0xffffu);
-      pf[r >> 3][(r & 7) + 1] = (short)(pk >> 16);
-    }
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(x[u][r] - mnew), p1 = __builtin_amdgcn_exp2f(x[u][r + 1] - mnew);
+        psum += p0 + p1;
+        const uint32_t pk = pack2(p0, p1);
+        pf[u][r >> 3][r & 7] = (short)(pk & 0xffffu);
+        pf[u][r >> 3][(r & 7) + 1] = (short)(pk >> 16);
+      }
     lrun = lrun * alpha + psum;
     // unconditional (alpha = 1 leaves o as it is): see the loop comment
 #pragma unroll
@@ -283,24 +343,23 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
     // V^T operand of dims 32 t + (l % 32): chunk 2m + h of the dimension's
     // row holds keys 16 m + 4 h + e and 16 m + 8 + 4 h + e (e < 4), the key
     // order of P^T's elements above
+    // (dimension row 32 t + l % 32 sits at byte voff[m] + 2048 t); fragment i is
+    // (u, m) = (i / 16, i / 8 % 2) of dims tile t = i % 8, so consecutive
+    // MFMAs update different accumulators
+    {
+      bf16x8 vf[32];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int dv = 32 * t + (lane & 31);
-      const uint16_t* vrow = bV + dv * kPaKB;
-      const int sw = swz_v(dv);
+      for (int i = 0; i < 32; ++i)
+        vf[i] = *reinterpret_cast<const bf16x8*>(bV[i >> 4] + voff[(i >> 3) & 1] + 2048 * (i & 7));
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + (((2 * m + h) ^ sw) * 8));
-        o[t] = mfma32(vf, pf[m], o[t]);
-      }
+      for (int i = 0; i < 32; ++i) o[i & 7] = mfma32(vf[i], pf[i >> 4][(i >> 3) & 1], o[i & 7]);
+      pipeline_reads<32>();
     }
   };
 #pragma unroll 1
   for (int ib = 0; ib < npad; ib += STAGES) {
-    body(std::integral_constant<int, 0>{}, ib);
-    body(std::integral_constant<int, 1>{}, ib + 1);
-    body(std::integral_constant<int, 2>{}, ib + 2);
-    body(std::integral_constant<int, 3>{}, ib + 3);
+    pair(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, ib);
+    pair(std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{}, ib + 2);
   }
   wait_vmcnt<0>();  // the trailing copies (never read) are done before the work-group ends
 

@@ -6,6 +6,9 @@ against the float64 oracle.
 - every step with teacher forcing: the oracle starts from the GPU's actions
   before the step, and the step's velocity (a_k+1 - a_k) / dt is gated like a
   layer output;
+- the sampler's tail alone (final AdaRMS, out-projection, Euler update) at the
+  layer gate: the last step's velocity against the oracle's tail applied to
+  the stack output the GPU produced;
 - graph replay == eager run, bit for bit, also on new noise; with and without
   the modulation table, bit for bit;
 - a small run end to end against the oracle's free run (cosine);
@@ -78,6 +81,25 @@ def teacher_forced_steps(c, sw, layers, steps=None):
     return worst
 
 
+def tail_teacher_forced(c, sw):
+    """Gate the last step's velocity against the oracle's final AdaRMS and
+    out-projection applied to the stack output the GPU produced (the stack's
+    x still holds it after the run): the sampler's own tail at the layer gate,
+    with none of the layers' rounding in between."""
+    k = c.n_steps - 1
+    traj = from_dev(c.traj)
+    x_last = from_dev(c.x)
+    cond = orc.time_condition(orc.step_time(k, c.n_steps), sw)
+    worst = 0.0
+    for b in range(c.B):
+        a_prev = c.noise[b].astype(np.float64) if k == 0 else traj[k - 1, b]
+        v_gpu = (traj[k, b] - a_prev) * (-c.n_steps)
+        v = orc.final_velocity(x_last[b], cond, sw["w_fmod"], sw["b_fmod"], sw["w_out"], sw["b_out"])
+        ratio, _ = gate(f"tail velocity step {k} request {b}", v_gpu, v)
+        worst = max(worst, ratio)
+    return worst
+
+
 def test_steps_teacher_forced(small):
     c = small
     c.reset()
@@ -85,6 +107,7 @@ def test_steps_teacher_forced(small):
     torch.cuda.synchronize()
     assert torch.equal(c.actions, c.traj[-1]), "actions differ from the last trajectory entry"
     sw, layers = c.oracle_inputs()
+    tail_teacher_forced(c, sw)
     teacher_forced_steps(c, sw, layers)
 
 
@@ -159,8 +182,9 @@ def test_full_size_steps_teacher_forced():
     c.sampler.run()
     torch.cuda.synchronize()
     sw, layers = c.oracle_inputs()
+    tail = tail_teacher_forced(c, sw)
     worst = teacher_forced_steps(c, sw, layers)
-    print(f"worst velocity ratio over the 10 steps: {worst:.3e}", flush=True)
+    print(f"worst velocity ratio over the 10 steps: {worst:.3e}; the tail alone: {tail:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("A", [16, 48, 128])
@@ -174,6 +198,7 @@ def test_action_dims(A):
     c.sampler.run()
     torch.cuda.synchronize()
     sw, layers = c.oracle_inputs()
+    tail_teacher_forced(c, sw)
     teacher_forced_steps(c, sw, layers)
     t = Case(2, 3, 2, 10, 576, 500, 576, 0.05, synth.BASE_SEED + 7400 + A, mod_table=True, A=A)
     t.sampler.run()
