@@ -155,7 +155,9 @@ hipError_t launch_image_merge(const uint16_t* tok, const uint16_t* img, const in
 // prefix attention of the prefill: q row-major [T][8][256]; k, v [4][kv_rows][256];
 // valid [T]; ctx tiled [TP][2048] (ctx_tiled) or row-major [T][8][256]; ws of
 // prefix_attention_ws_bytes(T) bytes for the split partials
-constexpr int kPrefixAttnSplit = 16;  // key blocks of 32 per split
+// split sizes (key blocks of 32 per work item) the launch chooses among; the
+// workspace is sized for the smallest
+constexpr int kPrefixAttnSplits[4] = {24, 20, 16, 12};
 int prefix_attn_items(int T, int sb);
 size_t prefix_attention_ws_bytes(int T);
 hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,

@@ -4,7 +4,11 @@
 // costs a read and a write around every multiply.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 #include "dmx_device.hpp"
 #include "dmx_internal.hpp"
@@ -61,11 +65,15 @@ __device__ __forceinline__ int swz_v(int d) { return (d >> 2) & 3; }
 // program order: kAhead reads, then MFMA / read pairs, then the last kAhead
 // MFMAs, so that reads stay in flight under the MFMAs instead of each
 // waiting for its own.
+// With LEAD false the first kAhead reads were issued earlier, in another
+// scheduling region.
 constexpr int kAhead = 4;
-template <int N>
+constexpr float kLazyLog2 = 8.0f;  // how far a logit may sit above the softmax reference (log2 units)
+template <int N, bool LEAD = true>
 __device__ __forceinline__ void pipeline_reads() {
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  for (int i = 0; i < kAhead; ++i)
+    if (LEAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
 #pragma unroll
   for (int i = 0; i < N - kAhead; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -177,7 +185,9 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
     else if constexpr (S == 2) return sKV2;
     else return sKV3;
   };
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept in a scalar register, so that the copies'
+  // LDS destinations and sources need no per-lane arithmetic
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x % kHK, item = blockIdx.x / kHK;
   PaItem it;
   if (!pa_item(item, T, sb, it)) return;  // uniform per work-group
@@ -203,17 +213,21 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
     const uint64_t b = __ballot(ok);
     if (lane == 0) sVis[i] = (uint32_t)b;
   }
-  // this wave's copy sources at the split's first block: K rows (a key past
-  // the tokens reads the last token's row; its logit is masked) and V^T rows
-  const uint16_t* ksrc[PIECES];
-  const uint16_t* vsrc[PIECES];
+  // this wave's copy sources: the split's K rows and V^T rows from uniform
+  // bases, plus per-lane 32-bit element offsets (a key past the tokens reads
+  // the last token's row; its logit is masked)
+  const uint16_t* kbase = k + ((size_t)g * kv_rows + (size_t)it.kb_lo * kPaKB) * kD;
+  const uint16_t* vbase = vt + ((size_t)g * (Tp / kPaKB) + it.kb_lo) * kD * kPaKB;
+  int krow[PIECES];
+  uint32_t kcol[PIECES], vofs[PIECES];
 #pragma unroll
   for (int d = 0; d < PIECES; ++d) {
     const int piece = wave * PIECES + d;
     const int j = piece * 2 + (lane >> 5);  // K: key row of the block
-    ksrc[d] = k + ((size_t)g * kv_rows + it.kb_lo * kPaKB + j) * kD + (((lane & 31) ^ swz_k(j)) * 8);
+    krow[d] = j;
+    kcol[d] = ((lane & 31) ^ swz_k(j)) * 8;
     const int dv = piece * 16 + (lane >> 2);  // V^T: dimension row
-    vsrc[d] = vt + (((size_t)g * (Tp / kPaKB) + it.kb_lo) * kD + dv) * kPaKB + (((lane & 3) ^ swz_v(dv)) * 8);
+    vofs[d] = dv * kPaKB + ((lane & 3) ^ swz_v(dv)) * 8;
   }
   const int last_key_row = T - 1 - it.kb_lo * kPaKB;  // rows past it are clamped
   wait_vmcnt<0>();
@@ -230,13 +244,13 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
   auto issue = [&](auto ST, int i) {
     uint16_t(*b)[kPaKB * kD] = stage(ST);
     const int ib = min(i, nblk - 1);
+    const uint16_t* vblk = vbase + (size_t)ib * kD * kPaKB;
 #pragma unroll
     for (int d = 0; d < PIECES; ++d) {
       const int piece = wave * PIECES + d;
-      const int j = piece * 2 + (lane >> 5);
-      const int over = max(0, ib * kPaKB + j - last_key_row);  // rows past the tokens: the last one
-      lds_copy16(ksrc[d] + ((size_t)ib * kPaKB - over) * kD, &b[0][piece * 512]);
-      lds_copy16(vsrc[d] + (size_t)ib * kD * kPaKB, &b[1][piece * 512]);
+      const uint32_t r = min(ib * kPaKB + krow[d], last_key_row);  // rows past the tokens: the last one
+      lds_copy16(kbase + (r * kD + kcol[d]), &b[0][piece * 512]);
+      lds_copy16(vblk + vofs[d], &b[1][piece * 512]);
     }
   };
   issue(std::integral_constant<int, 0>{}, 0);
@@ -316,30 +330,47 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * h + (r & 3);
         const uint32_t sel = (uint32_t)((int32_t)(keep << (31 - key)) >> 31);  // all ones when kept
-        x[u][r] = __uint_as_float((__float_as_uint(sacc[u][r] * sl2) & sel) | (__float_as_uint(-INFINITY) & ~sel));
+        x[u][r] = __uint_as_float((__float_as_uint(sacc[u][r]) & sel) | (__float_as_uint(-INFINITY) & ~sel));
         mloc = fmaxf(mloc, x[u][r]);
       }
     }
+    // Maxima in raw logit units; the scale log2(e) / 16 enters each exponent
+    // through one fused multiply-add.  mrun is the reference the exponents
+    // are taken against, not always the running maximum: it moves (and the
+    // accumulators are rescaled) only in rounds where some row of the wave
+    // saw a logit more than kLazyLog2 above it (in log2 units), so every
+    // exponent stays below 2^kLazyLog2 and most rounds skip the 128
+    // multiplies.  Sums and outputs share the reference, so o / l and the
+    // merge's weights are unchanged by where it sits.
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mnew = fmaxf(mrun, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // exp2(-inf) = 0 in hardware
-    mrun = mnew;
+    // the round's first V fragments go out before the branch
+    bf16x8 vf[32];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+      vf[i] = *reinterpret_cast<const bf16x8*>(bV[i >> 4] + voff[(i >> 3) & 1] + 2048 * (i & 7));
+    if (__builtin_amdgcn_ballot_w64((mloc - mrun) * sl2 > kLazyLog2) != 0) {
+      const float mnew = fmaxf(mrun, mloc);
+      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * sl2);  // exp2(-inf) = 0 in hardware
+      mrun = mnew;
+      lrun *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    }
+    const float nm = -mrun * sl2;
     bf16x8 pf[2][2];
     float psum = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(x[u][r] - mnew), p1 = __builtin_amdgcn_exp2f(x[u][r + 1] - mnew);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(x[u][r], sl2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(x[u][r + 1], sl2, nm));
         psum += p0 + p1;
         const uint32_t pk = pack2(p0, p1);
         pf[u][r >> 3][r & 7] = (short)(pk & 0xffffu);
         pf[u][r >> 3][(r & 7) + 1] = (short)(pk >> 16);
       }
-    lrun = lrun * alpha + psum;
-    // unconditional (alpha = 1 leaves o as it is): see the loop comment
-#pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    lrun += psum;
     // V^T operand of dims 32 t + (l % 32): chunk 2m + h of the dimension's
     // row holds keys 16 m + 4 h + e and 16 m + 8 + 4 h + e (e < 4), the key
     // order of P^T's elements above
@@ -347,13 +378,12 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
     // (u, m) = (i / 16, i / 8 % 2) of dims tile t = i % 8, so consecutive
     // MFMAs update different accumulators
     {
-      bf16x8 vf[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
+      for (int i = kAhead; i < 32; ++i)
         vf[i] = *reinterpret_cast<const bf16x8*>(bV[i >> 4] + voff[(i >> 3) & 1] + 2048 * (i & 7));
 #pragma unroll
       for (int i = 0; i < 32; ++i) o[i & 7] = mfma32(vf[i], pf[i >> 4][(i >> 3) & 1], o[i & 7]);
-      pipeline_reads<32>();
+      pipeline_reads<32, false>();
     }
   };
 #pragma unroll 1
@@ -378,7 +408,7 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
       }
     return;
   }
-  // partial of this split: [g][item][wave][32 rows][256] bf16 normalised, and (max, sum)
+  // partial of this split: [g][item][wave][32 rows][256] bf16 normalised, and (max, sum), the max scaled to log2 units as the merge expects
   const size_t pidx = ((size_t)g * items + item) * 4 + wave;
   uint16_t* po = part_o + (pidx * 32 + (lane & 31)) * kD;
 #pragma unroll
@@ -389,7 +419,7 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
       *reinterpret_cast<uint2*>(po + d) = make_uint2(pack2(o[t][4 * q4] * inv, o[t][4 * q4 + 1] * inv),
                                                      pack2(o[t][4 * q4 + 2] * inv, o[t][4 * q4 + 3] * inv));
     }
-  if (lane < 32) *reinterpret_cast<float2*>(part_ml + (pidx * 32 + lane) * 2) = make_float2(mrun, l);
+  if (lane < 32) *reinterpret_cast<float2*>(part_ml + (pidx * 32 + lane) * 2) = make_float2(mrun * sl2, l);
 }
 
 // Merge of the splits of one (KV head, query block, wave tile): for each of
@@ -453,13 +483,57 @@ __global__ __launch_bounds__(256) void k_prefix_attn_merge(int T, int sb, int it
 static size_t vt_bytes(int T) { return (size_t)kHK * kD * ((T + kPaKB - 1) / kPaKB * kPaKB) * 2; }
 
 size_t prefix_attention_ws_bytes(int T) {
-  const int items = prefix_attn_items(T, kPrefixAttnSplit);
+  const int items = prefix_attn_items(T, kPrefixAttnSplits[3]);  // the smallest split: the most items
   return vt_bytes(T) + (size_t)kHK * items * 4 * 32 * (kD * 2 + 2 * sizeof(float));
+}
+
+// Compute units of the current device (cached per device id).
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Split size for T tokens: the candidate whose work items finish first when
+// dealt in launch order to whichever CU frees up first (one work-group per
+// CU: the LDS ring fills it), an item costing its padded block count plus two
+// blocks of fixed work (queries in, outputs out); ties go to the larger split
+// (fewer partials to merge).  Host arithmetic only.
+static int prefix_attn_split(int T, int cus) {
+  int best = kPrefixAttnSplits[0];
+  long best_t = -1;
+  for (int sb : kPrefixAttnSplits) {
+    std::priority_queue<long, std::vector<long>, std::greater<long>> free_at;
+    for (int c = 0; c < cus; ++c) free_at.push(0);
+    long end = 0;
+    const int items = prefix_attn_items(T, sb);
+    for (int item = 0; item < items; ++item) {
+      PaItem it;
+      pa_item(item, T, sb, it);
+      const long cost = (it.kb_hi - it.kb_lo + 3) / 4 * 4 + 2;
+      for (int g = 0; g < kHK; ++g) {
+        const long t = free_at.top() + cost;
+        free_at.pop();
+        free_at.push(t);
+        end = std::max(end, t);
+      }
+    }
+    if (best_t < 0 || end < best_t) {
+      best_t = end;
+      best = sb;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,
                                    int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, void* ws, hipStream_t s) {
-  const int sb = kPrefixAttnSplit;
+  const int sb = prefix_attn_split(T, device_cus());
   const int items = prefix_attn_items(T, sb);
   const int Tp = (T + kPaKB - 1) / kPaKB * kPaKB;
   unsigned char* w = static_cast<unsigned char*>(ws);
