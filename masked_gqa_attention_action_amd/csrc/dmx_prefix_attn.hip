@@ -427,6 +427,10 @@ __global__ __launch_bounds__(256) void k_prefix_attn(const uint16_t* q, const ui
 // sum_s w_s (zero when no split saw a visible key), in split order.  One
 // work-group of 256 threads per (g, query block, tile); 8 threads per row,
 // 32 dims each.  Query blocks with a single split return at once.
+constexpr int kMergeBatch = 4;
+// splits of one query block at most: 4096 tokens, 12-block splits
+constexpr int kMergeMaxSplits = 12;
+static_assert(kMergeMaxSplits * kPrefixAttnSplits[3] * kPaKB >= 4096, "merge bound below the longest query block's splits");
 template <bool CTX_TILED>
 __global__ __launch_bounds__(256) void k_prefix_attn_merge(int T, int sb, int items, const uint16_t* part_o,
                                                           const float* part_ml, uint16_t* ctx) {
@@ -443,29 +447,54 @@ __global__ __launch_bounds__(256) void k_prefix_attn_merge(int T, int sb, int it
   const int row = qb * 64 + (tile & 1) * 32 + rr;
   if (row >= T) return;
   const int hq = g * kGroup + (tile >> 1);
+  // Every split's (max, sum) and the first batch's outputs are requested
+  // before any arithmetic, later batches as a whole: a few dependent loads
+  // per thread instead of two passes of one load per split.  The sums run in
+  // split order, as before.
+  float2 ml[kMergeMaxSplits];
+#pragma unroll
+  for (int s2 = 0; s2 < kMergeMaxSplits; ++s2)
+    if (s2 < ns) {
+      const size_t pidx = ((size_t)g * items + first + s2) * 4 + tile;
+      ml[s2] = *reinterpret_cast<const float2*>(part_ml + (pidx * 32 + rr) * 2);
+    }
+  uint4 raw[kMergeBatch][4];
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b)
+      if (s0 + b < ns) {
+        const size_t pidx = ((size_t)g * items + first + s0 + b) * 4 + tile;
+        const uint16_t* po = part_o + (pidx * 32 + rr) * kD + d0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) raw[b][c] = *reinterpret_cast<const uint4*>(po + c * 8);
+      }
+  };
+  fetch(0);
   float M = kNegBig;
-  for (int s2 = 0; s2 < ns; ++s2) {
-    const size_t pidx = ((size_t)g * items + first + s2) * 4 + tile;
-    M = fmaxf(M, part_ml[(pidx * 32 + rr) * 2]);
-  }
+#pragma unroll
+  for (int s2 = 0; s2 < kMergeMaxSplits; ++s2)
+    if (s2 < ns) M = fmaxf(M, ml[s2].x);
   float acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = 0.f;
   float L = 0.f;
-  for (int s2 = 0; s2 < ns; ++s2) {
-    const size_t pidx = ((size_t)g * items + first + s2) * 4 + tile;
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (pidx * 32 + rr) * 2);
-    const float w = ml.y * exp2f(ml.x - M);
-    L += w;
-    const uint16_t* po = part_o + (pidx * 32 + rr) * kD + d0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(po + c * 8);
-      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int s0 = 0; s0 < kMergeMaxSplits; s0 += kMergeBatch) {
+    if (s0 >= ns) break;
+    if (s0 > 0) fetch(s0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[c * 8 + 2 * e] += w * bf2f((uint16_t)(wv[e] & 0xffffu));
-        acc[c * 8 + 2 * e + 1] += w * bf2f((uint16_t)(wv[e] >> 16));
+    for (int b = 0; b < kMergeBatch; ++b) {
+      if (s0 + b >= ns) break;
+      const float w = ml[s0 + b].y * exp2f(ml[s0 + b].x - M);
+      L += w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t wv[4] = {raw[b][c].x, raw[b][c].y, raw[b][c].z, raw[b][c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[c * 8 + 2 * e] += w * bf2f((uint16_t)(wv[e] & 0xffffu));
+          acc[c * 8 + 2 * e + 1] += w * bf2f((uint16_t)(wv[e] >> 16));
+        }
       }
     }
   }
@@ -535,6 +564,7 @@ hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const u
                                    int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, void* ws, hipStream_t s) {
   const int sb = prefix_attn_split(T, device_cus());
   const int items = prefix_attn_items(T, sb);
+  if (((T + kPaKB - 1) / kPaKB + sb - 1) / sb > kMergeMaxSplits) return hipErrorInvalidValue;  // beyond the merge
   const int Tp = (T + kPaKB - 1) / kPaKB * kPaKB;
   unsigned char* w = static_cast<unsigned char*>(ws);
   uint16_t* vt = reinterpret_cast<uint16_t*>(w);
