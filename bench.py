@@ -433,6 +433,11 @@ def stack_c3(dmx, reps=3):
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def progress(msg):
+    """A line per finished phase, on stderr (stdout carries only the result)."""
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -476,6 +481,7 @@ def main():
     st.capture(stream)
     ms_step = time_replays(st, stream, args.warmup, args.steps)
     assert torch.isfinite(x.float()).all(), "non-finite activations"
+    progress(f"headline step timed: {ms_step:.4f} ms")
 
     # Reported beside the headline, never as it: the same step with the
     # modulation vectors read from a table filled once per timestep schedule,
@@ -556,6 +562,7 @@ def main():
         assert torch.isfinite(x.float()).all(), "non-finite activations"
         x.copy_(dev(rq.x[None]))
         torch.cuda.synchronize()
+        progress("variants timed")
 
     step_bytes = L * algorithmic_bytes_per_layer(B, C, P, visible)
     step_flops = L * layer_flops(B, C, visible)
@@ -597,14 +604,18 @@ def main():
             "note": "the next layer's two modulation GEMVs on the CUs the attention leaves idle: what they add to "
                     "the attention launch"}
         torch.cuda.synchronize()
+        progress("per-kernel timings done")
     extras = {}
     if args.extras:
         for name in ("c1", "c2", "c4", "c5"):
             extras[f"layer_{name}"] = layer_case(name)
+            progress(f"layer {name} timed")
         extras["prefix_qkv_c4"] = prefix_qkv_case()
         extras["prefix_layer_2048"] = prefix_layer_case()
+        progress("prefix workloads timed")
         extras["stack_c3"] = stack_c3(dmx)
         torch.cuda.synchronize()
+        progress("c3 stack timed")
     copy_gbs = copy_bandwidth()
     # a plain 256 MiB device copy, the run's last: the reference dispatch for
     # HBM byte counters
