@@ -52,20 +52,22 @@ def gate(name, got, ref, rel=ERR_REL_RMS, min_cos=MIN_COS):
     return err / max(rms, 1e-300), cos
 
 
-def stage_gate(name, got, ref, rel=ERR_REL_RMS, min_cos=MIN_COS):
+def stage_gate(name, got, ref, rel=ERR_REL_RMS, min_cos=MIN_COS, roundings=1):
     """Gate for a single stage whose output is stored as bf16: the layer gate
     plus one bf16 rounding of the output, element by element:
-    |err_i| <= rel * RMS(ref) + 2^-8 * |ref_i|, and cosine >= min_cos."""
+    |err_i| <= rel * RMS(ref) + roundings * 2^-8 * |ref_i|, and cosine >=
+    min_cos.  roundings > 1 where the path stores the value in bf16 that many
+    times on its way out (a split partial, then the merged output)."""
     got = np.asarray(got, dtype=np.float64).ravel()
     ref = np.asarray(ref, dtype=np.float64).ravel()
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{name}: non-finite output"
     rms = float(np.sqrt(np.mean(ref * ref)))
     err = np.abs(got - ref)
-    excess = float(np.max(err - 2.0 ** -8 * np.abs(ref)))
+    excess = float(np.max(err - roundings * 2.0 ** -8 * np.abs(ref)))
     cos = float(got @ ref / (np.linalg.norm(got) * np.linalg.norm(ref) + 1e-300))
     msg = (f"{name}: max|err|={float(err.max()):.3e} rms={rms:.3e} "
-           f"max(|err|-2^-8|ref|)/rms={excess / max(rms, 1e-300):.3e} cos={cos:.7f}")
+           f"max(|err|-{roundings}*2^-8|ref|)/rms={excess / max(rms, 1e-300):.3e} cos={cos:.7f}")
     print(msg, flush=True)
     assert excess <= rel * rms, msg
     assert cos >= min_cos, msg
