@@ -477,7 +477,6 @@ template <int MT>
 __global__ __launch_bounds__(kThreads) void k_step(const StepArgs a) {
   __shared__ StepSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lq = lane >> 4;
   const bool cw = tid < kCompute;
   const int w = blockIdx.x, x = w & 7, j = w >> 3, g = x >> 1;
   const int C = a.C, L = a.n_layers;
