@@ -560,9 +560,21 @@ static int prefix_attn_split(int T, int cus) {
   return best;
 }
 
+// prefix_attn_split, remembered per token count (the entry holds the CU
+// count it was computed for; concurrent callers can only store equal values)
+static int prefix_attn_split_cached(int T, int cus) {
+  static int cache[4097];
+  if (T < 1 || T > 4096 || cus >= (1 << 22)) return prefix_attn_split(T, cus);
+  const int e = cache[T];
+  if (e != 0 && (e >> 8) == cus) return e & 255;
+  const int sb = prefix_attn_split(T, cus);
+  cache[T] = (cus << 8) | sb;
+  return sb;
+}
+
 hipError_t launch_prefix_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint8_t* valid,
                                    int T, int kv_rows, uint16_t* ctx, bool ctx_tiled, void* ws, hipStream_t s) {
-  const int sb = prefix_attn_split(T, device_cus());
+  const int sb = prefix_attn_split_cached(T, device_cus());
   const int items = prefix_attn_items(T, sb);
   if (((T + kPaKB - 1) / kPaKB + sb - 1) / sb > kMergeMaxSplits) return hipErrorInvalidValue;  // beyond the merge
   const int Tp = (T + kPaKB - 1) / kPaKB * kPaKB;
