@@ -403,6 +403,28 @@ def test_layer_largest_shapes():
     assert torch.equal(out[15], single[0])
 
 
+def test_layer_maximum_shapes():
+    """The library's limits at once: 64 requests of 64 tokens at the 4096
+    bucket (4096 rows through the large-M projections, 66 splits per request
+    and KV head in the attention), valid lengths 3800..4096 with holes (16
+    seeded requests, each in four batch slots, to keep the host draws short);
+    requests 0, 40 and 63 against the oracle, and request 63 bit-equal to
+    its single-request run."""
+    B, C, P = 64, 64, 4096
+    wbits = synth.layer_weights(synth.BASE_SEED + 7900)
+    base = [synth.make_request(synth.BASE_SEED + 8000 + b, C, P, 3800, P, 1, 0.05) for b in range(16)]
+    reqs = [base[b % 16] for b in range(B)]
+    wd = device_weights(wbits)
+    out = run_layer(wbits, reqs, wd)
+    ow = oracle_weights(wbits)
+    for b in (0, 40, 63):
+        rq = reqs[b]
+        ref = orc.layer(f64(rq.x), f64(rq.cond), ow, f64(rq.k_pre[0]), f64(rq.v_pre[0]), rq.mask, rq.pos0)
+        gate(f"B={B} C={C} P_b={P} layer[b={b}]", from_dev(out[b]), ref)
+    single = run_layer(wbits, [reqs[63]], wd)
+    assert torch.equal(out[63], single[0])
+
+
 def test_layer_masked_rows_never_read():
     wl, wbits, reqs = layer_case("c4")
     wd = device_weights(wbits)
